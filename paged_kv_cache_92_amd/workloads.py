@@ -1,0 +1,336 @@
+"""Seeded synthetic workloads for the paged KV-cache hot path.
+
+This module only draws inputs: context lengths, a shuffled free list, query /
+key / value values, and the block tables and slot mappings that the block
+manager hands out for them.  It computes no attention.  Both the GPU path and
+the CPU oracle consume its output.
+
+Recipe (shared by every workload):
+
+* ``numpy.random.default_rng(seed)``; draw order lengths -> pool permutation
+  -> Q -> K -> V.
+* Values are N(0, 1) fp32, rounded once to the cache dtype with
+  round-to-nearest-even (fp16 through numpy, bf16 by the usual bit rounding).
+* The pool holds ceil(1.1 x blocks needed) blocks unless a workload fixes its
+  size; the free list is a seeded permutation of the pool, so a sequence's
+  blocks are scattered.
+* Every pool slot starts as a NaN bit pattern: slots the scatter does not
+  write must come through bit-identical, and unfilled slots of a last block
+  must never reach an output.
+* Block-table entries past a sequence's last block point at a pool block no
+  sequence holds (still NaN-filled), so a kernel that read past a sequence's
+  blocks would produce NaN rather than fault.
+
+The arrays carry raw bits: float32 for fp32, uint16 for fp16/bf16.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from .block_manager import BlockManager
+
+F32, F16, BF16 = 0, 1, 2
+DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
+_NAN_BITS = {F32: np.float32(np.nan), F16: np.uint16(0x7E00), BF16: np.uint16(0x7FC0)}
+
+
+def round_to(x: np.ndarray, dtype: int) -> np.ndarray:
+    """fp32 values -> raw bits of the cache dtype (round to nearest even)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == F32:
+        return x
+    if dtype == F16:
+        return x.astype(np.float16).view(np.uint16)
+    u = x.view(np.uint32)
+    lsb = (u >> 16) & 1
+    return ((u + np.uint32(0x7FFF) + lsb) >> 16).astype(np.uint16)
+
+
+def storage_dtype(dtype: int):
+    return np.float32 if dtype == F32 else np.uint16
+
+
+@dataclass
+class Op:
+    """One setup or step operation on the cache: a scatter or a block copy."""
+    kind: str                     # "scatter" or "copy"
+    key: np.ndarray | None = None
+    value: np.ndarray | None = None
+    slots: np.ndarray | None = None
+    pairs: np.ndarray | None = None
+
+
+@dataclass
+class Workload:
+    name: str
+    mode: str                     # "decode" or "prefill"
+    dtype: int
+    num_blocks: int
+    num_kv_heads: int
+    num_q_heads: int
+    head_dim: int
+    block_size: int
+    context_lens: np.ndarray      # int32 [S]
+    block_tables: np.ndarray      # int32 [S][max_blocks]
+    q: np.ndarray                 # [S][Hq][d] (decode) or [Tq][Hq][d] (prefill)
+    scale: float                  # fp32 1/sqrt(d)
+    setup: list = field(default_factory=list)   # Ops that fill the history
+    step_scatter: Op | None = None              # the step's new-token scatter
+    query_start_loc: np.ndarray | None = None   # int32 [S+1] (prefill)
+    seq_tokens_key: list = field(default_factory=list)    # per sequence [L][Hkv][d]
+    seq_tokens_value: list = field(default_factory=list)
+    partition_size: int = 0
+    max_context_len: int = 0
+    info: dict = field(default_factory=dict)
+
+    @property
+    def S(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    def empty_pools(self):
+        nb, H, B, d = self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim
+        st = storage_dtype(self.dtype)
+        k = np.full((nb, H, B, d), _NAN_BITS[self.dtype], dtype=st)
+        v = np.full((nb, H, d, B), _NAN_BITS[self.dtype], dtype=st)
+        return k, v
+
+    def kv_bytes(self) -> int:
+        """Bytes of live cached K and V that one attention pass reads once per KV head."""
+        elt = 4 if self.dtype == F32 else 2
+        return int(self.context_lens.astype(np.int64).sum()) * 2 * self.num_kv_heads * self.head_dim * elt
+
+
+def _scale(d: int) -> float:
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def _draw_values(rng, shape, dtype):
+    return round_to(rng.standard_normal(shape, dtype=np.float32), dtype)
+
+
+def _poison_block(bm: BlockManager) -> int:
+    held = set()
+    for sid in list(bm._seqs):
+        held.update(bm.seq(sid).block_table)
+    for b in range(bm.num_blocks - 1, -1, -1):
+        if b not in held:
+            return b
+    raise ValueError("pool has no unused block for table padding")
+
+
+def make_decode(name, seed, context_lens_fn, Hq, Hkv, d, B, dtype, max_context_len,
+                num_blocks=None, pool_factor=1.1, partition_size=0):
+    """Decode workload: every sequence holds ctx[s]-1 history tokens and appends one.
+
+    ``context_lens_fn(rng)`` draws the context lengths (post-append, so they
+    include the new token).  The step scatters the S new tokens, then attends.
+    """
+    rng = np.random.default_rng(seed)
+    ctx = np.asarray(context_lens_fn(rng), dtype=np.int32)
+    S = ctx.shape[0]
+    if (ctx < 1).any() or (ctx > max_context_len).any():
+        raise ValueError("context lengths must lie in [1, max_context_len]")
+    need = int(sum(-(-int(L) // B) for L in ctx))
+    nb = int(num_blocks) if num_blocks is not None else int(math.ceil(pool_factor * need))
+    if nb <= need:
+        raise ValueError("pool must hold at least one block more than the workload needs")
+    perm = rng.permutation(nb)
+    bm = BlockManager(nb, B, free_order=perm)
+    q = _draw_values(rng, (S, Hq, d), dtype)
+    total = int(ctx.astype(np.int64).sum())
+    keys = _draw_values(rng, (total, Hkv, d), dtype)
+    values = _draw_values(rng, (total, Hkv, d), dtype)
+    cu = np.concatenate([[0], np.cumsum(ctx.astype(np.int64))])
+    sids, hist_idx, hist_slots, new_slots = [], [], [], []
+    for s in range(S):
+        sid = bm.new_sequence()
+        sids.append(sid)
+        slots, copies = bm.append_tokens(sid, int(ctx[s]))
+        assert not copies
+        hist_idx.append(np.arange(cu[s], cu[s + 1] - 1))
+        hist_slots.append(slots[:-1])
+        new_slots.append(slots[-1])
+    hist_idx = np.concatenate(hist_idx)
+    new_idx = cu[1:] - 1
+    mbps = -(-max_context_len // B)
+    bt = bm.block_table_array(sids, mbps, pad=_poison_block(bm))
+    wl = Workload(name=name, mode="decode", dtype=dtype, num_blocks=nb, num_kv_heads=Hkv,
+                  num_q_heads=Hq, head_dim=d, block_size=B, context_lens=ctx, block_tables=bt,
+                  q=q, scale=_scale(d), partition_size=partition_size,
+                  max_context_len=int(max_context_len))
+    wl.setup.append(Op("scatter", key=np.ascontiguousarray(keys[hist_idx]),
+                       value=np.ascontiguousarray(values[hist_idx]),
+                       slots=np.concatenate(hist_slots).astype(np.int64)))
+    wl.step_scatter = Op("scatter", key=np.ascontiguousarray(keys[new_idx]),
+                         value=np.ascontiguousarray(values[new_idx]),
+                         slots=np.asarray(new_slots, dtype=np.int64))
+    wl.seq_tokens_key = [keys[cu[s]:cu[s + 1]] for s in range(S)]
+    wl.seq_tokens_value = [values[cu[s]:cu[s + 1]] for s in range(S)]
+    wl.info = {"blocks_needed": need, "tokens": total, "wasted_slots": bm.wasted_slots()}
+    return wl
+
+
+def make_prefill(name, seed, S, chunk, hist_fn, shared_prefix, Hq, Hkv, d, B, dtype,
+                 max_context_len, pool_factor=1.1, pair_sharing=True):
+    """Chunked-prefill workload over a paged cache with shared prefixes.
+
+    Sequences come in pairs (0,1), (2,3), ...; the first ``shared_prefix``
+    tokens of a pair are one draw held in the same physical blocks (reference
+    count 2).  Setup writes the shared prefixes, forks the partner, appends the
+    partner's own history (copy-on-write if the prefix ends inside a block),
+    then the first member's own history.  The step scatters every sequence's
+    ``chunk`` new tokens and runs the causal prefill for those rows.
+    """
+    rng = np.random.default_rng(seed)
+    hist = np.asarray(hist_fn(rng), dtype=np.int64)
+    assert hist.shape == (S,)
+    ctx = (hist + chunk).astype(np.int32)
+    if (ctx > max_context_len).any():
+        raise ValueError("history + chunk exceeds max_context_len")
+    if pair_sharing:
+        assert S % 2 == 0 and (hist >= shared_prefix).all()
+    # Blocks needed: unique blocks plus copy-on-write copies.
+    need = 0
+    for s in range(S):
+        own = -(-int(ctx[s]) // B)
+        if pair_sharing and s % 2 == 1:
+            own -= shared_prefix // B          # full shared blocks are not duplicated
+        need += own
+    nb = int(math.ceil(pool_factor * need)) + 1
+    perm = rng.permutation(nb)
+    bm = BlockManager(nb, B, free_order=perm)
+    Tq = S * chunk
+    q = _draw_values(rng, (Tq, Hq, d), dtype)
+    # One K/V draw per distinct token: a pair's partner reuses the shared prefix.
+    uniq = int(ctx.astype(np.int64).sum()) - (shared_prefix * (S // 2) if pair_sharing else 0)
+    kall = _draw_values(rng, (uniq, Hkv, d), dtype)
+    vall = _draw_values(rng, (uniq, Hkv, d), dtype)
+    seq_k, seq_v, cursor = [], [], 0
+    for s in range(S):
+        L = int(ctx[s])
+        if pair_sharing and s % 2 == 1:
+            own = L - shared_prefix
+            k = np.concatenate([seq_k[s - 1][:shared_prefix], kall[cursor:cursor + own]])
+            v = np.concatenate([seq_v[s - 1][:shared_prefix], vall[cursor:cursor + own]])
+            cursor += own
+        else:
+            k, v = kall[cursor:cursor + L], vall[cursor:cursor + L]
+            cursor += L
+        seq_k.append(k)
+        seq_v.append(v)
+    assert cursor == uniq
+
+    sids = [bm.new_sequence() if not (pair_sharing and s % 2 == 1) else None for s in range(S)]
+    phase1_k, phase1_v, phase1_s = [], [], []
+    phase2_k, phase2_v, phase2_s = [], [], []
+    copies_all = []
+    hist_done = [0] * S
+    for s in range(0, S, 2 if pair_sharing else 1):
+        if pair_sharing:
+            a = s
+            slots, cp = bm.append_tokens(sids[a], shared_prefix)
+            assert not cp
+            phase1_k.append(seq_k[a][:shared_prefix]); phase1_v.append(seq_v[a][:shared_prefix])
+            phase1_s.append(slots)
+            sids[a + 1] = bm.fork(sids[a])
+            hist_done[a] = hist_done[a + 1] = shared_prefix
+            for m in (a + 1, a):            # the partner diverges first
+                n = int(hist[m]) - shared_prefix
+                slots, cp = bm.append_tokens(sids[m], n)
+                copies_all.extend(cp)
+                phase2_k.append(seq_k[m][shared_prefix:hist[m]])
+                phase2_v.append(seq_v[m][shared_prefix:hist[m]])
+                phase2_s.append(slots)
+                hist_done[m] = int(hist[m])
+        else:
+            slots, cp = bm.append_tokens(sids[s], int(hist[s]))
+            phase1_k.append(seq_k[s][:hist[s]]); phase1_v.append(seq_v[s][:hist[s]])
+            phase1_s.append(slots)
+            hist_done[s] = int(hist[s])
+    step_k, step_v, step_s = [], [], []
+    for s in range(S):
+        slots, cp = bm.append_tokens(sids[s], chunk)
+        assert not cp, "chunk tokens land in private blocks"
+        step_k.append(seq_k[s][hist[s]:]); step_v.append(seq_v[s][hist[s]:])
+        step_s.append(slots)
+
+    def cat(xs, shape_tail):
+        xs = [x for x in xs if len(x)]
+        if not xs:
+            return np.zeros((0,) + shape_tail, dtype=storage_dtype(dtype))
+        return np.ascontiguousarray(np.concatenate(xs))
+
+    tail = (Hkv, d)
+    mbps = -(-max_context_len // B)
+    bt = bm.block_table_array(sids, mbps, pad=_poison_block(bm))
+    qsl = np.arange(0, Tq + 1, chunk, dtype=np.int32)
+    wl = Workload(name=name, mode="prefill", dtype=dtype, num_blocks=nb, num_kv_heads=Hkv,
+                  num_q_heads=Hq, head_dim=d, block_size=B, context_lens=ctx, block_tables=bt,
+                  q=q, scale=_scale(d), query_start_loc=qsl, max_context_len=int(max_context_len))
+    wl.setup.append(Op("scatter", key=cat(phase1_k, tail), value=cat(phase1_v, tail),
+                       slots=np.concatenate(phase1_s).astype(np.int64)))
+    if copies_all:
+        wl.setup.append(Op("copy", pairs=np.asarray(copies_all, dtype=np.int32).reshape(-1, 2)))
+    if phase2_s:
+        wl.setup.append(Op("scatter", key=cat(phase2_k, tail), value=cat(phase2_v, tail),
+                           slots=np.concatenate(phase2_s).astype(np.int64)))
+    wl.step_scatter = Op("scatter", key=cat(step_k, tail), value=cat(step_v, tail),
+                         slots=np.concatenate(step_s).astype(np.int64))
+    wl.seq_tokens_key = seq_k
+    wl.seq_tokens_value = seq_v
+    wl.info = {"blocks_needed": need, "cow_copies": len(copies_all), "histories": hist.tolist()}
+    return wl
+
+
+# ---------------------------------------------------------------------------
+# The five workloads (sizes as stated for each), plus small variants for tests.
+# ---------------------------------------------------------------------------
+
+def tiny_decode_f32():
+    """4 sequences, contexts {6,17,33,64}, 8 heads, d 64, B 16, 32-block pool, fp32."""
+    return make_decode("tiny_decode_f32", 1, lambda rng: [6, 17, 33, 64], Hq=8, Hkv=8, d=64, B=16,
+                       dtype=F32, max_context_len=64, num_blocks=32)
+
+
+def llama13b_decode_f16(S=64, lo=128, hi=2048, seed=2, partition_size=0):
+    """LLaMA-2-13B-shaped single-layer decode: 40 heads, d 128, B 16, fp16, L ~ U[lo, hi]."""
+    return make_decode(f"llama13b_decode_f16_S{S}", seed,
+                       lambda rng: rng.integers(lo, hi + 1, size=S), Hq=40, Hkv=40, d=128, B=16,
+                       dtype=F16, max_context_len=hi, partition_size=partition_size)
+
+
+def long_context_split_f16(S=16, lo=2048, hi=4096, seed=3, partition_size=512):
+    """Long-context decode with 512-token split-KV partitions: 40 heads, d 128, B 16, fp16."""
+    return make_decode(f"long_split_f16_S{S}", seed, lambda rng: rng.integers(lo, hi + 1, size=S),
+                       Hq=40, Hkv=40, d=128, B=16, dtype=F16, max_context_len=4096,
+                       partition_size=partition_size)
+
+
+def lognormal_lengths(S, median=1024, sigma=1.0, lo=16, hi=8192):
+    def draw(rng):
+        x = rng.lognormal(mean=math.log(median), sigma=sigma, size=S)
+        return np.clip(np.rint(x), lo, hi).astype(np.int64)
+    return draw
+
+
+def gqa_decode_bf16(B=16, S=256, seed=4, max_context_len=8192, lengths=None, partition_size=512):
+    """GQA decode: 32 query heads over 8 KV heads, d 128, bf16, lognormal(median 1024) lengths."""
+    fn = lengths or lognormal_lengths(S, hi=max_context_len)
+    return make_decode(f"gqa_decode_bf16_B{B}_S{S}", seed, fn, Hq=32, Hkv=8, d=128, B=B,
+                       dtype=BF16, max_context_len=max_context_len, partition_size=partition_size)
+
+
+def chunked_prefill_bf16(S=8, chunk=512, hist_lo=1024, hist_hi=3584, shared_prefix=1024, seed=5,
+                         Hq=32, Hkv=32, max_context_len=4096, hist_fn=None, pair_sharing=True):
+    """Chunked prefill: 512-row chunks over paged histories, pairs sharing their first tokens."""
+    fn = hist_fn or (lambda rng: rng.integers(hist_lo, hist_hi + 1, size=S))
+    return make_prefill(f"chunked_prefill_bf16_S{S}", seed, S, chunk, fn, shared_prefix, Hq=Hq,
+                        Hkv=Hkv, d=128, B=16, dtype=BF16, max_context_len=max_context_len,
+                        pair_sharing=pair_sharing)

@@ -1,0 +1,41 @@
+"""Drive the CPU oracle through a workload (test-side helper)."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+
+def fill_pools(wl, include_step=True):
+    """Oracle pools after the workload's setup ops (and, by default, the step's scatter)."""
+    k, v = wl.empty_pools()
+    ops = list(wl.setup) + ([wl.step_scatter] if include_step and wl.step_scatter else [])
+    for op in ops:
+        if op.kind == "scatter":
+            oracle.reshape_and_cache(k, v, wl.dtype, op.key, op.value, op.slots)
+        else:
+            oracle.copy_blocks(k, v, wl.dtype, op.pairs)
+    return k, v
+
+
+def reference_output(wl, k, v):
+    """fp64 oracle output of the workload's attention step over pools k, v."""
+    if wl.mode == "decode":
+        return oracle.paged_decode(k, v, wl.dtype, wl.q, wl.block_tables, wl.context_lens, wl.scale)
+    return oracle.paged_prefill(k, v, wl.dtype, wl.q, wl.query_start_loc, wl.context_lens,
+                                wl.block_tables, wl.scale)
+
+
+def sampled_rows(wl, k, v, rows):
+    """fp64 oracle output for selected query rows only (all heads)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    if wl.mode == "decode":
+        seq = rows
+        pos = wl.context_lens[rows] - 1
+    else:
+        qsl = wl.query_start_loc
+        seq = np.searchsorted(qsl, rows, side="right") - 1
+        qlen = qsl[seq + 1] - qsl[seq]
+        pos = wl.context_lens[seq] - qlen + (rows - qsl[seq])
+    return oracle.paged_attention_rows(k, v, wl.dtype, wl.q[rows], wl.block_tables, wl.context_lens,
+                                       seq, pos, wl.scale)
