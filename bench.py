@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache hot path on one MI355X.
+
+Default workload: LLaMA-2-13B-shaped single-layer decode (64 sequences,
+contexts U[128, 2048], 40 heads, head_dim 128, block_size 16, fp16 KV, pool
+1.1x the need with shuffled blocks).  One step = the reshape_and_cache
+scatter of the 64 new tokens + paged decode attention over every sequence's
+whole cache (+ the split-KV reduce when partitioned).  Inputs are resident
+in HBM before timing; two identical pool copies alternate between steps so
+the 256 MiB Infinity Cache cannot serve a step from the previous one.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}   # dense
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def make_workload(name, partition):
+    from paged_kv_cache_92_amd import workloads as W
+    if name == "llama13b":
+        wl = W.llama13b_decode_f16()
+        desc = "llama2-13b-shaped single-layer paged decode, fp16 KV"
+    elif name == "long_split":
+        wl = W.long_context_split_f16()
+        desc = "long-context split-KV paged decode, fp16 KV"
+    elif name in ("gqa16", "gqa32"):
+        wl = W.gqa_decode_bf16(B=16 if name == "gqa16" else 32)
+        desc = f"GQA 32q/8kv paged decode, bf16 KV, block {wl.block_size}"
+    elif name == "prefill":
+        wl = W.chunked_prefill_bf16()
+        desc = "chunked causal prefill over paged cache with shared prefixes, bf16"
+    elif name == "tiny":
+        wl = W.tiny_decode_f32()
+        desc = "tiny paged decode, fp32"
+    else:
+        raise SystemExit(f"unknown config {name}")
+    if partition is not None and wl.mode == "decode":
+        wl.partition_size = partition
+    return wl, desc
+
+
+def attention_flops(wl):
+    import numpy as np
+    d, Hq = wl.head_dim, wl.num_q_heads
+    if wl.mode == "decode":
+        return float(wl.context_lens.astype(np.int64).sum()) * Hq * d * 4
+    qsl = wl.query_start_loc
+    total = 0
+    for s in range(wl.S):
+        ql = int(qsl[s + 1] - qsl[s])
+        h = int(wl.context_lens[s]) - ql
+        # rows at positions h .. h+ql-1 attend to p+1 keys each
+        total += ql * (h + 1) + ql * (ql - 1) // 2
+    return float(total) * Hq * d * 4
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle as it stands, single-threaded, on a bounded sample of the same input."""
+    import numpy as np
+
+    import oracle
+    k, v = wl.empty_pools()
+    for op in wl.setup + [wl.step_scatter]:
+        if op.kind == "scatter":
+            oracle.reshape_and_cache(k, v, wl.dtype, op.key, op.value, op.slots)
+        else:
+            oracle.copy_blocks(k, v, wl.dtype, op.pairs)
+    elt = 4 if wl.dtype == 0 else 2
+    t0 = time.perf_counter()
+    n = 0
+    kv_bytes = 0
+    if wl.mode == "decode":
+        while n < wl.S and (time.perf_counter() - t0) < budget_s:
+            oracle.paged_attention_rows(k, v, wl.dtype, wl.q[n:n + 1], wl.block_tables,
+                                        wl.context_lens, [n], [int(wl.context_lens[n]) - 1], wl.scale)
+            kv_bytes += int(wl.context_lens[n]) * 2 * wl.num_kv_heads * wl.head_dim * elt
+            n += 1
+        el = time.perf_counter() - t0
+        return {"value": round(kv_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "tokens_per_s": round(n / el, 3),
+                "sample": f"decode of the first {n} of {wl.S} sequences (all {wl.num_q_heads} heads): "
+                          f"block-table reassembly + fp64 softmax attention, {el:.1f} s wall, 1 thread"}
+    qsl = wl.query_start_loc
+    flops = 0.0
+    rows = []
+    while n < qsl[-1] and (time.perf_counter() - t0) < budget_s:
+        s = int(np.searchsorted(qsl, n, side="right") - 1)
+        pos = int(wl.context_lens[s] - (qsl[s + 1] - qsl[s]) + (n - qsl[s]))
+        oracle.paged_attention_rows(k, v, wl.dtype, wl.q[n:n + 1], wl.block_tables, wl.context_lens,
+                                    [s], [pos], wl.scale)
+        flops += (pos + 1) * wl.num_q_heads * wl.head_dim * 4
+        rows.append(n)
+        n += 1
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} query rows of {int(qsl[-1])} (all {wl.num_q_heads} heads), "
+                      f"{el:.1f} s wall, 1 thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="llama13b",
+                    choices=["llama13b", "long_split", "gqa16", "gqa32", "prefill", "tiny"])
+    ap.add_argument("--partition", type=int, default=None,
+                    help="split-KV partition size in tokens (default: the workload's)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_92_amd as pkv
+    from paged_kv_cache_92_amd.runner import DeviceWorkload, new_cache
+
+    pkv.lib()
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    wl, desc = make_workload(args.config, args.partition)
+    log(f"[bench] generated {wl.name} in {time.time() - t0:.1f}s "
+        f"(pool {wl.num_blocks} blocks, KV {wl.kv_bytes() / 1e9:.3f} GB)")
+
+    # Two identical device copies of the cache; steps alternate between them.
+    copies = []
+    for i in range(2):
+        dw = DeviceWorkload(wl)
+        cache = new_cache(wl)
+        dw.fill(cache)
+        copies.append((dw, cache))
+    torch.cuda.synchronize()
+    log(f"[bench] uploaded and filled 2 x {copies[0][1].nbytes() / 1e9:.2f} GB pools")
+
+    dw0 = copies[0][0]
+    out = torch.empty_like(dw0.q)
+    ws = None
+    if wl.mode == "decode":
+        need = pkv.decode_workspace_bytes(wl.S, wl.num_q_heads, wl.head_dim, wl.max_context_len,
+                                          wl.partition_size)
+        if need:
+            ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def step(i, ev=None):
+        dw, cache = copies[i % 2]
+        dw.apply(cache, dw.step)
+        if ev is not None:
+            ev[0].record()
+        dw.attend(cache, out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_avg = float(np.mean(attn_ms))
+    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step, attention "
+        f"{attn_avg * 1e3:.1f} us avg (median {np.median(attn_ms) * 1e3:.1f}, "
+        f"min {np.min(attn_ms) * 1e3:.1f})")
+
+    dt = {0: "f32", 1: "f16", 2: "bf16"}[wl.dtype]
+    kv = wl.kv_bytes()
+    flops = attention_flops(wl)
+    res = {
+        "metric": "paged decode effective KV GB/s (% of HBM peak) + decode tokens/s, 13B shape",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dt, "data": "synthetic",
+    }
+    if wl.mode == "decode":
+        gbs_step = kv / (ms_step * 1e-3) / 1e9
+        gbs_attn = kv / (attn_avg * 1e-3) / 1e9
+        res.update({
+            "value": round(gbs_step, 2), "unit": "GB/s",
+            "pct_hbm_peak": round(100 * gbs_step / HBM_PEAK_GBS, 2),
+            "decode_tokens_per_s": round(wl.S / (ms_step * 1e-3), 1),
+            "decode_tokens_per_s_40_layer_attention_only": round(wl.S / (40 * ms_step * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs_attn, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs_attn / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "paged decode (partial + reduce when split)",
+                         "algorithmic_bytes_per_launch": kv,
+                         "avg_launch_us": round(attn_avg * 1e3, 2)},
+        })
+    else:
+        tf_step = flops / (ms_step * 1e-3) / 1e12
+        tf_attn = flops / (attn_avg * 1e-3) / 1e12
+        res.update({
+            "value": round(tf_step, 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(tf_attn, 2), "peak": MFMA_PEAK_TFLOPS[dt],
+                         "unit": "TFLOP/s", "frac": round(tf_attn / MFMA_PEAK_TFLOPS[dt], 4),
+                         "traffic": None, "kernel": "paged prefill",
+                         "algorithmic_flops_per_launch": flops,
+                         "avg_launch_us": round(attn_avg * 1e3, 2)},
+        })
+        res["metric"] = "chunked prefill attention TFLOP/s (% of MFMA peak)"
+    res["config"] = {"workload": desc, "seqs": wl.S, "q_heads": wl.num_q_heads,
+                     "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+                     "block_size": wl.block_size, "pool_blocks": wl.num_blocks,
+                     "total_context_tokens": int(wl.context_lens.sum()),
+                     "partition_size": wl.partition_size if wl.mode == "decode" else None,
+                     "kv_bytes": kv, "attention_flops": flops}
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,220 @@
+/*
+ * pkv — paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpkv.so.  Every pointer argument is device memory owned by the
+ * caller unless a comment says "host"; the library allocates nothing, frees
+ * nothing and keeps no handles between calls.  Every call validates its
+ * scalar arguments on the host, returns a status code (nothing is thrown
+ * across the ABI), and on PKV_OK has queued its kernels asynchronously on
+ * `stream`.  On any other status nothing was launched and pkv_last_error()
+ * describes the problem.
+ *
+ * Pages cited (titles as published):
+ *   [T] "'안녕하세요 반갑습니다'로 배우는 vLLM — KV Cache와 PagedAttention 완전 해부"
+ *       (hrletsgo.me)
+ *   [W] "[vLLM] PagedAttention: OS 페이징 기법으로 KV 캐시를 관리하는 방법"
+ *       (blog.secrett2633.cloud)
+ *   [R] "vLLM: LLM 서빙 메모리 최적화의 교과서" (velog.io/@doogunwo)
+ *   [S] "Sparse Computation and Memory Management for Efficient LLM Inference"
+ *       (pyy0715.github.io)
+ *
+ * ----------------------------------------------------------------------------
+ * The block pool ([T] step 5; [R] section "02. Idea: PagedAttention"; [S]
+ * section "PagedAttention: Borrowing from Operating Systems"): device memory
+ * cut into fixed-size blocks of `block_size` token slots.  A request's block
+ * table maps its logical block i to any physical block; a token's slot is
+ *
+ *     slot = physical_block * block_size + offset_in_block.
+ *
+ * Layout in HBM (this library's choice; the pages fix only "blocks of B
+ * tokens"):
+ *
+ *   k_pool  [num_blocks][num_kv_heads][block_size][head_dim]
+ *           a (block, head) key tile is B x d, token-major, contiguous;
+ *   v_pool  [num_blocks][num_kv_heads][head_dim][block_size]
+ *           a (block, head) value tile is d x B, dimension-major, contiguous,
+ *           so the B tokens of one value dimension are adjacent: the operand
+ *           shape that the P.V matrix-core products read directly.
+ *
+ * q, out, key and value rows are [tokens][heads][head_dim], contiguous.
+ * Query/output and cache share one dtype.  Supported: dtype f32/f16/bf16,
+ * head_dim 64 or 128, block_size 16 or 32.  Base pointers must be 16-byte
+ * aligned.
+ *
+ * Device-side contract (not checked on the device; pkv_validate_host checks
+ * it on host copies): block ids in the first ceil(L/B) table entries of a
+ * sequence lie in [0, num_blocks); 1 <= L <= max_blocks_per_seq * block_size;
+ * L <= max_context_len; no two tokens of one scatter share a slot.  The
+ * kernels never touch memory outside the pool for a block id out of range
+ * (that block is skipped) and clamp lengths to the table, so a broken
+ * contract gives wrong numbers, not a fault.
+ * ----------------------------------------------------------------------------
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = 1,     /* null pointer, bad size, misalignment, Hq % Hkv != 0, ... */
+  PKV_ERR_UNSUPPORTED = 2, /* a valid request this build has no kernel for */
+  PKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  PKV_ERR_HIP = 4          /* a HIP launch error (message from the runtime) */
+} pkv_status;
+
+/* Describes caller-owned device memory of one layer's cache. */
+typedef struct {
+  void *k_pool;          /* [num_blocks][num_kv_heads][block_size][head_dim] */
+  void *v_pool;          /* [num_blocks][num_kv_heads][head_dim][block_size] */
+  int64_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t block_size;    /* 16 or 32 */
+  int32_t head_dim;      /* 64 or 128 */
+  int32_t dtype;         /* pkv_dtype */
+} pkv_cache;
+
+/*
+ * Slot scatter, "reshape_and_cache".  [W] section "PagedAttention 커널:
+ * 비연속 메모리 접근": write_to_paged_cache passes the new tokens' key and
+ * value and their slot_mapping to reshape_and_cache, which stores each token
+ * in the slot named for it; [T] step 6: decode stores the new token's K/V in
+ * the next free slot of the request's last block.
+ *
+ *   key, value     [num_tokens][num_kv_heads][head_dim], cache dtype
+ *   slot_mapping   int64 [num_tokens]; a negative slot skips that token
+ *                  (padding); slots >= num_blocks * block_size are skipped too
+ *
+ * Bit-exact copy (no conversion).  Duplicate non-negative slots are a caller
+ * error with no defined winner.  num_tokens == 0 is a no-op.
+ */
+pkv_status pkv_reshape_and_cache(const pkv_cache *cache, const void *key, const void *value,
+                                 const int64_t *slot_mapping, int64_t num_tokens,
+                                 hipStream_t stream);
+
+/*
+ * Whole-block copy for copy-on-write.  [S] section "Copy-on-Write": before a
+ * sequence writes into a block whose reference count is above one, the block
+ * is copied to a new physical block (fused_block_copy) and the sequence's
+ * table is repointed; [T] step 9 (shared prompt blocks).  The decision and
+ * the table update are the caller's; this call copies the K and V tiles of
+ * every head for each pair.
+ *
+ *   src_dst  int32 [num_pairs][2] = (src, dst); every dst distinct and not a
+ *            src of any pair (copies are unordered).  Pairs with an id out of
+ *            range are skipped.  num_pairs == 0 is a no-op.
+ */
+pkv_status pkv_copy_blocks(const pkv_cache *cache, const int32_t *src_dst, int64_t num_pairs,
+                           hipStream_t stream);
+
+/*
+ * Workspace bytes pkv_paged_decode needs for these sizes (0 when every
+ * sequence fits one partition, i.e. partition_size == 0 or
+ * partition_size >= max_context_len).  Pure host arithmetic.
+ */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t partition_size);
+
+/*
+ * Paged decode attention: one new query per sequence over its whole cache.
+ * [R] section "01. Problem Definition": o_i = sum_{j<=i} softmax_j(q_i.k_j /
+ * sqrt(d)) v_j; eq. (4) of the same section 02 and [S] section "Block-level
+ * Attention Formulation": the same result computed block by block; [T]
+ * "부록": walk the blocks through the block table, load the keys, compute
+ * partial scores, update a running softmax normaliser, accumulate the
+ * weighted values.  Query head hq reads KV head hq / (Hq / Hkv) (grouped
+ * heads, [S] section "The Hidden Waste of KV Cache").
+ *
+ *   out, q            [num_seqs][num_q_heads][head_dim], cache dtype; out is
+ *                     rounded once (round to nearest even) from fp32
+ *   block_tables      int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens      int32 [num_seqs]; L_s counts every cached token,
+ *                     including the new one (scatter it first); L_s >= 1
+ *   max_context_len   host bound on every L_s (sizes the launch)
+ *   scale             the softmax scale, normally 1/sqrt(head_dim) in fp32
+ *   partition_size    0: one workgroup pass over each whole sequence;
+ *                     otherwise a multiple of block_size: each sequence is
+ *                     split into partitions of that many tokens, each
+ *                     partition writes (running max, denominator, weighted
+ *                     sum) to the workspace and a reduce kernel combines
+ *                     them (block-wise aggregation of partial results, [R]
+ *                     section 02 "Aggregation")
+ *   workspace         device scratch of >= pkv_decode_workspace_bytes(...)
+ *                     bytes, 16-byte aligned; may be NULL when that is 0
+ *
+ * Grouped heads (num_q_heads > num_kv_heads) with f16/bf16 run on the matrix
+ * cores with the group's queries stacked into one tile; other cases run the
+ * wavefront dot-product kernel.  Group size must be <= 16.
+ */
+pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, const void *q, int32_t num_q_heads,
+                            const int32_t *block_tables, int32_t max_blocks_per_seq,
+                            const int32_t *context_lens, int32_t num_seqs,
+                            int32_t max_context_len, float scale, int32_t partition_size,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Causal chunked prefill over the paged cache.  [S] section "Prefill-Decode
+ * Disaggregation": a long prompt is processed in chunks over several steps;
+ * [T] step 6 and [R] section 01: prefill processes all prompt tokens at once
+ * as a matrix-matrix product.  Sequence s owns query rows
+ * query_start_loc[s] .. query_start_loc[s+1]-1, the last qlen_s of its
+ * context_lens[s] cached tokens (scatter the chunk's K/V first): row i sits
+ * at position context_lens[s] - qlen_s + i and attends to positions 0..that
+ * position.  Blocks may be shared between sequences (prefix sharing).
+ *
+ *   out, q            [total_rows][num_q_heads][head_dim], f16 or bf16
+ *   query_start_loc   int32 [num_seqs + 1], non-decreasing, starts at 0
+ *   context_lens      int32 [num_seqs], >= qlen_s, >= 1
+ *   max_query_len     host bound on every qlen_s
+ *   max_context_len   host bound on every context_lens[s]
+ */
+pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, const void *q,
+                             int32_t num_q_heads, const int32_t *query_start_loc,
+                             const int32_t *context_lens, const int32_t *block_tables,
+                             int32_t max_blocks_per_seq, int32_t num_seqs, int32_t max_query_len,
+                             int32_t max_context_len, float scale, hipStream_t stream);
+
+/*
+ * Debug gather with the kernels' own address arithmetic: the contiguous
+ * K and V of every sequence, back to back, token-major.
+ *
+ *   k_out, v_out      [sum_s L_s][num_kv_heads][head_dim], cache dtype
+ *   cu_context_lens   int32 [num_seqs + 1], prefix sums of context_lens
+ */
+pkv_status pkv_gather_kv(const pkv_cache *cache, void *k_out, void *v_out,
+                         const int32_t *block_tables, int32_t max_blocks_per_seq,
+                         const int32_t *context_lens, const int32_t *cu_context_lens,
+                         int32_t num_seqs, int32_t max_context_len, hipStream_t stream);
+
+/*
+ * Host-side check of the device-side contract, on HOST copies of the
+ * integer inputs (any pointer may be NULL with its count 0 to skip that
+ * part): slots in range and unique, every L in [1, max_blocks*B], every
+ * table entry a sequence uses in [0, num_blocks).  Returns PKV_OK or
+ * PKV_ERR_INVALID with pkv_last_error() naming the first violation.
+ */
+pkv_status pkv_validate_host(const int64_t *slot_mapping, int64_t num_tokens,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                             const int32_t *context_lens, int32_t num_seqs, int64_t num_blocks,
+                             int32_t block_size);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *pkv_last_error(void);
+
+/* Library version string. */
+const char *pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

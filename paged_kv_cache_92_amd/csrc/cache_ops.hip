@@ -1,0 +1,164 @@
+// Cache maintenance kernels: slot scatter, copy-on-write block copy, and the
+// debug gather.  All are pure data movement (bit-exact, no conversion).
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+namespace {
+
+// Slot scatter ("reshape_and_cache", [vLLM] PagedAttention, blog.secrett2633.cloud,
+// section "PagedAttention 커널: 비연속 메모리 접근").  One thread moves one
+// 16-byte chunk of one (token, head) row: the key chunk is stored whole into
+// the token-major key tile, the value chunk is split into its elements, each
+// going to its dimension row of the dimension-major value tile.
+template <int EB>
+__global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict__ key,
+                                                      const uint8_t *__restrict__ value,
+                                                      const int64_t *__restrict__ slots,
+                                                      uint8_t *__restrict__ kpool,
+                                                      uint8_t *__restrict__ vpool, int64_t T, int H,
+                                                      int B, int D, int64_t nslots) {
+  constexpr int VEC = 16 / EB;
+  const int chunks = D / VEC;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= T * H * chunks) return;
+  const int c = (int)(idx % chunks);
+  const int64_t th = idx / chunks;
+  const int h = (int)(th % H);
+  const int64_t t = th / H;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= nslots) return;
+  const int64_t blk = slot / B;
+  const int off = (int)(slot - blk * B);
+  const size_t src = ((size_t)(t * H + h) * D + (size_t)c * VEC) * EB;
+  const u32x4 kc = load16(key + src);
+  const u32x4 vc = load16(value + src);
+  *(u32x4 *)(kpool + (((size_t)(blk * H + h) * B + off) * D + (size_t)c * VEC) * EB) = kc;
+  const size_t vrow = ((size_t)(blk * H + h) * D + (size_t)c * VEC) * B + off;  // element index
+  if constexpr (EB == 4) {
+    float *vp = (float *)vpool;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vp[vrow + (size_t)i * B] = __builtin_bit_cast(float, vc[i]);
+  } else {
+    uint16_t *vp = (uint16_t *)vpool;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vp[vrow + (size_t)(2 * i) * B] = (uint16_t)(vc[i] & 0xffffu);
+      vp[vrow + (size_t)(2 * i + 1) * B] = (uint16_t)(vc[i] >> 16);
+    }
+  }
+}
+
+// Copy-on-write block copy ("Sparse Computation and Memory Management...",
+// pyy0715.github.io, section "Copy-on-Write"): both tiles of every head of
+// block src go to block dst.  grid.y walks the pairs, grid.x strides over the
+// 16-byte chunks of one block.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t *__restrict__ kpool,
+                                                          uint8_t *__restrict__ vpool,
+                                                          const int32_t *__restrict__ pairs,
+                                                          int64_t nblocks, int64_t chunks) {
+  const int64_t p = blockIdx.y;
+  const int32_t src = pairs[2 * p], dst = pairs[2 * p + 1];
+  if (src < 0 || src >= nblocks || dst < 0 || dst >= nblocks) return;
+  const size_t tile = (size_t)chunks * 16;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < chunks;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const u32x4 a = load16(kpool + src * tile + i * 16);
+    const u32x4 b = load16(vpool + src * tile + i * 16);
+    *(u32x4 *)(kpool + dst * tile + i * 16) = a;
+    *(u32x4 *)(vpool + dst * tile + i * 16) = b;
+  }
+}
+
+// Debug gather with the attention kernels' address arithmetic: contiguous,
+// token-major K and V of every sequence.  One thread per 16-byte output chunk.
+template <int EB>
+__global__ __launch_bounds__(256) void gather_kernel(const uint8_t *__restrict__ kpool,
+                                                     const uint8_t *__restrict__ vpool,
+                                                     uint8_t *__restrict__ kout,
+                                                     uint8_t *__restrict__ vout,
+                                                     const int32_t *__restrict__ bt, int mbps,
+                                                     const int32_t *__restrict__ ctx,
+                                                     const int32_t *__restrict__ cu, int64_t nblocks,
+                                                     int H, int B, int D, int max_len) {
+  constexpr int VEC = 16 / EB;
+  const int chunks = D / VEC;
+  const int s = blockIdx.y;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)max_len * H * chunks) return;
+  const int c = (int)(idx % chunks);
+  const int h = (int)((idx / chunks) % H);
+  const int j = (int)(idx / ((int64_t)chunks * H));
+  const int L = min(ctx[s], mbps * B);
+  if (j >= L) return;
+  const int32_t blk = bt[(size_t)s * mbps + j / B];
+  if (blk < 0 || blk >= nblocks) return;
+  const int off = j % B;
+  const size_t dst = (((size_t)cu[s] + j) * H + h) * D + (size_t)c * VEC;
+  *(u32x4 *)(kout + dst * EB) = load16(kpool + (((size_t)(blk * (int64_t)H + h) * B + off) * D +
+                                               (size_t)c * VEC) * EB);
+  const size_t vrow = ((size_t)(blk * (int64_t)H + h) * D + (size_t)c * VEC) * B + off;
+  u32x4 packed;
+  if constexpr (EB == 4) {
+    const uint32_t *vp = (const uint32_t *)vpool;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) packed[i] = vp[vrow + (size_t)i * B];
+  } else {
+    const uint16_t *vp = (const uint16_t *)vpool;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      packed[i] = (uint32_t)vp[vrow + (size_t)(2 * i) * B] |
+                  ((uint32_t)vp[vrow + (size_t)(2 * i + 1) * B] << 16);
+  }
+  *(u32x4 *)(vout + dst * EB) = packed;
+}
+
+}  // namespace
+
+hipError_t launch_reshape_and_cache(const CacheDesc &c, const void *key, const void *value,
+                                    const int64_t *slots, int64_t T, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int EB = c.elt_bytes();
+  const int64_t work = T * c.H * (c.D * EB / 16);
+  const dim3 grid((unsigned)((work + 255) / 256));
+  const int64_t nslots = c.num_blocks * c.B;
+  if (EB == 4)
+    hipLaunchKernelGGL(scatter_kernel<4>, grid, dim3(256), 0, stream, (const uint8_t *)key,
+                       (const uint8_t *)value, slots, (uint8_t *)c.k, (uint8_t *)c.v, T, c.H, c.B,
+                       c.D, nslots);
+  else
+    hipLaunchKernelGGL(scatter_kernel<2>, grid, dim3(256), 0, stream, (const uint8_t *)key,
+                       (const uint8_t *)value, slots, (uint8_t *)c.k, (uint8_t *)c.v, T, c.H, c.B,
+                       c.D, nslots);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(const CacheDesc &c, const int32_t *pairs, int64_t n,
+                              hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t chunks = (int64_t)c.H * c.B * c.D * c.elt_bytes() / 16;
+  const int64_t gx = (chunks + 255) / 256;
+  const dim3 grid((unsigned)(gx < 64 ? gx : 64), (unsigned)n);
+  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, stream, (uint8_t *)c.k,
+                     (uint8_t *)c.v, pairs, c.num_blocks, chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_kv(const CacheDesc &c, void *k_out, void *v_out, const int32_t *bt,
+                            int mbps, const int32_t *ctx, const int32_t *cu, int S,
+                            int max_context_len, hipStream_t stream) {
+  const int EB = c.elt_bytes();
+  const int64_t work = (int64_t)max_context_len * c.H * (c.D * EB / 16);
+  const dim3 grid((unsigned)((work + 255) / 256), (unsigned)S);
+  if (EB == 4)
+    hipLaunchKernelGGL(gather_kernel<4>, grid, dim3(256), 0, stream, (const uint8_t *)c.k,
+                       (const uint8_t *)c.v, (uint8_t *)k_out, (uint8_t *)v_out, bt, mbps, ctx, cu,
+                       c.num_blocks, c.H, c.B, c.D, max_context_len);
+  else
+    hipLaunchKernelGGL(gather_kernel<2>, grid, dim3(256), 0, stream, (const uint8_t *)c.k,
+                       (const uint8_t *)c.v, (uint8_t *)k_out, (uint8_t *)v_out, bt, mbps, ctx, cu,
+                       c.num_blocks, c.H, c.B, c.D, max_context_len);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,276 @@
+// Paged decode attention on the vector ALUs: one workgroup (4 waves) per
+// (partition, query head, sequence).  The block-by-block walk follows
+// "vLLM — KV Cache와 PagedAttention 완전 해부" (hrletsgo.me), "부록": fetch
+// each block through the block table, compute the partial scores, update the
+// running softmax normaliser, accumulate the weighted values.  The result is
+// the token-wise softmax attention of "vLLM: LLM 서빙 메모리 최적화의 교과서"
+// (velog.io), section 01, rewritten block-wise as eq. (4) of section 02.
+//
+// Wave mapping of one block (B tokens):
+//   key tile  [B][D]  token-major: LPT lanes cover one token row with
+//             16-byte loads, so one wave load covers TPL = 64/LPT tokens and a
+//             block takes KL = B/TPL loads per lane.  Partial dot products
+//             are summed over the LPT lanes with DPP.
+//   value tile [D][B] dimension-major: a 16-byte chunk is VEC consecutive
+//             tokens of one dimension; CPR = B/VEC chunks per dimension row,
+//             VL = D*CPR/64 loads per lane.  Each lane accumulates its
+//             dimensions over its VEC tokens; the CPR lanes sharing a
+//             dimension are summed at the end.
+//   The B softmax weights move from the key layout to the value layout
+//   through a per-wave LDS slot.
+// The 4 waves take interleaved blocks of the partition and are merged
+// through LDS at the end; every score lives in the log2 domain (scores
+// scaled by scale*log2(e)) so that exp2 is a single instruction.
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kWaves = 4;
+
+template <typename E, int D, int BS>
+struct ValuCfg {
+  static constexpr int EB = E::kBytes;
+  static constexpr int VEC = 16 / EB;
+  static constexpr int LPT = D / VEC;
+  static constexpr int TPL = kWave / LPT;
+  static constexpr int KL = BS / TPL;
+  static constexpr int CPR = BS / VEC;
+  static constexpr int VL = D * CPR / kWave;
+  static_assert(LPT >= 1 && LPT <= kWave && kWave % LPT == 0, "key row must tile the wave");
+  static_assert(BS % TPL == 0, "block must be a whole number of key loads");
+  static_assert(CPR >= 1 && kWave % CPR == 0 && (D * CPR) % kWave == 0, "value tile mapping");
+};
+
+template <typename E, int D, int BS>
+__global__ __launch_bounds__(256) void decode_valu_kernel(
+    typename E::storage *__restrict__ out, const typename E::storage *__restrict__ q,
+    const typename E::storage *__restrict__ kpool, const typename E::storage *__restrict__ vpool,
+    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
+    int64_t num_blocks, int Hkv, int Hq, int mbps, float scale_log2, int part_tokens, int nparts,
+    float *__restrict__ ws_ml, float *__restrict__ ws_acc) {
+  using C = ValuCfg<E, D, BS>;
+  using T = typename E::storage;
+  const int part = blockIdx.x;
+  const int hq = blockIdx.y;
+  const int s = blockIdx.z;
+  const int L = min(context_lens[s], mbps * BS);
+  const int tok0 = part * part_tokens;
+  if (tok0 >= L) return;
+  const int tok1 = min(L, tok0 + part_tokens);
+  const int blk0 = tok0 / BS;
+  const int nblk = (tok1 - tok0 + BS - 1) / BS;
+  const int hkv = hq / (Hq / Hkv);
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = uniform(threadIdx.x >> 6);
+  const int g = lane / C::LPT;     // token slot of this lane in a key load
+  const int r = lane % C::LPT;     // 16-byte chunk of the key row
+  const int cp = lane % C::CPR;    // token chunk of the value row
+
+  __shared__ __attribute__((aligned(16))) float lds_p[kWaves][BS];
+  __shared__ float lds_m[kWaves];
+  __shared__ float lds_l[kWaves];
+  __shared__ float lds_acc[kWaves][D];
+
+  // Query slice of this lane, in fp32, pre-multiplied by scale*log2(e).
+  float qv[C::VEC];
+  {
+    const u32x4 qc = load16(q + ((size_t)s * Hq + hq) * D + r * C::VEC);
+    unpack16<E>(qc, qv);
+#pragma unroll
+    for (int i = 0; i < C::VEC; ++i) qv[i] *= scale_log2;
+  }
+
+  float m = -INFINITY;
+  float l = 0.f;
+  float acc[C::VL];
+#pragma unroll
+  for (int i = 0; i < C::VL; ++i) acc[i] = 0.f;
+
+  const int32_t *bt = block_tables + (size_t)s * mbps;
+  for (int b = w; b < nblk; b += kWaves) {
+    const int lb = blk0 + b;
+    const int64_t phys = uniform(bt[lb]);
+    if (phys < 0 || phys >= num_blocks) continue;
+    const T *kt = kpool + ((size_t)phys * Hkv + hkv) * (BS * D);
+    const T *vt = vpool + ((size_t)phys * Hkv + hkv) * (D * BS);
+    u32x4 kr[C::KL];
+    u32x4 vr[C::VL];
+#pragma unroll
+    for (int i = 0; i < C::KL; ++i) kr[i] = load16(kt + (i * C::TPL + g) * D + r * C::VEC);
+#pragma unroll
+    for (int i = 0; i < C::VL; ++i) vr[i] = load16(vt + (size_t)(kWave * i + lane) * C::VEC);
+
+    const int tbase = lb * BS;
+    const bool partial = tbase + BS > tok1;
+    float sc[C::KL];
+#pragma unroll
+    for (int i = 0; i < C::KL; ++i) {
+      float kf[C::VEC];
+      unpack16<E>(kr[i], kf);
+      float d0 = 0.f;
+#pragma unroll
+      for (int e = 0; e < C::VEC; ++e) d0 = fmaf(qv[e], kf[e], d0);
+      sc[i] = group_sum<C::LPT>(d0);
+      if (partial && tbase + i * C::TPL + g >= tok1) sc[i] = -INFINITY;
+    }
+    float mb = sc[0];
+#pragma unroll
+    for (int i = 1; i < C::KL; ++i) mb = fmaxf(mb, sc[i]);
+    mb = xor_max<C::LPT, kWave>(mb);
+    const float mnew = fmaxf(m, mb);
+    const float alpha = fast_exp2(m - mnew);
+    m = mnew;
+    if (r == 0) {
+#pragma unroll
+      for (int i = 0; i < C::KL; ++i) lds_p[w][i * C::TPL + g] = fast_exp2(sc[i] - mnew);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float p[C::VEC];
+#pragma unroll
+    for (int i = 0; i < C::VEC; i += 4) {
+      const f32x4 pv = *(const f32x4 *)&lds_p[w][cp * C::VEC + i];
+      p[i] = pv[0]; p[i + 1] = pv[1]; p[i + 2] = pv[2]; p[i + 3] = pv[3];
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < C::VEC; ++e) psum += p[e];
+    l = l * alpha + psum;
+#pragma unroll
+    for (int i = 0; i < C::VL; ++i) {
+      float vf[C::VEC];
+      unpack16<E>(vr[i], vf);
+      float a = acc[i] * alpha;
+      if (partial) {
+#pragma unroll
+        for (int e = 0; e < C::VEC; ++e) {
+          const float ve = (tbase + cp * C::VEC + e < tok1) ? vf[e] : 0.f;
+          a = fmaf(p[e], ve, a);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < C::VEC; ++e) a = fmaf(p[e], vf[e], a);
+      }
+      acc[i] = a;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // Sum each dimension over the CPR lanes that share it, and l over the same lanes.
+  l = group_sum<C::CPR>(l);
+#pragma unroll
+  for (int i = 0; i < C::VL; ++i) acc[i] = group_sum<C::CPR>(acc[i]);
+  if (cp == 0) {
+#pragma unroll
+    for (int i = 0; i < C::VL; ++i) lds_acc[w][(kWave * i + lane) / C::CPR] = acc[i];
+  }
+  if (lane == 0) {
+    lds_m[w] = m;
+    lds_l[w] = l;
+  }
+  __syncthreads();
+
+  for (int e = threadIdx.x; e < D; e += blockDim.x) {
+    float M = lds_m[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) M = fmaxf(M, lds_m[k]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+      const float f = fast_exp2(lds_m[k] - M);  // 0 for a wave that saw no block
+      num = fmaf(f, lds_acc[k][e], num);
+      den = fmaf(f, lds_l[k], den);
+    }
+    const int np = (L + part_tokens - 1) / part_tokens;
+    if (np == 1) {
+      store_elem<E>(out + ((size_t)s * Hq + hq) * D + e, num / den);
+    } else {
+      const size_t pi = ((size_t)s * Hq + hq) * nparts + part;
+      ws_acc[pi * D + e] = num;
+      if (e == 0) {
+        ws_ml[2 * pi] = M;
+        ws_ml[2 * pi + 1] = den;
+      }
+    }
+  }
+}
+
+// Cross-partition reduce: o = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+template <typename E, int D>
+__global__ __launch_bounds__(128) void decode_reduce_kernel(
+    typename E::storage *__restrict__ out, const int32_t *__restrict__ context_lens, int Hq,
+    int mbps_tokens, int part_tokens, int nparts, const float *__restrict__ ws_ml,
+    const float *__restrict__ ws_acc) {
+  const int hq = blockIdx.x;
+  const int s = blockIdx.y;
+  const int L = min(context_lens[s], mbps_tokens);
+  const int np = min((L + part_tokens - 1) / part_tokens, nparts);
+  if (np <= 1) return;
+  const size_t base = ((size_t)s * Hq + hq) * nparts;
+  float M = -INFINITY;
+  for (int p = 0; p < np; ++p) M = fmaxf(M, ws_ml[2 * (base + p)]);
+  for (int e = threadIdx.x; e < D; e += blockDim.x) {
+    float num = 0.f, den = 0.f;
+    for (int p = 0; p < np; ++p) {
+      const float f = fast_exp2(ws_ml[2 * (base + p)] - M);
+      num = fmaf(f, ws_acc[(base + p) * D + e], num);
+      den = fmaf(f, ws_ml[2 * (base + p) + 1], den);
+    }
+    store_elem<E>(out + ((size_t)s * Hq + hq) * D + e, num / den);
+  }
+}
+
+template <typename E, int D, int BS>
+void launch_valu_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
+  using T = typename E::storage;
+  const dim3 grid((unsigned)a.num_partitions, (unsigned)a.Hq, (unsigned)a.S);
+  hipLaunchKernelGGL((decode_valu_kernel<E, D, BS>), grid, dim3(256), 0, stream, (T *)a.out,
+                     (const T *)a.q, (const T *)c.k, (const T *)c.v, a.block_tables,
+                     a.context_lens, c.num_blocks, c.H, a.Hq, a.max_blocks_per_seq,
+                     a.scale * kLog2e, a.partition_tokens, a.num_partitions, a.ws_ml, a.ws_acc);
+}
+
+template <typename E>
+void launch_valu_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
+  if (c.D == 64 && c.B == 16) launch_valu_t<E, 64, 16>(c, a, stream);
+  else if (c.D == 64 && c.B == 32) launch_valu_t<E, 64, 32>(c, a, stream);
+  else if (c.D == 128 && c.B == 16) launch_valu_t<E, 128, 16>(c, a, stream);
+  else launch_valu_t<E, 128, 32>(c, a, stream);
+}
+
+template <typename E>
+void launch_reduce_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
+  using T = typename E::storage;
+  const dim3 grid((unsigned)a.Hq, (unsigned)a.S);
+  const int mt = a.max_blocks_per_seq * c.B;
+  if (c.D == 64)
+    hipLaunchKernelGGL((decode_reduce_kernel<E, 64>), grid, dim3(64), 0, stream, (T *)a.out,
+                       a.context_lens, a.Hq, mt, a.partition_tokens, a.num_partitions, a.ws_ml,
+                       a.ws_acc);
+  else
+    hipLaunchKernelGGL((decode_reduce_kernel<E, 128>), grid, dim3(128), 0, stream, (T *)a.out,
+                       a.context_lens, a.Hq, mt, a.partition_tokens, a.num_partitions, a.ws_ml,
+                       a.ws_acc);
+}
+
+}  // namespace
+
+hipError_t launch_decode_valu(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
+  if (c.dtype == 0) launch_valu_e<F32>(c, a, stream);
+  else if (c.dtype == 1) launch_valu_e<F16>(c, a, stream);
+  else launch_valu_e<BF16>(c, a, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_reduce(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
+  if (c.dtype == 0) launch_reduce_e<F32>(c, a, stream);
+  else if (c.dtype == 1) launch_reduce_e<F16>(c, a, stream);
+  else launch_reduce_e<BF16>(c, a, stream);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

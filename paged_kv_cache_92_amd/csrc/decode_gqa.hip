@@ -1,0 +1,254 @@
+// Grouped-query paged decode on the matrix cores (f16/bf16).
+//
+// G query heads share one KV head ("Sparse Computation and Memory Management
+// for Efficient LLM Inference", pyy0715.github.io, section "The Hidden Waste
+// of KV Cache": 32 query heads over 8 KV heads).  A workgroup (4 waves) owns
+// one (partition, KV head, sequence); the G queries are stacked into the N
+// columns of 16x16 matrix products so each key/value tile is read once for
+// the whole group.  Per 16-token sub-tile, each wave computes
+//
+//   S^T (16 tokens x 16 heads) = K (16 x D) . Q^T (D x 16)     16x16x32 MFMAs
+//   O^T (D x 16 heads)        += V^T (D x 16) . P^T (16 x 16)  16x16x16 MFMAs
+//
+// Lane l holds column l%16 (a query head) of S^T with tokens 4*(l/16)+j, which
+// is exactly the B-operand layout of P^T for the second product, so the
+// softmax weights never leave their registers.  V^T comes straight from the
+// dimension-major value tile (4 consecutive tokens of one dimension = 8
+// bytes per lane).  The running max and denominator are per head, i.e. per
+// lane column, as in the block-wise walk of "vLLM — KV Cache와 PagedAttention
+// 완전 해부" (hrletsgo.me), "부록".  Scores are kept in the log2 domain.
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kWaves = 4;
+
+template <typename E>
+struct Mfma;
+
+template <>
+struct Mfma<F16> {
+  __device__ static f32x4 qk(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static f32x4 pv(const u32x2 &a, const u32x2 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  }
+  __device__ static uint32_t pack2(float lo, float hi) {
+    return (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
+  }
+};
+
+template <>
+struct Mfma<BF16> {
+  __device__ static f32x4 qk(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static f32x4 pv(const u32x2 &a, const u32x2 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+  }
+  __device__ static uint32_t pack2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  }
+};
+
+template <typename E, int D, int BS>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(
+    uint16_t *__restrict__ out, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kpool,
+    const uint16_t *__restrict__ vpool, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ context_lens, int64_t num_blocks, int Hkv, int G, int mbps,
+    float scale_log2, int part_tokens, int nparts, float *__restrict__ ws_ml,
+    float *__restrict__ ws_acc) {
+  constexpr int KS = D / 32;    // k-steps of the score product
+  constexpr int NT = D / 16;    // 16-dimension tiles of the output
+  constexpr int SUB = BS / 16;  // 16-token sub-tiles per block
+  const int part = blockIdx.x;
+  const int hkv = blockIdx.y;
+  const int s = blockIdx.z;
+  const int L = min(context_lens[s], mbps * BS);
+  const int tok0 = part * part_tokens;
+  if (tok0 >= L) return;
+  const int tok1 = min(L, tok0 + part_tokens);
+  const int blk0 = tok0 / BS;
+  const int nblk = (tok1 - tok0 + BS - 1) / BS;
+  const int Hq = Hkv * G;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = uniform(threadIdx.x >> 6);
+  const int n16 = lane & 15;   // query head (column) / token row / dimension row
+  const int g4 = lane >> 4;    // k-group of the operands, row group of the result
+
+  __shared__ float lds_m[kWaves][16];
+  __shared__ float lds_l[kWaves][16];
+  __shared__ float lds_acc[kWaves][16][D + 1];
+
+  // Q^T operand: head n16 of the group (zero past G), dimensions 32*ks + 8*g4 .. +8.
+  u32x4 qb[KS];
+  {
+    const bool valid = n16 < G;
+    const uint16_t *qrow = q + ((size_t)s * Hq + hkv * G + (valid ? n16 : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qb[ks] = valid ? load16(qrow + 32 * ks + 8 * g4) : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  float m = -INFINITY;  // running max of head n16 (log2 domain)
+  float l = 0.f;        // this lane's share of the denominator of head n16
+  f32x4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t *bt = block_tables + (size_t)s * mbps;
+  for (int b = w; b < nblk; b += kWaves) {
+    const int lb = blk0 + b;
+    const int64_t phys = uniform(bt[lb]);
+    if (phys < 0 || phys >= num_blocks) continue;
+    const uint16_t *kt = kpool + ((size_t)phys * Hkv + hkv) * (BS * D);
+    const uint16_t *vt = vpool + ((size_t)phys * Hkv + hkv) * (D * BS);
+    u32x4 ka[SUB][KS];
+    u32x2 va[SUB][NT];
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        ka[sb][ks] = load16(kt + (16 * sb + n16) * D + 32 * ks + 8 * g4);
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        va[sb][nt] = load8(vt + (16 * nt + n16) * BS + 16 * sb + 4 * g4);
+
+    const int tbase = lb * BS;
+    const bool partial = tbase + BS > tok1;
+    f32x4 st[SUB];
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) x = Mfma<E>::qk(ka[sb][ks], qb[ks], x);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v = x[j] * scale_log2;
+        if (partial && tbase + 16 * sb + 4 * g4 + j >= tok1) v = -INFINITY;
+        x[j] = v;
+      }
+      st[sb] = x;
+    }
+    float mb = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mb = fmaxf(mb, st[sb][j]);
+    mb = xor_max<16, kWave>(mb);
+    const float mnew = fmaxf(m, mb);
+    const float alpha = fast_exp2(m - mnew);
+    m = mnew;
+    float psum = 0.f;
+    u32x2 pb[SUB];
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb) {
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[j] = fast_exp2(st[sb][j] - mnew);
+        psum += p[j];
+      }
+      pb[sb] = u32x2{Mfma<E>::pack2(p[0], p[1]), Mfma<E>::pack2(p[2], p[3])};
+    }
+    l = l * alpha + psum;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
+    if (partial) {
+      // Unfilled slots may hold anything (NaN included): zero their values.
+#pragma unroll
+      for (int sb = 0; sb < SUB; ++sb) {
+        const int t0 = tbase + 16 * sb + 4 * g4;
+        const uint32_t keep01 = (t0 < tok1 ? 0x0000ffffu : 0u) | (t0 + 1 < tok1 ? 0xffff0000u : 0u);
+        const uint32_t keep23 = (t0 + 2 < tok1 ? 0x0000ffffu : 0u) | (t0 + 3 < tok1 ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          va[sb][nt][0] &= keep01;
+          va[sb][nt][1] &= keep23;
+        }
+      }
+    }
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = Mfma<E>::pv(va[sb][nt], pb[sb], acc[nt]);
+  }
+
+  // Denominator of head n16: sum over the 4 row groups.
+  l = xor_sum<16, kWave>(l);
+  if (g4 == 0) {
+    lds_m[w][n16] = m;
+    lds_l[w][n16] = l;
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lds_acc[w][n16][16 * nt + 4 * g4 + j] = acc[nt][j];
+  __syncthreads();
+
+  const int np = (L + part_tokens - 1) / part_tokens;
+  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+    const int h = idx / D;
+    const int e = idx - h * D;
+    float M = lds_m[0][h];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) M = fmaxf(M, lds_m[k][h]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+      const float f = fast_exp2(lds_m[k][h] - M);
+      num = fmaf(f, lds_acc[k][h][e], num);
+      den = fmaf(f, lds_l[k][h], den);
+    }
+    const int hq = hkv * G + h;
+    if (np == 1) {
+      store_elem<E>(out + ((size_t)s * Hq + hq) * D + e, num / den);
+    } else {
+      const size_t pi = ((size_t)s * Hq + hq) * nparts + part;
+      ws_acc[pi * D + e] = num;
+      if (e == 0) {
+        ws_ml[2 * pi] = M;
+        ws_ml[2 * pi + 1] = den;
+      }
+    }
+  }
+}
+
+template <typename E, int D, int BS>
+void launch_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.num_partitions, (unsigned)c.H, (unsigned)a.S);
+  hipLaunchKernelGGL((decode_mfma_kernel<E, D, BS>), grid, dim3(256), 0, stream,
+                     (uint16_t *)a.out, (const uint16_t *)a.q, (const uint16_t *)c.k,
+                     (const uint16_t *)c.v, a.block_tables, a.context_lens, c.num_blocks, c.H,
+                     a.Hq / c.H, a.max_blocks_per_seq, a.scale * kLog2e, a.partition_tokens,
+                     a.num_partitions, a.ws_ml, a.ws_acc);
+}
+
+template <typename E>
+void launch_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
+  if (c.D == 64 && c.B == 16) launch_t<E, 64, 16>(c, a, stream);
+  else if (c.D == 64 && c.B == 32) launch_t<E, 64, 32>(c, a, stream);
+  else if (c.D == 128 && c.B == 16) launch_t<E, 128, 16>(c, a, stream);
+  else launch_t<E, 128, 32>(c, a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
+  if (c.dtype == 1) launch_e<F16>(c, a, stream);
+  else launch_e<BF16>(c, a, stream);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,289 @@
+// C ABI of libpkv.so: host-side argument validation and kernel dispatch.
+// The contract of every entry point is documented in include/pkv.h.
+#include "pkv.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <unordered_set>
+#include <vector>
+
+#include "pkv_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pkv_status fail(pkv_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pkv_status ok() {
+  g_err[0] = '\0';
+  return PKV_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+pkv_status check_cache(const pkv_cache *c, pkv::CacheDesc *d) {
+  if (!c) return fail(PKV_ERR_INVALID, "cache descriptor is NULL");
+  if (!c->k_pool || !c->v_pool) return fail(PKV_ERR_INVALID, "k_pool/v_pool is NULL");
+  if (!aligned16(c->k_pool) || !aligned16(c->v_pool))
+    return fail(PKV_ERR_INVALID, "k_pool/v_pool must be 16-byte aligned");
+  if (c->num_blocks <= 0) return fail(PKV_ERR_INVALID, "num_blocks must be > 0");
+  if (c->num_kv_heads <= 0) return fail(PKV_ERR_INVALID, "num_kv_heads must be > 0");
+  if (c->block_size != 16 && c->block_size != 32)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (16 or 32)", c->block_size);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", c->head_dim);
+  if (c->dtype != PKV_F32 && c->dtype != PKV_F16 && c->dtype != PKV_BF16)
+    return fail(PKV_ERR_INVALID, "unknown dtype %d", c->dtype);
+  d->k = c->k_pool;
+  d->v = c->v_pool;
+  d->num_blocks = c->num_blocks;
+  d->H = c->num_kv_heads;
+  d->B = c->block_size;
+  d->D = c->head_dim;
+  d->dtype = c->dtype;
+  return PKV_OK;
+}
+
+pkv_status hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+struct Partitioning {
+  int tokens;
+  int count;
+};
+
+Partitioning partitioning(int max_context_len, int partition_size, int B) {
+  Partitioning p;
+  if (partition_size <= 0 || partition_size >= max_context_len) {
+    p.tokens = (max_context_len + B - 1) / B * B;
+    p.count = 1;
+  } else {
+    p.tokens = partition_size;
+    p.count = (max_context_len + partition_size - 1) / partition_size;
+  }
+  return p;
+}
+
+size_t workspace_bytes(int S, int Hq, int D, const Partitioning &p) {
+  if (p.count <= 1) return 0;
+  const size_t n = (size_t)S * Hq * p.count;
+  const size_t ml = (n * 2 * sizeof(float) + 255) / 256 * 256;
+  return ml + n * D * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pkv_last_error(void) { return g_err; }
+
+const char *pkv_version(void) { return "pkv 0.1 gfx950"; }
+
+pkv_status pkv_reshape_and_cache(const pkv_cache *cache, const void *key, const void *value,
+                                 const int64_t *slot_mapping, int64_t num_tokens,
+                                 hipStream_t stream) {
+  pkv::CacheDesc c;
+  pkv_status st = check_cache(cache, &c);
+  if (st) return st;
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID, "num_tokens < 0");
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !slot_mapping) return fail(PKV_ERR_INVALID, "key/value/slot_mapping is NULL");
+  if (!aligned16(key) || !aligned16(value)) return fail(PKV_ERR_INVALID, "key/value must be 16-byte aligned");
+  return hip_status(pkv::launch_reshape_and_cache(c, key, value, slot_mapping, num_tokens, stream),
+                    "reshape_and_cache launch");
+}
+
+pkv_status pkv_copy_blocks(const pkv_cache *cache, const int32_t *src_dst, int64_t num_pairs,
+                           hipStream_t stream) {
+  pkv::CacheDesc c;
+  pkv_status st = check_cache(cache, &c);
+  if (st) return st;
+  if (num_pairs < 0) return fail(PKV_ERR_INVALID, "num_pairs < 0");
+  if (num_pairs == 0) return ok();
+  if (!src_dst) return fail(PKV_ERR_INVALID, "src_dst is NULL");
+  if (num_pairs > 65535) return fail(PKV_ERR_UNSUPPORTED, "at most 65535 pairs per call");
+  return hip_status(pkv::launch_copy_blocks(c, src_dst, num_pairs, stream), "copy_blocks launch");
+}
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  const Partitioning p = partitioning(max_context_len, partition_size, 16);
+  return workspace_bytes(num_seqs, num_q_heads, head_dim, p);
+}
+
+pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, const void *q, int32_t num_q_heads,
+                            const int32_t *block_tables, int32_t max_blocks_per_seq,
+                            const int32_t *context_lens, int32_t num_seqs,
+                            int32_t max_context_len, float scale, int32_t partition_size,
+                            void *workspace, size_t ws_bytes, hipStream_t stream) {
+  pkv::CacheDesc c;
+  pkv_status st = check_cache(cache, &c);
+  if (st) return st;
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID, "num_seqs < 0");
+  if (num_seqs == 0) return ok();
+  if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "at most 65535 sequences per call");
+  if (!out || !q || !block_tables || !context_lens)
+    return fail(PKV_ERR_INVALID, "out/q/block_tables/context_lens is NULL");
+  if (!aligned16(out) || !aligned16(q)) return fail(PKV_ERR_INVALID, "q/out must be 16-byte aligned");
+  if (num_q_heads <= 0 || num_q_heads % c.H != 0)
+    return fail(PKV_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, c.H);
+  if (num_q_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "too many query heads");
+  if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID, "max_blocks_per_seq must be > 0");
+  if (max_context_len <= 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * c.B)
+    return fail(PKV_ERR_INVALID, "max_context_len %d outside [1, max_blocks_per_seq*block_size]",
+                max_context_len);
+  if (partition_size < 0 || partition_size % c.B != 0)
+    return fail(PKV_ERR_INVALID, "partition_size %d must be 0 or a positive multiple of block_size %d",
+                partition_size, c.B);
+  const int G = num_q_heads / c.H;
+  const bool mfma = G > 1 && c.dtype != PKV_F32;
+  if (mfma && G > 16) return fail(PKV_ERR_UNSUPPORTED, "group size %d > 16", G);
+  const Partitioning p = partitioning(max_context_len, partition_size, c.B);
+  const size_t need = workspace_bytes(num_seqs, num_q_heads, c.D, p);
+  if (need > 0) {
+    if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if (ws_bytes < need)
+      return fail(PKV_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", ws_bytes, need);
+    if (!aligned16(workspace)) return fail(PKV_ERR_INVALID, "workspace must be 16-byte aligned");
+  }
+  pkv::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.Hq = num_q_heads;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.S = num_seqs;
+  a.max_context_len = max_context_len;
+  a.scale = scale;
+  a.partition_tokens = p.tokens;
+  a.num_partitions = p.count;
+  a.ws_ml = nullptr;
+  a.ws_acc = nullptr;
+  if (need > 0) {
+    const size_t n = (size_t)num_seqs * num_q_heads * p.count;
+    a.ws_ml = (float *)workspace;
+    a.ws_acc = (float *)((char *)workspace + (n * 2 * sizeof(float) + 255) / 256 * 256);
+  }
+  hipError_t e = mfma ? pkv::launch_decode_mfma(c, a, stream) : pkv::launch_decode_valu(c, a, stream);
+  if (e != hipSuccess) return hip_status(e, "paged_decode launch");
+  if (p.count > 1) {
+    e = pkv::launch_decode_reduce(c, a, stream);
+    if (e != hipSuccess) return hip_status(e, "paged_decode reduce launch");
+  }
+  return ok();
+}
+
+pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, const void *q,
+                             int32_t num_q_heads, const int32_t *query_start_loc,
+                             const int32_t *context_lens, const int32_t *block_tables,
+                             int32_t max_blocks_per_seq, int32_t num_seqs, int32_t max_query_len,
+                             int32_t max_context_len, float scale, hipStream_t stream) {
+  pkv::CacheDesc c;
+  pkv_status st = check_cache(cache, &c);
+  if (st) return st;
+  if (c.dtype == PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "prefill supports f16 and bf16");
+  if (num_seqs < 0 || max_query_len < 0) return fail(PKV_ERR_INVALID, "negative size");
+  if (num_seqs == 0 || max_query_len == 0) return ok();
+  if (!out || !q || !query_start_loc || !context_lens || !block_tables)
+    return fail(PKV_ERR_INVALID, "a required pointer is NULL");
+  if (!aligned16(out) || !aligned16(q)) return fail(PKV_ERR_INVALID, "q/out must be 16-byte aligned");
+  if (num_q_heads <= 0 || num_q_heads % c.H != 0)
+    return fail(PKV_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, c.H);
+  if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID, "max_blocks_per_seq must be > 0");
+  if (max_context_len <= 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * c.B)
+    return fail(PKV_ERR_INVALID, "max_context_len %d outside [1, max_blocks_per_seq*block_size]",
+                max_context_len);
+  if (max_query_len > max_context_len) return fail(PKV_ERR_INVALID, "max_query_len > max_context_len");
+  const int64_t work = (int64_t)num_seqs * num_q_heads * ((max_query_len + 127) / 128);
+  if (work >= (int64_t)1 << 31) return fail(PKV_ERR_UNSUPPORTED, "launch too large");
+  pkv::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.Hq = num_q_heads;
+  a.query_start_loc = query_start_loc;
+  a.context_lens = context_lens;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.S = num_seqs;
+  a.max_query_len = max_query_len;
+  a.max_context_len = max_context_len;
+  a.scale = scale;
+  return hip_status(pkv::launch_prefill(c, a, stream), "paged_prefill launch");
+}
+
+pkv_status pkv_gather_kv(const pkv_cache *cache, void *k_out, void *v_out,
+                         const int32_t *block_tables, int32_t max_blocks_per_seq,
+                         const int32_t *context_lens, const int32_t *cu_context_lens,
+                         int32_t num_seqs, int32_t max_context_len, hipStream_t stream) {
+  pkv::CacheDesc c;
+  pkv_status st = check_cache(cache, &c);
+  if (st) return st;
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID, "num_seqs < 0");
+  if (num_seqs == 0) return ok();
+  if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "at most 65535 sequences per call");
+  if (!k_out || !v_out || !block_tables || !context_lens || !cu_context_lens)
+    return fail(PKV_ERR_INVALID, "a required pointer is NULL");
+  if (!aligned16(k_out) || !aligned16(v_out)) return fail(PKV_ERR_INVALID, "outputs must be 16-byte aligned");
+  if (max_blocks_per_seq <= 0 || max_context_len <= 0 ||
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * c.B)
+    return fail(PKV_ERR_INVALID, "bad max_blocks_per_seq / max_context_len");
+  return hip_status(pkv::launch_gather_kv(c, k_out, v_out, block_tables, max_blocks_per_seq,
+                                          context_lens, cu_context_lens, num_seqs, max_context_len,
+                                          stream),
+                    "gather_kv launch");
+}
+
+pkv_status pkv_validate_host(const int64_t *slot_mapping, int64_t num_tokens,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                             const int32_t *context_lens, int32_t num_seqs, int64_t num_blocks,
+                             int32_t block_size) {
+  if (num_blocks <= 0 || block_size <= 0) return fail(PKV_ERR_INVALID, "bad pool geometry");
+  if (slot_mapping && num_tokens > 0) {
+    std::unordered_set<int64_t> seen;
+    seen.reserve((size_t)num_tokens * 2);
+    const int64_t nslots = num_blocks * block_size;
+    for (int64_t t = 0; t < num_tokens; ++t) {
+      const int64_t s = slot_mapping[t];
+      if (s < 0) continue;
+      if (s >= nslots)
+        return fail(PKV_ERR_INVALID, "slot_mapping[%lld] = %lld >= %lld slots", (long long)t,
+                    (long long)s, (long long)nslots);
+      if (!seen.insert(s).second)
+        return fail(PKV_ERR_INVALID, "slot %lld appears twice (token %lld)", (long long)s, (long long)t);
+    }
+  }
+  if (context_lens && num_seqs > 0) {
+    if (!block_tables || max_blocks_per_seq <= 0)
+      return fail(PKV_ERR_INVALID, "block_tables needed with context_lens");
+    for (int32_t s = 0; s < num_seqs; ++s) {
+      const int32_t L = context_lens[s];
+      if (L < 1 || (int64_t)L > (int64_t)max_blocks_per_seq * block_size)
+        return fail(PKV_ERR_INVALID, "context_lens[%d] = %d outside [1, %lld]", s, L,
+                    (long long)max_blocks_per_seq * block_size);
+      const int32_t nb = (L + block_size - 1) / block_size;
+      for (int32_t i = 0; i < nb; ++i) {
+        const int32_t b = block_tables[(size_t)s * max_blocks_per_seq + i];
+        if (b < 0 || b >= num_blocks)
+          return fail(PKV_ERR_INVALID, "block_tables[%d][%d] = %d outside [0, %lld)", s, i, b,
+                      (long long)num_blocks);
+      }
+    }
+  }
+  return ok();
+}
+
+}  // extern "C"

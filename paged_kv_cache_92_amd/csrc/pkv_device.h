@@ -1,0 +1,143 @@
+// Device-side helpers shared by the pkv HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Element tags: storage is float for fp32 and uint16_t bits for fp16/bf16.
+struct F32 {
+  using storage = float;
+  static constexpr int kBytes = 4;
+};
+struct F16 {
+  using storage = uint16_t;
+  static constexpr int kBytes = 2;
+};
+struct BF16 {
+  using storage = uint16_t;
+  static constexpr int kBytes = 2;
+};
+
+// ---- scalar conversions ---------------------------------------------------
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);  // round to nearest even
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even
+}
+
+template <typename E>
+__device__ __forceinline__ float lo_to_f32(uint32_t w);
+template <typename E>
+__device__ __forceinline__ float hi_to_f32(uint32_t w);
+template <>
+__device__ __forceinline__ float lo_to_f32<F16>(uint32_t w) { return f16_bits_to_f32(w & 0xffffu); }
+template <>
+__device__ __forceinline__ float hi_to_f32<F16>(uint32_t w) { return f16_bits_to_f32(w >> 16); }
+template <>
+__device__ __forceinline__ float lo_to_f32<BF16>(uint32_t w) { return bf16_bits_to_f32(w & 0xffffu); }
+template <>
+__device__ __forceinline__ float hi_to_f32<BF16>(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Unpack a 16-byte chunk into VEC floats (VEC = 4 for fp32, 8 for 16-bit).
+template <typename E>
+__device__ __forceinline__ void unpack16(const u32x4 &c, float *out);
+template <>
+__device__ __forceinline__ void unpack16<F32>(const u32x4 &c, float *out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = __builtin_bit_cast(float, c[i]);
+}
+template <>
+__device__ __forceinline__ void unpack16<F16>(const u32x4 &c, float *out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = lo_to_f32<F16>(c[i]);
+    out[2 * i + 1] = hi_to_f32<F16>(c[i]);
+  }
+}
+template <>
+__device__ __forceinline__ void unpack16<BF16>(const u32x4 &c, float *out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = lo_to_f32<BF16>(c[i]);
+    out[2 * i + 1] = hi_to_f32<BF16>(c[i]);
+  }
+}
+
+template <typename E>
+__device__ __forceinline__ void store_elem(typename E::storage *p, float x);
+template <>
+__device__ __forceinline__ void store_elem<F32>(float *p, float x) { *p = x; }
+template <>
+__device__ __forceinline__ void store_elem<F16>(uint16_t *p, float x) { *p = f32_to_f16_bits(x); }
+template <>
+__device__ __forceinline__ void store_elem<BF16>(uint16_t *p, float x) { *p = f32_to_bf16_bits(x); }
+
+// ---- wave reductions ---------------------------------------------------------
+// DPP row controls (within rows of 16 lanes): quad_perm [1,0,3,2] and
+// [2,3,0,1] swap neighbours at distance 1 and 2; half-row mirror pairs lane i
+// with 7-i of its 8-lane half; row mirror pairs i with 15-i.  Applied in that
+// order, each step adds a disjoint group, so after k steps every lane holds
+// the sum over its aligned group of 2^k lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xf, 0xf, false));
+}
+
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(WIDTH == 1 || WIDTH == 2 || WIDTH == 4 || WIDTH == 8 || WIDTH == 16 ||
+                    WIDTH == 32 || WIDTH == 64,
+                "power-of-two group");
+  if constexpr (WIDTH >= 2) x += dpp_f32<0xB1>(x);
+  if constexpr (WIDTH >= 4) x += dpp_f32<0x4E>(x);
+  if constexpr (WIDTH >= 8) x += dpp_f32<0x141>(x);
+  if constexpr (WIDTH >= 16) x += dpp_f32<0x140>(x);
+  if constexpr (WIDTH >= 32) x += __shfl_xor(x, 16);
+  if constexpr (WIDTH >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Max over lanes that differ only in bits [log2(FROM), log2(TO)) of the lane id.
+template <int FROM, int TO>
+__device__ __forceinline__ float xor_max(float x) {
+#pragma unroll
+  for (int m = FROM; m < TO; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+template <int FROM, int TO>
+__device__ __forceinline__ float xor_sum(float x) {
+#pragma unroll
+  for (int m = FROM; m < TO; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ u32x4 load16(const void *p) { return *(const u32x4 *)p; }
+__device__ __forceinline__ u32x2 load8(const void *p) { return *(const u32x2 *)p; }
+
+}  // namespace pkv

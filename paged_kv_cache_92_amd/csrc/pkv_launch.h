@@ -1,0 +1,68 @@
+// Internal launch interface between the C-ABI layer (pkv_api.cpp) and the
+// kernel translation units.  Host-only declarations; every launcher assumes
+// its arguments were validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct CacheDesc {
+  void *k;           // [num_blocks][H][B][D]
+  void *v;           // [num_blocks][H][D][B]
+  int64_t num_blocks;
+  int H, B, D;
+  int dtype;         // 0 f32, 1 f16, 2 bf16
+  int elt_bytes() const { return dtype == 0 ? 4 : 2; }
+};
+
+struct DecodeArgs {
+  void *out;
+  const void *q;
+  int Hq;
+  const int32_t *block_tables;
+  int max_blocks_per_seq;
+  const int32_t *context_lens;
+  int S;
+  int max_context_len;
+  float scale;
+  int partition_tokens;   // > 0, multiple of B
+  int num_partitions;     // ceil(max_context_len / partition_tokens)
+  float *ws_ml;           // [S][Hq][num_partitions][2] (max, denominator), log2 domain
+  float *ws_acc;          // [S][Hq][num_partitions][D] unnormalised weighted sums
+};
+
+struct PrefillArgs {
+  void *out;
+  const void *q;
+  int Hq;
+  const int32_t *query_start_loc;
+  const int32_t *context_lens;
+  const int32_t *block_tables;
+  int max_blocks_per_seq;
+  int S;
+  int max_query_len;
+  int max_context_len;
+  float scale;
+};
+
+hipError_t launch_reshape_and_cache(const CacheDesc &c, const void *key, const void *value,
+                                    const int64_t *slots, int64_t T, hipStream_t stream);
+hipError_t launch_copy_blocks(const CacheDesc &c, const int32_t *pairs, int64_t n,
+                              hipStream_t stream);
+hipError_t launch_gather_kv(const CacheDesc &c, void *k_out, void *v_out, const int32_t *bt,
+                            int mbps, const int32_t *ctx, const int32_t *cu, int S,
+                            int max_context_len, hipStream_t stream);
+
+// Wavefront dot-product decode (any dtype, one query head per workgroup).
+hipError_t launch_decode_valu(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream);
+// Matrix-core decode for grouped heads (f16/bf16, 2 <= G <= 16).
+hipError_t launch_decode_mfma(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream);
+// Combine split-KV partials into the output (only sequences with > 1 partition).
+hipError_t launch_decode_reduce(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream);
+// Matrix-core causal chunked prefill (f16/bf16).
+hipError_t launch_prefill(const CacheDesc &c, const PrefillArgs &a, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,286 @@
+// Causal chunked prefill over the paged cache on the matrix cores (f16/bf16).
+//
+// A chunk of a long prompt is processed as one step ("Sparse Computation and
+// Memory Management for Efficient LLM Inference", pyy0715.github.io, section
+// "Prefill-Decode Disaggregation"); all of its rows are known at once, so
+// attention is a matrix-matrix product ("vLLM: LLM 서빙 메모리 최적화의 교과서",
+// velog.io, section 01, prompt phase), causal over j <= i.
+//
+// Workgroup = 4 waves = one (sequence, query head, 128-row query tile); wave
+// w owns 32 rows.  The key/value positions 0..last row's position are walked
+// in 32-token tiles gathered through the block table into LDS (the next
+// tile's global loads are in flight while the current one is computed):
+//
+//   S^T (32 tokens x 32 rows) = K (32 x D) . Q^T (D x 32)     32x16 k-steps
+//   O^T (D x 32 rows)        += V^T (D x 32) . P^T (32 x 32)   2 k-steps/tile
+//
+// with 32x32x16 MFMAs.  The key rows are fed to the first product in a
+// permuted order chosen so that each lane's 16 result rows are, per 16-token
+// k-step of the second product, 8 consecutive tokens: the B operand P^T is
+// then built from the lane's own registers and the A operand V^T is one
+// 16-byte LDS read from the dimension-major value tile.  Online softmax per
+// row, log2 domain.  Tiles entirely in a wave's future are skipped.
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kQT = 32 * kWaves;  // query rows per workgroup
+constexpr int kKT = 32;           // key/value tokens per tile
+constexpr int kVPad = 8;          // LDS row padding (elements) against bank conflicts
+
+template <typename E>
+struct Mfma32;
+template <>
+struct Mfma32<F16> {
+  __device__ static f32x16 mma(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static uint32_t pack2(float lo, float hi) {
+    return (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
+  }
+};
+template <>
+struct Mfma32<BF16> {
+  __device__ static f32x16 mma(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static uint32_t pack2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  }
+};
+
+// Row i of the score product (i = 8a + 4h + b) holds tile token perm(i).
+__device__ __forceinline__ int perm_row(int i) {
+  const int a = i >> 3, h = (i >> 2) & 1, b = i & 3;
+  return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
+}
+
+template <typename E, int D, int BS>
+__global__ __launch_bounds__(256) void prefill_kernel(
+    uint16_t *__restrict__ out, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kpool,
+    const uint16_t *__restrict__ vpool, const int32_t *__restrict__ query_start_loc,
+    const int32_t *__restrict__ context_lens, const int32_t *__restrict__ block_tables,
+    int64_t num_blocks, int Hkv, int Hq, int mbps, int nqt, float scale_log2) {
+  constexpr int KS = D / 16;          // k-steps of the score product
+  constexpr int DT = D / 32;          // 32-dimension tiles of the output
+  constexpr int KCH = kKT * D / 8;    // 16-byte chunks of a key tile
+  constexpr int VCH = D * kKT / 8;    // 16-byte chunks of a value tile
+  constexpr int KPT = KCH / 256;      // key chunks per thread
+  constexpr int VPT = VCH / 256;      // value chunks per thread
+  static_assert(KCH % 256 == 0 && VCH % 256 == 0, "tile must split evenly over the workgroup");
+  constexpr int KROW = D + kVPad;     // LDS key row (elements)
+  constexpr int VROW = kKT + kVPad;   // LDS value row (elements)
+
+  // Work item: XCD-aware order keeps the tiles of one (sequence, head) on one
+  // XCD (consecutive block ids go round-robin over the 8 XCDs), longest tile first.
+  const int nwork = gridDim.x;
+  int wid = blockIdx.x;
+  if ((nwork & 7) == 0) wid = (wid & 7) * (nwork >> 3) + (wid >> 3);
+  const int qt = nqt - 1 - wid % nqt;
+  const int hq = (wid / nqt) % Hq;
+  const int s = wid / (nqt * Hq);
+
+  const int qs = query_start_loc[s];
+  const int qlen = query_start_loc[s + 1] - qs;
+  if (qt * kQT >= qlen) return;
+  const int ctx = min(context_lens[s], mbps * BS);
+  const int hist = ctx - qlen;
+  if (hist < 0) return;
+  const int hkv = hq / (Hq / Hkv);
+  const int32_t *bt = block_tables + (size_t)s * mbps;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = uniform(tid >> 6);
+  const int j32 = lane & 31;  // query column of this lane
+  const int h = lane >> 5;    // k-half / row group
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kKT * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VROW];
+
+  const int wrow0 = qt * kQT + 32 * w;                  // first chunk row of this wave
+  const int myrow = wrow0 + j32;
+  const int qpos = hist + min(myrow, qlen - 1);         // position of this lane's query
+  const int wave_max_pos = hist + min(wrow0 + 31, qlen - 1);
+  const int wg_max_pos = hist + min(qt * kQT + kQT - 1, qlen - 1);
+  const int ntiles = (wg_max_pos + kKT) / kKT;
+
+  // Q^T operand: query column j32, dimensions 16*ks + 8*h .. +8 (zero past the chunk).
+  u32x4 qb[KS];
+  {
+    const bool valid = myrow < qlen;
+    const uint16_t *qrow = q + ((size_t)(qs + (valid ? myrow : 0)) * Hq + hq) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = valid ? load16(qrow + 16 * ks + 8 * h) : u32x4{0, 0, 0, 0};
+  }
+
+  // Global -> register staging of one tile.
+  u32x4 kreg[KPT], vreg[VPT];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + 256 * i;
+      const int tok = c / (D / 8), ch = c % (D / 8);
+      const int pos = t * kKT + tok;
+      u32x4 x = {0, 0, 0, 0};
+      if (pos < ctx) {
+        const int32_t blk = bt[pos / BS];
+        if (blk >= 0 && blk < num_blocks)
+          x = load16(kpool + (((size_t)blk * Hkv + hkv) * BS + pos % BS) * D + 8 * ch);
+      }
+      kreg[i] = x;
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = tid + 256 * i;
+      const int e = c / (kKT / 8), g8 = c % (kKT / 8);
+      const int pos = t * kKT + 8 * g8;
+      u32x4 x = {0, 0, 0, 0};
+      if (pos < ctx) {
+        const int32_t blk = bt[pos / BS];
+        if (blk >= 0 && blk < num_blocks) {
+          x = load16(vpool + (((size_t)blk * Hkv + hkv) * D + e) * BS + pos % BS);
+          if (pos + 8 > ctx) {
+            // Slots past the context may hold anything: zero them.
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const uint32_t keep = (pos + 2 * k < ctx ? 0x0000ffffu : 0u) |
+                                    (pos + 2 * k + 1 < ctx ? 0xffff0000u : 0u);
+              x[k] &= keep;
+            }
+          }
+        }
+      }
+      vreg[i] = x;
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + 256 * i;
+      const int tok = c / (D / 8), ch = c % (D / 8);
+      *(u32x4 *)&sK[tok * KROW + 8 * ch] = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = tid + 256 * i;
+      const int e = c / (kKT / 8), g8 = c % (kKT / 8);
+      *(u32x4 *)&sV[e * VROW + 8 * g8] = vreg[i];
+    }
+  };
+
+  float m = -INFINITY, l = 0.f;
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+
+  const int krow = perm_row(j32);  // key row this lane feeds to the score product
+  load_tile(0);
+  for (int t = 0; t < ntiles; ++t) {
+    store_tile();
+    __syncthreads();
+    if (t + 1 < ntiles) load_tile(t + 1);
+    if (t * kKT <= wave_max_pos) {
+      f32x16 st;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 a = *(const u32x4 *)&sK[krow * KROW + 16 * ks + 8 * h];
+        st = Mfma32<E>::mma(a, qb[ks], st);
+      }
+      // Result item 4a+b is token row 8a+4h+b, i.e. tile token perm(8a+4h+b).
+      float mb = -INFINITY;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int pos = t * kKT + 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
+          float v = st[4 * a + b] * scale_log2;
+          if (pos > qpos) v = -INFINITY;
+          st[4 * a + b] = v;
+          mb = fmaxf(mb, v);
+        }
+      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      const float mnew = fmaxf(m, mb);
+      const float alpha = fast_exp2(m - mnew);
+      m = mnew;
+      float psum = 0.f;
+      u32x4 pb[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float p[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          p[k] = fast_exp2(st[8 * c + k] - mnew);
+          psum += p[k];
+        }
+        pb[c] = u32x4{Mfma32<E>::pack2(p[0], p[1]), Mfma32<E>::pack2(p[2], p[3]),
+                      Mfma32<E>::pack2(p[4], p[5]), Mfma32<E>::pack2(p[6], p[7])};
+      }
+      l = l * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const u32x4 a = *(const u32x4 *)&sV[(32 * dt + j32) * VROW + 16 * c + 8 * h];
+          acc[dt] = Mfma32<E>::mma(a, pb[c], acc[dt]);
+        }
+    }
+    __syncthreads();
+  }
+
+  // Lanes l and l^32 hold the two row halves of the same query column.
+  const float ltot = l + __shfl_xor(l, 32);
+  if (myrow < qlen) {
+    const float inv = 1.f / ltot;
+    uint16_t *orow = out + ((size_t)(qs + myrow) * Hq + hq) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int dim = 32 * dt + 8 * a + 4 * h;
+        const u32x2 pk = {Mfma32<E>::pack2(acc[dt][4 * a] * inv, acc[dt][4 * a + 1] * inv),
+                          Mfma32<E>::pack2(acc[dt][4 * a + 2] * inv, acc[dt][4 * a + 3] * inv)};
+        *(u32x2 *)(orow + dim) = pk;
+      }
+  }
+}
+
+template <typename E, int D, int BS>
+void launch_t(const CacheDesc &c, const PrefillArgs &a, hipStream_t stream) {
+  const int nqt = (a.max_query_len + kQT - 1) / kQT;
+  const int64_t nwork = (int64_t)a.S * a.Hq * nqt;
+  hipLaunchKernelGGL((prefill_kernel<E, D, BS>), dim3((unsigned)nwork), dim3(256), 0, stream,
+                     (uint16_t *)a.out, (const uint16_t *)a.q, (const uint16_t *)c.k,
+                     (const uint16_t *)c.v, a.query_start_loc, a.context_lens, a.block_tables,
+                     c.num_blocks, c.H, a.Hq, a.max_blocks_per_seq, nqt, a.scale * kLog2e);
+}
+
+template <typename E>
+void launch_e(const CacheDesc &c, const PrefillArgs &a, hipStream_t stream) {
+  if (c.D == 64 && c.B == 16) launch_t<E, 64, 16>(c, a, stream);
+  else if (c.D == 64 && c.B == 32) launch_t<E, 64, 32>(c, a, stream);
+  else if (c.D == 128 && c.B == 16) launch_t<E, 128, 16>(c, a, stream);
+  else launch_t<E, 128, 32>(c, a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const CacheDesc &c, const PrefillArgs &a, hipStream_t stream) {
+  if (a.max_query_len == 0 || a.S == 0) return hipSuccess;
+  if (c.dtype == 1) launch_e<F16>(c, a, stream);
+  else launch_e<BF16>(c, a, stream);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,95 @@
+"""Drive a synthetic workload through libpkv: host arrays -> device -> library calls.
+
+Used by the benchmark, the smoke check and the GPU tests.  Every computation
+is a library call; this module only uploads inputs and sequences the calls.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _binding as pkv
+from . import workloads as W
+
+TORCH_DTYPE = {W.F32: torch.float32, W.F16: torch.float16, W.BF16: torch.bfloat16}
+NAN_BITS = {W.F32: None, W.F16: 0x7E00, W.BF16: 0x7FC0}
+
+
+def to_device(bits: np.ndarray, dtype: int, device="cuda") -> torch.Tensor:
+    """Raw-bits numpy array -> device tensor of the cache dtype (same bits)."""
+    if dtype == W.F32:
+        return torch.from_numpy(np.ascontiguousarray(bits)).to(device)
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device)
+    return t.view(TORCH_DTYPE[dtype])
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> raw-bits numpy array (float32 or uint16)."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.float32:
+        return t.numpy()
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def values_of(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def new_cache(wl, device="cuda") -> pkv.PagedKVCache:
+    cache = pkv.PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim,
+                             TORCH_DTYPE[wl.dtype], device=device)
+    if wl.dtype == W.F32:
+        cache.k_pool.fill_(float("nan"))
+        cache.v_pool.fill_(float("nan"))
+    else:
+        cache.k_pool.view(torch.int16).fill_(NAN_BITS[wl.dtype])
+        cache.v_pool.view(torch.int16).fill_(NAN_BITS[wl.dtype])
+    return cache
+
+
+class DeviceWorkload:
+    """Device copies of a workload's integer inputs and query."""
+
+    def __init__(self, wl, device="cuda"):
+        self.wl = wl
+        self.block_tables = torch.from_numpy(wl.block_tables).to(device)
+        self.context_lens = torch.from_numpy(wl.context_lens).to(device)
+        self.q = to_device(wl.q, wl.dtype, device)
+        self.qsl = None if wl.query_start_loc is None else torch.from_numpy(wl.query_start_loc).to(device)
+        self.ops = []
+        for op in wl.setup:
+            self.ops.append(self._dev_op(op, device))
+        self.step = self._dev_op(wl.step_scatter, device)
+
+    def _dev_op(self, op, device):
+        if op.kind == "scatter":
+            return ("scatter", to_device(op.key, self.wl.dtype, device),
+                    to_device(op.value, self.wl.dtype, device), torch.from_numpy(op.slots).to(device))
+        return ("copy", torch.from_numpy(np.ascontiguousarray(op.pairs, dtype=np.int32)).to(device))
+
+    def apply(self, cache, op):
+        if op[0] == "scatter":
+            pkv.reshape_and_cache(cache, op[1], op[2], op[3])
+        else:
+            pkv.copy_blocks(cache, op[1])
+
+    def fill(self, cache):
+        for op in self.ops:
+            self.apply(cache, op)
+
+    def attend(self, cache, partition_size=None, out=None, workspace=None):
+        wl = self.wl
+        if wl.mode == "decode":
+            ps = wl.partition_size if partition_size is None else partition_size
+            return pkv.paged_decode(cache, self.q, self.block_tables, self.context_lens,
+                                    wl.max_context_len, scale=wl.scale, partition_size=ps, out=out,
+                                    workspace=workspace)
+        qlens = np.diff(wl.query_start_loc)
+        return pkv.paged_prefill(cache, self.q, self.qsl, self.context_lens, self.block_tables,
+                                 int(qlens.max()), wl.max_context_len, scale=wl.scale, out=out)
+
+    def run(self, cache, partition_size=None):
+        """Setup, then one step: scatter the new tokens and attend."""
+        self.fill(cache)
+        self.apply(cache, self.step)
+        return self.attend(cache, partition_size=partition_size)

@@ -1,0 +1,27 @@
+"""GPU test helpers: tolerance checks (device runner lives in the package)."""
+from __future__ import annotations
+
+import numpy as np
+
+from paged_kv_cache_92_amd import workloads as W
+from paged_kv_cache_92_amd.runner import (DeviceWorkload, bits_of, new_cache, to_device,  # noqa: F401
+                                          values_of)
+
+
+def tolerance(dtype):
+    return (1e-5, 1e-5) if dtype == W.F32 else (2e-3, 2e-3)
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, dtype, what=""):
+    """|got - ref| <= atol + rtol*|ref| elementwise, with the tolerance of the dtype."""
+    atol, rtol = tolerance(dtype)
+    err = np.abs(got - ref)
+    bound = atol + rtol * np.abs(ref)
+    bad = ~(err <= bound)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        worst = float(np.max(err / bound)) if np.isfinite(err).all() else float("inf")
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} elements out of tolerance "
+                             f"(worst err/bound {worst:.3f}); first at {idx.tolist()} "
+                             f"got {got[tuple(idx[0])]} ref {ref[tuple(idx[0])]}")
+    return float(np.max(err / bound)) if err.size else 0.0

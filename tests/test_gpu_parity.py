@@ -1,0 +1,347 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Scatter, copy and gather are compared bit for bit (whole pools, NaN-filled
+slots included); attention outputs within atol = rtol = 1e-5 (fp32) or 2e-3
+(fp16/bf16), |gpu - ref| <= atol + rtol*|ref|.  Small cases compare every
+output; the full-size workloads compare sampled rows that the oracle computes
+one by one, plus properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_92_amd as pkv
+from paged_kv_cache_92_amd import workloads as W
+from tests.gpu_run import (DeviceWorkload, assert_close, bits_of, new_cache, to_device, values_of)
+from tests.oracle_run import fill_pools, reference_output, sampled_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _pools_equal(cache, k_ref, v_ref, dtype):
+    kd = to_device(k_ref, dtype)
+    vd = to_device(v_ref, dtype)
+    if dtype == W.F32:
+        same_k = torch.equal(cache.k_pool.view(torch.int32), kd.view(torch.int32))
+        same_v = torch.equal(cache.v_pool.view(torch.int32), vd.view(torch.int32))
+    else:
+        same_k = torch.equal(cache.k_pool.view(torch.int16), kd.view(torch.int16))
+        same_v = torch.equal(cache.v_pool.view(torch.int16), vd.view(torch.int16))
+    assert same_k, "K pool differs from the oracle's"
+    assert same_v, "V pool differs from the oracle's"
+
+
+def _check_gather(cache, wl, dw):
+    ctx = wl.context_lens
+    cu = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)
+    k, v = pkv.gather_kv(cache, dw.block_tables, dw.context_lens, torch.from_numpy(cu).cuda(),
+                         int(cu[-1]), wl.max_context_len)
+    ref_k = np.concatenate(wl.seq_tokens_key)
+    ref_v = np.concatenate(wl.seq_tokens_value)
+    assert np.array_equal(bits_of(k).view(np.uint8), ref_k.view(np.uint8)), "gathered K differs"
+    assert np.array_equal(bits_of(v).view(np.uint8), ref_v.view(np.uint8)), "gathered V differs"
+
+
+def _full_check(wl, partition_size=None):
+    """Whole pool + whole output vs the oracle (small workloads)."""
+    k_ref, v_ref = fill_pools(wl)
+    ref = reference_output(wl, k_ref, v_ref)
+    dw = DeviceWorkload(wl)
+    cache = new_cache(wl)
+    out = dw.run(cache, partition_size=partition_size)
+    torch.cuda.synchronize()
+    _pools_equal(cache, k_ref, v_ref, wl.dtype)
+    _check_gather(cache, wl, dw)
+    return assert_close(values_of(out), ref, wl.dtype, wl.name), out, cache, dw
+
+
+# ----------------------------------------------------------------------------
+# Tiny decode, fp32 (4 sequences, contexts 6/17/33/64, 8 heads, d 64, 32-block pool)
+# ----------------------------------------------------------------------------
+
+def test_tiny_decode_f32():
+    wl = W.tiny_decode_f32()
+    worst, *_ = _full_check(wl)
+    print(f"tiny fp32 worst err/bound {worst:.3f}")
+
+
+# ----------------------------------------------------------------------------
+# Small decode variants: every dtype / head_dim / block_size / group / split
+# ----------------------------------------------------------------------------
+
+RAGGED = [1, 15, 16, 17, 31, 32, 33, 100, 255, 256, 257]
+
+
+@pytest.mark.parametrize("dtype", [W.F32, W.F16, W.BF16], ids=["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B", [16, 32])
+@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("part", [0, 64])
+def test_decode_variants(dtype, d, B, G, part):
+    wl = W.make_decode(f"var_{dtype}_{d}_{B}_{G}_{part}", 100 + d + B + G, lambda rng: RAGGED,
+                       Hq=2 * G, Hkv=2, d=d, B=B, dtype=dtype, max_context_len=320,
+                       partition_size=part)
+    _full_check(wl)
+
+
+def test_decode_group_sizes_on_matrix_cores():
+    for G in (2, 8, 16):
+        wl = W.make_decode(f"g{G}", 7 + G, lambda rng: [5, 16, 47, 200], Hq=G, Hkv=1, d=128, B=16,
+                           dtype=W.BF16, max_context_len=256, partition_size=0)
+        _full_check(wl)
+
+
+# ----------------------------------------------------------------------------
+# Exactness pins on the GPU path
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,G", [(W.F32, 1), (W.F16, 1), (W.BF16, 4)])
+def test_single_token_context_returns_its_value(dtype, G):
+    wl = W.make_decode("L1", 3, lambda rng: [1, 1, 1], Hq=2 * G, Hkv=2, d=128, B=16, dtype=dtype,
+                       max_context_len=16)
+    dw = DeviceWorkload(wl)
+    cache = new_cache(wl)
+    out = dw.run(cache)
+    got = bits_of(out)
+    for s in range(wl.S):
+        for hq in range(wl.num_q_heads):
+            assert np.array_equal(got[s, hq], wl.seq_tokens_value[s][0, hq // G])
+
+
+@pytest.mark.parametrize("dtype,G,part", [(W.F16, 1, 0), (W.F16, 1, 32), (W.BF16, 4, 0),
+                                          (W.BF16, 4, 64), (W.F32, 1, 0)])
+def test_dominant_key_selects_its_value_bitwise(dtype, G, part):
+    # One key per sequence has a score margin > 200 in log2 units over every
+    # other key: all other weights underflow to exactly 0 in fp32, so the
+    # output must be that position's value, bit for bit.  This pins the
+    # block-table indexing inside the attention kernels.
+    lens = [3, 40, 77, 130]
+    wl = W.make_decode("dom", 13, lambda rng: lens, Hq=2 * G, Hkv=2, d=128, B=16, dtype=dtype,
+                       max_context_len=160, partition_size=part)
+    one = W.round_to(np.ones(1, np.float32), dtype)[0]
+    zero = W.round_to(np.zeros(1, np.float32), dtype)[0]
+    wl.q[:] = one                       # q = all ones
+    rng = np.random.default_rng(0)
+    chosen = []
+    hist, step = wl.setup[0], wl.step_scatter
+    hist.key[:] = zero
+    step.key[:] = zero
+    cu = np.concatenate([[0], np.cumsum(np.array(lens) - 1)])
+    big = W.round_to(np.full(1, 40.0, np.float32), dtype)[0]   # score 40*128/sqrt(128) ~ 452
+    for s, L in enumerate(lens):
+        j = int(rng.integers(0, L))
+        chosen.append(j)
+        if j == L - 1:
+            step.key[s, :, :] = big
+        else:
+            hist.key[cu[s] + j, :, :] = big
+    wl.seq_tokens_key = []              # keys changed: gather check not used here
+    dw = DeviceWorkload(wl)
+    cache = new_cache(wl)
+    got = bits_of(dw.run(cache))
+    for s, L in enumerate(lens):
+        j = chosen[s]
+        vrow = wl.step_scatter.value[s] if j == L - 1 else hist.value[cu[s] + j]
+        for hq in range(wl.num_q_heads):
+            assert np.array_equal(got[s, hq], vrow[hq // G]), (s, hq, j)
+
+
+@pytest.mark.parametrize("dtype,G", [(W.F16, 1), (W.BF16, 4)])
+def test_physical_permutation_invariance_bitwise(dtype, G):
+    wl = W.make_decode("perm", 17, lambda rng: [9, 64, 150, 311], Hq=2 * G, Hkv=2, d=128, B=16,
+                       dtype=dtype, max_context_len=320, partition_size=64)
+    dw = DeviceWorkload(wl)
+    cache = new_cache(wl)
+    out1 = bits_of(dw.run(cache))
+    pi = np.random.default_rng(5).permutation(wl.num_blocks)
+    cache2 = new_cache(wl)
+    pit = torch.from_numpy(pi).cuda().long()
+    cache2.k_pool[pit] = cache.k_pool
+    cache2.v_pool[pit] = cache.v_pool
+    bt2 = torch.from_numpy(pi[wl.block_tables].astype(np.int32)).cuda()
+    out2 = pkv.paged_decode(cache2, dw.q, bt2, dw.context_lens, wl.max_context_len, scale=wl.scale,
+                            partition_size=64)
+    assert np.array_equal(out1, bits_of(out2))
+
+
+def test_repeated_runs_are_bit_identical():
+    wl = W.gqa_decode_bf16(B=16, S=12, max_context_len=1024,
+                           lengths=lambda rng: rng.integers(1, 1025, size=12), partition_size=128)
+    dw = DeviceWorkload(wl)
+    cache = new_cache(wl)
+    a = bits_of(dw.run(cache))
+    b = bits_of(dw.attend(cache))
+    assert np.array_equal(a, b)
+
+
+def test_empty_calls_are_no_ops():
+    wl = W.tiny_decode_f32()
+    cache = new_cache(wl)
+    before = bits_of(cache.k_pool).copy()
+    empty = torch.empty((0, wl.num_kv_heads, wl.head_dim), device="cuda")
+    pkv.reshape_and_cache(cache, empty, empty, torch.empty(0, dtype=torch.int64, device="cuda"))
+    pkv.copy_blocks(cache, torch.empty((0, 2), dtype=torch.int32, device="cuda"))
+    q = torch.empty((0, wl.num_q_heads, wl.head_dim), device="cuda")
+    out = pkv.paged_decode(cache, q, torch.empty((0, 4), dtype=torch.int32, device="cuda"),
+                           torch.empty(0, dtype=torch.int32, device="cuda"), 64)
+    torch.cuda.synchronize()
+    assert out.shape[0] == 0
+    assert np.array_equal(bits_of(cache.k_pool).view(np.uint32), before.view(np.uint32))
+
+
+def test_negative_slots_are_skipped_and_copy_blocks_copies():
+    wl = W.make_decode("neg", 23, lambda rng: [20, 40], Hq=2, Hkv=2, d=64, B=16, dtype=W.F16,
+                       max_context_len=48)
+    op = wl.step_scatter
+    op.slots[0] = -1
+    wl.setup.append(W.Op("copy", pairs=np.array([[wl.block_tables[1, 0], wl.num_blocks - 2]],
+                                                np.int32)))
+    k_ref, v_ref = fill_pools(wl)
+    dw = DeviceWorkload(wl)
+    cache = new_cache(wl)
+    dw.fill(cache)
+    dw.apply(cache, dw.step)
+    torch.cuda.synchronize()
+    _pools_equal(cache, k_ref, v_ref, wl.dtype)
+
+
+# ----------------------------------------------------------------------------
+# Prefill variants
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16], ids=["f16", "bf16"])
+@pytest.mark.parametrize("d,B,G", [(128, 16, 1), (128, 32, 4), (64, 16, 2), (64, 32, 1)])
+def test_prefill_variants(dtype, d, B, G):
+    # Ragged chunks (1 row up to more than one 128-row tile), histories from 0.
+    hist = np.array([0, 5, 16, 33, 200, 7])
+    chunks = [1, 37, 128, 130, 64, 256]
+    wl = _ragged_prefill(dtype, d, B, G, hist, chunks)
+    assert np.array_equal(wl.query_start_loc, np.concatenate([[0], np.cumsum(chunks)]))
+    _full_check(wl)
+
+
+def _ragged_prefill(dtype, d, B, G, hist, chunks):
+    """Prefill workload whose sequences have different chunk lengths."""
+    from paged_kv_cache_92_amd.block_manager import BlockManager
+    rng = np.random.default_rng(77 + d + B + G)
+    S = len(hist)
+    ctx = (np.asarray(hist) + np.asarray(chunks)).astype(np.int32)
+    need = int(sum(-(-int(L) // B) for L in ctx))
+    nb = need + 8
+    bm = BlockManager(nb, B, free_order=rng.permutation(nb))
+    Hkv, Hq = 2, 2 * G
+    Tq = int(sum(chunks))
+    q = W.round_to(rng.standard_normal((Tq, Hq, d), dtype=np.float32), dtype)
+    seq_k, seq_v, sids = [], [], []
+    hk, hv, hs, sk, sv, ss = [], [], [], [], [], []
+    for s in range(S):
+        L = int(ctx[s])
+        k = W.round_to(rng.standard_normal((L, Hkv, d), dtype=np.float32), dtype)
+        v = W.round_to(rng.standard_normal((L, Hkv, d), dtype=np.float32), dtype)
+        seq_k.append(k); seq_v.append(v)
+        sid = bm.new_sequence(); sids.append(sid)
+        sl, _ = bm.append_tokens(sid, L)
+        h = int(hist[s])
+        hk.append(k[:h]); hv.append(v[:h]); hs.append(sl[:h])
+        sk.append(k[h:]); sv.append(v[h:]); ss.append(sl[h:])
+    mbps = 512 // B
+    bt = bm.block_table_array(sids, mbps, pad=W._poison_block(bm))
+    wl = W.Workload(name="ragged_prefill", mode="prefill", dtype=dtype, num_blocks=nb,
+                    num_kv_heads=Hkv, num_q_heads=Hq, head_dim=d, block_size=B, context_lens=ctx,
+                    block_tables=bt, q=q, scale=W._scale(d),
+                    query_start_loc=np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32),
+                    max_context_len=512)
+    wl.setup.append(W.Op("scatter", key=np.concatenate(hk), value=np.concatenate(hv),
+                         slots=np.concatenate(hs).astype(np.int64)))
+    wl.step_scatter = W.Op("scatter", key=np.concatenate(sk), value=np.concatenate(sv),
+                           slots=np.concatenate(ss).astype(np.int64))
+    wl.seq_tokens_key, wl.seq_tokens_value = seq_k, seq_v
+    return wl
+
+
+def test_prefill_shared_prefix_with_copy_on_write():
+    # Shared prefix of 20 tokens ends inside block 1: the partner's first own
+    # token forces a block copy before its history is written.
+    wl = W.chunked_prefill_bf16(S=4, chunk=96, shared_prefix=20, Hq=4, Hkv=4, max_context_len=512,
+                                hist_fn=lambda rng: np.array([30, 41, 200, 150]))
+    assert wl.info["cow_copies"] == 2
+    _full_check(wl)
+
+
+def test_prefill_single_row_chunks_match_decode():
+    # A chunk of one row is a decode step: both kernels must agree with the oracle.
+    wl = W.make_decode("as_decode", 41, lambda rng: [1, 17, 64, 300], Hq=4, Hkv=4, d=128, B=16,
+                       dtype=W.BF16, max_context_len=320)
+    k_ref, v_ref = fill_pools(wl)
+    ref = reference_output(wl, k_ref, v_ref)
+    dw = DeviceWorkload(wl)
+    cache = new_cache(wl)
+    dec = dw.run(cache)
+    qsl = torch.arange(0, wl.S + 1, dtype=torch.int32, device="cuda")
+    pre = pkv.paged_prefill(cache, dw.q, qsl, dw.context_lens, dw.block_tables, 1,
+                            wl.max_context_len, scale=wl.scale)
+    assert_close(values_of(dec), ref, wl.dtype, "decode")
+    assert_close(values_of(pre), ref, wl.dtype, "prefill")
+
+
+# ----------------------------------------------------------------------------
+# Full-size workloads (launch configuration as benchmarked): whole pools bit
+# for bit, outputs on sampled rows
+# ----------------------------------------------------------------------------
+
+def _sampled_check(wl, rows, partition_size=None):
+    k_ref, v_ref = fill_pools(wl)
+    dw = DeviceWorkload(wl)
+    cache = new_cache(wl)
+    out = dw.run(cache, partition_size=partition_size)
+    torch.cuda.synchronize()
+    _pools_equal(cache, k_ref, v_ref, wl.dtype)
+    ref = sampled_rows(wl, k_ref, v_ref, rows)
+    got = values_of(out)
+    worst = assert_close(got[rows], ref, wl.dtype, wl.name)
+    assert np.isfinite(got).all(), "non-finite output"
+    return worst, out, cache, dw
+
+
+def _decode_rows(wl, n, seed):
+    L = wl.context_lens
+    rng = np.random.default_rng(seed)
+    rows = {int(np.argmin(L)), int(np.argmax(L))}
+    rows.update(int(x) for x in rng.choice(wl.S, size=min(n, wl.S), replace=False))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("part", [0, 256, 512])
+def test_llama13b_decode_full(part):
+    wl = W.llama13b_decode_f16()
+    worst, *_ = _sampled_check(wl, _decode_rows(wl, 8, 1), partition_size=part)
+    print(f"13B decode partition {part}: worst err/bound {worst:.3f}")
+
+
+def test_long_context_split_full():
+    wl = W.long_context_split_f16()
+    worst, out, cache, dw = _sampled_check(wl, _decode_rows(wl, 6, 2))
+    # Property at full size: the split result matches the unsplit one everywhere.
+    whole = dw.attend(cache, partition_size=0)
+    assert_close(values_of(out), values_of(whole).astype(np.float64), wl.dtype, "split vs unsplit")
+    print(f"split decode worst err/bound {worst:.3f}")
+
+
+@pytest.mark.parametrize("B", [16, 32])
+def test_gqa_decode_full(B):
+    wl = W.gqa_decode_bf16(B=B)
+    worst, *_ = _sampled_check(wl, _decode_rows(wl, 14, 3))
+    print(f"GQA B={B} worst err/bound {worst:.3f}")
+
+
+def test_chunked_prefill_full():
+    wl = W.chunked_prefill_bf16()
+    rng = np.random.default_rng(4)
+    qsl = wl.query_start_loc
+    rows = set()
+    for s in range(wl.S):
+        rows.update([int(qsl[s]), int(qsl[s + 1] - 1)])
+        rows.update(int(x) for x in rng.integers(qsl[s], qsl[s + 1], size=4))
+    worst, *_ = _sampled_check(wl, sorted(rows))
+    print(f"prefill worst err/bound {worst:.3f}")
