@@ -134,8 +134,9 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  * weighted values.  Query head hq reads KV head hq / (Hq / Hkv) (grouped
  * heads, [S] section "The Hidden Waste of KV Cache").
  *
- *   out, q            [num_seqs][num_q_heads][head_dim], cache dtype; out is
- *                     rounded once (round to nearest even) from fp32
+ *   out, q            [num_seqs][num_q_heads][head_dim]; q in the cache dtype
+ *   out_dtype         the cache dtype (out rounded once, to nearest even, from
+ *                     the fp32 result) or PKV_F32 (the fp32 result itself)
  *   block_tables      int32 [num_seqs][max_blocks_per_seq]
  *   context_lens      int32 [num_seqs]; L_s counts every cached token,
  *                     including the new one (scatter it first); L_s >= 1
@@ -155,7 +156,8 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  * cores with the group's queries stacked into one tile; other cases run the
  * wavefront dot-product kernel.  Group size must be <= 16.
  */
-pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, const void *q, int32_t num_q_heads,
+pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype, const void *q,
+                            int32_t num_q_heads,
                             const int32_t *block_tables, int32_t max_blocks_per_seq,
                             const int32_t *context_lens, int32_t num_seqs,
                             int32_t max_context_len, float scale, int32_t partition_size,
@@ -171,13 +173,14 @@ pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, const void *q, in
  * at position context_lens[s] - qlen_s + i and attends to positions 0..that
  * position.  Blocks may be shared between sequences (prefix sharing).
  *
- *   out, q            [total_rows][num_q_heads][head_dim], f16 or bf16
+ *   out, q            [total_rows][num_q_heads][head_dim]; cache dtype f16 or
+ *                     bf16; out_dtype as for pkv_paged_decode
  *   query_start_loc   int32 [num_seqs + 1], non-decreasing, starts at 0
  *   context_lens      int32 [num_seqs], >= qlen_s, >= 1
  *   max_query_len     host bound on every qlen_s
  *   max_context_len   host bound on every context_lens[s]
  */
-pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, const void *q,
+pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, int32_t out_dtype, const void *q,
                              int32_t num_q_heads, const int32_t *query_start_loc,
                              const int32_t *context_lens, const int32_t *block_tables,
                              int32_t max_blocks_per_seq, int32_t num_seqs, int32_t max_query_len,

@@ -54,8 +54,8 @@ def lib() -> ctypes.CDLL:
         L.pkv_copy_blocks.argtypes = [cp, vp, i64, vp]
         L.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.pkv_decode_workspace_bytes.restype = sz
-        L.pkv_paged_decode.argtypes = [cp, vp, vp, i32, vp, i32, vp, i32, i32, f32, i32, vp, sz, vp]
-        L.pkv_paged_prefill.argtypes = [cp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, f32, vp]
+        L.pkv_paged_decode.argtypes = [cp, vp, i32, vp, i32, vp, i32, vp, i32, i32, f32, i32, vp, sz, vp]
+        L.pkv_paged_prefill.argtypes = [cp, vp, i32, vp, i32, vp, vp, vp, i32, i32, i32, i32, f32, vp]
         L.pkv_gather_kv.argtypes = [cp, vp, vp, vp, i32, vp, vp, i32, i32, vp]
         L.pkv_validate_host.argtypes = [vp, i64, vp, i32, vp, i32, i64, i32]
         L.pkv_last_error.restype = ctypes.c_char_p
@@ -150,23 +150,37 @@ def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, par
                                                 partition_size))
 
 
+def _out(q, out, out_dtype):
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    elif out_dtype is not None and out.dtype != out_dtype:
+        raise ValueError("out does not have out_dtype")
+    if out.dtype not in _TORCH_TO_PKV:
+        raise ValueError(f"unsupported output dtype {out.dtype}")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have the shape of q")
+    return out
+
+
 def paged_decode(cache: PagedKVCache, q, block_tables, context_lens, max_context_len, scale=None,
-                 partition_size=0, out=None, workspace=None):
-    """Decode attention: q [S][Hq][d] -> out [S][Hq][d] over each sequence's paged cache."""
+                 partition_size=0, out=None, workspace=None, out_dtype=None):
+    """Decode attention: q [S][Hq][d] -> out [S][Hq][d] over each sequence's paged cache.
+
+    ``out_dtype`` is the cache dtype (default: the fp32 result rounded once) or
+    torch.float32 (the fp32 result itself)."""
     S, Hq, dq = q.shape
     if dq != cache.head_dim:
         raise ValueError("q head_dim does not match the cache")
     if scale is None:
         scale = 1.0 / math.sqrt(cache.head_dim)
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out(q, out, out_dtype)
     need = decode_workspace_bytes(S, Hq, cache.head_dim, max_context_len, partition_size)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.nbytes if workspace is not None else 0
     d = cache.desc()
-    _check(lib().pkv_paged_decode(ctypes.byref(d), _dev_ptr(out, "out", cache.dtype),
+    _check(lib().pkv_paged_decode(ctypes.byref(d), _dev_ptr(out, "out"), _TORCH_TO_PKV[out.dtype],
                                   _dev_ptr(q, "q", cache.dtype), Hq,
                                   _dev_ptr(block_tables, "block_tables", torch.int32),
                                   block_tables.shape[1],
@@ -177,18 +191,17 @@ def paged_decode(cache: PagedKVCache, q, block_tables, context_lens, max_context
 
 
 def paged_prefill(cache: PagedKVCache, q, query_start_loc, context_lens, block_tables,
-                  max_query_len, max_context_len, scale=None, out=None):
+                  max_query_len, max_context_len, scale=None, out=None, out_dtype=None):
     """Causal chunked prefill: q [Tq][Hq][d] rows of each sequence's last chunk -> out [Tq][Hq][d]."""
     Tq, Hq, dq = q.shape
     if dq != cache.head_dim:
         raise ValueError("q head_dim does not match the cache")
     if scale is None:
         scale = 1.0 / math.sqrt(cache.head_dim)
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out(q, out, out_dtype)
     S = context_lens.shape[0]
     d = cache.desc()
-    _check(lib().pkv_paged_prefill(ctypes.byref(d), _dev_ptr(out, "out", cache.dtype),
+    _check(lib().pkv_paged_prefill(ctypes.byref(d), _dev_ptr(out, "out"), _TORCH_TO_PKV[out.dtype],
                                    _dev_ptr(q, "q", cache.dtype), Hq,
                                    _dev_ptr(query_start_loc, "query_start_loc", torch.int32),
                                    _dev_ptr(context_lens, "context_lens", torch.int32),

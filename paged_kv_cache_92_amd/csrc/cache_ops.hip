@@ -38,7 +38,10 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict_
   if constexpr (EB == 4) {
     float *vp = (float *)vpool;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vp[vrow + (size_t)i * B] = __builtin_bit_cast(float, vc[i]);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t u = vc[i];
+      vp[vrow + (size_t)i * B] = as_f32(u);
+    }
   } else {
     uint16_t *vp = (uint16_t *)vpool;
 #pragma unroll

@@ -45,7 +45,7 @@ struct ValuCfg {
 
 template <typename E, int D, int BS>
 __global__ __launch_bounds__(256) void decode_valu_kernel(
-    typename E::storage *__restrict__ out, const typename E::storage *__restrict__ q,
+    void *__restrict__ out, int out_f32, const typename E::storage *__restrict__ q,
     const typename E::storage *__restrict__ kpool, const typename E::storage *__restrict__ vpool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
     int64_t num_blocks, int Hkv, int Hq, int mbps, float scale_log2, int part_tokens, int nparts,
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(
     }
     const int np = (L + part_tokens - 1) / part_tokens;
     if (np == 1) {
-      store_elem<E>(out + ((size_t)s * Hq + hq) * D + e, num / den);
+      store_out<E>(out, ((size_t)s * Hq + hq) * D + e, num / den, out_f32);
     } else {
       const size_t pi = ((size_t)s * Hq + hq) * nparts + part;
       ws_acc[pi * D + e] = num;
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(
 // Cross-partition reduce: o = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
 template <typename E, int D>
 __global__ __launch_bounds__(128) void decode_reduce_kernel(
-    typename E::storage *__restrict__ out, const int32_t *__restrict__ context_lens, int Hq,
+    void *__restrict__ out, int out_f32, const int32_t *__restrict__ context_lens, int Hq,
     int mbps_tokens, int part_tokens, int nparts, const float *__restrict__ ws_ml,
     const float *__restrict__ ws_acc) {
   const int hq = blockIdx.x;
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(128) void decode_reduce_kernel(
       num = fmaf(f, ws_acc[(base + p) * D + e], num);
       den = fmaf(f, ws_ml[2 * (base + p) + 1], den);
     }
-    store_elem<E>(out + ((size_t)s * Hq + hq) * D + e, num / den);
+    store_out<E>(out, ((size_t)s * Hq + hq) * D + e, num / den, out_f32);
   }
 }
 
@@ -228,8 +228,8 @@ template <typename E, int D, int BS>
 void launch_valu_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
   using T = typename E::storage;
   const dim3 grid((unsigned)a.num_partitions, (unsigned)a.Hq, (unsigned)a.S);
-  hipLaunchKernelGGL((decode_valu_kernel<E, D, BS>), grid, dim3(256), 0, stream, (T *)a.out,
-                     (const T *)a.q, (const T *)c.k, (const T *)c.v, a.block_tables,
+  hipLaunchKernelGGL((decode_valu_kernel<E, D, BS>), grid, dim3(256), 0, stream, a.out,
+                     (int)a.out_f32, (const T *)a.q, (const T *)c.k, (const T *)c.v, a.block_tables,
                      a.context_lens, c.num_blocks, c.H, a.Hq, a.max_blocks_per_seq,
                      a.scale * kLog2e, a.partition_tokens, a.num_partitions, a.ws_ml, a.ws_acc);
 }
@@ -248,12 +248,12 @@ void launch_reduce_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream
   const dim3 grid((unsigned)a.Hq, (unsigned)a.S);
   const int mt = a.max_blocks_per_seq * c.B;
   if (c.D == 64)
-    hipLaunchKernelGGL((decode_reduce_kernel<E, 64>), grid, dim3(64), 0, stream, (T *)a.out,
-                       a.context_lens, a.Hq, mt, a.partition_tokens, a.num_partitions, a.ws_ml,
+    hipLaunchKernelGGL((decode_reduce_kernel<E, 64>), grid, dim3(64), 0, stream, a.out,
+                       (int)a.out_f32, a.context_lens, a.Hq, mt, a.partition_tokens, a.num_partitions, a.ws_ml,
                        a.ws_acc);
   else
-    hipLaunchKernelGGL((decode_reduce_kernel<E, 128>), grid, dim3(128), 0, stream, (T *)a.out,
-                       a.context_lens, a.Hq, mt, a.partition_tokens, a.num_partitions, a.ws_ml,
+    hipLaunchKernelGGL((decode_reduce_kernel<E, 128>), grid, dim3(128), 0, stream, a.out,
+                       (int)a.out_f32, a.context_lens, a.Hq, mt, a.partition_tokens, a.num_partitions, a.ws_ml,
                        a.ws_acc);
 }
 

@@ -28,8 +28,12 @@ constexpr int kWaves = 4;
 template <typename E>
 struct Mfma;
 
+// kSplitP: the softmax weights P enter the P.V product as hi + lo bf16 pairs
+// (bf16 alone keeps 8 significant bits, too coarse for 2e-3 output accuracy);
+// fp16 keeps 11 bits and goes in as one operand.
 template <>
 struct Mfma<F16> {
+  static constexpr bool kSplitP = false;
   __device__ static f32x4 qk(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -45,6 +49,7 @@ struct Mfma<F16> {
 
 template <>
 struct Mfma<BF16> {
+  static constexpr bool kSplitP = true;
   __device__ static f32x4 qk(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -60,7 +65,7 @@ struct Mfma<BF16> {
 
 template <typename E, int D, int BS>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(
-    uint16_t *__restrict__ out, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kpool,
+    void *__restrict__ out, int out_f32, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kpool,
     const uint16_t *__restrict__ vpool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, int64_t num_blocks, int Hkv, int G, int mbps,
     float scale_log2, int part_tokens, int nparts, float *__restrict__ ws_ml,
@@ -151,7 +156,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     const float alpha = fast_exp2(m - mnew);
     m = mnew;
     float psum = 0.f;
-    u32x2 pb[SUB];
+    u32x2 pb[SUB], pl[SUB];
 #pragma unroll
     for (int sb = 0; sb < SUB; ++sb) {
       float p[4];
@@ -160,7 +165,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
         p[j] = fast_exp2(st[sb][j] - mnew);
         psum += p[j];
       }
-      pb[sb] = u32x2{Mfma<E>::pack2(p[0], p[1]), Mfma<E>::pack2(p[2], p[3])};
+      if constexpr (Mfma<E>::kSplitP) {
+        uint32_t h[4], lo[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) split_bf16(p[j], h[j], lo[j]);
+        pb[sb] = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+        pl[sb] = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+      } else {
+        pb[sb] = u32x2{Mfma<E>::pack2(p[0], p[1]), Mfma<E>::pack2(p[2], p[3])};
+      }
     }
     l = l * alpha + psum;
 #pragma unroll
@@ -182,7 +195,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
 #pragma unroll
     for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt] = Mfma<E>::pv(va[sb][nt], pb[sb], acc[nt]);
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[nt] = Mfma<E>::pv(va[sb][nt], pb[sb], acc[nt]);
+        if constexpr (Mfma<E>::kSplitP) acc[nt] = Mfma<E>::pv(va[sb][nt], pl[sb], acc[nt]);
+      }
   }
 
   // Denominator of head n16: sum over the 4 row groups.
@@ -213,7 +229,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     }
     const int hq = hkv * G + h;
     if (np == 1) {
-      store_elem<E>(out + ((size_t)s * Hq + hq) * D + e, num / den);
+      store_out<E>(out, ((size_t)s * Hq + hq) * D + e, num / den, out_f32);
     } else {
       const size_t pi = ((size_t)s * Hq + hq) * nparts + part;
       ws_acc[pi * D + e] = num;
@@ -228,8 +244,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
 template <typename E, int D, int BS>
 void launch_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
   const dim3 grid((unsigned)a.num_partitions, (unsigned)c.H, (unsigned)a.S);
-  hipLaunchKernelGGL((decode_mfma_kernel<E, D, BS>), grid, dim3(256), 0, stream,
-                     (uint16_t *)a.out, (const uint16_t *)a.q, (const uint16_t *)c.k,
+  hipLaunchKernelGGL((decode_mfma_kernel<E, D, BS>), grid, dim3(256), 0, stream, a.out,
+                     (int)a.out_f32, (const uint16_t *)a.q, (const uint16_t *)c.k,
                      (const uint16_t *)c.v, a.block_tables, a.context_lens, c.num_blocks, c.H,
                      a.Hq / c.H, a.max_blocks_per_seq, a.scale * kLog2e, a.partition_tokens,
                      a.num_partitions, a.ws_ml, a.ws_acc);

@@ -122,7 +122,8 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
   return workspace_bytes(num_seqs, num_q_heads, head_dim, p);
 }
 
-pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, const void *q, int32_t num_q_heads,
+pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype, const void *q,
+                            int32_t num_q_heads,
                             const int32_t *block_tables, int32_t max_blocks_per_seq,
                             const int32_t *context_lens, int32_t num_seqs,
                             int32_t max_context_len, float scale, int32_t partition_size,
@@ -136,6 +137,8 @@ pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, const void *q, in
   if (!out || !q || !block_tables || !context_lens)
     return fail(PKV_ERR_INVALID, "out/q/block_tables/context_lens is NULL");
   if (!aligned16(out) || !aligned16(q)) return fail(PKV_ERR_INVALID, "q/out must be 16-byte aligned");
+  if (out_dtype != c.dtype && out_dtype != PKV_F32)
+    return fail(PKV_ERR_INVALID, "out_dtype must be the cache dtype or PKV_F32");
   if (num_q_heads <= 0 || num_q_heads % c.H != 0)
     return fail(PKV_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                 num_q_heads, c.H);
@@ -160,6 +163,7 @@ pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, const void *q, in
   }
   pkv::DecodeArgs a;
   a.out = out;
+  a.out_f32 = out_dtype == PKV_F32;
   a.q = q;
   a.Hq = num_q_heads;
   a.block_tables = block_tables;
@@ -186,7 +190,7 @@ pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, const void *q, in
   return ok();
 }
 
-pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, const void *q,
+pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, int32_t out_dtype, const void *q,
                              int32_t num_q_heads, const int32_t *query_start_loc,
                              const int32_t *context_lens, const int32_t *block_tables,
                              int32_t max_blocks_per_seq, int32_t num_seqs, int32_t max_query_len,
@@ -200,6 +204,8 @@ pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, const void *q,
   if (!out || !q || !query_start_loc || !context_lens || !block_tables)
     return fail(PKV_ERR_INVALID, "a required pointer is NULL");
   if (!aligned16(out) || !aligned16(q)) return fail(PKV_ERR_INVALID, "q/out must be 16-byte aligned");
+  if (out_dtype != c.dtype && out_dtype != PKV_F32)
+    return fail(PKV_ERR_INVALID, "out_dtype must be the cache dtype or PKV_F32");
   if (num_q_heads <= 0 || num_q_heads % c.H != 0)
     return fail(PKV_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                 num_q_heads, c.H);
@@ -212,6 +218,7 @@ pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, const void *q,
   if (work >= (int64_t)1 << 31) return fail(PKV_ERR_UNSUPPORTED, "launch too large");
   pkv::PrefillArgs a;
   a.out = out;
+  a.out_f32 = out_dtype == PKV_F32;
   a.q = q;
   a.Hq = num_q_heads;
   a.query_start_loc = query_start_loc;

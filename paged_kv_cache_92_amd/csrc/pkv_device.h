@@ -33,6 +33,9 @@ struct BF16 {
 };
 
 // ---- scalar conversions ---------------------------------------------------
+// Bit casts take their source by value: clang has been seen to read element 0
+// when __builtin_bit_cast is applied directly to an ext-vector element.
+__device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
@@ -65,7 +68,10 @@ __device__ __forceinline__ void unpack16(const u32x4 &c, float *out);
 template <>
 __device__ __forceinline__ void unpack16<F32>(const u32x4 &c, float *out) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) out[i] = __builtin_bit_cast(float, c[i]);
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t u = c[i];
+    out[i] = as_f32(u);
+  }
 }
 template <>
 __device__ __forceinline__ void unpack16<F16>(const u32x4 &c, float *out) {
@@ -84,6 +90,13 @@ __device__ __forceinline__ void unpack16<BF16>(const u32x4 &c, float *out) {
   }
 }
 
+// p = hi + lo with hi and lo in bf16: hi = RNE(p), lo = RNE(p - hi), so the
+// pair carries 16 significant bits (|p - hi - lo| <= 2^-17 |p|).
+__device__ __forceinline__ void split_bf16(float p, uint32_t &hi, uint32_t &lo) {
+  hi = f32_to_bf16_bits(p);
+  lo = f32_to_bf16_bits(p - bf16_bits_to_f32(hi));
+}
+
 template <typename E>
 __device__ __forceinline__ void store_elem(typename E::storage *p, float x);
 template <>
@@ -92,6 +105,16 @@ template <>
 __device__ __forceinline__ void store_elem<F16>(uint16_t *p, float x) { *p = f32_to_f16_bits(x); }
 template <>
 __device__ __forceinline__ void store_elem<BF16>(uint16_t *p, float x) { *p = f32_to_bf16_bits(x); }
+
+// Attention outputs go out either in the cache dtype (rounded once, to
+// nearest even, from fp32) or as the fp32 value itself.
+template <typename E>
+__device__ __forceinline__ void store_out(void *out, size_t idx, float x, bool out_f32) {
+  if (out_f32)
+    ((float *)out)[idx] = x;
+  else
+    store_elem<E>((typename E::storage *)out + idx, x);
+}
 
 // ---- wave reductions ---------------------------------------------------------
 // DPP row controls (within rows of 16 lanes): quad_perm [1,0,3,2] and

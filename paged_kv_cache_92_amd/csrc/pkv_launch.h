@@ -20,6 +20,7 @@ struct CacheDesc {
 
 struct DecodeArgs {
   void *out;
+  bool out_f32;           // out is fp32 instead of the cache dtype
   const void *q;
   int Hq;
   const int32_t *block_tables;
@@ -36,6 +37,7 @@ struct DecodeArgs {
 
 struct PrefillArgs {
   void *out;
+  bool out_f32;
   const void *q;
   int Hq;
   const int32_t *query_start_loc;

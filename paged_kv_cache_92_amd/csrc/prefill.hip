@@ -33,8 +33,10 @@ constexpr int kVPad = 8;          // LDS row padding (elements) against bank con
 
 template <typename E>
 struct Mfma32;
+// kSplitP: bf16 softmax weights enter P.V as hi + lo pairs (see split_bf16).
 template <>
 struct Mfma32<F16> {
+  static constexpr bool kSplitP = false;
   __device__ static f32x16 mma(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -45,6 +47,7 @@ struct Mfma32<F16> {
 };
 template <>
 struct Mfma32<BF16> {
+  static constexpr bool kSplitP = true;
   __device__ static f32x16 mma(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -62,7 +65,7 @@ __device__ __forceinline__ int perm_row(int i) {
 
 template <typename E, int D, int BS>
 __global__ __launch_bounds__(256) void prefill_kernel(
-    uint16_t *__restrict__ out, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kpool,
+    void *__restrict__ out, int out_f32, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kpool,
     const uint16_t *__restrict__ vpool, const int32_t *__restrict__ query_start_loc,
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ block_tables,
     int64_t num_blocks, int Hkv, int Hq, int mbps, int nqt, float scale_log2) {
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       const float alpha = fast_exp2(m - mnew);
       m = mnew;
       float psum = 0.f;
-      u32x4 pb[2];
+      u32x4 pb[2], pl[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         float p[8];
@@ -222,8 +225,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(
           p[k] = fast_exp2(st[8 * c + k] - mnew);
           psum += p[k];
         }
-        pb[c] = u32x4{Mfma32<E>::pack2(p[0], p[1]), Mfma32<E>::pack2(p[2], p[3]),
-                      Mfma32<E>::pack2(p[4], p[5]), Mfma32<E>::pack2(p[6], p[7])};
+        if constexpr (Mfma32<E>::kSplitP) {
+          uint32_t h[8], lo[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) split_bf16(p[k], h[k], lo[k]);
+          pb[c] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                        h[6] | (h[7] << 16)};
+          pl[c] = u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16),
+                        lo[6] | (lo[7] << 16)};
+        } else {
+          pb[c] = u32x4{Mfma32<E>::pack2(p[0], p[1]), Mfma32<E>::pack2(p[2], p[3]),
+                        Mfma32<E>::pack2(p[4], p[5]), Mfma32<E>::pack2(p[6], p[7])};
+        }
       }
       l = l * alpha + psum;
 #pragma unroll
@@ -234,6 +247,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         for (int dt = 0; dt < DT; ++dt) {
           const u32x4 a = *(const u32x4 *)&sV[(32 * dt + j32) * VROW + 16 * c + 8 * h];
           acc[dt] = Mfma32<E>::mma(a, pb[c], acc[dt]);
+          if constexpr (Mfma32<E>::kSplitP) acc[dt] = Mfma32<E>::mma(a, pl[c], acc[dt]);
         }
     }
     __syncthreads();
@@ -243,15 +257,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   const float ltot = l + __shfl_xor(l, 32);
   if (myrow < qlen) {
     const float inv = 1.f / ltot;
-    uint16_t *orow = out + ((size_t)(qs + myrow) * Hq + hq) * D;
+    const size_t orow = ((size_t)(qs + myrow) * Hq + hq) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int dim = 32 * dt + 8 * a + 4 * h;
-        const u32x2 pk = {Mfma32<E>::pack2(acc[dt][4 * a] * inv, acc[dt][4 * a + 1] * inv),
-                          Mfma32<E>::pack2(acc[dt][4 * a + 2] * inv, acc[dt][4 * a + 3] * inv)};
-        *(u32x2 *)(orow + dim) = pk;
+        const float o0 = acc[dt][4 * a] * inv, o1 = acc[dt][4 * a + 1] * inv;
+        const float o2 = acc[dt][4 * a + 2] * inv, o3 = acc[dt][4 * a + 3] * inv;
+        if (out_f32) {
+          *(f32x4 *)((float *)out + orow + dim) = f32x4{o0, o1, o2, o3};
+        } else {
+          *(u32x2 *)((uint16_t *)out + orow + dim) =
+              u32x2{Mfma32<E>::pack2(o0, o1), Mfma32<E>::pack2(o2, o3)};
+        }
       }
   }
 }
@@ -261,7 +280,7 @@ void launch_t(const CacheDesc &c, const PrefillArgs &a, hipStream_t stream) {
   const int nqt = (a.max_query_len + kQT - 1) / kQT;
   const int64_t nwork = (int64_t)a.S * a.Hq * nqt;
   hipLaunchKernelGGL((prefill_kernel<E, D, BS>), dim3((unsigned)nwork), dim3(256), 0, stream,
-                     (uint16_t *)a.out, (const uint16_t *)a.q, (const uint16_t *)c.k,
+                     a.out, (int)a.out_f32, (const uint16_t *)a.q, (const uint16_t *)c.k,
                      (const uint16_t *)c.v, a.query_start_loc, a.context_lens, a.block_tables,
                      c.num_blocks, c.H, a.Hq, a.max_blocks_per_seq, nqt, a.scale * kLog2e);
 }

@@ -77,16 +77,17 @@ class DeviceWorkload:
         for op in self.ops:
             self.apply(cache, op)
 
-    def attend(self, cache, partition_size=None, out=None, workspace=None):
+    def attend(self, cache, partition_size=None, out=None, workspace=None, out_dtype=None):
         wl = self.wl
         if wl.mode == "decode":
             ps = wl.partition_size if partition_size is None else partition_size
             return pkv.paged_decode(cache, self.q, self.block_tables, self.context_lens,
                                     wl.max_context_len, scale=wl.scale, partition_size=ps, out=out,
-                                    workspace=workspace)
+                                    workspace=workspace, out_dtype=out_dtype)
         qlens = np.diff(wl.query_start_loc)
         return pkv.paged_prefill(cache, self.q, self.qsl, self.context_lens, self.block_tables,
-                                 int(qlens.max()), wl.max_context_len, scale=wl.scale, out=out)
+                                 int(qlens.max()), wl.max_context_len, scale=wl.scale, out=out,
+                                 out_dtype=out_dtype)
 
     def run(self, cache, partition_size=None):
         """Setup, then one step: scatter the new tokens and attend."""

@@ -25,3 +25,15 @@ def assert_close(got: np.ndarray, ref: np.ndarray, dtype, what=""):
                              f"(worst err/bound {worst:.3f}); first at {idx.tolist()} "
                              f"got {got[tuple(idx[0])]} ref {ref[tuple(idx[0])]}")
     return float(np.max(err / bound)) if err.size else 0.0
+
+
+def assert_rounded(out_dt, out_f32, dtype, what=""):
+    """The cache-dtype output is the fp32 output rounded once to nearest even."""
+    import numpy as np
+    from paged_kv_cache_92_amd.runner import bits_of
+    got = bits_of(out_dt)
+    want = W.round_to(bits_of(out_f32).astype(np.float32), dtype)
+    if not np.array_equal(got.view(np.uint8), want.view(np.uint8)):
+        bad = np.argwhere(got != want)[:5]
+        raise AssertionError(f"{what}: {int((got != want).sum())} outputs are not the rounded fp32 "
+                             f"result; first at {bad.tolist()}")

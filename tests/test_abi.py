@@ -56,35 +56,37 @@ def test_cache_descriptor_checks(kw, status):
     assert lib.pkv_last_error().decode()
 
 
+def _decode(d, out=FAKE, out_dtype=1, q=FAKE, Hq=2, bt=FAKE, mbps=4, ctx=FAKE, S=2, maxlen=64,
+            part=0, ws=None, ws_bytes=0):
+    return pkv.lib().pkv_paged_decode(ctypes.byref(d), out, out_dtype, q, Hq, bt, mbps, ctx, S,
+                                      maxlen, 0.125, part, ws, ws_bytes, None)
+
+
 def test_decode_argument_checks():
     lib = pkv.lib()
     d = _desc()
-    # Hq not a multiple of Hkv
-    assert lib.pkv_paged_decode(ctypes.byref(d), FAKE, FAKE, 3, FAKE, 4, FAKE, 2, 64, 0.125, 0, None, 0, None) == 1
+    assert _decode(d, Hq=3) == 1                      # Hq not a multiple of Hkv
     assert "multiple" in lib.pkv_last_error().decode()
-    # max_context_len beyond the table
-    assert lib.pkv_paged_decode(ctypes.byref(d), FAKE, FAKE, 2, FAKE, 4, FAKE, 2, 65, 0.125, 0, None, 0, None) == 1
-    # partition not a multiple of the block size
-    assert lib.pkv_paged_decode(ctypes.byref(d), FAKE, FAKE, 2, FAKE, 4, FAKE, 2, 64, 0.125, 24, None, 0, None) == 1
-    # split needs a workspace
-    assert lib.pkv_paged_decode(ctypes.byref(d), FAKE, FAKE, 2, FAKE, 4, FAKE, 2, 64, 0.125, 16, None, 0, None) == 3
-    assert lib.pkv_paged_decode(ctypes.byref(d), FAKE, FAKE, 2, FAKE, 4, FAKE, 2, 64, 0.125, 16, FAKE, 8, None) == 3
-    # group size above 16 on the matrix-core path
-    d2 = _desc(num_kv_heads=1)
-    assert lib.pkv_paged_decode(ctypes.byref(d2), FAKE, FAKE, 32, FAKE, 4, FAKE, 2, 64, 0.125, 0, None, 0, None) == 2
-    # null pointers
-    assert lib.pkv_paged_decode(ctypes.byref(d), None, FAKE, 2, FAKE, 4, FAKE, 2, 64, 0.125, 0, None, 0, None) == 1
-    # zero sequences is a no-op
-    assert lib.pkv_paged_decode(ctypes.byref(d), None, None, 2, None, 4, None, 0, 64, 0.125, 0, None, 0, None) == 0
+    assert _decode(d, maxlen=65) == 1                 # max_context_len beyond the table
+    assert _decode(d, part=24) == 1                   # partition not a multiple of the block
+    assert _decode(d, part=16) == 3                   # split needs a workspace
+    assert _decode(d, part=16, ws=FAKE, ws_bytes=8) == 3
+    assert _decode(d, out_dtype=2) == 1               # bf16 output for an fp16 cache
+    assert _decode(_desc(num_kv_heads=1), Hq=32) == 2  # group size above 16 on the matrix cores
+    assert _decode(d, out=None) == 1                  # null pointer
+    assert _decode(d, out=None, q=None, bt=None, ctx=None, S=0) == 0   # zero sequences: no-op
+
+
+def _prefill(d, out_dtype=1, S=1, maxq=16, maxlen=64):
+    return pkv.lib().pkv_paged_prefill(ctypes.byref(d), FAKE, out_dtype, FAKE, 2, FAKE, FAKE, FAKE,
+                                       4, S, maxq, maxlen, 0.125, None)
 
 
 def test_prefill_argument_checks():
-    lib = pkv.lib()
-    d32 = _desc(dtype=0)
-    assert lib.pkv_paged_prefill(ctypes.byref(d32), FAKE, FAKE, 2, FAKE, FAKE, FAKE, 4, 1, 16, 64, 0.125, None) == 2
-    d = _desc()
-    assert lib.pkv_paged_prefill(ctypes.byref(d), FAKE, FAKE, 2, FAKE, FAKE, FAKE, 4, 1, 65, 64, 0.125, None) == 1
-    assert lib.pkv_paged_prefill(ctypes.byref(d), FAKE, FAKE, 2, FAKE, FAKE, FAKE, 4, 0, 16, 64, 0.125, None) == 0
+    assert _prefill(_desc(dtype=0), out_dtype=0) == 2   # fp32 cache: no prefill kernel
+    assert _prefill(_desc(), maxq=65) == 1
+    assert _prefill(_desc(), out_dtype=2) == 1
+    assert _prefill(_desc(), S=0) == 0
 
 
 def test_empty_scatter_and_copy_are_no_ops():

@@ -13,7 +13,8 @@ import torch
 import oracle
 import paged_kv_cache_92_amd as pkv
 from paged_kv_cache_92_amd import workloads as W
-from tests.gpu_run import (DeviceWorkload, assert_close, bits_of, new_cache, to_device, values_of)
+from tests.gpu_run import (DeviceWorkload, assert_close, assert_rounded, bits_of, new_cache,
+                           to_device, values_of)
 from tests.oracle_run import fill_pools, reference_output, sampled_rows
 
 pytestmark = pytest.mark.gpu
@@ -50,10 +51,13 @@ def _full_check(wl, partition_size=None):
     dw = DeviceWorkload(wl)
     cache = new_cache(wl)
     out = dw.run(cache, partition_size=partition_size)
+    o32 = dw.attend(cache, partition_size=partition_size, out_dtype=torch.float32)
     torch.cuda.synchronize()
     _pools_equal(cache, k_ref, v_ref, wl.dtype)
     _check_gather(cache, wl, dw)
-    return assert_close(values_of(out), ref, wl.dtype, wl.name), out, cache, dw
+    worst = assert_close(values_of(o32), ref, wl.dtype, wl.name)
+    assert_rounded(out, o32, wl.dtype, wl.name)
+    return worst, out, cache, dw
 
 
 # ----------------------------------------------------------------------------
@@ -277,10 +281,11 @@ def test_prefill_single_row_chunks_match_decode():
     ref = reference_output(wl, k_ref, v_ref)
     dw = DeviceWorkload(wl)
     cache = new_cache(wl)
-    dec = dw.run(cache)
+    dw.run(cache)
+    dec = dw.attend(cache, out_dtype=torch.float32)
     qsl = torch.arange(0, wl.S + 1, dtype=torch.int32, device="cuda")
     pre = pkv.paged_prefill(cache, dw.q, qsl, dw.context_lens, dw.block_tables, 1,
-                            wl.max_context_len, scale=wl.scale)
+                            wl.max_context_len, scale=wl.scale, out_dtype=torch.float32)
     assert_close(values_of(dec), ref, wl.dtype, "decode")
     assert_close(values_of(pre), ref, wl.dtype, "prefill")
 
@@ -295,12 +300,14 @@ def _sampled_check(wl, rows, partition_size=None):
     dw = DeviceWorkload(wl)
     cache = new_cache(wl)
     out = dw.run(cache, partition_size=partition_size)
+    o32 = dw.attend(cache, partition_size=partition_size, out_dtype=torch.float32)
     torch.cuda.synchronize()
     _pools_equal(cache, k_ref, v_ref, wl.dtype)
     ref = sampled_rows(wl, k_ref, v_ref, rows)
-    got = values_of(out)
+    got = values_of(o32)
     worst = assert_close(got[rows], ref, wl.dtype, wl.name)
     assert np.isfinite(got).all(), "non-finite output"
+    assert_rounded(out, o32, wl.dtype, wl.name)
     return worst, out, cache, dw
 
 
@@ -323,8 +330,9 @@ def test_long_context_split_full():
     wl = W.long_context_split_f16()
     worst, out, cache, dw = _sampled_check(wl, _decode_rows(wl, 6, 2))
     # Property at full size: the split result matches the unsplit one everywhere.
-    whole = dw.attend(cache, partition_size=0)
-    assert_close(values_of(out), values_of(whole).astype(np.float64), wl.dtype, "split vs unsplit")
+    split = dw.attend(cache, out_dtype=torch.float32)
+    whole = dw.attend(cache, partition_size=0, out_dtype=torch.float32)
+    assert_close(values_of(split), values_of(whole), wl.dtype, "split vs unsplit")
     print(f"split decode worst err/bound {worst:.3f}")
 
 
