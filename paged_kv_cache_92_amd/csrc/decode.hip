@@ -21,13 +21,20 @@
 // The 4 waves take interleaved blocks of the partition and are merged
 // through LDS at the end; every score lives in the log2 domain (scores
 // scaled by scale*log2(e)) so that exp2 is a single instruction.
+#include <algorithm>
+
 #include "pkv_device.h"
 #include "pkv_launch.h"
+#include "pkv_plan.h"
 
 namespace pkv {
 namespace {
 
 constexpr int kWaves = 4;
+#ifndef PKV_VALU_NB
+#define PKV_VALU_NB 1
+#endif
+constexpr int kValuNB = PKV_VALU_NB;
 
 template <typename E, int D, int BS>
 struct ValuCfg {
@@ -38,23 +45,33 @@ struct ValuCfg {
   static constexpr int KL = BS / TPL;
   static constexpr int CPR = BS / VEC;
   static constexpr int VL = D * CPR / kWave;
+  // VGPRs holding one block's key and value loads.
+  static constexpr int kLoadRegs = 4 * (KL + VL) * kValuNB;
   static_assert(LPT >= 1 && LPT <= kWave && kWave % LPT == 0, "key row must tile the wave");
   static_assert(BS % TPL == 0, "block must be a whole number of key loads");
   static_assert(CPR >= 1 && kWave % CPR == 0 && (D * CPR) % kWave == 0, "value tile mapping");
 };
 
 template <typename E, int D, int BS>
-__global__ __launch_bounds__(256) void decode_valu_kernel(
-    void *__restrict__ out, int out_f32, const typename E::storage *__restrict__ q,
-    const typename E::storage *__restrict__ kpool, const typename E::storage *__restrict__ vpool,
-    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    int64_t num_blocks, int Hkv, int Hq, int mbps, float scale_log2, int part_tokens, int nparts,
-    float *__restrict__ ws_ml, float *__restrict__ ws_acc) {
+struct ValuLds {
+  float p[kWaves][BS] __attribute__((aligned(16)));
+  float m[kWaves];
+  float l[kWaves];
+  float acc[kWaves][D];
+};
+
+// One work item: partition `part` of sequence s for query head hq.  NB
+// blocks per wave are loaded before any of them is computed.
+template <typename E, int D, int BS, int NB>
+__device__ __forceinline__ void valu_item(
+    ValuLds<E, D, BS> &sh, int s, int part, int hq, void *__restrict__ out, int out_f32,
+    const typename E::storage *__restrict__ q, const typename E::storage *__restrict__ kpool,
+    const typename E::storage *__restrict__ vpool, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ context_lens, int64_t num_blocks, int Hkv, int Hq, int mbps,
+    float scale_log2, int part_tokens, int nparts, float *__restrict__ ws_ml,
+    float *__restrict__ ws_acc) {
   using C = ValuCfg<E, D, BS>;
   using T = typename E::storage;
-  const int part = blockIdx.x;
-  const int hq = blockIdx.y;
-  const int s = blockIdx.z;
   const int L = min(context_lens[s], mbps * BS);
   const int tok0 = part * part_tokens;
   if (tok0 >= L) return;
@@ -69,19 +86,13 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(
   const int r = lane % C::LPT;     // 16-byte chunk of the key row
   const int cp = lane % C::CPR;    // token chunk of the value row
 
-  __shared__ __attribute__((aligned(16))) float lds_p[kWaves][BS];
-  __shared__ float lds_m[kWaves];
-  __shared__ float lds_l[kWaves];
-  __shared__ float lds_acc[kWaves][D];
+  auto &lds_p = sh.p;
+  auto &lds_m = sh.m;
+  auto &lds_l = sh.l;
+  auto &lds_acc = sh.acc;
 
-  // Query slice of this lane, in fp32, pre-multiplied by scale*log2(e).
-  float qv[C::VEC];
-  {
-    const u32x4 qc = load16(q + ((size_t)s * Hq + hq) * D + r * C::VEC);
-    unpack16<E>(qc, qv);
-#pragma unroll
-    for (int i = 0; i < C::VEC; ++i) qv[i] *= scale_log2;
-  }
+  // Query chunk of this lane, kept in its packed input format.
+  const u32x4 qc = load16(q + ((size_t)s * Hq + hq) * D + r * C::VEC);
 
   float m = -INFINITY;
   float l = 0.f;
@@ -90,6 +101,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(
   for (int i = 0; i < C::VL; ++i) acc[i] = 0.f;
 
   const int32_t *bt = block_tables + (size_t)s * mbps;
+  if constexpr (NB == 1) {
   for (int b = w; b < nblk; b += kWaves) {
     const int lb = blk0 + b;
     const int64_t phys = uniform(bt[lb]);
@@ -99,21 +111,16 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(
     u32x4 kr[C::KL];
     u32x4 vr[C::VL];
 #pragma unroll
-    for (int i = 0; i < C::KL; ++i) kr[i] = load16(kt + (i * C::TPL + g) * D + r * C::VEC);
+    for (int i = 0; i < C::KL; ++i) kr[i] = load16_stream(kt + (i * C::TPL + g) * D + r * C::VEC);
 #pragma unroll
-    for (int i = 0; i < C::VL; ++i) vr[i] = load16(vt + (size_t)(kWave * i + lane) * C::VEC);
-
+    for (int i = 0; i < C::VL; ++i) vr[i] = load16_stream(vt + (size_t)(kWave * i + lane) * C::VEC);
+    {
     const int tbase = lb * BS;
     const bool partial = tbase + BS > tok1;
     float sc[C::KL];
 #pragma unroll
     for (int i = 0; i < C::KL; ++i) {
-      float kf[C::VEC];
-      unpack16<E>(kr[i], kf);
-      float d0 = 0.f;
-#pragma unroll
-      for (int e = 0; e < C::VEC; ++e) d0 = fmaf(qv[e], kf[e], d0);
-      sc[i] = group_sum<C::LPT>(d0);
+      sc[i] = group_sum<C::LPT>(dot16<E>(kr[i], qc)) * scale_log2;
       if (partial && tbase + i * C::TPL + g >= tok1) sc[i] = -INFINITY;
     }
     float mb = sc[0];
@@ -127,9 +134,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(
 #pragma unroll
       for (int i = 0; i < C::KL; ++i) lds_p[w][i * C::TPL + g] = fast_exp2(sc[i] - mnew);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     float p[C::VEC];
 #pragma unroll
     for (int i = 0; i < C::VEC; i += 4) {
@@ -146,6 +151,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(
       unpack16<E>(vr[i], vf);
       float a = acc[i] * alpha;
       if (partial) {
+        // Unfilled slots may hold anything (NaN included): their values count as 0.
 #pragma unroll
         for (int e = 0; e < C::VEC; ++e) {
           const float ve = (tbase + cp * C::VEC + e < tok1) ? vf[e] : 0.f;
@@ -158,6 +164,139 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(
       acc[i] = a;
     }
     __builtin_amdgcn_wave_barrier();
+    }
+  }
+  } else {
+  for (int b = w; b < nblk; b += 2 * kWaves) {
+    // Two blocks of this wave in flight at once.
+    const int lb0 = blk0 + b, lb1 = blk0 + b + kWaves;
+    const bool has1 = b + kWaves < nblk;
+    const int64_t phys0 = uniform(bt[lb0]);
+    const int64_t phys1 = has1 ? uniform(bt[lb1]) : phys0;
+    const bool ok0 = phys0 >= 0 && phys0 < num_blocks;
+    const bool ok1 = has1 && phys1 >= 0 && phys1 < num_blocks;
+    const T *kt0 = kpool + ((size_t)(ok0 ? phys0 : 0) * Hkv + hkv) * (BS * D);
+    const T *vt0 = vpool + ((size_t)(ok0 ? phys0 : 0) * Hkv + hkv) * (D * BS);
+    const T *kt1 = kpool + ((size_t)(ok1 ? phys1 : 0) * Hkv + hkv) * (BS * D);
+    const T *vt1 = vpool + ((size_t)(ok1 ? phys1 : 0) * Hkv + hkv) * (D * BS);
+    u32x4 kr0[C::KL], vr0[C::VL], kr1[C::KL], vr1[C::VL];
+    if (ok0) {
+#pragma unroll
+      for (int i = 0; i < C::KL; ++i) kr0[i] = load16_stream(kt0 + (i * C::TPL + g) * D + r * C::VEC);
+#pragma unroll
+      for (int i = 0; i < C::VL; ++i) vr0[i] = load16_stream(vt0 + (size_t)(kWave * i + lane) * C::VEC);
+    }
+    if (ok1) {
+#pragma unroll
+      for (int i = 0; i < C::KL; ++i) kr1[i] = load16_stream(kt1 + (i * C::TPL + g) * D + r * C::VEC);
+#pragma unroll
+      for (int i = 0; i < C::VL; ++i) vr1[i] = load16_stream(vt1 + (size_t)(kWave * i + lane) * C::VEC);
+    }
+    if (ok0)
+    {
+    const int tbase = lb0 * BS;
+    const bool partial = tbase + BS > tok1;
+    float sc[C::KL];
+#pragma unroll
+    for (int i = 0; i < C::KL; ++i) {
+      sc[i] = group_sum<C::LPT>(dot16<E>(kr0[i], qc)) * scale_log2;
+      if (partial && tbase + i * C::TPL + g >= tok1) sc[i] = -INFINITY;
+    }
+    float mb = sc[0];
+#pragma unroll
+    for (int i = 1; i < C::KL; ++i) mb = fmaxf(mb, sc[i]);
+    mb = xor_max<C::LPT, kWave>(mb);
+    const float mnew = fmaxf(m, mb);
+    const float alpha = fast_exp2(m - mnew);
+    m = mnew;
+    if (r == 0) {
+#pragma unroll
+      for (int i = 0; i < C::KL; ++i) lds_p[w][i * C::TPL + g] = fast_exp2(sc[i] - mnew);
+    }
+    __builtin_amdgcn_wave_barrier();
+    float p[C::VEC];
+#pragma unroll
+    for (int i = 0; i < C::VEC; i += 4) {
+      const f32x4 pv = *(const f32x4 *)&lds_p[w][cp * C::VEC + i];
+      p[i] = pv[0]; p[i + 1] = pv[1]; p[i + 2] = pv[2]; p[i + 3] = pv[3];
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < C::VEC; ++e) psum += p[e];
+    l = l * alpha + psum;
+#pragma unroll
+    for (int i = 0; i < C::VL; ++i) {
+      float vf[C::VEC];
+      unpack16<E>(vr0[i], vf);
+      float a = acc[i] * alpha;
+      if (partial) {
+        // Unfilled slots may hold anything (NaN included): their values count as 0.
+#pragma unroll
+        for (int e = 0; e < C::VEC; ++e) {
+          const float ve = (tbase + cp * C::VEC + e < tok1) ? vf[e] : 0.f;
+          a = fmaf(p[e], ve, a);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < C::VEC; ++e) a = fmaf(p[e], vf[e], a);
+      }
+      acc[i] = a;
+    }
+    __builtin_amdgcn_wave_barrier();
+    }
+    if (ok1)
+    {
+    const int tbase = lb1 * BS;
+    const bool partial = tbase + BS > tok1;
+    float sc[C::KL];
+#pragma unroll
+    for (int i = 0; i < C::KL; ++i) {
+      sc[i] = group_sum<C::LPT>(dot16<E>(kr1[i], qc)) * scale_log2;
+      if (partial && tbase + i * C::TPL + g >= tok1) sc[i] = -INFINITY;
+    }
+    float mb = sc[0];
+#pragma unroll
+    for (int i = 1; i < C::KL; ++i) mb = fmaxf(mb, sc[i]);
+    mb = xor_max<C::LPT, kWave>(mb);
+    const float mnew = fmaxf(m, mb);
+    const float alpha = fast_exp2(m - mnew);
+    m = mnew;
+    if (r == 0) {
+#pragma unroll
+      for (int i = 0; i < C::KL; ++i) lds_p[w][i * C::TPL + g] = fast_exp2(sc[i] - mnew);
+    }
+    __builtin_amdgcn_wave_barrier();
+    float p[C::VEC];
+#pragma unroll
+    for (int i = 0; i < C::VEC; i += 4) {
+      const f32x4 pv = *(const f32x4 *)&lds_p[w][cp * C::VEC + i];
+      p[i] = pv[0]; p[i + 1] = pv[1]; p[i + 2] = pv[2]; p[i + 3] = pv[3];
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < C::VEC; ++e) psum += p[e];
+    l = l * alpha + psum;
+#pragma unroll
+    for (int i = 0; i < C::VL; ++i) {
+      float vf[C::VEC];
+      unpack16<E>(vr1[i], vf);
+      float a = acc[i] * alpha;
+      if (partial) {
+        // Unfilled slots may hold anything (NaN included): their values count as 0.
+#pragma unroll
+        for (int e = 0; e < C::VEC; ++e) {
+          const float ve = (tbase + cp * C::VEC + e < tok1) ? vf[e] : 0.f;
+          a = fmaf(p[e], ve, a);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < C::VEC; ++e) a = fmaf(p[e], vf[e], a);
+      }
+      acc[i] = a;
+    }
+    __builtin_amdgcn_wave_barrier();
+    }
+  }
   }
 
   // Sum each dimension over the CPR lanes that share it, and l over the same lanes.
@@ -185,7 +324,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(
       num = fmaf(f, lds_acc[k][e], num);
       den = fmaf(f, lds_l[k], den);
     }
-    const int np = (L + part_tokens - 1) / part_tokens;
+    const int np = num_partitions_of(L, part_tokens);
     if (np == 1) {
       store_out<E>(out, ((size_t)s * Hq + hq) * D + e, num / den, out_f32);
     } else {
@@ -196,6 +335,41 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(
         ws_ml[2 * pi + 1] = den;
       }
     }
+  }
+}
+
+// PLAN: persistent grid over the compact partition plan (S <= kPlanMaxSeqs);
+// otherwise one workgroup per (partition, query head, sequence) grid cell.
+template <typename E, int D, int BS, bool PLAN>
+// The grid path (one item per workgroup) with at most 32 VGPRs of loads per
+// block fits 64 VGPRs, i.e. 8 waves per SIMD, without spills; other variants
+// keep the compiler's choice.
+__global__ __launch_bounds__(256, (!PLAN && ValuCfg<E, D, BS>::kLoadRegs <= 32) ? 8 : 1) void
+decode_valu_kernel(
+    void *__restrict__ out, int out_f32, const typename E::storage *__restrict__ q,
+    const typename E::storage *__restrict__ kpool, const typename E::storage *__restrict__ vpool,
+    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
+    int64_t num_blocks, int Hkv, int Hq, int S, int mbps, float scale_log2, int part_tokens,
+    int nparts, float *__restrict__ ws_ml, float *__restrict__ ws_acc) {
+  __shared__ ValuLds<E, D, BS> sh;
+  if constexpr (PLAN) {
+    extern __shared__ int plan[];
+    __shared__ int scan[16];
+    const int total = build_plan(plan, scan, context_lens, S, mbps * BS, part_tokens);
+    const int nitems = total * Hq;
+    for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
+      const int hq = it % Hq;
+      const int j = it / Hq;
+      const int s = plan_sequence(plan, S, j);
+      valu_item<E, D, BS, kValuNB>(sh, s, j - plan[s], hq, out, out_f32, q, kpool, vpool, block_tables,
+                          context_lens, num_blocks, Hkv, Hq, mbps, scale_log2, part_tokens, nparts,
+                          ws_ml, ws_acc);
+      __syncthreads();  // the merge buffers are reused by the next item
+    }
+  } else {
+    valu_item<E, D, BS, kValuNB>(sh, blockIdx.z, blockIdx.x, blockIdx.y, out, out_f32, q, kpool, vpool,
+                        block_tables, context_lens, num_blocks, Hkv, Hq, mbps, scale_log2,
+                        part_tokens, nparts, ws_ml, ws_acc);
   }
 }
 
@@ -227,11 +401,30 @@ __global__ __launch_bounds__(128) void decode_reduce_kernel(
 template <typename E, int D, int BS>
 void launch_valu_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
   using T = typename E::storage;
-  const dim3 grid((unsigned)a.num_partitions, (unsigned)a.Hq, (unsigned)a.S);
-  hipLaunchKernelGGL((decode_valu_kernel<E, D, BS>), grid, dim3(256), 0, stream, a.out,
-                     (int)a.out_f32, (const T *)a.q, (const T *)c.k, (const T *)c.v, a.block_tables,
-                     a.context_lens, c.num_blocks, c.H, a.Hq, a.max_blocks_per_seq,
-                     a.scale * kLog2e, a.partition_tokens, a.num_partitions, a.ws_ml, a.ws_acc);
+  const float sl = a.scale * kLog2e;
+  // Persistent plan grid when sequences split into several partitions (it
+  // launches nothing for empty partitions); without a split every grid cell
+  // has work and the hardware scheduler balances the uneven lengths itself.
+#ifndef PKV_GRID_FACTOR
+#define PKV_GRID_FACTOR 4
+#endif
+  if (a.num_partitions > 1 && a.S <= kPlanMaxSeqs) {
+    auto kern = decode_valu_kernel<E, D, BS, true>;
+    const size_t lds = sizeof(int) * (a.S + 1);
+    const int64_t cells = (int64_t)a.S * a.num_partitions * a.Hq;
+    const int grid = (int)std::min<int64_t>(cells, PKV_GRID_FACTOR * (int64_t)resident_workgroups((const void *)kern, 256, lds));
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, a.out, (int)a.out_f32,
+                       (const T *)a.q, (const T *)c.k, (const T *)c.v, a.block_tables,
+                       a.context_lens, c.num_blocks, c.H, a.Hq, a.S, a.max_blocks_per_seq, sl,
+                       a.partition_tokens, a.num_partitions, a.ws_ml, a.ws_acc);
+  } else {
+    const dim3 grid((unsigned)a.num_partitions, (unsigned)a.Hq, (unsigned)a.S);
+    hipLaunchKernelGGL((decode_valu_kernel<E, D, BS, false>), grid, dim3(256), 0, stream, a.out,
+                       (int)a.out_f32, (const T *)a.q, (const T *)c.k, (const T *)c.v,
+                       a.block_tables, a.context_lens, c.num_blocks, c.H, a.Hq, a.S,
+                       a.max_blocks_per_seq, sl, a.partition_tokens, a.num_partitions, a.ws_ml,
+                       a.ws_acc);
+  }
 }
 
 template <typename E>
@@ -244,7 +437,6 @@ void launch_valu_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) 
 
 template <typename E>
 void launch_reduce_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
-  using T = typename E::storage;
   const dim3 grid((unsigned)a.Hq, (unsigned)a.S);
   const int mt = a.max_blocks_per_seq * c.B;
   if (c.D == 64)

@@ -17,8 +17,11 @@
 // bytes per lane).  The running max and denominator are per head, i.e. per
 // lane column, as in the block-wise walk of "vLLM — KV Cache와 PagedAttention
 // 완전 해부" (hrletsgo.me), "부록".  Scores are kept in the log2 domain.
+#include <algorithm>
+
 #include "pkv_device.h"
 #include "pkv_launch.h"
+#include "pkv_plan.h"
 
 namespace pkv {
 namespace {
@@ -63,9 +66,12 @@ struct Mfma<BF16> {
   }
 };
 
+// One work item: partition `part` of sequence s for the G query heads of KV
+// head hkv.  `lds_dyn` holds the cross-wave merge buffers.
 template <typename E, int D, int BS>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(
-    void *__restrict__ out, int out_f32, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kpool,
+__device__ __forceinline__ void mfma_item(
+    float *lds_dyn, int s, int part, int hkv, void *__restrict__ out, int out_f32,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kpool,
     const uint16_t *__restrict__ vpool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, int64_t num_blocks, int Hkv, int G, int mbps,
     float scale_log2, int part_tokens, int nparts, float *__restrict__ ws_ml,
@@ -73,9 +79,6 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   constexpr int KS = D / 32;    // k-steps of the score product
   constexpr int NT = D / 16;    // 16-dimension tiles of the output
   constexpr int SUB = BS / 16;  // 16-token sub-tiles per block
-  const int part = blockIdx.x;
-  const int hkv = blockIdx.y;
-  const int s = blockIdx.z;
   const int L = min(context_lens[s], mbps * BS);
   const int tok0 = part * part_tokens;
   if (tok0 >= L) return;
@@ -89,9 +92,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   const int n16 = lane & 15;   // query head (column) / token row / dimension row
   const int g4 = lane >> 4;    // k-group of the operands, row group of the result
 
-  __shared__ float lds_m[kWaves][16];
-  __shared__ float lds_l[kWaves][16];
-  __shared__ float lds_acc[kWaves][16][D + 1];
+  // Cross-wave merge buffers, sized for the G live heads:
+  // m[kWaves][16], l[kWaves][16], acc[kWaves][G][D + 1].
+  float *lds_m = lds_dyn;
+  float *lds_l = lds_dyn + kWaves * 16;
+  float *lds_acc = lds_dyn + 2 * kWaves * 16;
+  auto acc_at = [&](int wv, int h, int e) -> float & { return lds_acc[(wv * G + h) * (D + 1) + e]; };
 
   // Q^T operand: head n16 of the group (zero past G), dimensions 32*ks + 8*g4 .. +8.
   u32x4 qb[KS];
@@ -123,12 +129,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        ka[sb][ks] = load16(kt + (16 * sb + n16) * D + 32 * ks + 8 * g4);
+        ka[sb][ks] = load16_stream(kt + (16 * sb + n16) * D + 32 * ks + 8 * g4);
 #pragma unroll
     for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        va[sb][nt] = load8(vt + (16 * nt + n16) * BS + 16 * sb + 4 * g4);
+        va[sb][nt] = load8_stream(vt + (16 * nt + n16) * BS + 16 * sb + 4 * g4);
 
     const int tbase = lb * BS;
     const bool partial = tbase + BS > tok1;
@@ -204,28 +210,30 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   // Denominator of head n16: sum over the 4 row groups.
   l = xor_sum<16, kWave>(l);
   if (g4 == 0) {
-    lds_m[w][n16] = m;
-    lds_l[w][n16] = l;
+    lds_m[w * 16 + n16] = m;
+    lds_l[w * 16 + n16] = l;
   }
+  if (n16 < G) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lds_acc[w][n16][16 * nt + 4 * g4 + j] = acc[nt][j];
+      for (int j = 0; j < 4; ++j) acc_at(w, n16, 16 * nt + 4 * g4 + j) = acc[nt][j];
+  }
   __syncthreads();
 
-  const int np = (L + part_tokens - 1) / part_tokens;
+  const int np = num_partitions_of(L, part_tokens);
   for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
     const int h = idx / D;
     const int e = idx - h * D;
-    float M = lds_m[0][h];
+    float M = lds_m[h];
 #pragma unroll
-    for (int k = 1; k < kWaves; ++k) M = fmaxf(M, lds_m[k][h]);
+    for (int k = 1; k < kWaves; ++k) M = fmaxf(M, lds_m[k * 16 + h]);
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int k = 0; k < kWaves; ++k) {
-      const float f = fast_exp2(lds_m[k][h] - M);
-      num = fmaf(f, lds_acc[k][h][e], num);
-      den = fmaf(f, lds_l[k][h], den);
+      const float f = fast_exp2(lds_m[k * 16 + h] - M);
+      num = fmaf(f, acc_at(k, h, e), num);
+      den = fmaf(f, lds_l[k * 16 + h], den);
     }
     const int hq = hkv * G + h;
     if (np == 1) {
@@ -241,14 +249,71 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   }
 }
 
+// PLAN: persistent grid over the compact partition plan (S <= kPlanMaxSeqs);
+// otherwise one workgroup per (partition, KV head, sequence) grid cell.
+// Dynamic LDS: [plan: S + 1 ints, padded to 16 bytes][merge buffers].
+template <typename E, int D, int BS, bool PLAN>
+#ifndef PKV_MFMA_MIN_WAVES
+#define PKV_MFMA_MIN_WAVES 4
+#endif
+__global__ __launch_bounds__(256, PKV_MFMA_MIN_WAVES) void decode_mfma_kernel(
+    void *__restrict__ out, int out_f32, const uint16_t *__restrict__ q,
+    const uint16_t *__restrict__ kpool, const uint16_t *__restrict__ vpool,
+    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
+    int64_t num_blocks, int Hkv, int G, int S, int mbps, float scale_log2, int part_tokens,
+    int nparts, float *__restrict__ ws_ml, float *__restrict__ ws_acc) {
+  extern __shared__ __attribute__((aligned(16))) int dyn[];
+  if constexpr (PLAN) {
+    __shared__ int scan[16];
+    int *plan = dyn;
+    float *merge = (float *)(dyn + ((S + 1 + 3) & ~3));
+    const int total = build_plan(plan, scan, context_lens, S, mbps * BS, part_tokens);
+    const int nitems = total * Hkv;
+    for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
+      const int hkv = it % Hkv;
+      const int j = it / Hkv;
+      const int s = plan_sequence(plan, S, j);
+      mfma_item<E, D, BS>(merge, s, j - plan[s], hkv, out, out_f32, q, kpool, vpool,
+                          block_tables, context_lens, num_blocks, Hkv, G, mbps, scale_log2,
+                          part_tokens, nparts, ws_ml, ws_acc);
+      __syncthreads();  // the merge buffers are reused by the next item
+    }
+  } else {
+    mfma_item<E, D, BS>((float *)dyn, blockIdx.z, blockIdx.x, blockIdx.y, out, out_f32, q, kpool,
+                        vpool, block_tables, context_lens, num_blocks, Hkv, G, mbps, scale_log2,
+                        part_tokens, nparts, ws_ml, ws_acc);
+  }
+}
+
 template <typename E, int D, int BS>
 void launch_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.num_partitions, (unsigned)c.H, (unsigned)a.S);
-  hipLaunchKernelGGL((decode_mfma_kernel<E, D, BS>), grid, dim3(256), 0, stream, a.out,
-                     (int)a.out_f32, (const uint16_t *)a.q, (const uint16_t *)c.k,
-                     (const uint16_t *)c.v, a.block_tables, a.context_lens, c.num_blocks, c.H,
-                     a.Hq / c.H, a.max_blocks_per_seq, a.scale * kLog2e, a.partition_tokens,
-                     a.num_partitions, a.ws_ml, a.ws_acc);
+  const int G = a.Hq / c.H;
+  const size_t merge = sizeof(float) * (2 * kWaves * 16 + (size_t)kWaves * G * (D + 1));
+  const float sl = a.scale * kLog2e;
+  // Persistent plan grid when sequences split into several partitions (it
+  // launches nothing for empty partitions); without a split every grid cell
+  // has work and the hardware scheduler balances the uneven lengths itself.
+#ifndef PKV_GRID_FACTOR
+#define PKV_GRID_FACTOR 4
+#endif
+  if (a.num_partitions > 1 && a.S <= kPlanMaxSeqs) {
+    auto kern = decode_mfma_kernel<E, D, BS, true>;
+    const size_t lds = sizeof(int) * (size_t)((a.S + 1 + 3) & ~3) + merge;
+    const int64_t cells = (int64_t)a.S * a.num_partitions * c.H;
+    const int grid = (int)std::min<int64_t>(cells, PKV_GRID_FACTOR * (int64_t)resident_workgroups((const void *)kern, 256, lds));
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, a.out, (int)a.out_f32,
+                       (const uint16_t *)a.q, (const uint16_t *)c.k, (const uint16_t *)c.v,
+                       a.block_tables, a.context_lens, c.num_blocks, c.H, G, a.S,
+                       a.max_blocks_per_seq, sl, a.partition_tokens, a.num_partitions, a.ws_ml,
+                       a.ws_acc);
+  } else {
+    const dim3 grid((unsigned)a.num_partitions, (unsigned)c.H, (unsigned)a.S);
+    hipLaunchKernelGGL((decode_mfma_kernel<E, D, BS, false>), grid, dim3(256), merge, stream, a.out,
+                       (int)a.out_f32, (const uint16_t *)a.q, (const uint16_t *)c.k,
+                       (const uint16_t *)c.v, a.block_tables, a.context_lens, c.num_blocks, c.H, G,
+                       a.S, a.max_blocks_per_seq, sl, a.partition_tokens, a.num_partitions, a.ws_ml,
+                       a.ws_acc);
+  }
 }
 
 template <typename E>

@@ -5,6 +5,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <map>
+#include <mutex>
+#include <tuple>
 #include <unordered_set>
 #include <vector>
 
@@ -82,6 +85,32 @@ size_t workspace_bytes(int S, int Hq, int D, const Partitioning &p) {
 }
 
 }  // namespace
+
+namespace pkv {
+
+int resident_workgroups(const void *kernel, int threads, size_t lds_bytes) {
+  static std::mutex mu;
+  static std::map<std::tuple<const void *, size_t, int>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  const size_t lds_key = (lds_bytes + 1023) / 1024;
+  const auto key = std::make_tuple(kernel, lds_key, dev);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds_key * 1024) !=
+          hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 1;
+  const int n = per_cu * cus;
+  cache[key] = n;
+  return n;
+}
+
+}  // namespace pkv
 
 extern "C" {
 

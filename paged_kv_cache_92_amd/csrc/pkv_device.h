@@ -90,6 +90,45 @@ __device__ __forceinline__ void unpack16<BF16>(const u32x4 &c, float *out) {
   }
 }
 
+// q.k over one 16-byte chunk, accumulated in fp32.  For 16-bit inputs each
+// pair product is exact in fp32 (v_dot2_f32_f16 / v_dot2_f32_bf16); q is the
+// matching chunk of the query in the same packed format.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <typename E>
+__device__ __forceinline__ float dot16(const u32x4 &k, const u32x4 &q);
+template <>
+__device__ __forceinline__ float dot16<F32>(const u32x4 &k, const u32x4 &q) {
+  float d = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t ku = k[i], qu = q[i];
+    d = fmaf(as_f32(qu), as_f32(ku), d);
+  }
+  return d;
+}
+template <>
+__device__ __forceinline__ float dot16<F16>(const u32x4 &k, const u32x4 &q) {
+  float d = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t ku = k[i], qu = q[i];
+    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qu), __builtin_bit_cast(f16x2, ku), d, false);
+  }
+  return d;
+}
+template <>
+__device__ __forceinline__ float dot16<BF16>(const u32x4 &k, const u32x4 &q) {
+  float d = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t ku = k[i], qu = q[i];
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qu), __builtin_bit_cast(bf16x2, ku),
+                                        d, false);
+  }
+  return d;
+}
+
 // p = hi + lo with hi and lo in bf16: hi = RNE(p), lo = RNE(p - hi), so the
 // pair carries 16 significant bits (|p - hi - lo| <= 2^-17 |p|).
 __device__ __forceinline__ void split_bf16(float p, uint32_t &hi, uint32_t &lo) {
@@ -162,5 +201,13 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 
 __device__ __forceinline__ u32x4 load16(const void *p) { return *(const u32x4 *)p; }
 __device__ __forceinline__ u32x2 load8(const void *p) { return *(const u32x2 *)p; }
+// Streaming loads for data read once per launch (the decode kernels' key and
+// value tiles): the non-temporal hint keeps them from displacing reusable lines.
+__device__ __forceinline__ u32x4 load16_stream(const void *p) {
+  return __builtin_nontemporal_load((const u32x4 *)p);
+}
+__device__ __forceinline__ u32x2 load8_stream(const void *p) {
+  return __builtin_nontemporal_load((const u32x2 *)p);
+}
 
 }  // namespace pkv

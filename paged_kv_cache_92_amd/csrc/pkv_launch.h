@@ -50,6 +50,11 @@ struct PrefillArgs {
   float scale;
 };
 
+// Workgroups of `kernel` (with `threads` threads and `lds_bytes` of dynamic
+// LDS) that the current device keeps resident at once: the size of a
+// persistent grid.  Cached per (kernel, LDS size, device).
+int resident_workgroups(const void *kernel, int threads, size_t lds_bytes);
+
 hipError_t launch_reshape_and_cache(const CacheDesc &c, const void *key, const void *value,
                                     const int64_t *slots, int64_t T, hipStream_t stream);
 hipError_t launch_copy_blocks(const CacheDesc &c, const int32_t *pairs, int64_t n,

@@ -299,7 +299,7 @@ def tiny_decode_f32():
                        dtype=F32, max_context_len=64, num_blocks=32)
 
 
-def llama13b_decode_f16(S=64, lo=128, hi=2048, seed=2, partition_size=0):
+def llama13b_decode_f16(S=64, lo=128, hi=2048, seed=2, partition_size=512):
     """LLaMA-2-13B-shaped single-layer decode: 40 heads, d 128, B 16, fp16, L ~ U[lo, hi]."""
     return make_decode(f"llama13b_decode_f16_S{S}", seed,
                        lambda rng: rng.integers(lo, hi + 1, size=S), Hq=40, Hkv=40, d=128, B=16,
@@ -320,7 +320,7 @@ def lognormal_lengths(S, median=1024, sigma=1.0, lo=16, hi=8192):
     return draw
 
 
-def gqa_decode_bf16(B=16, S=256, seed=4, max_context_len=8192, lengths=None, partition_size=512):
+def gqa_decode_bf16(B=16, S=256, seed=4, max_context_len=8192, lengths=None, partition_size=1024):
     """GQA decode: 32 query heads over 8 KV heads, d 128, bf16, lognormal(median 1024) lengths."""
     fn = lengths or lognormal_lengths(S, hi=max_context_len)
     return make_decode(f"gqa_decode_bf16_B{B}_S{S}", seed, fn, Hq=32, Hkv=8, d=128, B=B,

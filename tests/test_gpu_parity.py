@@ -353,3 +353,15 @@ def test_chunked_prefill_full():
         rows.update(int(x) for x in rng.integers(qsl[s], qsl[s + 1], size=4))
     worst, *_ = _sampled_check(wl, sorted(rows))
     print(f"prefill worst err/bound {worst:.3f}")
+
+
+@pytest.mark.parametrize("dtype,G,part", [(W.F16, 1, 0), (W.F16, 1, 16), (W.BF16, 2, 32)])
+def test_decode_beyond_plan_limit_uses_grid_path(dtype, G, part):
+    # More sequences than the in-LDS partition plan holds (8192): the kernels
+    # run one workgroup per (partition, head, sequence) cell instead.
+    S = 8200
+    wl = W.make_decode(f"many_{G}_{part}", 61 + G + part,
+                       lambda rng: rng.integers(1, 49, size=S), Hq=2 * G, Hkv=2, d=64, B=16,
+                       dtype=dtype, max_context_len=48, partition_size=part)
+    _full_check(wl)
+
