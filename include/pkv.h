@@ -141,7 +141,8 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   context_lens      int32 [num_seqs]; L_s counts every cached token,
  *                     including the new one (scatter it first); L_s >= 1
  *   max_context_len   host bound on every L_s (sizes the launch)
- *   scale             the softmax scale, normally 1/sqrt(head_dim) in fp32
+ *   scale             the softmax scale, normally 1/sqrt(head_dim) in fp32;
+ *                     must be positive and finite
  *   partition_size    0: one workgroup pass over each whole sequence;
  *                     otherwise a multiple of block_size: each sequence is
  *                     split into partitions of that many tokens, each

@@ -1,5 +1,7 @@
 // Cache maintenance kernels: slot scatter, copy-on-write block copy, and the
 // debug gather.  All are pure data movement (bit-exact, no conversion).
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -7,48 +9,71 @@ namespace pkv {
 namespace {
 
 // Slot scatter ("reshape_and_cache", [vLLM] PagedAttention, blog.secrett2633.cloud,
-// section "PagedAttention 커널: 비연속 메모리 접근").  One thread moves one
-// 16-byte chunk of one (token, head) row: the key chunk is stored whole into
-// the token-major key tile, the value chunk is split into its elements, each
-// going to its dimension row of the dimension-major value tile.
-template <int EB>
+// section "PagedAttention 커널: 비연속 메모리 접근").  One workgroup moves 16
+// consecutive tokens of one head.  Key rows are copied 16 bytes at a time into
+// the token-major key tiles.  Value rows are transposed through LDS so that
+// lanes write consecutive tokens of one dimension: when the 16 slots are
+// consecutive (a prompt chunk) each dimension row of a value tile receives
+// contiguous runs.  Any slot mapping is handled (negative or out-of-range
+// slots are skipped).
+template <int EB, int D>
 __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict__ key,
                                                       const uint8_t *__restrict__ value,
                                                       const int64_t *__restrict__ slots,
                                                       uint8_t *__restrict__ kpool,
                                                       uint8_t *__restrict__ vpool, int64_t T, int H,
-                                                      int B, int D, int64_t nslots) {
-  constexpr int VEC = 16 / EB;
-  const int chunks = D / VEC;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= T * H * chunks) return;
-  const int c = (int)(idx % chunks);
-  const int64_t th = idx / chunks;
-  const int h = (int)(th % H);
-  const int64_t t = th / H;
-  const int64_t slot = slots[t];
-  if (slot < 0 || slot >= nslots) return;
-  const int64_t blk = slot / B;
-  const int off = (int)(slot - blk * B);
-  const size_t src = ((size_t)(t * H + h) * D + (size_t)c * VEC) * EB;
-  const u32x4 kc = load16(key + src);
-  const u32x4 vc = load16(value + src);
-  *(u32x4 *)(kpool + (((size_t)(blk * H + h) * B + off) * D + (size_t)c * VEC) * EB) = kc;
-  const size_t vrow = ((size_t)(blk * H + h) * D + (size_t)c * VEC) * B + off;  // element index
-  if constexpr (EB == 4) {
-    float *vp = (float *)vpool;
+                                                      int B, int64_t nslots) {
+  constexpr int kTok = 16;
+  constexpr int VEC = 16 / EB;       // elements per 16-byte chunk
+  constexpr int CH = D / VEC;        // chunks per (token, head) row
+  using Elem = typename std::conditional<EB == 4, uint32_t, uint16_t>::type;
+  __shared__ int64_t sslot[kTok];
+  __shared__ Elem sv[D][kTok + 1];
+
+  const int h = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * kTok;
+  const int tid = threadIdx.x;
+  if (tid < kTok) {
+    const int64_t t = t0 + tid;
+    int64_t sl = t < T ? slots[t] : -1;
+    if (sl >= nslots) sl = -1;
+    sslot[tid] = sl;
+  }
+  __syncthreads();
+  const int lgB = B == 32 ? 5 : 4;   // block_size is 16 or 32
+  for (int c = tid; c < kTok * CH; c += blockDim.x) {
+    const int tt = c / CH, ch = c % CH;
+    const int64_t t = t0 + tt;
+    if (t >= T) continue;
+    const size_t src = ((size_t)t * H + h) * D + (size_t)ch * VEC;
+    const u32x4 vc = load16(value + src * EB);
+    // value chunk -> LDS, dimension-major
+    if constexpr (EB == 4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t u = vc[i];
-      vp[vrow + (size_t)i * B] = as_f32(u);
-    }
-  } else {
-    uint16_t *vp = (uint16_t *)vpool;
+      for (int i = 0; i < 4; ++i) sv[ch * VEC + i][tt] = vc[i];
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      vp[vrow + (size_t)(2 * i) * B] = (uint16_t)(vc[i] & 0xffffu);
-      vp[vrow + (size_t)(2 * i + 1) * B] = (uint16_t)(vc[i] >> 16);
+      for (int i = 0; i < 4; ++i) {
+        sv[ch * VEC + 2 * i][tt] = (uint16_t)(vc[i] & 0xffffu);
+        sv[ch * VEC + 2 * i + 1][tt] = (uint16_t)(vc[i] >> 16);
+      }
     }
+    const int64_t sl = sslot[tt];
+    if (sl < 0) continue;
+    const int64_t blk = sl >> lgB;
+    const int off = (int)(sl & (B - 1));
+    *(u32x4 *)(kpool + (((size_t)(blk * H + h) * B + off) * D + (size_t)ch * VEC) * EB) =
+        load16(key + src * EB);
+  }
+  __syncthreads();
+  Elem *vp = (Elem *)vpool;
+  for (int c = tid; c < D * kTok; c += blockDim.x) {
+    const int tt = c % kTok, e = c / kTok;
+    const int64_t sl = sslot[tt];
+    if (sl < 0) continue;
+    const int64_t blk = sl >> lgB;
+    const int off = (int)(sl & (B - 1));
+    vp[((size_t)(blk * H + h) * D + e) * B + off] = sv[e][tt];
   }
 }
 
@@ -121,18 +146,19 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t *__restrict__
 hipError_t launch_reshape_and_cache(const CacheDesc &c, const void *key, const void *value,
                                     const int64_t *slots, int64_t T, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const int EB = c.elt_bytes();
-  const int64_t work = T * c.H * (c.D * EB / 16);
-  const dim3 grid((unsigned)((work + 255) / 256));
+  const dim3 grid((unsigned)((T + 15) / 16), (unsigned)c.H);
   const int64_t nslots = c.num_blocks * c.B;
-  if (EB == 4)
-    hipLaunchKernelGGL(scatter_kernel<4>, grid, dim3(256), 0, stream, (const uint8_t *)key,
-                       (const uint8_t *)value, slots, (uint8_t *)c.k, (uint8_t *)c.v, T, c.H, c.B,
-                       c.D, nslots);
-  else
-    hipLaunchKernelGGL(scatter_kernel<2>, grid, dim3(256), 0, stream, (const uint8_t *)key,
-                       (const uint8_t *)value, slots, (uint8_t *)c.k, (uint8_t *)c.v, T, c.H, c.B,
-                       c.D, nslots);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const uint8_t *)key, (const uint8_t *)value,
+                       slots, (uint8_t *)c.k, (uint8_t *)c.v, T, c.H, c.B, nslots);
+  };
+  if (c.elt_bytes() == 4) {
+    if (c.D == 64) go(scatter_kernel<4, 64>);
+    else go(scatter_kernel<4, 128>);
+  } else {
+    if (c.D == 64) go(scatter_kernel<2, 64>);
+    else go(scatter_kernel<2, 128>);
+  }
   return hipGetLastError();
 }
 

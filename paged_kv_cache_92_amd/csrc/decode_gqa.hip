@@ -61,9 +61,7 @@ struct Mfma<BF16> {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
                                                      __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
   }
-  __device__ static uint32_t pack2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
-  }
+  __device__ static uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
 };
 
 // One work item: partition `part` of sequence s for the G query heads of KV
@@ -172,11 +170,11 @@ __device__ __forceinline__ void mfma_item(
         psum += p[j];
       }
       if constexpr (Mfma<E>::kSplitP) {
-        uint32_t h[4], lo[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) split_bf16(p[j], h[j], lo[j]);
-        pb[sb] = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-        pl[sb] = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+        uint32_t h0, l0, h1, l1;
+        split_bf16x2(p[0], p[1], h0, l0);
+        split_bf16x2(p[2], p[3], h1, l1);
+        pb[sb] = u32x2{h0, h1};
+        pl[sb] = u32x2{l0, l1};
       } else {
         pb[sb] = u32x2{Mfma<E>::pack2(p[0], p[1]), Mfma<E>::pack2(p[2], p[3])};
       }

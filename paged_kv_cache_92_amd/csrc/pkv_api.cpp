@@ -2,6 +2,7 @@
 // The contract of every entry point is documented in include/pkv.h.
 #include "pkv.h"
 
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -128,6 +129,8 @@ pkv_status pkv_reshape_and_cache(const pkv_cache *cache, const void *key, const 
   if (num_tokens == 0) return ok();
   if (!key || !value || !slot_mapping) return fail(PKV_ERR_INVALID, "key/value/slot_mapping is NULL");
   if (!aligned16(key) || !aligned16(value)) return fail(PKV_ERR_INVALID, "key/value must be 16-byte aligned");
+  if ((num_tokens + 15) / 16 > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "too many tokens per call");
+  if (c.H > 65535) return fail(PKV_ERR_UNSUPPORTED, "too many KV heads");
   return hip_status(pkv::launch_reshape_and_cache(c, key, value, slot_mapping, num_tokens, stream),
                     "reshape_and_cache launch");
 }
@@ -176,6 +179,7 @@ pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype
   if (max_context_len <= 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * c.B)
     return fail(PKV_ERR_INVALID, "max_context_len %d outside [1, max_blocks_per_seq*block_size]",
                 max_context_len);
+  if (!(scale > 0.f) || !(scale < INFINITY)) return fail(PKV_ERR_INVALID, "scale must be positive and finite");
   if (partition_size < 0 || partition_size % c.B != 0)
     return fail(PKV_ERR_INVALID, "partition_size %d must be 0 or a positive multiple of block_size %d",
                 partition_size, c.B);
@@ -243,6 +247,7 @@ pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, int32_t out_dtyp
     return fail(PKV_ERR_INVALID, "max_context_len %d outside [1, max_blocks_per_seq*block_size]",
                 max_context_len);
   if (max_query_len > max_context_len) return fail(PKV_ERR_INVALID, "max_query_len > max_context_len");
+  if (!(scale > 0.f) || !(scale < INFINITY)) return fail(PKV_ERR_INVALID, "scale must be positive and finite");
   const int64_t work = (int64_t)num_seqs * num_q_heads * ((max_query_len + 127) / 128);
   if (work >= (int64_t)1 << 31) return fail(PKV_ERR_UNSUPPORTED, "launch too large");
   pkv::PrefillArgs a;

@@ -17,6 +17,8 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Element tags: storage is float for fp32 and uint16_t bits for fp16/bf16.
 struct F32 {
@@ -93,8 +95,6 @@ __device__ __forceinline__ void unpack16<BF16>(const u32x4 &c, float *out) {
 // q.k over one 16-byte chunk, accumulated in fp32.  For 16-bit inputs each
 // pair product is exact in fp32 (v_dot2_f32_f16 / v_dot2_f32_bf16); q is the
 // matching chunk of the query in the same packed format.
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 template <typename E>
 __device__ __forceinline__ float dot16(const u32x4 &k, const u32x4 &q);
 template <>
@@ -129,11 +129,19 @@ __device__ __forceinline__ float dot16<BF16>(const u32x4 &k, const u32x4 &q) {
   return d;
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (round to nearest even), one instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
 // p = hi + lo with hi and lo in bf16: hi = RNE(p), lo = RNE(p - hi), so the
-// pair carries 16 significant bits (|p - hi - lo| <= 2^-17 |p|).
-__device__ __forceinline__ void split_bf16(float p, uint32_t &hi, uint32_t &lo) {
-  hi = f32_to_bf16_bits(p);
-  lo = f32_to_bf16_bits(p - bf16_bits_to_f32(hi));
+// pair carries 16 significant bits (|p - hi - lo| <= 2^-17 |p|).  Works on
+// two values at once; hi and lo come back packed as the MFMA operands want.
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - as_f32(hi << 16), b - as_f32(hi & 0xffff0000u));
 }
 
 template <typename E>

@@ -28,12 +28,12 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kQT = 32 * kWaves;  // query rows per workgroup
-constexpr int kKT = 32;           // key/value tokens per tile
+constexpr int kKT = 64;           // key/value tokens per tile
 constexpr int kVPad = 8;          // LDS row padding (elements) against bank conflicts
 
 template <typename E>
 struct Mfma32;
-// kSplitP: bf16 softmax weights enter P.V as hi + lo pairs (see split_bf16).
+// kSplitP: bf16 softmax weights enter P.V as hi + lo pairs (see split_bf16x2).
 template <>
 struct Mfma32<F16> {
   static constexpr bool kSplitP = false;
@@ -45,30 +45,38 @@ struct Mfma32<F16> {
     return (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
   }
 };
+#ifndef PKV_PREFILL_SPLIT_P
+#define PKV_PREFILL_SPLIT_P 1
+#endif
 template <>
 struct Mfma32<BF16> {
-  static constexpr bool kSplitP = true;
+  static constexpr bool kSplitP = PKV_PREFILL_SPLIT_P;
   __device__ static f32x16 mma(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
-  __device__ static uint32_t pack2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
-  }
+  __device__ static uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
 };
 
-// Row i of the score product (i = 8a + 4h + b) holds tile token perm(i).
+// Row i of a 32-token score product (i = 8a + 4h + b) holds token perm(i) of
+// its half-tile.
 __device__ __forceinline__ int perm_row(int i) {
   const int a = i >> 3, h = (i >> 2) & 1, b = i & 3;
   return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
 }
 
+// Lazy rescaling: a row keeps its reference maximum until a new score beats it
+// by more than 2^kRescaleLog2; weights stay <= 2^kRescaleLog2 meanwhile (no
+// overflow in fp32 or bf16), and the final o = acc / l is unaffected.
+constexpr float kRescaleLog2 = 8.f;
+
 template <typename E, int D, int BS>
-__global__ __launch_bounds__(256) void prefill_kernel(
-    void *__restrict__ out, int out_f32, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kpool,
-    const uint16_t *__restrict__ vpool, const int32_t *__restrict__ query_start_loc,
-    const int32_t *__restrict__ context_lens, const int32_t *__restrict__ block_tables,
-    int64_t num_blocks, int Hkv, int Hq, int mbps, int nqt, float scale_log2) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(
+    void *__restrict__ out, int out_f32, const uint16_t *__restrict__ q,
+    const uint16_t *__restrict__ kpool, const uint16_t *__restrict__ vpool,
+    const int32_t *__restrict__ query_start_loc, const int32_t *__restrict__ context_lens,
+    const int32_t *__restrict__ block_tables, int64_t num_blocks, int Hkv, int Hq, int mbps,
+    int nqt, float scale_log2) {
   constexpr int KS = D / 16;          // k-steps of the score product
   constexpr int DT = D / 32;          // 32-dimension tiles of the output
   constexpr int KCH = kKT * D / 8;    // 16-byte chunks of a key tile
@@ -95,7 +103,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   const int hist = ctx - qlen;
   if (hist < 0) return;
   const int hkv = hq / (Hq / Hkv);
-  const int32_t *bt = block_tables + (size_t)s * mbps;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -105,13 +112,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[kKT * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t sV[D * VROW];
+  extern __shared__ int sBT[];  // block ids of the positions this workgroup reads
 
   const int wrow0 = qt * kQT + 32 * w;                  // first chunk row of this wave
   const int myrow = wrow0 + j32;
   const int qpos = hist + min(myrow, qlen - 1);         // position of this lane's query
+  const int wave_min_pos = hist + min(wrow0, qlen - 1);
   const int wave_max_pos = hist + min(wrow0 + 31, qlen - 1);
   const int wg_max_pos = hist + min(qt * kQT + kQT - 1, qlen - 1);
   const int ntiles = (wg_max_pos + kKT) / kKT;
+
+  // Stage the block table once; tile loads then look block ids up in LDS.
+  {
+    const int32_t *bt = block_tables + (size_t)s * mbps;
+    const int nbt = min((ntiles * kKT + BS - 1) / BS, mbps);
+    for (int i = tid; i < nbt; i += 256) {
+      const int32_t b = bt[i];
+      sBT[i] = (b >= 0 && b < num_blocks) ? b : -1;
+    }
+  }
 
   // Q^T operand: query column j32, dimensions 16*ks + 8*h .. +8 (zero past the chunk).
   u32x4 qb[KS];
@@ -121,136 +140,139 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qb[ks] = valid ? load16(qrow + 16 * ks + 8 * h) : u32x4{0, 0, 0, 0};
   }
+  __syncthreads();
 
-  // Global -> register staging of one tile.
+  // Global -> register staging of one tile.  Thread tid moves key chunks
+  // (token tid/KCR + KTPI*i, dims 8*(tid%KCR)..) and value chunks (dimension
+  // tid/8 + 32*i, tokens 8*(tid%8)..+8); a block id comes from the staged table.
+  constexpr int KCR = D / 8;          // 16-byte chunks per key row
+  constexpr int KTPI = 256 / KCR;     // key tokens covered per chunk round
   u32x4 kreg[KPT], vreg[VPT];
   auto load_tile = [&](int t) {
+    const int t0 = t * kKT;
+    const bool full = t0 + kKT <= ctx;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int c = tid + 256 * i;
-      const int tok = c / (D / 8), ch = c % (D / 8);
-      const int pos = t * kKT + tok;
-      u32x4 x = {0, 0, 0, 0};
-      if (pos < ctx) {
-        const int32_t blk = bt[pos / BS];
-        if (blk >= 0 && blk < num_blocks)
-          x = load16(kpool + (((size_t)blk * Hkv + hkv) * BS + pos % BS) * D + 8 * ch);
-      }
-      kreg[i] = x;
+      const int tok = tid / KCR + KTPI * i;
+      const int pos = t0 + tok;
+      // Positions past the context read a harmless in-pool address; their
+      // scores are masked.  An invalid block id (a broken caller contract)
+      // reads block 0 instead of faulting.
+      const int blk = (full || pos < ctx) ? max(sBT[pos / BS], 0) : 0;
+      kreg[i] = load16(kpool + (((size_t)blk * Hkv + hkv) * BS + pos % BS) * D + 8 * (tid % KCR));
     }
+    {
+      const int pos = t0 + 8 * (tid % 8);
+      const int blk = (full || pos < ctx) ? max(sBT[pos / BS], 0) : 0;
+      const uint16_t *vblk = vpool + ((size_t)blk * Hkv + hkv) * D * BS + pos % BS;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int c = tid + 256 * i;
-      const int e = c / (kKT / 8), g8 = c % (kKT / 8);
-      const int pos = t * kKT + 8 * g8;
-      u32x4 x = {0, 0, 0, 0};
-      if (pos < ctx) {
-        const int32_t blk = bt[pos / BS];
-        if (blk >= 0 && blk < num_blocks) {
-          x = load16(vpool + (((size_t)blk * Hkv + hkv) * D + e) * BS + pos % BS);
-          if (pos + 8 > ctx) {
-            // Slots past the context may hold anything: zero them.
+      for (int i = 0; i < VPT; ++i) {
+        const int e = tid / 8 + 32 * i;
+        u32x4 x = load16(vblk + (size_t)e * BS);
+        if (!full && pos + 8 > ctx) {
+          // Slots past the context may hold anything: zero them.
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const uint32_t keep = (pos + 2 * k < ctx ? 0x0000ffffu : 0u) |
-                                    (pos + 2 * k + 1 < ctx ? 0xffff0000u : 0u);
-              x[k] &= keep;
-            }
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t keep = (pos + 2 * k < ctx ? 0x0000ffffu : 0u) |
+                                  (pos + 2 * k + 1 < ctx ? 0xffff0000u : 0u);
+            x[k] &= keep;
           }
         }
+        vreg[i] = x;
       }
-      vreg[i] = x;
     }
   };
   auto store_tile = [&]() {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + 256 * i;
-      const int tok = c / (D / 8), ch = c % (D / 8);
-      *(u32x4 *)&sK[tok * KROW + 8 * ch] = kreg[i];
-    }
+    for (int i = 0; i < KPT; ++i)
+      *(u32x4 *)&sK[(tid / KCR + KTPI * i) * KROW + 8 * (tid % KCR)] = kreg[i];
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int c = tid + 256 * i;
-      const int e = c / (kKT / 8), g8 = c % (kKT / 8);
-      *(u32x4 *)&sV[e * VROW + 8 * g8] = vreg[i];
-    }
+    for (int i = 0; i < VPT; ++i)
+      *(u32x4 *)&sV[(tid / 8 + 32 * i) * VROW + 8 * (tid % 8)] = vreg[i];
   };
 
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f;  // m in scaled log2 units
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+  const f32x16 zero16 = {};
 
-  const int krow = perm_row(j32);  // key row this lane feeds to the score product
+  const int krow = perm_row(j32);  // key row (within a 32-token half) this lane feeds
   load_tile(0);
   for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();  // every wave is done reading the previous tile
     store_tile();
     __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);
-    if (t * kKT <= wave_max_pos) {
-      f32x16 st;
+    if (t + 1 < ntiles) load_tile(t + 1);  // in flight while this tile is computed
+    if (t * kKT > wave_max_pos) continue;  // entirely in this wave's future
+    constexpr int HALVES = kKT / 32;
+    f32x16 st[HALVES];  // raw scores q.k
 #pragma unroll
-      for (int i = 0; i < 16; ++i) st[i] = 0.f;
+    for (int hf = 0; hf < HALVES; ++hf) {
+      const uint16_t *krp = &sK[(32 * hf + krow) * KROW + 8 * h];
+      st[hf] = Mfma32<E>::mma(*(const u32x4 *)krp, qb[0], zero16);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 a = *(const u32x4 *)&sK[krow * KROW + 16 * ks + 8 * h];
-        st = Mfma32<E>::mma(a, qb[ks], st);
-      }
-      // Result item 4a+b is token row 8a+4h+b, i.e. tile token perm(8a+4h+b).
-      float mb = -INFINITY;
+      for (int ks = 1; ks < KS; ++ks) st[hf] = Mfma32<E>::mma(*(const u32x4 *)(krp + 16 * ks), qb[ks], st[hf]);
+    }
+    // Item 4a+b of half hf is tile token 32*hf + perm(8a+4h+b); only tiles
+    // that cross this wave's diagonal need the causal mask.
+    if (t * kKT + kKT - 1 > wave_min_pos) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int hf = 0; hf < HALVES; ++hf)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int pos = t * kKT + 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
-          float v = st[4 * a + b] * scale_log2;
-          if (pos > qpos) v = -INFINITY;
-          st[4 * a + b] = v;
-          mb = fmaxf(mb, v);
-        }
-      mb = fmaxf(mb, __shfl_xor(mb, 32));
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int pos = t * kKT + 32 * hf + 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
+            if (pos > qpos) st[hf][4 * a + b] = -INFINITY;
+          }
+    }
+    float mraw = -INFINITY;
+#pragma unroll
+    for (int hf = 0; hf < HALVES; ++hf)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, st[hf][i]);
+    mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+    const float mb = mraw * scale_log2;  // scale > 0: the max commutes with scaling
+    if (__any(mb > m + kRescaleLog2)) {
       const float mnew = fmaxf(m, mb);
-      const float alpha = fast_exp2(m - mnew);
+      const float alpha = fast_exp2(m - mnew);  // 1 for rows that keep their reference
       m = mnew;
-      float psum = 0.f;
-      u32x4 pb[2], pl[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        float p[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          p[k] = fast_exp2(st[8 * c + k] - mnew);
-          psum += p[k];
-        }
-        if constexpr (Mfma32<E>::kSplitP) {
-          uint32_t h[8], lo[8];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) split_bf16(p[k], h[k], lo[k]);
-          pb[c] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                        h[6] | (h[7] << 16)};
-          pl[c] = u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16),
-                        lo[6] | (lo[7] << 16)};
-        } else {
-          pb[c] = u32x4{Mfma32<E>::pack2(p[0], p[1]), Mfma32<E>::pack2(p[2], p[3]),
-                        Mfma32<E>::pack2(p[4], p[5]), Mfma32<E>::pack2(p[6], p[7])};
-        }
-      }
-      l = l * alpha + psum;
+      l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const u32x4 a = *(const u32x4 *)&sV[(32 * dt + j32) * VROW + 16 * c + 8 * h];
-          acc[dt] = Mfma32<E>::mma(a, pb[c], acc[dt]);
-          if constexpr (Mfma32<E>::kSplitP) acc[dt] = Mfma32<E>::mma(a, pl[c], acc[dt]);
-        }
     }
-    __syncthreads();
+    float psum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2 * HALVES; ++c) {
+      const int hf = c >> 1, c2 = c & 1;
+      float p[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        p[k] = fast_exp2(fmaf(st[hf][8 * c2 + k], scale_log2, -m));
+        psum += p[k];
+      }
+      u32x4 pb, pl;
+      if constexpr (Mfma32<E>::kSplitP) {
+        uint32_t h[4], lo[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) split_bf16x2(p[2 * k], p[2 * k + 1], h[k], lo[k]);
+        pb = u32x4{h[0], h[1], h[2], h[3]};
+        pl = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      } else {
+        pb = u32x4{Mfma32<E>::pack2(p[0], p[1]), Mfma32<E>::pack2(p[2], p[3]),
+                   Mfma32<E>::pack2(p[4], p[5]), Mfma32<E>::pack2(p[6], p[7])};
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const u32x4 a = *(const u32x4 *)&sV[(32 * dt + j32) * VROW + 16 * c + 8 * h];
+        acc[dt] = Mfma32<E>::mma(a, pb, acc[dt]);
+        if constexpr (Mfma32<E>::kSplitP) acc[dt] = Mfma32<E>::mma(a, pl, acc[dt]);
+      }
+    }
+    l += psum;
   }
 
   // Lanes l and l^32 hold the two row halves of the same query column.
@@ -279,7 +301,8 @@ template <typename E, int D, int BS>
 void launch_t(const CacheDesc &c, const PrefillArgs &a, hipStream_t stream) {
   const int nqt = (a.max_query_len + kQT - 1) / kQT;
   const int64_t nwork = (int64_t)a.S * a.Hq * nqt;
-  hipLaunchKernelGGL((prefill_kernel<E, D, BS>), dim3((unsigned)nwork), dim3(256), 0, stream,
+  const size_t lds = sizeof(int) * (size_t)a.max_blocks_per_seq;   // staged block table
+  hipLaunchKernelGGL((prefill_kernel<E, D, BS>), dim3((unsigned)nwork), dim3(256), lds, stream,
                      a.out, (int)a.out_f32, (const uint16_t *)a.q, (const uint16_t *)c.k,
                      (const uint16_t *)c.v, a.query_start_loc, a.context_lens, a.block_tables,
                      c.num_blocks, c.H, a.Hq, a.max_blocks_per_seq, nqt, a.scale * kLog2e);
