@@ -69,6 +69,35 @@ def attention_flops(wl):
     return float(total) * Hq * d * 4
 
 
+def kernel_source_sha():
+    """First 16 hex digits of sha256 over the HIP sources, headers and C++ API, in name order."""
+    import glob
+    import hashlib
+    csrc = os.path.join(ROOT, "paged_kv_cache_92_amd", "csrc")
+    h = hashlib.sha256()
+    for pat in ("*.hip", "*.h", "*.cpp"):
+        for f in sorted(glob.glob(os.path.join(csrc, pat))):
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config):
+    """HBM bytes per launch of the dominant kernel, from the committed rocprofv3 counter runs.
+
+    None unless the counters were taken on the kernel sources as they are now."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = t.get(config)
+    if e is None or t.get("source_sha") != kernel_source_sha():
+        return None
+    return int(round(e["fetch_bytes"] + e["write_bytes"]))
+
+
 def cpu_baseline(wl, budget_s):
     """The oracle as it stands, single-threaded, on a bounded sample of the same input."""
     import numpy as np
@@ -123,6 +152,8 @@ def main():
                     help="split-KV partition size in tokens (default: the workload's)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build",
@@ -135,8 +166,18 @@ def main():
     import paged_kv_cache_92_amd as pkv
     from paged_kv_cache_92_amd.runner import DeviceWorkload, new_cache
 
-    pkv.lib()
     torch.cuda.set_device(0)
+    if args.copy_probe_mib:
+        # A copy of known size: reads and writes exactly n bytes per launch.
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": args.steps}), flush=True)
+        return
+    pkv.lib()
     t0 = time.time()
     wl, desc = make_workload(args.config, args.partition)
     log(f"[bench] generated {wl.name} in {time.time() - t0:.1f}s "
@@ -210,7 +251,8 @@ def main():
             "decode_tokens_per_s": round(wl.S / (ms_step * 1e-3), 1),
             "decode_tokens_per_s_40_layer_attention_only": round(wl.S / (40 * ms_step * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs_attn, 2), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs_attn / HBM_PEAK_GBS, 4), "traffic": None,
+                         "unit": "GB/s", "frac": round(gbs_attn / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(args.config),
                          "kernel": "paged decode (partial + reduce when split)",
                          "algorithmic_bytes_per_launch": kv,
                          "avg_launch_us": round(attn_avg * 1e3, 2)},
@@ -222,7 +264,7 @@ def main():
             "value": round(tf_step, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf_attn, 2), "peak": MFMA_PEAK_TFLOPS[dt],
                          "unit": "TFLOP/s", "frac": round(tf_attn / MFMA_PEAK_TFLOPS[dt], 4),
-                         "traffic": None, "kernel": "paged prefill",
+                         "traffic": measured_traffic(args.config), "kernel": "paged prefill",
                          "algorithmic_flops_per_launch": flops,
                          "avg_launch_us": round(attn_avg * 1e3, 2)},
         })
