@@ -29,13 +29,19 @@
  * Layout in HBM (this library's choice; the pages fix only "blocks of B
  * tokens"):
  *
- *   k_pool  [num_blocks][num_kv_heads][block_size][head_dim]
- *           a (block, head) key tile is B x d, token-major, contiguous;
+ *   k_pool  [num_blocks][num_kv_heads][head_dim/X][block_size][X],
+ *           X = 64 bytes / element size (32 fp16/bf16 values, 16 fp32
+ *           values): each key row is cut into 64-byte pieces and a block's
+ *           pieces of one dimension range sit together, so 16 tokens x 64
+ *           bytes of a (block, head) key tile are one contiguous KiB; element
+ *           (block, head, offset, e) is at
+ *           (((block*H + head)*(d/X) + e/X)*B + offset)*X + e%X;
  *   v_pool  [num_blocks][num_kv_heads][head_dim][block_size]
  *           a (block, head) value tile is d x B, dimension-major, contiguous,
  *           so the B tokens of one value dimension are adjacent: the operand
  *           shape that the P.V matrix-core products read directly.
  *
+ * A (block, head) tile of either pool is B*d contiguous elements.
  * q, out, key and value rows are [tokens][heads][head_dim], contiguous.
  * Query/output and cache share one dtype.  Supported: dtype f32/f16/bf16,
  * head_dim 64 or 128, block_size 16 or 32.  Base pointers must be 16-byte

@@ -8,8 +8,9 @@ with numpy arrays.
 
 Arrays carry raw element bits: ``float32`` for fp32 and ``uint16`` for fp16
 and bf16, with the dtype code (0 fp32, 1 fp16, 2 bf16) passed alongside.
-Pools use the library's documented layout: K ``[num_blocks][H][B][d]``,
-V ``[num_blocks][H][d][B]``; slot = block * B + offset.
+Pools use the library's documented layout: K ``[num_blocks][H][d/X][B][X]``
+with X = 64 bytes / element size, V ``[num_blocks][H][d][B]``;
+slot = block * B + offset.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 (closed forms, worked examples from the pages, invariants and special cases).
@@ -93,7 +94,10 @@ def _check(rc: int, what: str):
 
 
 def _geom(k_pool: np.ndarray, v_pool: np.ndarray, dtype: int):
-    nb, H, B, d = k_pool.shape
+    if k_pool.ndim != 5 or k_pool.shape[4] != 64 // np.dtype(_STORAGE[dtype]).itemsize:
+        raise OracleError(f"K pool shape {k_pool.shape} is not [nb][H][d/X][B][X]")
+    nb, H, nc, B, x = k_pool.shape
+    d = nc * x
     if v_pool.shape != (nb, H, d, B):
         raise OracleError(f"V pool shape {v_pool.shape} does not match K pool {k_pool.shape}")
     if k_pool.dtype != _STORAGE[dtype] or v_pool.dtype != _STORAGE[dtype]:

@@ -19,7 +19,10 @@
  *
  * Pool layout (an interface contract of the library, restated here; the
  * pages fix only "fixed-size blocks of B token slots", [T] step 5):
- *   K pool  [num_blocks][H][B][d]  element (blk,h,off,e) at ((blk*H+h)*B+off)*d+e
+ *   K pool  [num_blocks][H][d/X][B][X], X = 64 bytes / element size (32
+ *           fp16/bf16 values, 16 fp32 values): a key row is cut into 64-byte
+ *           pieces and the B pieces of one dimension range are adjacent;
+ *           element (blk,h,off,e) at (((blk*H+h)*(d/X)+e/X)*B+off)*X+e%X
  *   V pool  [num_blocks][H][d][B]  element (blk,h,off,e) at ((blk*H+h)*d+e)*B+off
  *   slot s  = blk*B + off          (token slot off inside physical block blk)
  *
@@ -83,8 +86,9 @@ static void copy_elt(void *dst, size_t di, const void *src, size_t si, int dtype
     ((uint16_t *)dst)[di] = ((const uint16_t *)src)[si];
 }
 
-static size_t k_index(int64_t blk, int h, int off, int e, int H, int B, int d) {
-  return ((size_t)(blk * H + h) * B + off) * d + e;
+static size_t k_index(int64_t blk, int h, int off, int e, int H, int B, int d, int dtype) {
+  const int X = 64 / (int)elt_size(dtype);
+  return (((size_t)(blk * H + h) * (size_t)(d / X) + (size_t)(e / X)) * B + off) * X + e % X;
 }
 
 static size_t v_index(int64_t blk, int h, int off, int e, int H, int B, int d) {
@@ -94,6 +98,7 @@ static size_t v_index(int64_t blk, int h, int off, int e, int H, int B, int d) {
 static int check_geometry(int dtype, int64_t num_blocks, int H, int B, int d) {
   if (dtype != ORC_F32 && dtype != ORC_F16 && dtype != ORC_BF16) return ORC_ERR_ARG;
   if (num_blocks <= 0 || H <= 0 || B <= 0 || d <= 0) return ORC_ERR_ARG;
+  if (d % (64 / (int)elt_size(dtype)) != 0) return ORC_ERR_ARG; /* whole 64-byte key pieces */
   return ORC_OK;
 }
 
@@ -133,7 +138,7 @@ int oracle_reshape_and_cache(void *k_pool, void *v_pool, int dtype, int64_t num_
     for (int h = 0; h < H; ++h) {
       for (int e = 0; e < d; ++e) {
         size_t src = ((size_t)t * H + h) * d + e;
-        copy_elt(k_pool, k_index(blk, h, off, e, H, B, d), key, src, dtype);
+        copy_elt(k_pool, k_index(blk, h, off, e, H, B, d, dtype), key, src, dtype);
         copy_elt(v_pool, v_index(blk, h, off, e, H, B, d), value, src, dtype);
       }
     }
@@ -210,7 +215,7 @@ int oracle_gather_kv(const void *k_pool, const void *v_pool, int dtype, int64_t 
       for (int h = 0; h < H; ++h)
         for (int e = 0; e < d; ++e) {
           size_t dst = (row * H + h) * d + e;
-          copy_elt(k_out, dst, k_pool, k_index(blk, h, off, e, H, B, d), dtype);
+          copy_elt(k_out, dst, k_pool, k_index(blk, h, off, e, H, B, d, dtype), dtype);
           copy_elt(v_out, dst, v_pool, v_index(blk, h, off, e, H, B, d), dtype);
         }
     }
@@ -229,7 +234,7 @@ static int reassemble(const void *k_pool, const void *v_pool, int dtype, int64_t
     for (int h = 0; h < H; ++h)
       for (int e = 0; e < d; ++e) {
         size_t dst = ((size_t)j * H + h) * d + e;
-        Kc[dst] = load_elt(k_pool, k_index(blk, h, off, e, H, B, d), dtype);
+        Kc[dst] = load_elt(k_pool, k_index(blk, h, off, e, H, B, d, dtype), dtype);
         Vc[dst] = load_elt(v_pool, v_index(blk, h, off, e, H, B, d), dtype);
       }
   }

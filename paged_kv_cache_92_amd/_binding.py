@@ -91,9 +91,11 @@ def _dev_ptr(t: torch.Tensor | None, name: str, dtype=None):
 class PagedKVCache:
     """One layer's paged K/V pool in HBM.
 
-    ``k_pool`` is [num_blocks][num_kv_heads][block_size][head_dim] and
-    ``v_pool`` is [num_blocks][num_kv_heads][head_dim][block_size]: a block's
-    key tile is token-major, its value tile dimension-major.
+    ``k_pool`` is [num_blocks][num_kv_heads][head_dim/X][block_size][X] with
+    X = 64 bytes / element size (key rows cut into 64-byte pieces, the
+    block's pieces of one dimension range adjacent) and ``v_pool`` is
+    [num_blocks][num_kv_heads][head_dim][block_size] (value tile
+    dimension-major).
     """
 
     def __init__(self, num_blocks, num_kv_heads, block_size, head_dim, dtype=torch.float16,
@@ -105,7 +107,10 @@ class PagedKVCache:
         self.dtype = dtype
         if dtype not in _TORCH_TO_PKV:
             raise ValueError(f"unsupported dtype {dtype}")
-        kshape = (self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim)
+        x = 64 // torch.tensor([], dtype=dtype).element_size()
+        if self.head_dim % x:
+            raise ValueError(f"head_dim must be a multiple of {x}")
+        kshape = (self.num_blocks, self.num_kv_heads, self.head_dim // x, self.block_size, x)
         vshape = (self.num_blocks, self.num_kv_heads, self.head_dim, self.block_size)
         self.k_pool = k_pool if k_pool is not None else torch.empty(kshape, dtype=dtype, device=device)
         self.v_pool = v_pool if v_pool is not None else torch.empty(vshape, dtype=dtype, device=device)

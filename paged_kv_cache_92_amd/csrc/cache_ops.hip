@@ -11,7 +11,7 @@ namespace {
 // Slot scatter ("reshape_and_cache", [vLLM] PagedAttention, blog.secrett2633.cloud,
 // section "PagedAttention 커널: 비연속 메모리 접근").  One workgroup moves 16
 // consecutive tokens of one head.  Key rows are copied 16 bytes at a time into
-// the token-major key tiles.  Value rows are transposed through LDS so that
+// the key tiles, whose rows are cut into 64-byte pieces ([D/X][B][X]).  Value rows are transposed through LDS so that
 // lanes write consecutive tokens of one dimension: when the 16 slots are
 // consecutive (a prompt chunk) each dimension row of a value tile receives
 // contiguous runs.  Any slot mapping is handled (negative or out-of-range
@@ -26,6 +26,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict_
   constexpr int kTok = 16;
   constexpr int VEC = 16 / EB;       // elements per 16-byte chunk
   constexpr int CH = D / VEC;        // chunks per (token, head) row
+  constexpr int X = 64 / EB;         // elements per 64-byte key piece (4 chunks)
+  constexpr int NC = D / X;          // key pieces per row
   using Elem = typename std::conditional<EB == 4, uint32_t, uint16_t>::type;
   __shared__ int64_t sslot[kTok];
   __shared__ Elem sv[D][kTok + 1];
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict_
     if (sl < 0) continue;
     const int64_t blk = sl >> lgB;
     const int off = (int)(sl & (B - 1));
-    *(u32x4 *)(kpool + (((size_t)(blk * H + h) * B + off) * D + (size_t)ch * VEC) * EB) =
+    *(u32x4 *)(kpool + ((((size_t)(blk * H + h) * NC + ch / 4) * B + off) * X + (ch % 4) * VEC) * EB) =
         load16(key + src * EB);
   }
   __syncthreads();
@@ -110,7 +112,9 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t *__restrict__
                                                      const int32_t *__restrict__ cu, int64_t nblocks,
                                                      int H, int B, int D, int max_len) {
   constexpr int VEC = 16 / EB;
+  constexpr int X = 64 / EB;
   const int chunks = D / VEC;
+  const int NC = D / X;
   const int s = blockIdx.y;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)max_len * H * chunks) return;
@@ -123,8 +127,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t *__restrict__
   if (blk < 0 || blk >= nblocks) return;
   const int off = j % B;
   const size_t dst = (((size_t)cu[s] + j) * H + h) * D + (size_t)c * VEC;
-  *(u32x4 *)(kout + dst * EB) = load16(kpool + (((size_t)(blk * (int64_t)H + h) * B + off) * D +
-                                               (size_t)c * VEC) * EB);
+  *(u32x4 *)(kout + dst * EB) = load16(
+      kpool + ((((size_t)(blk * (int64_t)H + h) * NC + c / 4) * B + off) * X + (c % 4) * VEC) * EB);
   const size_t vrow = ((size_t)(blk * (int64_t)H + h) * D + (size_t)c * VEC) * B + off;
   u32x4 packed;
   if constexpr (EB == 4) {

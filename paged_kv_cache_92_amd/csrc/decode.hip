@@ -7,10 +7,12 @@
 // (velog.io), section 01, rewritten block-wise as eq. (4) of section 02.
 //
 // Wave mapping of one block (B tokens):
-//   key tile  [B][D]  token-major: LPT lanes cover one token row with
-//             16-byte loads, so one wave load covers TPL = 64/LPT tokens and a
-//             block takes KL = B/TPL loads per lane.  Partial dot products
-//             are summed over the LPT lanes with DPP.
+//   key tile  [D/X][B][X] (X = 64 bytes of a key row): lane = 4*t + k holds
+//             16-byte piece k of token t's X-wide slice, so one wave load
+//             reads 16 tokens x 64 bytes = 1 KiB contiguous, and a block takes
+//             KL = (D/X)*(B/16) loads per lane.  Each lane's partial dot
+//             product covers D/4 dimensions; the 4 lanes of a quad are summed
+//             with two DPP steps.
 //   value tile [D][B] dimension-major: a 16-byte chunk is VEC consecutive
 //             tokens of one dimension; CPR = B/VEC chunks per dimension row,
 //             VL = D*CPR/64 loads per lane.  Each lane accumulates its
@@ -31,24 +33,20 @@ namespace pkv {
 namespace {
 
 constexpr int kWaves = 4;
-#ifndef PKV_VALU_NB
-#define PKV_VALU_NB 1
-#endif
-constexpr int kValuNB = PKV_VALU_NB;
 
 template <typename E, int D, int BS>
 struct ValuCfg {
   static constexpr int EB = E::kBytes;
-  static constexpr int VEC = 16 / EB;
-  static constexpr int LPT = D / VEC;
-  static constexpr int TPL = kWave / LPT;
-  static constexpr int KL = BS / TPL;
+  static constexpr int VEC = 16 / EB;   // elements per 16-byte load
+  static constexpr int X = 64 / EB;     // elements per 64-byte key piece
+  static constexpr int NC = D / X;      // key pieces per row
+  static constexpr int TG = BS / 16;    // 16-token groups per block
+  static constexpr int KL = NC * TG;
   static constexpr int CPR = BS / VEC;
   static constexpr int VL = D * CPR / kWave;
   // VGPRs holding one block's key and value loads.
-  static constexpr int kLoadRegs = 4 * (KL + VL) * kValuNB;
-  static_assert(LPT >= 1 && LPT <= kWave && kWave % LPT == 0, "key row must tile the wave");
-  static_assert(BS % TPL == 0, "block must be a whole number of key loads");
+  static constexpr int kLoadRegs = 4 * (KL + VL);
+  static_assert(D % X == 0 && BS % 16 == 0, "key tile mapping");
   static_assert(CPR >= 1 && kWave % CPR == 0 && (D * CPR) % kWave == 0, "value tile mapping");
 };
 
@@ -60,9 +58,8 @@ struct ValuLds {
   float acc[kWaves][D];
 };
 
-// One work item: partition `part` of sequence s for query head hq.  NB
-// blocks per wave are loaded before any of them is computed.
-template <typename E, int D, int BS, int NB>
+// One work item: partition `part` of sequence s for query head hq.
+template <typename E, int D, int BS>
 __device__ __forceinline__ void valu_item(
     ValuLds<E, D, BS> &sh, int s, int part, int hq, void *__restrict__ out, int out_f32,
     const typename E::storage *__restrict__ q, const typename E::storage *__restrict__ kpool,
@@ -82,8 +79,8 @@ __device__ __forceinline__ void valu_item(
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = uniform(threadIdx.x >> 6);
-  const int g = lane / C::LPT;     // token slot of this lane in a key load
-  const int r = lane % C::LPT;     // 16-byte chunk of the key row
+  const int kq = lane & 3;         // 16-byte piece within a 64-byte key slice
+  const int kt = lane >> 2;        // token within a 16-token group
   const int cp = lane % C::CPR;    // token chunk of the value row
 
   auto &lds_p = sh.p;
@@ -91,8 +88,13 @@ __device__ __forceinline__ void valu_item(
   auto &lds_l = sh.l;
   auto &lds_acc = sh.acc;
 
-  // Query chunk of this lane, kept in its packed input format.
-  const u32x4 qc = load16(q + ((size_t)s * Hq + hq) * D + r * C::VEC);
+  // The query dimensions this lane multiplies, kept in the packed input format.
+  u32x4 qc[C::NC];
+  {
+    const T *qrow = q + ((size_t)s * Hq + hq) * D + kq * C::VEC;
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) qc[c] = load16(qrow + c * C::X);
+  }
 
   float m = -INFINITY;
   float l = 0.f;
@@ -101,38 +103,44 @@ __device__ __forceinline__ void valu_item(
   for (int i = 0; i < C::VL; ++i) acc[i] = 0.f;
 
   const int32_t *bt = block_tables + (size_t)s * mbps;
-  if constexpr (NB == 1) {
   for (int b = w; b < nblk; b += kWaves) {
     const int lb = blk0 + b;
     const int64_t phys = uniform(bt[lb]);
     if (phys < 0 || phys >= num_blocks) continue;
-    const T *kt = kpool + ((size_t)phys * Hkv + hkv) * (BS * D);
-    const T *vt = vpool + ((size_t)phys * Hkv + hkv) * (D * BS);
+    const T *ktile = kpool + ((size_t)phys * Hkv + hkv) * (BS * D);
+    const T *vtile = vpool + ((size_t)phys * Hkv + hkv) * (D * BS);
     u32x4 kr[C::KL];
     u32x4 vr[C::VL];
 #pragma unroll
-    for (int i = 0; i < C::KL; ++i) kr[i] = load16_stream(kt + (i * C::TPL + g) * D + r * C::VEC);
+    for (int c = 0; c < C::NC; ++c)
 #pragma unroll
-    for (int i = 0; i < C::VL; ++i) vr[i] = load16_stream(vt + (size_t)(kWave * i + lane) * C::VEC);
-    {
+      for (int r = 0; r < C::TG; ++r)
+        kr[c * C::TG + r] = load16_stream(ktile + (c * BS + 16 * r + kt) * C::X + kq * C::VEC);
+#pragma unroll
+    for (int i = 0; i < C::VL; ++i) vr[i] = load16_stream(vtile + (size_t)(kWave * i + lane) * C::VEC);
+
     const int tbase = lb * BS;
     const bool partial = tbase + BS > tok1;
-    float sc[C::KL];
+    float sc[C::TG];
 #pragma unroll
-    for (int i = 0; i < C::KL; ++i) {
-      sc[i] = group_sum<C::LPT>(dot16<E>(kr[i], qc)) * scale_log2;
-      if (partial && tbase + i * C::TPL + g >= tok1) sc[i] = -INFINITY;
+    for (int r = 0; r < C::TG; ++r) {
+      float x = dot16<E>(kr[r], qc[0]);
+#pragma unroll
+      for (int c = 1; c < C::NC; ++c) x += dot16<E>(kr[c * C::TG + r], qc[c]);
+      x = group_sum<4>(x) * scale_log2;
+      if (partial && tbase + 16 * r + kt >= tok1) x = -INFINITY;
+      sc[r] = x;
     }
     float mb = sc[0];
 #pragma unroll
-    for (int i = 1; i < C::KL; ++i) mb = fmaxf(mb, sc[i]);
-    mb = xor_max<C::LPT, kWave>(mb);
+    for (int r = 1; r < C::TG; ++r) mb = fmaxf(mb, sc[r]);
+    mb = quad_uniform_max(mb);
     const float mnew = fmaxf(m, mb);
     const float alpha = fast_exp2(m - mnew);
     m = mnew;
-    if (r == 0) {
+    if (kq == 0) {
 #pragma unroll
-      for (int i = 0; i < C::KL; ++i) lds_p[w][i * C::TPL + g] = fast_exp2(sc[i] - mnew);
+      for (int r = 0; r < C::TG; ++r) lds_p[w][16 * r + kt] = fast_exp2(sc[r] - mnew);
     }
     __builtin_amdgcn_wave_barrier();
     float p[C::VEC];
@@ -164,139 +172,6 @@ __device__ __forceinline__ void valu_item(
       acc[i] = a;
     }
     __builtin_amdgcn_wave_barrier();
-    }
-  }
-  } else {
-  for (int b = w; b < nblk; b += 2 * kWaves) {
-    // Two blocks of this wave in flight at once.
-    const int lb0 = blk0 + b, lb1 = blk0 + b + kWaves;
-    const bool has1 = b + kWaves < nblk;
-    const int64_t phys0 = uniform(bt[lb0]);
-    const int64_t phys1 = has1 ? uniform(bt[lb1]) : phys0;
-    const bool ok0 = phys0 >= 0 && phys0 < num_blocks;
-    const bool ok1 = has1 && phys1 >= 0 && phys1 < num_blocks;
-    const T *kt0 = kpool + ((size_t)(ok0 ? phys0 : 0) * Hkv + hkv) * (BS * D);
-    const T *vt0 = vpool + ((size_t)(ok0 ? phys0 : 0) * Hkv + hkv) * (D * BS);
-    const T *kt1 = kpool + ((size_t)(ok1 ? phys1 : 0) * Hkv + hkv) * (BS * D);
-    const T *vt1 = vpool + ((size_t)(ok1 ? phys1 : 0) * Hkv + hkv) * (D * BS);
-    u32x4 kr0[C::KL], vr0[C::VL], kr1[C::KL], vr1[C::VL];
-    if (ok0) {
-#pragma unroll
-      for (int i = 0; i < C::KL; ++i) kr0[i] = load16_stream(kt0 + (i * C::TPL + g) * D + r * C::VEC);
-#pragma unroll
-      for (int i = 0; i < C::VL; ++i) vr0[i] = load16_stream(vt0 + (size_t)(kWave * i + lane) * C::VEC);
-    }
-    if (ok1) {
-#pragma unroll
-      for (int i = 0; i < C::KL; ++i) kr1[i] = load16_stream(kt1 + (i * C::TPL + g) * D + r * C::VEC);
-#pragma unroll
-      for (int i = 0; i < C::VL; ++i) vr1[i] = load16_stream(vt1 + (size_t)(kWave * i + lane) * C::VEC);
-    }
-    if (ok0)
-    {
-    const int tbase = lb0 * BS;
-    const bool partial = tbase + BS > tok1;
-    float sc[C::KL];
-#pragma unroll
-    for (int i = 0; i < C::KL; ++i) {
-      sc[i] = group_sum<C::LPT>(dot16<E>(kr0[i], qc)) * scale_log2;
-      if (partial && tbase + i * C::TPL + g >= tok1) sc[i] = -INFINITY;
-    }
-    float mb = sc[0];
-#pragma unroll
-    for (int i = 1; i < C::KL; ++i) mb = fmaxf(mb, sc[i]);
-    mb = xor_max<C::LPT, kWave>(mb);
-    const float mnew = fmaxf(m, mb);
-    const float alpha = fast_exp2(m - mnew);
-    m = mnew;
-    if (r == 0) {
-#pragma unroll
-      for (int i = 0; i < C::KL; ++i) lds_p[w][i * C::TPL + g] = fast_exp2(sc[i] - mnew);
-    }
-    __builtin_amdgcn_wave_barrier();
-    float p[C::VEC];
-#pragma unroll
-    for (int i = 0; i < C::VEC; i += 4) {
-      const f32x4 pv = *(const f32x4 *)&lds_p[w][cp * C::VEC + i];
-      p[i] = pv[0]; p[i + 1] = pv[1]; p[i + 2] = pv[2]; p[i + 3] = pv[3];
-    }
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < C::VEC; ++e) psum += p[e];
-    l = l * alpha + psum;
-#pragma unroll
-    for (int i = 0; i < C::VL; ++i) {
-      float vf[C::VEC];
-      unpack16<E>(vr0[i], vf);
-      float a = acc[i] * alpha;
-      if (partial) {
-        // Unfilled slots may hold anything (NaN included): their values count as 0.
-#pragma unroll
-        for (int e = 0; e < C::VEC; ++e) {
-          const float ve = (tbase + cp * C::VEC + e < tok1) ? vf[e] : 0.f;
-          a = fmaf(p[e], ve, a);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < C::VEC; ++e) a = fmaf(p[e], vf[e], a);
-      }
-      acc[i] = a;
-    }
-    __builtin_amdgcn_wave_barrier();
-    }
-    if (ok1)
-    {
-    const int tbase = lb1 * BS;
-    const bool partial = tbase + BS > tok1;
-    float sc[C::KL];
-#pragma unroll
-    for (int i = 0; i < C::KL; ++i) {
-      sc[i] = group_sum<C::LPT>(dot16<E>(kr1[i], qc)) * scale_log2;
-      if (partial && tbase + i * C::TPL + g >= tok1) sc[i] = -INFINITY;
-    }
-    float mb = sc[0];
-#pragma unroll
-    for (int i = 1; i < C::KL; ++i) mb = fmaxf(mb, sc[i]);
-    mb = xor_max<C::LPT, kWave>(mb);
-    const float mnew = fmaxf(m, mb);
-    const float alpha = fast_exp2(m - mnew);
-    m = mnew;
-    if (r == 0) {
-#pragma unroll
-      for (int i = 0; i < C::KL; ++i) lds_p[w][i * C::TPL + g] = fast_exp2(sc[i] - mnew);
-    }
-    __builtin_amdgcn_wave_barrier();
-    float p[C::VEC];
-#pragma unroll
-    for (int i = 0; i < C::VEC; i += 4) {
-      const f32x4 pv = *(const f32x4 *)&lds_p[w][cp * C::VEC + i];
-      p[i] = pv[0]; p[i + 1] = pv[1]; p[i + 2] = pv[2]; p[i + 3] = pv[3];
-    }
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < C::VEC; ++e) psum += p[e];
-    l = l * alpha + psum;
-#pragma unroll
-    for (int i = 0; i < C::VL; ++i) {
-      float vf[C::VEC];
-      unpack16<E>(vr1[i], vf);
-      float a = acc[i] * alpha;
-      if (partial) {
-        // Unfilled slots may hold anything (NaN included): their values count as 0.
-#pragma unroll
-        for (int e = 0; e < C::VEC; ++e) {
-          const float ve = (tbase + cp * C::VEC + e < tok1) ? vf[e] : 0.f;
-          a = fmaf(p[e], ve, a);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < C::VEC; ++e) a = fmaf(p[e], vf[e], a);
-      }
-      acc[i] = a;
-    }
-    __builtin_amdgcn_wave_barrier();
-    }
-  }
   }
 
   // Sum each dimension over the CPR lanes that share it, and l over the same lanes.
@@ -340,11 +215,11 @@ __device__ __forceinline__ void valu_item(
 
 // PLAN: persistent grid over the compact partition plan (S <= kPlanMaxSeqs);
 // otherwise one workgroup per (partition, query head, sequence) grid cell.
-template <typename E, int D, int BS, bool PLAN>
-// The grid path (one item per workgroup) with at most 32 VGPRs of loads per
-// block fits 64 VGPRs, i.e. 8 waves per SIMD, without spills; other variants
+// The grid path asks for 8 waves per SIMD (64 VGPRs) only where one block's
+// loads plus the query slice fit that budget without spills; other variants
 // keep the compiler's choice.
-__global__ __launch_bounds__(256, (!PLAN && ValuCfg<E, D, BS>::kLoadRegs <= 32) ? 8 : 1) void
+template <typename E, int D, int BS, bool PLAN>
+__global__ __launch_bounds__(256, (!PLAN && ValuCfg<E, D, BS>::kLoadRegs + 4 * ValuCfg<E, D, BS>::NC <= 24) ? 8 : 1) void
 decode_valu_kernel(
     void *__restrict__ out, int out_f32, const typename E::storage *__restrict__ q,
     const typename E::storage *__restrict__ kpool, const typename E::storage *__restrict__ vpool,
@@ -361,13 +236,13 @@ decode_valu_kernel(
       const int hq = it % Hq;
       const int j = it / Hq;
       const int s = plan_sequence(plan, S, j);
-      valu_item<E, D, BS, kValuNB>(sh, s, j - plan[s], hq, out, out_f32, q, kpool, vpool, block_tables,
+      valu_item<E, D, BS>(sh, s, j - plan[s], hq, out, out_f32, q, kpool, vpool, block_tables,
                           context_lens, num_blocks, Hkv, Hq, mbps, scale_log2, part_tokens, nparts,
                           ws_ml, ws_acc);
       __syncthreads();  // the merge buffers are reused by the next item
     }
   } else {
-    valu_item<E, D, BS, kValuNB>(sh, blockIdx.z, blockIdx.x, blockIdx.y, out, out_f32, q, kpool, vpool,
+    valu_item<E, D, BS>(sh, blockIdx.z, blockIdx.x, blockIdx.y, out, out_f32, q, kpool, vpool,
                         block_tables, context_lens, num_blocks, Hkv, Hq, mbps, scale_log2,
                         part_tokens, nparts, ws_ml, ws_acc);
   }

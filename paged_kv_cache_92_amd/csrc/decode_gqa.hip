@@ -14,7 +14,10 @@
 // is exactly the B-operand layout of P^T for the second product, so the
 // softmax weights never leave their registers.  V^T comes straight from the
 // dimension-major value tile (4 consecutive tokens of one dimension = 8
-// bytes per lane).  The running max and denominator are per head, i.e. per
+// bytes per lane; for 32-token blocks 8 tokens = 16 bytes and 16x16x32
+// products).  K^T operands come from the key tile's 64-byte pieces: one
+// k-step of 32 dimensions is one piece, so a wave load reads 16 tokens x 64
+// bytes contiguously.  The running max and denominator are per head, i.e. per
 // lane column, as in the block-wise walk of "vLLM — KV Cache와 PagedAttention
 // 완전 해부" (hrletsgo.me), "부록".  Scores are kept in the log2 domain.
 #include <algorithm>
@@ -64,6 +67,15 @@ struct Mfma<BF16> {
   __device__ static uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
 };
 
+// Token (within the block) that row i of score sub-tile sb holds.  For 32-token
+// blocks, rows 4g..4g+3 of sub-tiles 0 and 1 are tokens 8g..8g+7, the k-range
+// of lane group g in a 16x16x32 product.
+template <int BS>
+__device__ __forceinline__ int token_of_row(int sb, int i) {
+  if constexpr (BS == 32) return 8 * (i >> 2) + 4 * sb + (i & 3);
+  else return 16 * sb + i;
+}
+
 // One work item: partition `part` of sequence s for the G query heads of KV
 // head hkv.  `lds_dyn` holds the cross-wave merge buffers.
 template <typename E, int D, int BS>
@@ -77,6 +89,10 @@ __device__ __forceinline__ void mfma_item(
   constexpr int KS = D / 32;    // k-steps of the score product
   constexpr int NT = D / 16;    // 16-dimension tiles of the output
   constexpr int SUB = BS / 16;  // 16-token sub-tiles per block
+  // 32-token blocks: the two sub-tiles' score rows are interleaved so each
+  // lane ends up with 8 consecutive tokens, and P.V runs as 16x16x32 products
+  // over 16-byte V^T operands.
+  constexpr bool kWide = BS == 32;
   const int L = min(context_lens[s], mbps * BS);
   const int tok0 = part * part_tokens;
   if (tok0 >= L) return;
@@ -122,17 +138,25 @@ __device__ __forceinline__ void mfma_item(
     const uint16_t *kt = kpool + ((size_t)phys * Hkv + hkv) * (BS * D);
     const uint16_t *vt = vpool + ((size_t)phys * Hkv + hkv) * (D * BS);
     u32x4 ka[SUB][KS];
-    u32x2 va[SUB][NT];
 #pragma unroll
     for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        ka[sb][ks] = load16_stream(kt + (16 * sb + n16) * D + 32 * ks + 8 * g4);
+        ka[sb][ks] = load16_stream(kt + (ks * BS + token_of_row<BS>(sb, n16)) * 32 + 8 * g4);
+    // V^T operand: dimension row 16*nt + n16; tokens 8*g4 .. +8 (wide) or
+    // 16*sb + 4*g4 .. +4 of sub-tile sb.
+    u32x4 vw[kWide ? NT : 1];
+    u32x2 va[kWide ? 1 : SUB][kWide ? 1 : NT];
+    if constexpr (kWide) {
 #pragma unroll
-    for (int sb = 0; sb < SUB; ++sb)
+      for (int nt = 0; nt < NT; ++nt) vw[nt] = load16_stream(vt + (16 * nt + n16) * BS + 8 * g4);
+    } else {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        va[sb][nt] = load8_stream(vt + (16 * nt + n16) * BS + 16 * sb + 4 * g4);
+      for (int sb = 0; sb < SUB; ++sb)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          va[sb][nt] = load8_stream(vt + (16 * nt + n16) * BS + 16 * sb + 4 * g4);
+    }
 
     const int tbase = lb * BS;
     const bool partial = tbase + BS > tok1;
@@ -145,7 +169,7 @@ __device__ __forceinline__ void mfma_item(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float v = x[j] * scale_log2;
-        if (partial && tbase + 16 * sb + 4 * g4 + j >= tok1) v = -INFINITY;
+        if (partial && tbase + token_of_row<BS>(sb, 4 * g4 + j) >= tok1) v = -INFINITY;
         x[j] = v;
       }
       st[sb] = x;
@@ -159,8 +183,10 @@ __device__ __forceinline__ void mfma_item(
     const float mnew = fmaxf(m, mb);
     const float alpha = fast_exp2(m - mnew);
     m = mnew;
+    // Softmax weights of this lane's tokens, packed as P^T operands (hi and,
+    // for bf16, lo parts), in the token order of the lane's V^T rows.
+    uint32_t ph[2 * SUB], plo[2 * SUB];
     float psum = 0.f;
-    u32x2 pb[SUB], pl[SUB];
 #pragma unroll
     for (int sb = 0; sb < SUB; ++sb) {
       float p[4];
@@ -170,13 +196,11 @@ __device__ __forceinline__ void mfma_item(
         psum += p[j];
       }
       if constexpr (Mfma<E>::kSplitP) {
-        uint32_t h0, l0, h1, l1;
-        split_bf16x2(p[0], p[1], h0, l0);
-        split_bf16x2(p[2], p[3], h1, l1);
-        pb[sb] = u32x2{h0, h1};
-        pl[sb] = u32x2{l0, l1};
+        split_bf16x2(p[0], p[1], ph[2 * sb], plo[2 * sb]);
+        split_bf16x2(p[2], p[3], ph[2 * sb + 1], plo[2 * sb + 1]);
       } else {
-        pb[sb] = u32x2{Mfma<E>::pack2(p[0], p[1]), Mfma<E>::pack2(p[2], p[3])};
+        ph[2 * sb] = Mfma<E>::pack2(p[0], p[1]);
+        ph[2 * sb + 1] = Mfma<E>::pack2(p[2], p[3]);
       }
     }
     l = l * alpha + psum;
@@ -184,25 +208,46 @@ __device__ __forceinline__ void mfma_item(
     for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
     if (partial) {
       // Unfilled slots may hold anything (NaN included): zero their values.
+      if constexpr (kWide) {
+        const int t0 = tbase + 8 * g4;
 #pragma unroll
-      for (int sb = 0; sb < SUB; ++sb) {
-        const int t0 = tbase + 16 * sb + 4 * g4;
-        const uint32_t keep01 = (t0 < tok1 ? 0x0000ffffu : 0u) | (t0 + 1 < tok1 ? 0xffff0000u : 0u);
-        const uint32_t keep23 = (t0 + 2 < tok1 ? 0x0000ffffu : 0u) | (t0 + 3 < tok1 ? 0xffff0000u : 0u);
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t keep = (t0 + 2 * k < tok1 ? 0x0000ffffu : 0u) |
+                                (t0 + 2 * k + 1 < tok1 ? 0xffff0000u : 0u);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          va[sb][nt][0] &= keep01;
-          va[sb][nt][1] &= keep23;
+          for (int nt = 0; nt < NT; ++nt) vw[nt][k] &= keep;
+        }
+      } else {
+#pragma unroll
+        for (int sb = 0; sb < SUB; ++sb) {
+          const int t0 = tbase + 16 * sb + 4 * g4;
+          const uint32_t keep01 = (t0 < tok1 ? 0x0000ffffu : 0u) | (t0 + 1 < tok1 ? 0xffff0000u : 0u);
+          const uint32_t keep23 = (t0 + 2 < tok1 ? 0x0000ffffu : 0u) | (t0 + 3 < tok1 ? 0xffff0000u : 0u);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            va[sb][nt][0] &= keep01;
+            va[sb][nt][1] &= keep23;
+          }
         }
       }
     }
-#pragma unroll
-    for (int sb = 0; sb < SUB; ++sb)
+    if constexpr (kWide) {
+      const u32x4 pw = {ph[0], ph[1], ph[2], ph[3]};
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        acc[nt] = Mfma<E>::pv(va[sb][nt], pb[sb], acc[nt]);
-        if constexpr (Mfma<E>::kSplitP) acc[nt] = Mfma<E>::pv(va[sb][nt], pl[sb], acc[nt]);
+        acc[nt] = Mfma<E>::qk(vw[nt], pw, acc[nt]);
+        if constexpr (Mfma<E>::kSplitP) acc[nt] = Mfma<E>::qk(vw[nt], u32x4{plo[0], plo[1], plo[2], plo[3]}, acc[nt]);
       }
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < SUB; ++sb)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          acc[nt] = Mfma<E>::pv(va[sb][nt], u32x2{ph[2 * sb], ph[2 * sb + 1]}, acc[nt]);
+          if constexpr (Mfma<E>::kSplitP)
+            acc[nt] = Mfma<E>::pv(va[sb][nt], u32x2{plo[2 * sb], plo[2 * sb + 1]}, acc[nt]);
+        }
+    }
   }
 
   // Denominator of head n16: sum over the 4 row groups.

@@ -189,6 +189,15 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Wave-wide max of a value that is already uniform within each quad: the
+// half-row mirror then pairs whole quads, the row mirror whole half-rows.
+__device__ __forceinline__ float quad_uniform_max(float x) {
+  x = fmaxf(x, dpp_f32<0x141>(x));
+  x = fmaxf(x, dpp_f32<0x140>(x));
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
 // Max over lanes that differ only in bits [log2(FROM), log2(TO)) of the lane id.
 template <int FROM, int TO>
 __device__ __forceinline__ float xor_max(float x) {

@@ -142,24 +142,27 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   }
   __syncthreads();
 
-  // Global -> register staging of one tile.  Thread tid moves key chunks
-  // (token tid/KCR + KTPI*i, dims 8*(tid%KCR)..) and value chunks (dimension
-  // tid/8 + 32*i, tokens 8*(tid%8)..+8); a block id comes from the staged table.
-  constexpr int KCR = D / 8;          // 16-byte chunks per key row
-  constexpr int KTPI = 256 / KCR;     // key tokens covered per chunk round
+  // Global -> register staging of one tile.  Thread tid moves key pieces
+  // (token tid/4, bytes 16*(tid%4).. of each 64-byte piece of the row, so a
+  // wave reads 16 tokens x 64 bytes contiguously per piece) and value chunks
+  // (dimension tid/8 + 32*i, tokens 8*(tid%8)..+8); a block id comes from the
+  // staged table.
+  constexpr int KX = 32;              // elements per 64-byte key piece
+  static_assert(KPT == D / KX, "one key piece per chunk round");
+  const int ktok = tid >> 2, ksub = tid & 3;
   u32x4 kreg[KPT], vreg[VPT];
   auto load_tile = [&](int t) {
     const int t0 = t * kKT;
     const bool full = t0 + kKT <= ctx;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int tok = tid / KCR + KTPI * i;
-      const int pos = t0 + tok;
+    {
+      const int pos = t0 + ktok;
       // Positions past the context read a harmless in-pool address; their
       // scores are masked.  An invalid block id (a broken caller contract)
       // reads block 0 instead of faulting.
       const int blk = (full || pos < ctx) ? max(sBT[pos / BS], 0) : 0;
-      kreg[i] = load16(kpool + (((size_t)blk * Hkv + hkv) * BS + pos % BS) * D + 8 * (tid % KCR));
+      const uint16_t *kb = kpool + (((size_t)blk * Hkv + hkv) * KPT * BS + pos % BS) * KX + 8 * ksub;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) kreg[i] = load16(kb + (size_t)i * BS * KX);
     }
     {
       const int pos = t0 + 8 * (tid % 8);
@@ -184,8 +187,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   };
   auto store_tile = [&]() {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      *(u32x4 *)&sK[(tid / KCR + KTPI * i) * KROW + 8 * (tid % KCR)] = kreg[i];
+    for (int i = 0; i < KPT; ++i) *(u32x4 *)&sK[ktok * KROW + KX * i + 8 * ksub] = kreg[i];
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
       *(u32x4 *)&sV[(tid / 8 + 32 * i) * VROW + 8 * (tid % 8)] = vreg[i];

@@ -97,7 +97,8 @@ class Workload:
     def empty_pools(self):
         nb, H, B, d = self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim
         st = storage_dtype(self.dtype)
-        k = np.full((nb, H, B, d), _NAN_BITS[self.dtype], dtype=st)
+        x = 64 // np.dtype(st).itemsize           # key rows in 64-byte pieces
+        k = np.full((nb, H, d // x, B, x), _NAN_BITS[self.dtype], dtype=st)
         v = np.full((nb, H, d, B), _NAN_BITS[self.dtype], dtype=st)
         return k, v
 

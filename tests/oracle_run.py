@@ -6,6 +6,12 @@ import numpy as np
 import oracle
 
 
+def key_rows(k):
+    """K pool [nb][H][d/X][B][X] as [nb][H][B][d] (a copy): element (blk, h, off, e)."""
+    nb, H, nc, B, x = k.shape
+    return k.transpose(0, 1, 3, 2, 4).reshape(nb, H, B, nc * x)
+
+
 def fill_pools(wl, include_step=True):
     """Oracle pools after the workload's setup ops (and, by default, the step's scatter)."""
     k, v = wl.empty_pools()

@@ -20,6 +20,7 @@ MUTATIONS = [
     ("block-table index", "bt_row[j / B]", "bt_row[j % B]", ["test_scatter_then_gather_round_trip"]),
     ("slot offset", "int off = (int)(s % B);", "int off = (int)((s + 1) % B);",
      ["test_scatter_then_gather_round_trip"]),
+    ("K piece order", "* B + off) * X + e % X", "* B + off) * X + (e + 1) % X", ["test_slot_worked_example"]),
     ("V layout transposed", "* d + e) * B + off", "* B + off) * d + e", ["test_slot_worked_example"]),
     ("normaliser sign", "Z += z[j];", "Z -= z[j];", ["test_weights_are_softmax_and_sum_to_one"]),
     ("normalisation dropped", "double w = z[j] / Z;", "double w = z[j];",
