@@ -136,6 +136,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));  // RNE
+}
+
+// Two bf16 values (one 32-bit word) re-encoded as two fp16 values.  Exact for
+// |x| in [2^-17, 65504]; smaller magnitudes round on the fp16 subnormal grid
+// (absolute error <= 2^-25); a bf16 value of magnitude >= 65536 has no fp16
+// encoding, so the running maximum `amax` of the magnitudes seen is kept for
+// the caller to check against kF16Limit.
+constexpr float kF16Limit = 65536.f;  // the smallest bf16 magnitude fp16 cannot hold
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, float &amax) {
+  const float a = as_f32(w << 16), b = as_f32(w & 0xffff0000u);
+  amax = fmaxf(amax, fmaxf(fabsf(a), fabsf(b)));
+  return pack_f16x2(a, b);
+}
+
 // p = hi + lo with hi and lo in bf16: hi = RNE(p), lo = RNE(p - hi), so the
 // pair carries 16 significant bits (|p - hi - lo| <= 2^-17 |p|).  Works on
 // two values at once; hi and lo come back packed as the MFMA operands want.

@@ -20,6 +20,8 @@
 // then built from the lane's own registers and the A operand V^T is one
 // 16-byte LDS read from the dimension-major value tile.  Online softmax per
 // row, log2 domain.  Tiles entirely in a wave's future are skipped.
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -41,22 +43,26 @@ struct Mfma32<F16> {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
-  __device__ static uint32_t pack2(float lo, float hi) {
-    return (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
-  }
+  __device__ static uint32_t pack2(float lo, float hi) { return pack_f16x2(lo, hi); }
 };
-#ifndef PKV_PREFILL_SPLIT_P
-#define PKV_PREFILL_SPLIT_P 1
-#endif
 template <>
 struct Mfma32<BF16> {
-  static constexpr bool kSplitP = PKV_PREFILL_SPLIT_P;
+  static constexpr bool kSplitP = true;
   __device__ static f32x16 mma(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
   __device__ static uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
 };
+
+// bf16 inputs run P.V on the fp16 matrix cores: value tiles are re-encoded to
+// fp16 when staged in LDS (exact over fp16's range) and the softmax weights
+// pack to fp16 (11 significant bits, against 8 in bf16, so no hi + lo split).
+// A tile holding a value outside fp16's range is flagged while staged and
+// takes the exact bf16 route instead (values read from HBM, weights split).
+#ifndef PKV_PREFILL_CONV_V
+#define PKV_PREFILL_CONV_V 1
+#endif
 
 // Row i of a 32-token score product (i = 8a + 4h + b) holds token perm(i) of
 // its half-tile.
@@ -110,8 +116,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   const int j32 = lane & 31;  // query column of this lane
   const int h = lane >> 5;    // k-half / row group
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kKT * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VROW];
+  // Two LDS tile buffers: tile t+1 is stored while tile t is computed.
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKT * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VROW];
   extern __shared__ int sBT[];  // block ids of the positions this workgroup reads
 
   const int wrow0 = qt * kQT + 32 * w;                  // first chunk row of this wave
@@ -123,6 +130,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   const int ntiles = (wg_max_pos + kKT) / kKT;
 
   // Stage the block table once; tile loads then look block ids up in LDS.
+  __shared__ int sOvf;  // a staged value lay outside fp16's range
+  if (tid == 0) sOvf = 0;
   {
     const int32_t *bt = block_tables + (size_t)s * mbps;
     const int nbt = min((ntiles * kKT + BS - 1) / BS, mbps);
@@ -185,97 +194,132 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       }
     }
   };
-  auto store_tile = [&]() {
+  // Staging of one tile into LDS buffer buf.  CONV: values re-encoded to fp16;
+  // returns (through sOvf) whether any of them lay outside fp16's range.
+  auto store_tile = [&](auto conv, int buf) {
+    constexpr bool CONV = decltype(conv)::value;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) *(u32x4 *)&sK[ktok * KROW + KX * i + 8 * ksub] = kreg[i];
+    for (int i = 0; i < KPT; ++i) *(u32x4 *)&sK[buf][ktok * KROW + KX * i + 8 * ksub] = kreg[i];
+    float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i)
-      *(u32x4 *)&sV[(tid / 8 + 32 * i) * VROW + 8 * (tid % 8)] = vreg[i];
+    for (int i = 0; i < VPT; ++i) {
+      u32x4 x = vreg[i];
+      if constexpr (CONV) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = bf16x2_to_f16x2(x[k], amax);
+      }
+      *(u32x4 *)&sV[buf][(tid / 8 + 32 * i) * VROW + 8 * (tid % 8)] = x;
+    }
+    if (CONV && amax >= kF16Limit) sOvf = 1;
   };
 
-  float m = -INFINITY, l = 0.f;  // m in scaled log2 units
+  float m, l;  // running max (scaled log2 units) and this lane's denominator share
   f32x16 acc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
   const f32x16 zero16 = {};
-
   const int krow = perm_row(j32);  // key row (within a 32-token half) this lane feeds
-  load_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile();
+
+  // The whole walk over the key/value tiles.  CONV (bf16 only): P.V on the
+  // fp16 matrix cores; the walk reports whether every staged value fit fp16.
+  auto attend = [&](auto conv) -> bool {
+    constexpr bool CONV = decltype(conv)::value;
+    using PV = typename std::conditional<CONV, Mfma32<F16>, Mfma32<E>>::type;
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+    load_tile(0);
+    store_tile(conv, 0);
     __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);  // in flight while this tile is computed
-    if (t * kKT > wave_max_pos) continue;  // entirely in this wave's future
-    constexpr int HALVES = kKT / 32;
-    f32x16 st[HALVES];  // raw scores q.k
+    for (int t = 0; t < ntiles; ++t) {
+      const int cur = t & 1;
+      if (t + 1 < ntiles) load_tile(t + 1);  // in flight while this tile is computed
+      if (t * kKT <= wave_max_pos) {         // else entirely in this wave's future
+        constexpr int HALVES = kKT / 32;
+        f32x16 st[HALVES];  // raw scores q.k
 #pragma unroll
-    for (int hf = 0; hf < HALVES; ++hf) {
-      const uint16_t *krp = &sK[(32 * hf + krow) * KROW + 8 * h];
-      st[hf] = Mfma32<E>::mma(*(const u32x4 *)krp, qb[0], zero16);
+        for (int hf = 0; hf < HALVES; ++hf) {
+          const uint16_t *krp = &sK[cur][(32 * hf + krow) * KROW + 8 * h];
+          st[hf] = Mfma32<E>::mma(*(const u32x4 *)krp, qb[0], zero16);
 #pragma unroll
-      for (int ks = 1; ks < KS; ++ks) st[hf] = Mfma32<E>::mma(*(const u32x4 *)(krp + 16 * ks), qb[ks], st[hf]);
-    }
-    // Item 4a+b of half hf is tile token 32*hf + perm(8a+4h+b); only tiles
-    // that cross this wave's diagonal need the causal mask.
-    if (t * kKT + kKT - 1 > wave_min_pos) {
+          for (int ks = 1; ks < KS; ++ks) st[hf] = Mfma32<E>::mma(*(const u32x4 *)(krp + 16 * ks), qb[ks], st[hf]);
+        }
+        // Item 4a+b of half hf is tile token 32*hf + perm(8a+4h+b); only tiles
+        // that cross this wave's diagonal need the causal mask.
+        if (t * kKT + kKT - 1 > wave_min_pos) {
 #pragma unroll
-      for (int hf = 0; hf < HALVES; ++hf)
+          for (int hf = 0; hf < HALVES; ++hf)
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < 4; ++a)
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int pos = t * kKT + 32 * hf + 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
-            if (pos > qpos) st[hf][4 * a + b] = -INFINITY;
+              for (int b = 0; b < 4; ++b) {
+                const int pos = t * kKT + 32 * hf + 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
+                if (pos > qpos) st[hf][4 * a + b] = -INFINITY;
+              }
+        }
+        float mraw = -INFINITY;
+#pragma unroll
+        for (int hf = 0; hf < HALVES; ++hf)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, st[hf][i]);
+        mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+        const float mb = mraw * scale_log2;  // scale > 0: the max commutes with scaling
+        if (__any(mb > m + kRescaleLog2)) {
+          const float mnew = fmaxf(m, mb);
+          const float alpha = fast_exp2(m - mnew);  // 1 for rows that keep their reference
+          m = mnew;
+          l *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+        }
+        float psum = 0.f;
+#pragma unroll
+        for (int c = 0; c < 2 * HALVES; ++c) {
+          // This lane's 8 weights of k-step c (16 tokens) against the value
+          // rows 32dt + j32, tokens 16c + 8h .. +8 of the staged tile.
+          const int hf = c >> 1, c2 = c & 1;
+          float p[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            p[k] = fast_exp2(fmaf(st[hf][8 * c2 + k], scale_log2, -m));
+            psum += p[k];
           }
-    }
-    float mraw = -INFINITY;
+          u32x4 pb, pl;
+          if constexpr (PV::kSplitP) {
+            uint32_t hi[4], lo[4];
 #pragma unroll
-    for (int hf = 0; hf < HALVES; ++hf)
+            for (int k = 0; k < 4; ++k) split_bf16x2(p[2 * k], p[2 * k + 1], hi[k], lo[k]);
+            pb = u32x4{hi[0], hi[1], hi[2], hi[3]};
+            pl = u32x4{lo[0], lo[1], lo[2], lo[3]};
+          } else {
+            pb = u32x4{PV::pack2(p[0], p[1]), PV::pack2(p[2], p[3]), PV::pack2(p[4], p[5]),
+                       PV::pack2(p[6], p[7])};
+          }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, st[hf][i]);
-    mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
-    const float mb = mraw * scale_log2;  // scale > 0: the max commutes with scaling
-    if (__any(mb > m + kRescaleLog2)) {
-      const float mnew = fmaxf(m, mb);
-      const float alpha = fast_exp2(m - mnew);  // 1 for rows that keep their reference
-      m = mnew;
-      l *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-    }
-    float psum = 0.f;
-#pragma unroll
-    for (int c = 0; c < 2 * HALVES; ++c) {
-      const int hf = c >> 1, c2 = c & 1;
-      float p[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        p[k] = fast_exp2(fmaf(st[hf][8 * c2 + k], scale_log2, -m));
-        psum += p[k];
+          for (int dt = 0; dt < DT; ++dt) {
+            const u32x4 a = *(const u32x4 *)&sV[cur][(32 * dt + j32) * VROW + 16 * c + 8 * h];
+            acc[dt] = PV::mma(a, pb, acc[dt]);
+            if constexpr (PV::kSplitP) acc[dt] = PV::mma(a, pl, acc[dt]);
+          }
+        }
+        l += psum;
       }
-      u32x4 pb, pl;
-      if constexpr (Mfma32<E>::kSplitP) {
-        uint32_t h[4], lo[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) split_bf16x2(p[2 * k], p[2 * k + 1], h[k], lo[k]);
-        pb = u32x4{h[0], h[1], h[2], h[3]};
-        pl = u32x4{lo[0], lo[1], lo[2], lo[3]};
-      } else {
-        pb = u32x4{Mfma32<E>::pack2(p[0], p[1]), Mfma32<E>::pack2(p[2], p[3]),
-                   Mfma32<E>::pack2(p[4], p[5]), Mfma32<E>::pack2(p[6], p[7])};
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const u32x4 a = *(const u32x4 *)&sV[(32 * dt + j32) * VROW + 16 * c + 8 * h];
-        acc[dt] = Mfma32<E>::mma(a, pb, acc[dt]);
-        if constexpr (Mfma32<E>::kSplitP) acc[dt] = Mfma32<E>::mma(a, pl, acc[dt]);
-      }
+      // The other buffer was last read in the previous iteration, before the
+      // barrier that ended it; the barrier below publishes tile t+1.
+      if (t + 1 < ntiles) store_tile(conv, cur ^ 1);
+      __syncthreads();
     }
-    l += psum;
-  }
+    return !CONV || uniform(sOvf) == 0;
+  };
+
+  // bf16: the fp16 route first; if any staged value lay outside fp16's range
+  // (a flag every thread reads after the walk's last barrier), the whole walk
+  // is redone on the exact bf16 route.  Nothing was written meanwhile.
+  constexpr bool kConvV = std::is_same<E, BF16>::value && PKV_PREFILL_CONV_V;
+  bool done = false;
+  if constexpr (kConvV) done = attend(std::true_type{});
+  if (!done) attend(std::false_type{});
 
   // Lanes l and l^32 hold the two row halves of the same query column.
   const float ltot = l + __shfl_xor(l, 32);

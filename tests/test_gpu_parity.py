@@ -264,6 +264,25 @@ def _ragged_prefill(dtype, d, B, G, hist, chunks):
     return wl
 
 
+def test_prefill_bf16_values_beyond_f16_range():
+    # Values of magnitude >= 65536 exist in bf16 but not in fp16: the tiles that
+    # hold them must still give the exact result (they leave the fp16 route).
+    hist, chunks = np.array([70, 0, 150]), [100, 64, 40]
+    wl = _ragged_prefill(W.BF16, 128, 16, 2, hist, chunks)
+    hcu = np.concatenate([[0], np.cumsum(hist)])
+    ccu = np.concatenate([[0], np.cumsum(chunks)])
+    for s, j in [(0, 3), (0, 130), (2, 64), (2, 189)]:
+        if j < hist[s]:
+            arr, i = wl.setup[0].value, hcu[s] + j
+        else:
+            arr, i = wl.step_scatter.value, ccu[s] + j - hist[s]
+        big = W.round_to((arr[i].astype(np.uint32) << 16).view(np.float32) * 3e5, W.BF16)
+        arr[i] = big
+        wl.seq_tokens_value[s][j] = big
+    assert (wl.step_scatter.value.view(np.uint16) & 0x7FFF).max() >= 0x4780
+    _full_check(wl)
+
+
 def test_prefill_shared_prefix_with_copy_on_write():
     # Shared prefix of 20 tokens ends inside block 1: the partner's first own
     # token forces a block copy before its history is written.
