@@ -19,6 +19,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 // Element tags: storage is float for fp32 and uint16_t bits for fp16/bf16.
 struct F32 {
@@ -142,14 +143,16 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
 
 // Two bf16 values (one 32-bit word) re-encoded as two fp16 values.  Exact for
 // |x| in [2^-17, 65504]; smaller magnitudes round on the fp16 subnormal grid
-// (absolute error <= 2^-25); a bf16 value of magnitude >= 65536 has no fp16
-// encoding, so the running maximum `amax` of the magnitudes seen is kept for
-// the caller to check against kF16Limit.
-constexpr float kF16Limit = 65536.f;  // the smallest bf16 magnitude fp16 cannot hold
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, float &amax) {
-  const float a = as_f32(w << 16), b = as_f32(w & 0xffff0000u);
-  amax = fmaxf(amax, fmaxf(fabsf(a), fabsf(b)));
-  return pack_f16x2(a, b);
+// (absolute error <= 2^-25).  A bf16 value of magnitude >= 65536 has no fp16
+// encoding: `mag` keeps the running maximum of the magnitude bits (sign
+// cleared, compared as integers, which orders non-negative floats) for
+// bf16_beyond_f16 to check.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, u16x2 &mag) {
+  mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2, w & 0x7fff7fffu));
+  return pack_f16x2(as_f32(w << 16), as_f32(w & 0xffff0000u));
+}
+__device__ __forceinline__ bool bf16_beyond_f16(u16x2 mag) {
+  return (mag[0] > mag[1] ? mag[0] : mag[1]) >= 0x4780u;  // 0x4780 = 65536 in bf16
 }
 
 // p = hi + lo with hi and lo in bf16: hi = RNE(p), lo = RNE(p - hi), so the

@@ -200,17 +200,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     constexpr bool CONV = decltype(conv)::value;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) *(u32x4 *)&sK[buf][ktok * KROW + KX * i + 8 * ksub] = kreg[i];
-    float amax = 0.f;
+    u16x2 mag = {0, 0};
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       u32x4 x = vreg[i];
       if constexpr (CONV) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) x[k] = bf16x2_to_f16x2(x[k], amax);
+        for (int k = 0; k < 4; ++k) x[k] = bf16x2_to_f16x2(x[k], mag);
       }
       *(u32x4 *)&sV[buf][(tid / 8 + 32 * i) * VROW + 8 * (tid % 8)] = x;
     }
-    if (CONV && amax >= kF16Limit) sOvf = 1;
+    if (CONV && bf16_beyond_f16(mag)) sOvf = 1;
   };
 
   float m, l;  // running max (scaled log2 units) and this lane's denominator share
@@ -235,19 +235,24 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     for (int t = 0; t < ntiles; ++t) {
       const int cur = t & 1;
       if (t + 1 < ntiles) load_tile(t + 1);  // in flight while this tile is computed
-      if (t * kKT <= wave_max_pos) {         // else entirely in this wave's future
+      // One tile's scores, softmax update and P.V.
+      auto tile = [&]() {
         constexpr int HALVES = kKT / 32;
         f32x16 st[HALVES];  // raw scores q.k
+        const uint16_t *krp = &sK[cur][krow * KROW + 8 * h];
 #pragma unroll
-        for (int hf = 0; hf < HALVES; ++hf) {
-          const uint16_t *krp = &sK[cur][(32 * hf + krow) * KROW + 8 * h];
-          st[hf] = Mfma32<E>::mma(*(const u32x4 *)krp, qb[0], zero16);
+        for (int hf = 0; hf < HALVES; ++hf)
+          st[hf] = Mfma32<E>::mma(*(const u32x4 *)(krp + 32 * hf * KROW), qb[0], zero16);
 #pragma unroll
-          for (int ks = 1; ks < KS; ++ks) st[hf] = Mfma32<E>::mma(*(const u32x4 *)(krp + 16 * ks), qb[ks], st[hf]);
-        }
-        // Item 4a+b of half hf is tile token 32*hf + perm(8a+4h+b); only tiles
-        // that cross this wave's diagonal need the causal mask.
-        if (t * kKT + kKT - 1 > wave_min_pos) {
+        for (int ks = 1; ks < KS; ++ks)
+#pragma unroll
+          for (int hf = 0; hf < HALVES; ++hf)  // independent chains back to back
+            st[hf] = Mfma32<E>::mma(*(const u32x4 *)(krp + 32 * hf * KROW + 16 * ks), qb[ks], st[hf]);
+        // Item 4a+b of half hf is tile token 32*hf + perm(8a+4h+b).  Only a
+        // tile that crosses this wave's diagonal needs the causal mask (the
+        // hint keeps the compiler from turning the branch into selects that
+        // every tile would pay for).
+        if (__builtin_expect(t * kKT + kKT - 1 > wave_min_pos, 0)) {
 #pragma unroll
           for (int hf = 0; hf < HALVES; ++hf)
 #pragma unroll
@@ -304,6 +309,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
           }
         }
         l += psum;
+      };
+      if (t * kKT <= wave_max_pos) {  // else entirely in this wave's future
+        tile();
       }
       // The other buffer was last read in the previous iteration, before the
       // barrier that ended it; the barrier below publishes tile t+1.
