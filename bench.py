@@ -197,7 +197,7 @@ def main():
     out = torch.empty_like(dw0.q)
     ws = None
     if wl.mode == "decode":
-        need = pkv.decode_workspace_bytes(wl.S, wl.num_q_heads, wl.head_dim, wl.max_context_len,
+        need = pkv.decode_workspace_bytes(copies[0][1], wl.S, wl.num_q_heads, wl.max_context_len,
                                           wl.partition_size)
         if need:
             ws = torch.empty(need, dtype=torch.uint8, device="cuda")

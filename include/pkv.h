@@ -122,12 +122,18 @@ pkv_status pkv_reshape_and_cache(const pkv_cache *cache, const void *key, const 
 pkv_status pkv_copy_blocks(const pkv_cache *cache, const int32_t *src_dst, int64_t num_pairs,
                            hipStream_t stream);
 
+/* partition_size value: let the library split the work (see pkv_paged_decode). */
+#define PKV_PARTITION_AUTO (-1)
+
 /*
- * Workspace bytes pkv_paged_decode needs for these sizes (0 when every
- * sequence fits one partition, i.e. partition_size == 0 or
- * partition_size >= max_context_len).  Pure host arithmetic.
+ * Workspace bytes pkv_paged_decode needs for a call with these arguments (0
+ * when it needs none: partition_size 0, or every sequence fits one
+ * partition).  With PKV_PARTITION_AUTO the size depends on how many
+ * workgroups the current device keeps resident, so query it on the device
+ * the call will run on.  Returns 0 for invalid arguments (the decode call
+ * then reports them).
  */
-size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+size_t pkv_decode_workspace_bytes(const pkv_cache *cache, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t max_context_len, int32_t partition_size);
 
 /*
@@ -150,12 +156,17 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   scale             the softmax scale, normally 1/sqrt(head_dim) in fp32;
  *                     must be positive and finite
  *   partition_size    0: one workgroup pass over each whole sequence;
- *                     otherwise a multiple of block_size: each sequence is
- *                     split into partitions of that many tokens, each
- *                     partition writes (running max, denominator, weighted
- *                     sum) to the workspace and a reduce kernel combines
- *                     them (block-wise aggregation of partial results, [R]
- *                     section 02 "Aggregation")
+ *                     a positive multiple of block_size: each sequence is
+ *                     split into partitions of that many tokens starting at
+ *                     position 0, each partition writes (running max,
+ *                     denominator, weighted sum) to the workspace and a
+ *                     reduce kernel combines them (block-wise aggregation of
+ *                     partial results, [R] section 02 "Aggregation");
+ *                     PKV_PARTITION_AUTO: the blocks of all (sequence, head)
+ *                     pairs are dealt out in equal contiguous shares, one
+ *                     per resident workgroup, and pairs cut between shares
+ *                     are combined the same way (up to 8192 sequences; more
+ *                     run as partition_size 0)
  *   workspace         device scratch of >= pkv_decode_workspace_bytes(...)
  *                     bytes, 16-byte aligned; may be NULL when that is 0
  *

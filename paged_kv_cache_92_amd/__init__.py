@@ -7,8 +7,10 @@ of ``libpkv.so`` (``include/pkv.h``).  This package is the thin Python
 binding over that library (ctypes + torch device memory and streams), plus
 the host-side block manager and the seeded synthetic workloads.
 """
-from ._binding import (PagedKVCache, PkvError, copy_blocks, decode_workspace_bytes, gather_kv,
-                       lib, paged_decode, paged_prefill, reshape_and_cache, validate_host, version)
+from ._binding import (PARTITION_AUTO, PagedKVCache, PkvError, copy_blocks, decode_workspace_bytes,
+                       gather_kv, lib, paged_decode, paged_prefill, reshape_and_cache, validate_host,
+                       version)
 
-__all__ = ["PagedKVCache", "PkvError", "copy_blocks", "decode_workspace_bytes", "gather_kv", "lib",
-           "paged_decode", "paged_prefill", "reshape_and_cache", "validate_host", "version"]
+__all__ = ["PARTITION_AUTO", "PagedKVCache", "PkvError", "copy_blocks", "decode_workspace_bytes",
+           "gather_kv", "lib", "paged_decode", "paged_prefill", "reshape_and_cache", "validate_host",
+           "version"]

@@ -52,7 +52,7 @@ def lib() -> ctypes.CDLL:
         cp = ctypes.POINTER(PkvCacheDesc)
         L.pkv_reshape_and_cache.argtypes = [cp, vp, vp, vp, i64, vp]
         L.pkv_copy_blocks.argtypes = [cp, vp, i64, vp]
-        L.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.pkv_decode_workspace_bytes.argtypes = [cp, i32, i32, i32, i32]
         L.pkv_decode_workspace_bytes.restype = sz
         L.pkv_paged_decode.argtypes = [cp, vp, i32, vp, i32, vp, i32, vp, i32, i32, f32, i32, vp, sz, vp]
         L.pkv_paged_prefill.argtypes = [cp, vp, i32, vp, i32, vp, vp, vp, i32, i32, i32, i32, f32, vp]
@@ -150,9 +150,14 @@ def copy_blocks(cache: PagedKVCache, src_dst):
                                  _stream()))
 
 
-def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_size):
-    return int(lib().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
-                                                partition_size))
+PARTITION_AUTO = -1   # partition_size: balanced split over the resident workgroups
+
+
+def decode_workspace_bytes(cache: "PagedKVCache", num_seqs, num_q_heads, max_context_len,
+                           partition_size):
+    d = cache.desc()
+    return int(lib().pkv_decode_workspace_bytes(ctypes.byref(d), int(num_seqs), int(num_q_heads),
+                                                int(max_context_len), int(partition_size)))
 
 
 def _out(q, out, out_dtype):
@@ -179,7 +184,7 @@ def paged_decode(cache: PagedKVCache, q, block_tables, context_lens, max_context
     if scale is None:
         scale = 1.0 / math.sqrt(cache.head_dim)
     out = _out(q, out, out_dtype)
-    need = decode_workspace_bytes(S, Hq, cache.head_dim, max_context_len, partition_size)
+    need = decode_workspace_bytes(cache, S, Hq, max_context_len, partition_size)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None

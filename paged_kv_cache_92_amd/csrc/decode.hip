@@ -58,23 +58,24 @@ struct ValuLds {
   float acc[kWaves][D];
 };
 
-// One work item: partition `part` of sequence s for query head hq.
+// One work item: blocks [b0, b1) of sequence s for query head hq; the merged
+// result goes to the output or to a workspace partial row (dest).
 template <typename E, int D, int BS>
 __device__ __forceinline__ void valu_item(
-    ValuLds<E, D, BS> &sh, int s, int part, int hq, void *__restrict__ out, int out_f32,
-    const typename E::storage *__restrict__ q, const typename E::storage *__restrict__ kpool,
-    const typename E::storage *__restrict__ vpool, const int32_t *__restrict__ block_tables,
-    const int32_t *__restrict__ context_lens, int64_t num_blocks, int Hkv, int Hq, int mbps,
-    float scale_log2, int part_tokens, int nparts, float *__restrict__ ws_ml,
+    ValuLds<E, D, BS> &sh, int s, int hq, int b0, int b1, Dest dest, void *__restrict__ out,
+    int out_f32, const typename E::storage *__restrict__ q,
+    const typename E::storage *__restrict__ kpool, const typename E::storage *__restrict__ vpool,
+    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
+    int64_t num_blocks, int Hkv, int Hq, int mbps, float scale_log2, float *__restrict__ ws_ml,
     float *__restrict__ ws_acc) {
   using C = ValuCfg<E, D, BS>;
   using T = typename E::storage;
   const int L = min(context_lens[s], mbps * BS);
-  const int tok0 = part * part_tokens;
-  if (tok0 >= L) return;
-  const int tok1 = min(L, tok0 + part_tokens);
-  const int blk0 = tok0 / BS;
-  const int nblk = (tok1 - tok0 + BS - 1) / BS;
+  const int tok0 = b0 * BS;
+  const int tok1 = min(L, b1 * BS);
+  if (tok0 >= tok1) return;
+  const int blk0 = b0;
+  const int nblk = b1 - b0;
   const int hkv = hq / (Hq / Hkv);
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -199,11 +200,10 @@ __device__ __forceinline__ void valu_item(
       num = fmaf(f, lds_acc[k][e], num);
       den = fmaf(f, lds_l[k], den);
     }
-    const int np = num_partitions_of(L, part_tokens);
-    if (np == 1) {
+    if (dest.base < 0) {
       store_out<E>(out, ((size_t)s * Hq + hq) * D + e, num / den, out_f32);
     } else {
-      const size_t pi = ((size_t)s * Hq + hq) * nparts + part;
+      const size_t pi = dest.base;
       ws_acc[pi * D + e] = num;
       if (e == 0) {
         ws_ml[2 * pi] = M;
@@ -213,39 +213,28 @@ __device__ __forceinline__ void valu_item(
   }
 }
 
-// PLAN: persistent grid over the compact partition plan (S <= kPlanMaxSeqs);
-// otherwise one workgroup per (partition, query head, sequence) grid cell.
-// The grid path asks for 8 waves per SIMD (64 VGPRs) only where one block's
+// SCHED: kSchedGrid (one workgroup per grid cell), kSchedPlan (fixed
+// partitions over a persistent grid) or kSchedFlat (balanced ranges).  The
+// grid schedule asks for 8 waves per SIMD (64 VGPRs) only where one block's
 // loads plus the query slice fit that budget without spills; other variants
 // keep the compiler's choice.
-template <typename E, int D, int BS, bool PLAN>
-__global__ __launch_bounds__(256, (!PLAN && ValuCfg<E, D, BS>::kLoadRegs + 4 * ValuCfg<E, D, BS>::NC <= 24) ? 8 : 1) void
+template <typename E, int D, int BS, int SCHED>
+__global__ __launch_bounds__(256, (SCHED == kSchedGrid && ValuCfg<E, D, BS>::kLoadRegs + 4 * ValuCfg<E, D, BS>::NC <= 24) ? 8 : 1) void
 decode_valu_kernel(
     void *__restrict__ out, int out_f32, const typename E::storage *__restrict__ q,
     const typename E::storage *__restrict__ kpool, const typename E::storage *__restrict__ vpool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
     int64_t num_blocks, int Hkv, int Hq, int S, int mbps, float scale_log2, int part_tokens,
-    int nparts, float *__restrict__ ws_ml, float *__restrict__ ws_acc) {
+    int nparts, float *__restrict__ ws_ml, float *__restrict__ ws_acc, int *__restrict__ ws_hdr) {
   __shared__ ValuLds<E, D, BS> sh;
-  if constexpr (PLAN) {
-    extern __shared__ int plan[];
-    __shared__ int scan[16];
-    const int total = build_plan(plan, scan, context_lens, S, mbps * BS, part_tokens);
-    const int nitems = total * Hq;
-    for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
-      const int hq = it % Hq;
-      const int j = it / Hq;
-      const int s = plan_sequence(plan, S, j);
-      valu_item<E, D, BS>(sh, s, j - plan[s], hq, out, out_f32, q, kpool, vpool, block_tables,
-                          context_lens, num_blocks, Hkv, Hq, mbps, scale_log2, part_tokens, nparts,
-                          ws_ml, ws_acc);
-      __syncthreads();  // the merge buffers are reused by the next item
-    }
-  } else {
-    valu_item<E, D, BS>(sh, blockIdx.z, blockIdx.x, blockIdx.y, out, out_f32, q, kpool, vpool,
-                        block_tables, context_lens, num_blocks, Hkv, Hq, mbps, scale_log2,
-                        part_tokens, nparts, ws_ml, ws_acc);
-  }
+  extern __shared__ int plan[];
+  __shared__ int scan[16];
+  run_schedule<SCHED>(
+      [&](int s, int hq, int b0, int b1, Dest dest) {
+        valu_item<E, D, BS>(sh, s, hq, b0, b1, dest, out, out_f32, q, kpool, vpool, block_tables,
+                            context_lens, num_blocks, Hkv, Hq, mbps, scale_log2, ws_ml, ws_acc);
+      },
+      plan, scan, context_lens, S, mbps * BS, BS, Hq, 1, part_tokens, nparts, ws_hdr);
 }
 
 // Cross-partition reduce: o = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
@@ -273,32 +262,63 @@ __global__ __launch_bounds__(128) void decode_reduce_kernel(
   }
 }
 
+// Balanced-schedule reduce: the partial rows of every segment that spans
+// several workgroup ranges (see run_schedule), combined as above.  HU head
+// units per sequence, G query heads per unit.
+template <typename E, int D>
+__global__ __launch_bounds__(128) void decode_reduce_flat_kernel(
+    void *__restrict__ out, int out_f32, const int *__restrict__ ws_hdr, int Hq, int HU, int G,
+    const float *__restrict__ ws_ml, const float *__restrict__ ws_acc) {
+  const int hq = blockIdx.x;
+  const int s = blockIdx.y;
+  const int g = hq % G;
+  const FlatSegment f = flat_segment(ws_hdr, s, hq / G, HU);
+  if (f.w1 <= f.w0) return;
+  auto row = [&](int w) -> size_t {
+    const int slot = (w == f.w0 && f.w0_last) ? 2 * w + 1 : 2 * w;
+    return (size_t)slot * G + g;
+  };
+  float M = -INFINITY;
+  for (int w = f.w0; w <= f.w1; ++w) M = fmaxf(M, ws_ml[2 * row(w)]);
+  for (int e = threadIdx.x; e < D; e += blockDim.x) {
+    float num = 0.f, den = 0.f;
+    for (int w = f.w0; w <= f.w1; ++w) {
+      const size_t r = row(w);
+      const float fct = fast_exp2(ws_ml[2 * r] - M);
+      num = fmaf(fct, ws_acc[r * D + e], num);
+      den = fmaf(fct, ws_ml[2 * r + 1], den);
+    }
+    store_out<E>(out, ((size_t)s * Hq + hq) * D + e, num / den, out_f32);
+  }
+}
+
 template <typename E, int D, int BS>
 void launch_valu_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
   using T = typename E::storage;
   const float sl = a.scale * kLog2e;
-  // Persistent plan grid when sequences split into several partitions (it
-  // launches nothing for empty partitions); without a split every grid cell
-  // has work and the hardware scheduler balances the uneven lengths itself.
+  const size_t lds = sizeof(int) * (a.S + 1);
+  auto go = [&](auto kern, dim3 grid, size_t dyn) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), dyn, stream, a.out, (int)a.out_f32, (const T *)a.q,
+                       (const T *)c.k, (const T *)c.v, a.block_tables, a.context_lens,
+                       c.num_blocks, c.H, a.Hq, a.S, a.max_blocks_per_seq, sl, a.partition_tokens,
+                       a.num_partitions, a.ws_ml, a.ws_acc, a.ws_hdr);
+  };
+  // Fixed partitions run a persistent grid over the non-empty cells (a 3-D
+  // grid would launch a workgroup for every empty partition); without a split
+  // every grid cell has work and the hardware balances uneven lengths itself.
 #ifndef PKV_GRID_FACTOR
 #define PKV_GRID_FACTOR 4
 #endif
-  if (a.num_partitions > 1 && a.S <= kPlanMaxSeqs) {
-    auto kern = decode_valu_kernel<E, D, BS, true>;
-    const size_t lds = sizeof(int) * (a.S + 1);
+  if (a.flat) {
+    go(decode_valu_kernel<E, D, BS, kSchedFlat>, dim3(a.flat_grid), lds);
+  } else if (a.num_partitions > 1 && a.S <= kPlanMaxSeqs) {
+    auto kern = decode_valu_kernel<E, D, BS, kSchedPlan>;
     const int64_t cells = (int64_t)a.S * a.num_partitions * a.Hq;
     const int grid = (int)std::min<int64_t>(cells, PKV_GRID_FACTOR * (int64_t)resident_workgroups((const void *)kern, 256, lds));
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, a.out, (int)a.out_f32,
-                       (const T *)a.q, (const T *)c.k, (const T *)c.v, a.block_tables,
-                       a.context_lens, c.num_blocks, c.H, a.Hq, a.S, a.max_blocks_per_seq, sl,
-                       a.partition_tokens, a.num_partitions, a.ws_ml, a.ws_acc);
+    go(kern, dim3(grid), lds);
   } else {
-    const dim3 grid((unsigned)a.num_partitions, (unsigned)a.Hq, (unsigned)a.S);
-    hipLaunchKernelGGL((decode_valu_kernel<E, D, BS, false>), grid, dim3(256), 0, stream, a.out,
-                       (int)a.out_f32, (const T *)a.q, (const T *)c.k, (const T *)c.v,
-                       a.block_tables, a.context_lens, c.num_blocks, c.H, a.Hq, a.S,
-                       a.max_blocks_per_seq, sl, a.partition_tokens, a.num_partitions, a.ws_ml,
-                       a.ws_acc);
+    go(decode_valu_kernel<E, D, BS, kSchedGrid>,
+       dim3((unsigned)a.num_partitions, (unsigned)a.Hq, (unsigned)a.S), 0);
   }
 }
 
@@ -310,18 +330,38 @@ void launch_valu_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) 
   else launch_valu_t<E, 128, 32>(c, a, stream);
 }
 
+template <typename E, int D, int BS>
+int flat_grid_t(int S) {
+  return resident_workgroups((const void *)decode_valu_kernel<E, D, BS, kSchedFlat>, 256,
+                             sizeof(int) * (S + 1));
+}
+
+template <typename E>
+int flat_grid_e(const CacheDesc &c, int S) {
+  if (c.D == 64 && c.B == 16) return flat_grid_t<E, 64, 16>(S);
+  if (c.D == 64 && c.B == 32) return flat_grid_t<E, 64, 32>(S);
+  if (c.D == 128 && c.B == 16) return flat_grid_t<E, 128, 16>(S);
+  return flat_grid_t<E, 128, 32>(S);
+}
+
 template <typename E>
 void launch_reduce_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
   const dim3 grid((unsigned)a.Hq, (unsigned)a.S);
   const int mt = a.max_blocks_per_seq * c.B;
-  if (c.D == 64)
-    hipLaunchKernelGGL((decode_reduce_kernel<E, 64>), grid, dim3(64), 0, stream, a.out,
-                       (int)a.out_f32, a.context_lens, a.Hq, mt, a.partition_tokens, a.num_partitions, a.ws_ml,
-                       a.ws_acc);
-  else
-    hipLaunchKernelGGL((decode_reduce_kernel<E, 128>), grid, dim3(128), 0, stream, a.out,
-                       (int)a.out_f32, a.context_lens, a.Hq, mt, a.partition_tokens, a.num_partitions, a.ws_ml,
-                       a.ws_acc);
+  const int G = a.Hq / c.H;
+  const bool mfma = G > 1 && c.dtype != 0;
+  const int HU = mfma ? c.H : a.Hq, GU = mfma ? G : 1;
+  auto go = [&](auto kern_part, auto kern_flat, int threads) {
+    if (a.flat)
+      hipLaunchKernelGGL(kern_flat, grid, dim3(threads), 0, stream, a.out, (int)a.out_f32,
+                         (const int *)a.ws_hdr, a.Hq, HU, GU, a.ws_ml, a.ws_acc);
+    else
+      hipLaunchKernelGGL(kern_part, grid, dim3(threads), 0, stream, a.out, (int)a.out_f32,
+                         a.context_lens, a.Hq, mt, a.partition_tokens, a.num_partitions, a.ws_ml,
+                         a.ws_acc);
+  };
+  if (c.D == 64) go(decode_reduce_kernel<E, 64>, decode_reduce_flat_kernel<E, 64>, 64);
+  else go(decode_reduce_kernel<E, 128>, decode_reduce_flat_kernel<E, 128>, 128);
 }
 
 }  // namespace
@@ -331,6 +371,12 @@ hipError_t launch_decode_valu(const CacheDesc &c, const DecodeArgs &a, hipStream
   else if (c.dtype == 1) launch_valu_e<F16>(c, a, stream);
   else launch_valu_e<BF16>(c, a, stream);
   return hipGetLastError();
+}
+
+int decode_valu_flat_grid(const CacheDesc &c, int S) {
+  if (c.dtype == 0) return flat_grid_e<F32>(c, S);
+  if (c.dtype == 1) return flat_grid_e<F16>(c, S);
+  return flat_grid_e<BF16>(c, S);
 }
 
 hipError_t launch_decode_reduce(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {

@@ -76,16 +76,17 @@ __device__ __forceinline__ int token_of_row(int sb, int i) {
   else return 16 * sb + i;
 }
 
-// One work item: partition `part` of sequence s for the G query heads of KV
-// head hkv.  `lds_dyn` holds the cross-wave merge buffers.
+// One work item: blocks [b0, b1) of sequence s for the G query heads of KV
+// head hkv; head h's merged result goes to the output or to workspace
+// partial row dest.base + h * dest.stride.  `lds_dyn` holds the cross-wave
+// merge buffers.
 template <typename E, int D, int BS>
 __device__ __forceinline__ void mfma_item(
-    float *lds_dyn, int s, int part, int hkv, void *__restrict__ out, int out_f32,
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kpool,
+    float *lds_dyn, int s, int hkv, int b0, int b1, Dest dest, void *__restrict__ out,
+    int out_f32, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kpool,
     const uint16_t *__restrict__ vpool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, int64_t num_blocks, int Hkv, int G, int mbps,
-    float scale_log2, int part_tokens, int nparts, float *__restrict__ ws_ml,
-    float *__restrict__ ws_acc) {
+    float scale_log2, float *__restrict__ ws_ml, float *__restrict__ ws_acc) {
   constexpr int KS = D / 32;    // k-steps of the score product
   constexpr int NT = D / 16;    // 16-dimension tiles of the output
   constexpr int SUB = BS / 16;  // 16-token sub-tiles per block
@@ -94,11 +95,11 @@ __device__ __forceinline__ void mfma_item(
   // over 16-byte V^T operands.
   constexpr bool kWide = BS == 32;
   const int L = min(context_lens[s], mbps * BS);
-  const int tok0 = part * part_tokens;
-  if (tok0 >= L) return;
-  const int tok1 = min(L, tok0 + part_tokens);
-  const int blk0 = tok0 / BS;
-  const int nblk = (tok1 - tok0 + BS - 1) / BS;
+  const int tok0 = b0 * BS;
+  const int tok1 = min(L, b1 * BS);
+  if (tok0 >= tok1) return;
+  const int blk0 = b0;
+  const int nblk = b1 - b0;
   const int Hq = Hkv * G;
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -264,7 +265,6 @@ __device__ __forceinline__ void mfma_item(
   }
   __syncthreads();
 
-  const int np = num_partitions_of(L, part_tokens);
   for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
     const int h = idx / D;
     const int e = idx - h * D;
@@ -279,10 +279,10 @@ __device__ __forceinline__ void mfma_item(
       den = fmaf(f, lds_l[k * 16 + h], den);
     }
     const int hq = hkv * G + h;
-    if (np == 1) {
+    if (dest.base < 0) {
       store_out<E>(out, ((size_t)s * Hq + hq) * D + e, num / den, out_f32);
     } else {
-      const size_t pi = ((size_t)s * Hq + hq) * nparts + part;
+      const size_t pi = (size_t)dest.base + (size_t)h * dest.stride;
       ws_acc[pi * D + e] = num;
       if (e == 0) {
         ws_ml[2 * pi] = M;
@@ -292,70 +292,63 @@ __device__ __forceinline__ void mfma_item(
   }
 }
 
-// PLAN: persistent grid over the compact partition plan (S <= kPlanMaxSeqs);
-// otherwise one workgroup per (partition, KV head, sequence) grid cell.
-// Dynamic LDS: [plan: S + 1 ints, padded to 16 bytes][merge buffers].
-template <typename E, int D, int BS, bool PLAN>
+// SCHED as for the wavefront kernel.  Dynamic LDS: [plan: S + 1 ints,
+// padded to 16 bytes][merge buffers].
 #ifndef PKV_MFMA_MIN_WAVES
 #define PKV_MFMA_MIN_WAVES 4
 #endif
+template <typename E, int D, int BS, int SCHED>
 __global__ __launch_bounds__(256, PKV_MFMA_MIN_WAVES) void decode_mfma_kernel(
     void *__restrict__ out, int out_f32, const uint16_t *__restrict__ q,
     const uint16_t *__restrict__ kpool, const uint16_t *__restrict__ vpool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
     int64_t num_blocks, int Hkv, int G, int S, int mbps, float scale_log2, int part_tokens,
-    int nparts, float *__restrict__ ws_ml, float *__restrict__ ws_acc) {
+    int nparts, float *__restrict__ ws_ml, float *__restrict__ ws_acc, int *__restrict__ ws_hdr) {
   extern __shared__ __attribute__((aligned(16))) int dyn[];
-  if constexpr (PLAN) {
-    __shared__ int scan[16];
-    int *plan = dyn;
-    float *merge = (float *)(dyn + ((S + 1 + 3) & ~3));
-    const int total = build_plan(plan, scan, context_lens, S, mbps * BS, part_tokens);
-    const int nitems = total * Hkv;
-    for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
-      const int hkv = it % Hkv;
-      const int j = it / Hkv;
-      const int s = plan_sequence(plan, S, j);
-      mfma_item<E, D, BS>(merge, s, j - plan[s], hkv, out, out_f32, q, kpool, vpool,
-                          block_tables, context_lens, num_blocks, Hkv, G, mbps, scale_log2,
-                          part_tokens, nparts, ws_ml, ws_acc);
-      __syncthreads();  // the merge buffers are reused by the next item
-    }
-  } else {
-    mfma_item<E, D, BS>((float *)dyn, blockIdx.z, blockIdx.x, blockIdx.y, out, out_f32, q, kpool,
-                        vpool, block_tables, context_lens, num_blocks, Hkv, G, mbps, scale_log2,
-                        part_tokens, nparts, ws_ml, ws_acc);
-  }
+  __shared__ int scan[16];
+  int *plan = dyn;
+  float *merge = (float *)(dyn + (SCHED == kSchedGrid ? 0 : ((S + 1 + 3) & ~3)));
+  run_schedule<SCHED>(
+      [&](int s, int hkv, int b0, int b1, Dest dest) {
+        mfma_item<E, D, BS>(merge, s, hkv, b0, b1, dest, out, out_f32, q, kpool, vpool,
+                            block_tables, context_lens, num_blocks, Hkv, G, mbps, scale_log2,
+                            ws_ml, ws_acc);
+      },
+      plan, scan, context_lens, S, mbps * BS, BS, Hkv, G, part_tokens, nparts, ws_hdr);
+}
+
+template <typename E, int D, int BS>
+size_t merge_bytes(int G) {
+  return sizeof(float) * (2 * kWaves * 16 + (size_t)kWaves * G * (D + 1));
 }
 
 template <typename E, int D, int BS>
 void launch_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
   const int G = a.Hq / c.H;
-  const size_t merge = sizeof(float) * (2 * kWaves * 16 + (size_t)kWaves * G * (D + 1));
+  const size_t merge = merge_bytes<E, D, BS>(G);
+  const size_t plan = sizeof(int) * (size_t)((a.S + 1 + 3) & ~3);
   const float sl = a.scale * kLog2e;
-  // Persistent plan grid when sequences split into several partitions (it
-  // launches nothing for empty partitions); without a split every grid cell
-  // has work and the hardware scheduler balances the uneven lengths itself.
-#ifndef PKV_GRID_FACTOR
-#define PKV_GRID_FACTOR 4
-#endif
-  if (a.num_partitions > 1 && a.S <= kPlanMaxSeqs) {
-    auto kern = decode_mfma_kernel<E, D, BS, true>;
-    const size_t lds = sizeof(int) * (size_t)((a.S + 1 + 3) & ~3) + merge;
-    const int64_t cells = (int64_t)a.S * a.num_partitions * c.H;
-    const int grid = (int)std::min<int64_t>(cells, PKV_GRID_FACTOR * (int64_t)resident_workgroups((const void *)kern, 256, lds));
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, a.out, (int)a.out_f32,
+  auto go = [&](auto kern, dim3 grid, size_t dyn) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), dyn, stream, a.out, (int)a.out_f32,
                        (const uint16_t *)a.q, (const uint16_t *)c.k, (const uint16_t *)c.v,
                        a.block_tables, a.context_lens, c.num_blocks, c.H, G, a.S,
                        a.max_blocks_per_seq, sl, a.partition_tokens, a.num_partitions, a.ws_ml,
-                       a.ws_acc);
+                       a.ws_acc, a.ws_hdr);
+  };
+  // Schedules as for the wavefront kernel.
+#ifndef PKV_GRID_FACTOR
+#define PKV_GRID_FACTOR 4
+#endif
+  if (a.flat) {
+    go(decode_mfma_kernel<E, D, BS, kSchedFlat>, dim3(a.flat_grid), plan + merge);
+  } else if (a.num_partitions > 1 && a.S <= kPlanMaxSeqs) {
+    auto kern = decode_mfma_kernel<E, D, BS, kSchedPlan>;
+    const int64_t cells = (int64_t)a.S * a.num_partitions * c.H;
+    const int grid = (int)std::min<int64_t>(cells, PKV_GRID_FACTOR * (int64_t)resident_workgroups((const void *)kern, 256, plan + merge));
+    go(kern, dim3(grid), plan + merge);
   } else {
-    const dim3 grid((unsigned)a.num_partitions, (unsigned)c.H, (unsigned)a.S);
-    hipLaunchKernelGGL((decode_mfma_kernel<E, D, BS, false>), grid, dim3(256), merge, stream, a.out,
-                       (int)a.out_f32, (const uint16_t *)a.q, (const uint16_t *)c.k,
-                       (const uint16_t *)c.v, a.block_tables, a.context_lens, c.num_blocks, c.H, G,
-                       a.S, a.max_blocks_per_seq, sl, a.partition_tokens, a.num_partitions, a.ws_ml,
-                       a.ws_acc);
+    go(decode_mfma_kernel<E, D, BS, kSchedGrid>,
+       dim3((unsigned)a.num_partitions, (unsigned)c.H, (unsigned)a.S), merge);
   }
 }
 
@@ -367,12 +360,30 @@ void launch_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
   else launch_t<E, 128, 32>(c, a, stream);
 }
 
+template <typename E, int D, int BS>
+int flat_grid_t(int G, int S) {
+  const size_t dyn = sizeof(int) * (size_t)((S + 1 + 3) & ~3) + merge_bytes<E, D, BS>(G);
+  return resident_workgroups((const void *)decode_mfma_kernel<E, D, BS, kSchedFlat>, 256, dyn);
+}
+
+template <typename E>
+int flat_grid_e(const CacheDesc &c, int G, int S) {
+  if (c.D == 64 && c.B == 16) return flat_grid_t<E, 64, 16>(G, S);
+  if (c.D == 64 && c.B == 32) return flat_grid_t<E, 64, 32>(G, S);
+  if (c.D == 128 && c.B == 16) return flat_grid_t<E, 128, 16>(G, S);
+  return flat_grid_t<E, 128, 32>(G, S);
+}
+
 }  // namespace
 
 hipError_t launch_decode_mfma(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
   if (c.dtype == 1) launch_e<F16>(c, a, stream);
   else launch_e<BF16>(c, a, stream);
   return hipGetLastError();
+}
+
+int decode_mfma_flat_grid(const CacheDesc &c, int G, int S) {
+  return c.dtype == 1 ? flat_grid_e<F16>(c, G, S) : flat_grid_e<BF16>(c, G, S);
 }
 
 }  // namespace pkv

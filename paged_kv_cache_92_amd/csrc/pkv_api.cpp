@@ -78,11 +78,41 @@ Partitioning partitioning(int max_context_len, int partition_size, int B) {
   return p;
 }
 
-size_t workspace_bytes(int S, int Hq, int D, const Partitioning &p) {
-  if (p.count <= 1) return 0;
-  const size_t n = (size_t)S * Hq * p.count;
-  const size_t ml = (n * 2 * sizeof(float) + 255) / 256 * 256;
-  return ml + n * D * sizeof(float);
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+// How a decode call is scheduled and where its workspace pieces live.
+struct DecodePlan {
+  bool mfma = false;   // grouped heads on the matrix cores
+  bool flat = false;   // balanced schedule
+  int flat_grid = 0;
+  Partitioning part{0, 1};
+  size_t off_ml = 0, off_acc = 0, bytes = 0;
+  bool reduce() const { return flat || part.count > 1; }
+};
+
+// Assumes a validated cache and sizes.
+DecodePlan plan_decode(const pkv::CacheDesc &c, int S, int Hq, int max_context_len,
+                       int partition_size) {
+  DecodePlan d;
+  const int G = Hq / c.H;
+  d.mfma = G > 1 && c.dtype != PKV_F32;
+  if (partition_size == PKV_PARTITION_AUTO && S <= pkv::kPlanMaxSeqs) {
+    d.flat = true;
+    d.flat_grid = d.mfma ? pkv::decode_mfma_flat_grid(c, G, S) : pkv::decode_valu_flat_grid(c, S);
+    const size_t rows = (size_t)2 * d.flat_grid * (d.mfma ? G : 1);
+    d.off_ml = round256(sizeof(int) * ((size_t)pkv::kFlatPrefixAt + S + 1));
+    d.off_acc = d.off_ml + round256(rows * 2 * sizeof(float));
+    d.bytes = d.off_acc + rows * c.D * sizeof(float);
+    return d;
+  }
+  d.part = partitioning(max_context_len, partition_size == PKV_PARTITION_AUTO ? 0 : partition_size, c.B);
+  if (d.part.count > 1) {
+    const size_t rows = (size_t)S * Hq * d.part.count;
+    d.off_ml = 0;
+    d.off_acc = round256(rows * 2 * sizeof(float));
+    d.bytes = d.off_acc + rows * c.D * sizeof(float);
+  }
+  return d;
 }
 
 }  // namespace
@@ -147,11 +177,13 @@ pkv_status pkv_copy_blocks(const pkv_cache *cache, const int32_t *src_dst, int64
   return hip_status(pkv::launch_copy_blocks(c, src_dst, num_pairs, stream), "copy_blocks launch");
 }
 
-size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+size_t pkv_decode_workspace_bytes(const pkv_cache *cache, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t max_context_len, int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
-  const Partitioning p = partitioning(max_context_len, partition_size, 16);
-  return workspace_bytes(num_seqs, num_q_heads, head_dim, p);
+  pkv::CacheDesc c;
+  if (check_cache(cache, &c) != PKV_OK) return 0;
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_q_heads % c.H != 0 || max_context_len <= 0)
+    return 0;
+  return plan_decode(c, num_seqs, num_q_heads, max_context_len, partition_size).bytes;
 }
 
 pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype, const void *q,
@@ -180,14 +212,14 @@ pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype
     return fail(PKV_ERR_INVALID, "max_context_len %d outside [1, max_blocks_per_seq*block_size]",
                 max_context_len);
   if (!(scale > 0.f) || !(scale < INFINITY)) return fail(PKV_ERR_INVALID, "scale must be positive and finite");
-  if (partition_size < 0 || partition_size % c.B != 0)
-    return fail(PKV_ERR_INVALID, "partition_size %d must be 0 or a positive multiple of block_size %d",
+  if (partition_size != PKV_PARTITION_AUTO && (partition_size < 0 || partition_size % c.B != 0))
+    return fail(PKV_ERR_INVALID,
+                "partition_size %d must be PKV_PARTITION_AUTO, 0 or a positive multiple of block_size %d",
                 partition_size, c.B);
   const int G = num_q_heads / c.H;
-  const bool mfma = G > 1 && c.dtype != PKV_F32;
-  if (mfma && G > 16) return fail(PKV_ERR_UNSUPPORTED, "group size %d > 16", G);
-  const Partitioning p = partitioning(max_context_len, partition_size, c.B);
-  const size_t need = workspace_bytes(num_seqs, num_q_heads, c.D, p);
+  if (G > 1 && c.dtype != PKV_F32 && G > 16) return fail(PKV_ERR_UNSUPPORTED, "group size %d > 16", G);
+  const DecodePlan plan = plan_decode(c, num_seqs, num_q_heads, max_context_len, partition_size);
+  const size_t need = plan.bytes;
   if (need > 0) {
     if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required", need);
     if (ws_bytes < need)
@@ -205,18 +237,21 @@ pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype
   a.S = num_seqs;
   a.max_context_len = max_context_len;
   a.scale = scale;
-  a.partition_tokens = p.tokens;
-  a.num_partitions = p.count;
+  a.partition_tokens = plan.part.tokens;
+  a.num_partitions = plan.part.count;
+  a.flat = plan.flat;
+  a.flat_grid = plan.flat_grid;
   a.ws_ml = nullptr;
   a.ws_acc = nullptr;
+  a.ws_hdr = nullptr;
   if (need > 0) {
-    const size_t n = (size_t)num_seqs * num_q_heads * p.count;
-    a.ws_ml = (float *)workspace;
-    a.ws_acc = (float *)((char *)workspace + (n * 2 * sizeof(float) + 255) / 256 * 256);
+    a.ws_hdr = plan.flat ? (int *)workspace : nullptr;
+    a.ws_ml = (float *)((char *)workspace + plan.off_ml);
+    a.ws_acc = (float *)((char *)workspace + plan.off_acc);
   }
-  hipError_t e = mfma ? pkv::launch_decode_mfma(c, a, stream) : pkv::launch_decode_valu(c, a, stream);
+  hipError_t e = plan.mfma ? pkv::launch_decode_mfma(c, a, stream) : pkv::launch_decode_valu(c, a, stream);
   if (e != hipSuccess) return hip_status(e, "paged_decode launch");
-  if (p.count > 1) {
+  if (plan.reduce()) {
     e = pkv::launch_decode_reduce(c, a, stream);
     if (e != hipSuccess) return hip_status(e, "paged_decode reduce launch");
   }

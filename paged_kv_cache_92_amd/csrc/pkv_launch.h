@@ -9,8 +9,16 @@
 
 namespace pkv {
 
+// Sequences per launch that the decode kernels' in-LDS prefix supports;
+// beyond it they run one workgroup per grid cell.
+constexpr int kPlanMaxSeqs = 8192;
+
+// Balanced-schedule workspace header (ints): [0] units per workgroup, [1]
+// total units, then from kFlatPrefixAt the prefix sums of units per sequence.
+constexpr int kFlatPrefixAt = 64;
+
 struct CacheDesc {
-  void *k;           // [num_blocks][H][B][D]
+  void *k;           // [num_blocks][H][D/X][B][X], X = 64 bytes / element
   void *v;           // [num_blocks][H][D][B]
   int64_t num_blocks;
   int H, B, D;
@@ -31,8 +39,14 @@ struct DecodeArgs {
   float scale;
   int partition_tokens;   // > 0, multiple of B
   int num_partitions;     // ceil(max_context_len / partition_tokens)
-  float *ws_ml;           // [S][Hq][num_partitions][2] (max, denominator), log2 domain
-  float *ws_acc;          // [S][Hq][num_partitions][D] unnormalised weighted sums
+  bool flat;              // balanced schedule (partition fields unused)
+  int flat_grid;          // its workgroup count
+  // Partial rows (running max and denominator in the log2 domain, weighted
+  // sums): fixed partitions [S][Hq][num_partitions], balanced schedule
+  // [2 * flat_grid][G].  ws_hdr: the balanced schedule's header.
+  float *ws_ml;
+  float *ws_acc;
+  int *ws_hdr;
 };
 
 struct PrefillArgs {
@@ -67,7 +81,11 @@ hipError_t launch_gather_kv(const CacheDesc &c, void *k_out, void *v_out, const 
 hipError_t launch_decode_valu(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream);
 // Matrix-core decode for grouped heads (f16/bf16, 2 <= G <= 16).
 hipError_t launch_decode_mfma(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream);
-// Combine split-KV partials into the output (only sequences with > 1 partition).
+// Workgroup count of the balanced schedule (the resident capacity of the
+// device for that kernel): sizes its workspace.
+int decode_valu_flat_grid(const CacheDesc &c, int S);
+int decode_mfma_flat_grid(const CacheDesc &c, int G, int S);
+// Combine split-KV partials into the output (only segments that were split).
 hipError_t launch_decode_reduce(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream);
 // Matrix-core causal chunked prefill (f16/bf16).
 hipError_t launch_prefill(const CacheDesc &c, const PrefillArgs &a, hipStream_t stream);

@@ -1,31 +1,45 @@
-// Work plan of the split-KV decode kernels.
+// Work schedules of the decode kernels.
 //
-// A sequence of L tokens splits into ceil(L / P) partitions of P tokens (the
-// block-wise partial results that "vLLM: LLM 서빙 메모리 최적화의 교과서",
-// velog.io, section 02 "Aggregation" combines).  The kernels run a persistent
-// grid: every workgroup first builds, in LDS, the exclusive prefix sum of
-// partitions per sequence, then walks the non-empty (sequence, partition,
-// head) items round-robin.  No workgroup is launched for an empty partition
-// and no host knowledge of the lengths is needed.
+// Attention of one (sequence, head) over its blocks can be cut into pieces
+// whose partial results (running max, denominator, weighted sum) combine
+// exactly: the block-wise aggregation of "vLLM: LLM 서빙 메모리 최적화의
+// 교과서" (velog.io), section 02 "Aggregation".  Three ways to hand the pieces
+// to workgroups:
+//
+//   kSchedGrid  one workgroup per (partition, head unit, sequence) grid cell;
+//   kSchedPlan  fixed partitions of P tokens, walked round-robin by a
+//               persistent grid over the non-empty cells only: every
+//               workgroup first builds in LDS the prefix sum of partitions
+//               per sequence (from the device-side lengths);
+//   kSchedFlat  balanced: all (sequence, head unit, block) units in one row,
+//               cut into gridDim.x equal contiguous ranges, one per resident
+//               workgroup.  A range covers at most two pieces that are not
+//               whole (sequence, head unit) segments, its first and its last;
+//               they go to workspace slots 2w and 2w+1, every whole segment
+//               straight to the output.
+//
+// A "head unit" is what one item computes: a query head (wavefront kernel)
+// or a KV head with its G query heads (matrix-core kernel).
 #pragma once
 
 #include "pkv_device.h"
+#include "pkv_launch.h"
 
 namespace pkv {
 
-// Sequences per launch that the in-LDS plan supports; beyond it the kernels
-// fall back to one workgroup per (partition, head, sequence) grid cell.
-constexpr int kPlanMaxSeqs = 8192;
+constexpr int kSchedGrid = 0;
+constexpr int kSchedPlan = 1;
+constexpr int kSchedFlat = 2;
 
 __device__ __forceinline__ int num_partitions_of(int L, int part_tokens) {
   return L > 0 ? (L + part_tokens - 1) / part_tokens : 0;
 }
 
-// Builds prefix[0..S] in LDS: prefix[s] = partitions of sequences 0..s-1.
-// Every thread of the workgroup must call it; returns prefix[S].
-// `scratch` is LDS for one int per wave (at most 16 waves).
+// Builds prefix[0..S] in LDS: prefix[s] = sum over sequences 0..s-1 of
+// mult * ceil(min(L, cap) / part_tokens).  Every thread of the workgroup must
+// call it; returns prefix[S].  `scratch` is LDS for one int per wave.
 __device__ inline int build_plan(int *prefix, int *scratch, const int32_t *__restrict__ context_lens,
-                                 int S, int cap, int part_tokens) {
+                                 int S, int cap, int part_tokens, int mult) {
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
   const int lane = tid & (kWave - 1);
@@ -34,7 +48,7 @@ __device__ inline int build_plan(int *prefix, int *scratch, const int32_t *__res
   const int s0 = min(S, tid * chunk);
   const int s1 = min(S, s0 + chunk);
   int mine = 0;
-  for (int s = s0; s < s1; ++s) mine += num_partitions_of(min(context_lens[s], cap), part_tokens);
+  for (int s = s0; s < s1; ++s) mine += mult * num_partitions_of(min(context_lens[s], cap), part_tokens);
   // Inclusive scan within the wave, then across waves.
   int x = mine;
 #pragma unroll
@@ -49,14 +63,14 @@ __device__ inline int build_plan(int *prefix, int *scratch, const int32_t *__res
   int run = base + x - mine;
   for (int s = s0; s < s1; ++s) {
     prefix[s] = run;
-    run += num_partitions_of(min(context_lens[s], cap), part_tokens);
+    run += mult * num_partitions_of(min(context_lens[s], cap), part_tokens);
   }
   if (tid == nthreads - 1) prefix[S] = run;
   __syncthreads();
   return prefix[S];
 }
 
-// Sequence owning partition-list entry j: the s with prefix[s] <= j < prefix[s+1].
+// Sequence owning entry j: the s with prefix[s] <= j < prefix[s+1].
 __device__ __forceinline__ int plan_sequence(const int *prefix, int S, int j) {
   int lo = 0, hi = S;  // invariant: prefix[lo] <= j < prefix[hi]
   while (hi - lo > 1) {
@@ -65,6 +79,95 @@ __device__ __forceinline__ int plan_sequence(const int *prefix, int S, int j) {
     else hi = mid;
   }
   return lo;
+}
+
+// Where an item's result goes: dest < 0 the output; otherwise head g of the
+// item writes partial row dest + g * stride of the workspace.
+struct Dest {
+  int base;
+  int stride;
+};
+
+// Hands this workgroup's items to item(s, hu, b0, b1, dest): blocks
+// [b0, b1) of sequence s for head unit hu.  `lds` holds S + 1 ints (plan
+// and flat schedules); `scan` one int per wave.  HU head units per
+// sequence, G heads per unit, P = part_tokens (plan and grid schedules).
+template <int SCHED, typename Item>
+__device__ __forceinline__ void run_schedule(Item &&item, int *lds, int *scan,
+                                             const int32_t *__restrict__ context_lens, int S,
+                                             int cap, int BS, int HU, int G, int part_tokens,
+                                             int nparts, int *__restrict__ ws_hdr) {
+  const int part_blocks = part_tokens / BS;
+  if constexpr (SCHED == kSchedGrid) {
+    const int s = blockIdx.z, hu = blockIdx.y, part = blockIdx.x;
+    const int nb = num_partitions_of(min(context_lens[s], cap), BS);
+    const int b0 = part * part_blocks;
+    if (b0 >= nb) return;
+    const bool whole = nb <= part_blocks;
+    item(s, hu, b0, min(nb, b0 + part_blocks),
+         whole ? Dest{-1, 0} : Dest{(s * HU + hu) * G * nparts + part, nparts});
+  } else if constexpr (SCHED == kSchedPlan) {
+    const int total = build_plan(lds, scan, context_lens, S, cap, part_tokens, 1);
+    const int nitems = total * HU;
+    for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
+      const int hu = it % HU;
+      const int j = it / HU;
+      const int s = plan_sequence(lds, S, j);
+      const int part = j - lds[s];
+      const int nb = num_partitions_of(min(context_lens[s], cap), BS);
+      const int b0 = part * part_blocks;
+      const bool whole = nb <= part_blocks;
+      item(s, hu, b0, min(nb, b0 + part_blocks),
+           whole ? Dest{-1, 0} : Dest{(s * HU + hu) * G * nparts + part, nparts});
+      __syncthreads();  // the item's LDS merge buffers are reused by the next one
+    }
+  } else {
+    const int U = build_plan(lds, scan, context_lens, S, cap, BS, HU);
+    const int W = gridDim.x;
+    const int C = (U + W - 1) / W;
+    const int w = blockIdx.x;
+    if (w == 0) {
+      for (int i = threadIdx.x; i <= S; i += blockDim.x) ws_hdr[kFlatPrefixAt + i] = lds[i];
+      if (threadIdx.x == 0) {
+        ws_hdr[0] = C;
+        ws_hdr[1] = U;
+      }
+    }
+    const int u0 = w * C, u1 = min(U, u0 + C);
+    for (int u = u0; u < u1;) {
+      const int s = plan_sequence(lds, S, u);
+      const int nb = (lds[s + 1] - lds[s]) / HU;  // blocks of one head unit of s
+      const int r = u - lds[s];
+      const int hu = r / nb, b = r - hu * nb;
+      const int e = min(u1, u + (nb - b));
+      const bool whole = b == 0 && e - u == nb;
+      item(s, hu, b, b + (e - u), whole ? Dest{-1, 0} : Dest{(u == u0 ? 2 * w : 2 * w + 1) * G, 1});
+      __syncthreads();
+      u = e;
+    }
+  }
+}
+
+// Balanced schedule: which workgroup ranges touched segment (s, hu).  Their
+// partial rows are slot * G + g with slot 2*w, except 2*w0 + 1 when the
+// segment was w0's last piece; w0 == w1 means the segment went straight to
+// the output.
+struct FlatSegment {
+  int w0, w1;     // workgroups whose ranges touch the segment
+  bool w0_last;   // the segment is w0's last piece (slot 2*w0 + 1)
+};
+__device__ __forceinline__ FlatSegment flat_segment(const int *__restrict__ ws_hdr, int s, int hu,
+                                                    int HU) {
+  const int C = ws_hdr[0];
+  const int p0 = ws_hdr[kFlatPrefixAt + s], p1 = ws_hdr[kFlatPrefixAt + s + 1];
+  const int nb = (p1 - p0) / HU;
+  FlatSegment f{0, 0, false};
+  if (nb == 0 || C == 0) return f;
+  const int a = p0 + hu * nb;
+  f.w0 = a / C;
+  f.w1 = (a + nb - 1) / C;
+  f.w0_last = a > f.w0 * C;
+  return f;
 }
 
 }  // namespace pkv

@@ -81,7 +81,7 @@ RAGGED = [1, 15, 16, 17, 31, 32, 33, 100, 255, 256, 257]
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("B", [16, 32])
 @pytest.mark.parametrize("G", [1, 4])
-@pytest.mark.parametrize("part", [0, 64])
+@pytest.mark.parametrize("part", [0, 64, -1], ids=["whole", "p64", "auto"])
 def test_decode_variants(dtype, d, B, G, part):
     wl = W.make_decode(f"var_{dtype}_{d}_{B}_{G}_{part}", 100 + d + B + G, lambda rng: RAGGED,
                        Hq=2 * G, Hkv=2, d=d, B=B, dtype=dtype, max_context_len=320,
@@ -114,7 +114,8 @@ def test_single_token_context_returns_its_value(dtype, G):
 
 
 @pytest.mark.parametrize("dtype,G,part", [(W.F16, 1, 0), (W.F16, 1, 32), (W.BF16, 4, 0),
-                                          (W.BF16, 4, 64), (W.F32, 1, 0)])
+                                          (W.BF16, 4, 64), (W.F32, 1, 0), (W.F16, 1, -1),
+                                          (W.BF16, 4, -1)])
 def test_dominant_key_selects_its_value_bitwise(dtype, G, part):
     # One key per sequence has a score margin > 200 in log2 units over every
     # other key: all other weights underflow to exactly 0 in fp32, so the
@@ -338,7 +339,7 @@ def _decode_rows(wl, n, seed):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("part", [0, 256, 512])
+@pytest.mark.parametrize("part", [0, 256, 512, -1])
 def test_llama13b_decode_full(part):
     wl = W.llama13b_decode_f16()
     worst, *_ = _sampled_check(wl, _decode_rows(wl, 8, 1), partition_size=part)
@@ -355,11 +356,23 @@ def test_long_context_split_full():
     print(f"split decode worst err/bound {worst:.3f}")
 
 
-@pytest.mark.parametrize("B", [16, 32])
-def test_gqa_decode_full(B):
+@pytest.mark.parametrize("B,part", [(16, 1024), (32, 1024), (16, -1), (32, -1)])
+def test_gqa_decode_full(B, part):
     wl = W.gqa_decode_bf16(B=B)
-    worst, *_ = _sampled_check(wl, _decode_rows(wl, 14, 3))
-    print(f"GQA B={B} worst err/bound {worst:.3f}")
+    worst, *_ = _sampled_check(wl, _decode_rows(wl, 14, 3), partition_size=part)
+    print(f"GQA B={B} partition {part} worst err/bound {worst:.3f}")
+
+
+def test_balanced_split_matches_fixed_partitions_at_full_size():
+    # Property at full size: the balanced schedule (segments cut wherever the
+    # equal shares end) agrees with fixed 512-token partitions everywhere.
+    wl = W.long_context_split_f16()
+    dw = DeviceWorkload(wl)
+    cache = new_cache(wl)
+    dw.run(cache)
+    auto = dw.attend(cache, partition_size=-1, out_dtype=torch.float32)
+    fixed = dw.attend(cache, partition_size=512, out_dtype=torch.float32)
+    assert_close(values_of(auto), values_of(fixed), wl.dtype, "balanced vs fixed partitions")
 
 
 def test_chunked_prefill_full():
@@ -374,7 +387,8 @@ def test_chunked_prefill_full():
     print(f"prefill worst err/bound {worst:.3f}")
 
 
-@pytest.mark.parametrize("dtype,G,part", [(W.F16, 1, 0), (W.F16, 1, 16), (W.BF16, 2, 32)])
+@pytest.mark.parametrize("dtype,G,part", [(W.F16, 1, 0), (W.F16, 1, 16), (W.BF16, 2, 32),
+                                          (W.BF16, 2, -1)])
 def test_decode_beyond_plan_limit_uses_grid_path(dtype, G, part):
     # More sequences than the in-LDS partition plan holds (8192): the kernels
     # run one workgroup per (partition, head, sequence) cell instead.
