@@ -283,7 +283,7 @@ pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, int32_t out_dtyp
                 max_context_len);
   if (max_query_len > max_context_len) return fail(PKV_ERR_INVALID, "max_query_len > max_context_len");
   if (!(scale > 0.f) || !(scale < INFINITY)) return fail(PKV_ERR_INVALID, "scale must be positive and finite");
-  const int64_t work = (int64_t)num_seqs * num_q_heads * ((max_query_len + 127) / 128);
+  const int64_t work = (int64_t)num_seqs * num_q_heads * ((max_query_len + 255) / 256);
   if (work >= (int64_t)1 << 31) return fail(PKV_ERR_UNSUPPORTED, "launch too large");
   pkv::PrefillArgs a;
   a.out = out;

@@ -6,7 +6,7 @@
 // attention is a matrix-matrix product ("vLLM: LLM 서빙 메모리 최적화의 교과서",
 // velog.io, section 01, prompt phase), causal over j <= i.
 //
-// Workgroup = 4 waves = one (sequence, query head, 128-row query tile); wave
+// Workgroup = 8 waves = one (sequence, query head, 256-row query tile); wave
 // w owns 32 rows.  The key/value positions 0..last row's position are walked
 // in 32-token tiles gathered through the block table into LDS (the next
 // tile's global loads are in flight while the current one is computed):
@@ -28,7 +28,11 @@
 namespace pkv {
 namespace {
 
-constexpr int kWaves = 4;
+#ifndef PKV_PREFILL_WAVES
+#define PKV_PREFILL_WAVES 8
+#endif
+constexpr int kWaves = PKV_PREFILL_WAVES;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kQT = 32 * kWaves;  // query rows per workgroup
 constexpr int kKT = 64;           // key/value tokens per tile
 constexpr int kVPad = 8;          // LDS row padding (elements) against bank conflicts
@@ -77,7 +81,7 @@ __device__ __forceinline__ int perm_row(int i) {
 constexpr float kRescaleLog2 = 8.f;
 
 template <typename E, int D, int BS>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(
+__global__ __launch_bounds__(kThreads, 512 / kThreads) void prefill_kernel(
     void *__restrict__ out, int out_f32, const uint16_t *__restrict__ q,
     const uint16_t *__restrict__ kpool, const uint16_t *__restrict__ vpool,
     const int32_t *__restrict__ query_start_loc, const int32_t *__restrict__ context_lens,
@@ -87,9 +91,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   constexpr int DT = D / 32;          // 32-dimension tiles of the output
   constexpr int KCH = kKT * D / 8;    // 16-byte chunks of a key tile
   constexpr int VCH = D * kKT / 8;    // 16-byte chunks of a value tile
-  constexpr int KPT = KCH / 256;      // key chunks per thread
-  constexpr int VPT = VCH / 256;      // value chunks per thread
-  static_assert(KCH % 256 == 0 && VCH % 256 == 0, "tile must split evenly over the workgroup");
+  constexpr int KPT = KCH / kThreads; // key chunks per thread
+  constexpr int VPT = VCH / kThreads; // value chunks per thread
+  static_assert(KCH % kThreads == 0 && VCH % kThreads == 0, "tile must split evenly over the workgroup");
   constexpr int KROW = D + kVPad;     // LDS key row (elements)
   constexpr int VROW = kKT + kVPad;   // LDS value row (elements)
 
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   {
     const int32_t *bt = block_tables + (size_t)s * mbps;
     const int nbt = min((ntiles * kKT + BS - 1) / BS, mbps);
-    for (int i = tid; i < nbt; i += 256) {
+    for (int i = tid; i < nbt; i += kThreads) {
       const int32_t b = bt[i];
       sBT[i] = (b >= 0 && b < num_blocks) ? b : -1;
     }
@@ -152,13 +156,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   __syncthreads();
 
   // Global -> register staging of one tile.  Thread tid moves key pieces
-  // (token tid/4, bytes 16*(tid%4).. of each 64-byte piece of the row, so a
-  // wave reads 16 tokens x 64 bytes contiguously per piece) and value chunks
-  // (dimension tid/8 + 32*i, tokens 8*(tid%8)..+8); a block id comes from the
-  // staged table.
+  // (token (tid/4) % 64, bytes 16*(tid%4).. of 64-byte pieces
+  // tid/256 + KPR*i of the row, so a wave reads 16 tokens x 64 bytes
+  // contiguously) and value chunks (dimension tid/8 + VDR*i, tokens
+  // 8*(tid%8)..+8); a block id comes from the staged table.
   constexpr int KX = 32;              // elements per 64-byte key piece
-  static_assert(KPT == D / KX, "one key piece per chunk round");
-  const int ktok = tid >> 2, ksub = tid & 3;
+  constexpr int KPR = kThreads / 256; // key pieces per chunk round
+  constexpr int VDR = kThreads / 8;   // value dimensions per chunk round
+  static_assert(KPT * KPR == D / KX, "whole key pieces per chunk round");
+  const int ktok = (tid >> 2) & (kKT - 1), ksub = tid & 3, kpc = tid >> 8;
   u32x4 kreg[KPT], vreg[VPT];
   auto load_tile = [&](int t) {
     const int t0 = t * kKT;
@@ -169,9 +175,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       // scores are masked.  An invalid block id (a broken caller contract)
       // reads block 0 instead of faulting.
       const int blk = (full || pos < ctx) ? max(sBT[pos / BS], 0) : 0;
-      const uint16_t *kb = kpool + (((size_t)blk * Hkv + hkv) * KPT * BS + pos % BS) * KX + 8 * ksub;
+      const uint16_t *kb = kpool + ((size_t)blk * Hkv + hkv) * D * BS + (pos % BS) * KX + 8 * ksub;
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) kreg[i] = load16(kb + (size_t)i * BS * KX);
+      for (int i = 0; i < KPT; ++i) kreg[i] = load16(kb + (size_t)(kpc + KPR * i) * BS * KX);
     }
     {
       const int pos = t0 + 8 * (tid % 8);
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       const uint16_t *vblk = vpool + ((size_t)blk * Hkv + hkv) * D * BS + pos % BS;
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
-        const int e = tid / 8 + 32 * i;
+        const int e = tid / 8 + VDR * i;
         u32x4 x = load16(vblk + (size_t)e * BS);
         if (!full && pos + 8 > ctx) {
           // Slots past the context may hold anything: zero them.
@@ -199,7 +205,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   auto store_tile = [&](auto conv, int buf) {
     constexpr bool CONV = decltype(conv)::value;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) *(u32x4 *)&sK[buf][ktok * KROW + KX * i + 8 * ksub] = kreg[i];
+    for (int i = 0; i < KPT; ++i) *(u32x4 *)&sK[buf][ktok * KROW + KX * (kpc + KPR * i) + 8 * ksub] = kreg[i];
     u16x2 mag = {0, 0};
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -208,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 #pragma unroll
         for (int k = 0; k < 4; ++k) x[k] = bf16x2_to_f16x2(x[k], mag);
       }
-      *(u32x4 *)&sV[buf][(tid / 8 + 32 * i) * VROW + 8 * (tid % 8)] = x;
+      *(u32x4 *)&sV[buf][(tid / 8 + VDR * i) * VROW + 8 * (tid % 8)] = x;
     }
     if (CONV && bf16_beyond_f16(mag)) sOvf = 1;
   };
@@ -356,7 +362,7 @@ void launch_t(const CacheDesc &c, const PrefillArgs &a, hipStream_t stream) {
   const int nqt = (a.max_query_len + kQT - 1) / kQT;
   const int64_t nwork = (int64_t)a.S * a.Hq * nqt;
   const size_t lds = sizeof(int) * (size_t)a.max_blocks_per_seq;   // staged block table
-  hipLaunchKernelGGL((prefill_kernel<E, D, BS>), dim3((unsigned)nwork), dim3(256), lds, stream,
+  hipLaunchKernelGGL((prefill_kernel<E, D, BS>), dim3((unsigned)nwork), dim3(kThreads), lds, stream,
                      a.out, (int)a.out_f32, (const uint16_t *)a.q, (const uint16_t *)c.k,
                      (const uint16_t *)c.v, a.query_start_loc, a.context_lens, a.block_tables,
                      c.num_blocks, c.H, a.Hq, a.max_blocks_per_seq, nqt, a.scale * kLog2e);
