@@ -30,11 +30,13 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def make_workload(name, partition):
+def make_workload(name, partition, block_size=16, placement="shuffled"):
     from paged_kv_cache_92_amd import workloads as W
     if name == "llama13b":
-        wl = W.llama13b_decode_f16()
+        wl = W.llama13b_decode_f16(B=block_size, placement=placement)
         desc = "llama2-13b-shaped single-layer paged decode, fp16 KV"
+        if block_size != 16 or placement != "shuffled":
+            desc += f" (block {block_size}, {placement} blocks)"
     elif name == "long_split":
         wl = W.long_context_split_f16()
         desc = "long-context split-KV paged decode, fp16 KV"
@@ -150,6 +152,10 @@ def main():
                     choices=["llama13b", "long_split", "gqa16", "gqa32", "prefill", "tiny"])
     ap.add_argument("--partition", type=int, default=None,
                     help="split-KV partition size in tokens (default: the workload's)")
+    ap.add_argument("--block-size", type=int, default=16, choices=[16, 32],
+                    help="block size of the llama13b workload (paging-overhead sweep)")
+    ap.add_argument("--placement", default="shuffled", choices=["shuffled", "contiguous"],
+                    help="physical block order of the llama13b workload (paging-overhead sweep)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -179,7 +185,9 @@ def main():
         return
     pkv.lib()
     t0 = time.time()
-    wl, desc = make_workload(args.config, args.partition)
+    if args.config != "llama13b" and (args.block_size != 16 or args.placement != "shuffled"):
+        raise SystemExit("--block-size/--placement apply to the llama13b workload only")
+    wl, desc = make_workload(args.config, args.partition, args.block_size, args.placement)
     log(f"[bench] generated {wl.name} in {time.time() - t0:.1f}s "
         f"(pool {wl.num_blocks} blocks, KV {wl.kv_bytes() / 1e9:.3f} GB)")
 
@@ -272,6 +280,7 @@ def main():
     res["config"] = {"workload": desc, "seqs": wl.S, "q_heads": wl.num_q_heads,
                      "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                      "block_size": wl.block_size, "pool_blocks": wl.num_blocks,
+                     "placement": args.placement,
                      "total_context_tokens": int(wl.context_lens.sum()),
                      "partition_size": wl.partition_size if wl.mode == "decode" else None,
                      "kv_bytes": kv, "attention_flops": flops}

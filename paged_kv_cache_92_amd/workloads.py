@@ -127,11 +127,15 @@ def _poison_block(bm: BlockManager) -> int:
 
 
 def make_decode(name, seed, context_lens_fn, Hq, Hkv, d, B, dtype, max_context_len,
-                num_blocks=None, pool_factor=1.1, partition_size=0):
+                num_blocks=None, pool_factor=1.1, partition_size=0, placement="shuffled"):
     """Decode workload: every sequence holds ctx[s]-1 history tokens and appends one.
 
     ``context_lens_fn(rng)`` draws the context lengths (post-append, so they
     include the new token).  The step scatters the S new tokens, then attends.
+    ``placement``: "shuffled" hands out physical blocks in a seeded random
+    order; "contiguous" in pool order, so each sequence's blocks are
+    consecutive and in logical order (an identity-like block table).  The
+    values drawn are the same either way.
     """
     rng = np.random.default_rng(seed)
     ctx = np.asarray(context_lens_fn(rng), dtype=np.int32)
@@ -143,6 +147,10 @@ def make_decode(name, seed, context_lens_fn, Hq, Hkv, d, B, dtype, max_context_l
     if nb <= need:
         raise ValueError("pool must hold at least one block more than the workload needs")
     perm = rng.permutation(nb)
+    if placement == "contiguous":
+        perm = np.arange(nb)
+    elif placement != "shuffled":
+        raise ValueError(f"unknown placement {placement}")
     bm = BlockManager(nb, B, free_order=perm)
     q = _draw_values(rng, (S, Hq, d), dtype)
     total = int(ctx.astype(np.int64).sum())
@@ -300,11 +308,13 @@ def tiny_decode_f32():
                        dtype=F32, max_context_len=64, num_blocks=32)
 
 
-def llama13b_decode_f16(S=64, lo=128, hi=2048, seed=2, partition_size=512):
+def llama13b_decode_f16(S=64, lo=128, hi=2048, seed=2, partition_size=512, B=16,
+                        placement="shuffled"):
     """LLaMA-2-13B-shaped single-layer decode: 40 heads, d 128, B 16, fp16, L ~ U[lo, hi]."""
     return make_decode(f"llama13b_decode_f16_S{S}", seed,
-                       lambda rng: rng.integers(lo, hi + 1, size=S), Hq=40, Hkv=40, d=128, B=16,
-                       dtype=F16, max_context_len=hi, partition_size=partition_size)
+                       lambda rng: rng.integers(lo, hi + 1, size=S), Hq=40, Hkv=40, d=128, B=B,
+                       dtype=F16, max_context_len=hi, partition_size=partition_size,
+                       placement=placement)
 
 
 def long_context_split_f16(S=16, lo=2048, hi=4096, seed=3, partition_size=512):

@@ -398,3 +398,51 @@ def test_decode_beyond_plan_limit_uses_grid_path(dtype, G, part):
                        dtype=dtype, max_context_len=48, partition_size=part)
     _full_check(wl)
 
+
+
+@pytest.mark.parametrize("dtype,G", [(W.F16, 1), (W.BF16, 2)])
+def test_pool_beyond_4_gib_addresses_correctly(dtype, G):
+    # Blocks at the far end of a pool larger than 4 GiB (byte offsets past
+    # 2^32): scatter, copy, gather, decode and prefill over them must give
+    # exactly what the same blocks give at the start of a small pool.
+    wl = W.make_decode("far", 5, lambda rng: [300, 17, 1024, 64], Hq=8 * G, Hkv=8, d=128, B=16,
+                       dtype=dtype, max_context_len=1024)
+    dw = DeviceWorkload(wl)
+    small = new_cache(wl)
+    dw.fill(small)                                 # history only
+    NB = 140_000                                   # 140000 * 32 KiB per pool > 4 GiB
+    off = NB - wl.num_blocks
+    big = pkv.PagedKVCache(NB, 8, 16, 128, small.k_pool.dtype)
+    assert big.k_pool.nbytes > 4 << 30
+    big.k_pool[off:] = small.k_pool
+    big.v_pool[off:] = small.v_pool
+    dw.apply(small, dw.step)
+    step = wl.step_scatter
+    pkv.reshape_and_cache(big, to_device(step.key, dtype), to_device(step.value, dtype),
+                          torch.from_numpy(step.slots + off * wl.block_size).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(big.k_pool[off:].view(torch.int16), small.k_pool.view(torch.int16))
+    assert torch.equal(big.v_pool[off:].view(torch.int16), small.v_pool.view(torch.int16))
+    bt2 = dw.block_tables + off
+    for part in (0, 64, -1):
+        a = pkv.paged_decode(small, dw.q, dw.block_tables, dw.context_lens, wl.max_context_len,
+                             scale=wl.scale, partition_size=part, out_dtype=torch.float32)
+        b = pkv.paged_decode(big, dw.q, bt2, dw.context_lens, wl.max_context_len, scale=wl.scale,
+                             partition_size=part, out_dtype=torch.float32)
+        assert torch.equal(a, b), f"decode partition {part}"
+    qsl = torch.arange(0, wl.S + 1, dtype=torch.int32, device="cuda")
+    a = pkv.paged_prefill(small, dw.q, qsl, dw.context_lens, dw.block_tables, 1, wl.max_context_len,
+                          scale=wl.scale, out_dtype=torch.float32)
+    b = pkv.paged_prefill(big, dw.q, qsl, dw.context_lens, bt2, 1, wl.max_context_len,
+                          scale=wl.scale, out_dtype=torch.float32)
+    assert torch.equal(a, b), "prefill"
+    ctx = wl.context_lens
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)).cuda()
+    ga = pkv.gather_kv(small, dw.block_tables, dw.context_lens, cu, int(ctx.sum()), wl.max_context_len)
+    gb = pkv.gather_kv(big, bt2, dw.context_lens, cu, int(ctx.sum()), wl.max_context_len)
+    assert all(torch.equal(x.view(torch.int16), y.view(torch.int16)) for x, y in zip(ga, gb))
+    # Copy the last block of the pool onto its first: both ends of the range.
+    pkv.copy_blocks(big, torch.tensor([[NB - 1, 0]], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(big.k_pool[0].view(torch.int16), big.k_pool[NB - 1].view(torch.int16))
+    assert torch.equal(big.v_pool[0].view(torch.int16), big.v_pool[NB - 1].view(torch.int16))
