@@ -27,8 +27,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pkv_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-F32, F16, BF16 = 0, 1, 2
-_STORAGE = {F32: np.float32, F16: np.uint16, BF16: np.uint16}
+F32, F16, BF16, FP8 = 0, 1, 2, 3
+_STORAGE = {F32: np.float32, F16: np.uint16, BF16: np.uint16, FP8: np.uint8}
 
 _ERRORS = {-1: "bad argument", -2: "index out of range", -3: "duplicate destination", -4: "out of memory"}
 
@@ -66,19 +66,26 @@ def _load(path: str | None = None) -> ctypes.CDLL:
             build()
         lib = ctypes.CDLL(path or _LIB_PATH)
         vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+        f64 = ctypes.c_double
         lib.oracle_reshape_and_cache.argtypes = [vp, vp, i32, i64, i32, i32, i32, vp, vp, vp, i64]
+        lib.oracle_reshape_and_cache_fp8.argtypes = [vp, vp, i32, f32, f32, i64, i32, i32, i32, vp, vp,
+                                                     vp, i64]
         lib.oracle_copy_blocks.argtypes = [vp, vp, i32, i64, i32, i32, i32, vp, i64]
         lib.oracle_gather_kv.argtypes = [vp, vp, i32, i64, i32, i32, i32, vp, i32, vp, i32, vp, vp]
-        lib.oracle_paged_attention_rows.argtypes = [vp, vp, i32, i64, i32, i32, i32, vp, i32, vp, i32,
-                                                   vp, i32, vp, vp, i64, f32, vp]
-        lib.oracle_paged_decode.argtypes = [vp, vp, i32, i64, i32, i32, i32, vp, i32, vp, i32, vp, i32,
-                                            f32, vp]
-        lib.oracle_paged_prefill.argtypes = [vp, vp, i32, i64, i32, i32, i32, vp, i32, vp, vp, vp, i32,
-                                             i32, f32, vp]
+        lib.oracle_paged_attention_rows.argtypes = [vp, vp, i32, i32, f64, f64, i64, i32, i32, i32, vp,
+                                                   i32, vp, i32, vp, i32, vp, vp, i64, f32, vp]
+        lib.oracle_paged_decode.argtypes = [vp, vp, i32, i32, f64, f64, i64, i32, i32, i32, vp, i32, vp,
+                                            i32, vp, i32, f32, vp]
+        lib.oracle_paged_prefill.argtypes = [vp, vp, i32, i32, f64, f64, i64, i32, i32, i32, vp, i32, vp,
+                                             vp, vp, i32, i32, f32, vp]
         lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
         lib.oracle_f16_to_double.restype = ctypes.c_double
         lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
         lib.oracle_bf16_to_double.restype = ctypes.c_double
+        lib.oracle_fp8_to_double.argtypes = [ctypes.c_uint8]
+        lib.oracle_fp8_to_double.restype = ctypes.c_double
+        lib.oracle_fp8_from_float.argtypes = [ctypes.c_float]
+        lib.oracle_fp8_from_float.restype = ctypes.c_uint8
         _lib = lib
     return _lib
 
@@ -105,14 +112,24 @@ def _geom(k_pool: np.ndarray, v_pool: np.ndarray, dtype: int):
     return nb, H, B, d
 
 
-def reshape_and_cache(k_pool, v_pool, dtype, key, value, slots):
-    """Scatter key/value [T][H][d] into the pools (in place) at ``slots`` [T] (int64, <0 = skip)."""
+def reshape_and_cache(k_pool, v_pool, dtype, key, value, slots, in_dtype=None, k_scale=1.0,
+                      v_scale=1.0):
+    """Scatter key/value [T][H][d] into the pools (in place) at ``slots`` [T] (int64, <0 = skip).
+
+    ``dtype`` is the pools' dtype; for an FP8 cache, key/value are ``in_dtype``
+    (F16 or BF16) bits and are quantised with the per-tensor scales."""
     nb, H, B, d = _geom(k_pool, v_pool, dtype)
     slots = np.ascontiguousarray(slots, dtype=np.int64)
     key = np.ascontiguousarray(key)
     value = np.ascontiguousarray(value)
     T = slots.shape[0]
     assert key.shape == (T, H, d) and value.shape == (T, H, d)
+    if dtype == FP8:
+        _check(_load().oracle_reshape_and_cache_fp8(_ptr(k_pool), _ptr(v_pool), in_dtype,
+                                                    float(k_scale), float(v_scale), nb, H, B, d,
+                                                    _ptr(key), _ptr(value), _ptr(slots), T),
+               "reshape_and_cache")
+        return
     _check(_load().oracle_reshape_and_cache(_ptr(k_pool), _ptr(v_pool), dtype, nb, H, B, d,
                                             _ptr(key), _ptr(value), _ptr(slots), T),
            "reshape_and_cache")
@@ -141,8 +158,11 @@ def gather_kv(k_pool, v_pool, dtype, block_tables, context_lens):
 
 
 def paged_attention_rows(k_pool, v_pool, dtype, q, block_tables, context_lens, row_seq, row_pos,
-                         scale):
-    """fp64 attention for query rows q [n][Hq][d] at (row_seq[r], row_pos[r]); returns [n][Hq][d]."""
+                         scale, q_dtype=None, k_scale=1.0, v_scale=1.0):
+    """fp64 attention for query rows q [n][Hq][d] at (row_seq[r], row_pos[r]); returns [n][Hq][d].
+
+    q is in ``q_dtype`` (default: the cache dtype; F16/BF16 over an FP8 cache,
+    whose entries read as code * k_scale / code * v_scale)."""
     nb, Hkv, B, d = _geom(k_pool, v_pool, dtype)
     q = np.ascontiguousarray(q)
     n, Hq, dq = q.shape
@@ -152,14 +172,17 @@ def paged_attention_rows(k_pool, v_pool, dtype, q, block_tables, context_lens, r
     rs = np.ascontiguousarray(row_seq, dtype=np.int32)
     rp = np.ascontiguousarray(row_pos, dtype=np.int32)
     out = np.zeros((n, Hq, d), dtype=np.float64)
-    _check(_load().oracle_paged_attention_rows(_ptr(k_pool), _ptr(v_pool), dtype, nb, Hkv, B, d,
+    qd = dtype if q_dtype is None else q_dtype
+    _check(_load().oracle_paged_attention_rows(_ptr(k_pool), _ptr(v_pool), dtype, qd, float(k_scale),
+                                               float(v_scale), nb, Hkv, B, d,
                                                _ptr(q), Hq, _ptr(bt), bt.shape[1], _ptr(ctx),
                                                ctx.shape[0], _ptr(rs), _ptr(rp), n, float(scale),
                                                _ptr(out)), "paged_attention_rows")
     return out
 
 
-def paged_decode(k_pool, v_pool, dtype, q, block_tables, context_lens, scale):
+def paged_decode(k_pool, v_pool, dtype, q, block_tables, context_lens, scale, q_dtype=None,
+                 k_scale=1.0, v_scale=1.0):
     """fp64 decode output [S][Hq][d]: each sequence's query over all its ctx tokens."""
     nb, Hkv, B, d = _geom(k_pool, v_pool, dtype)
     q = np.ascontiguousarray(q)
@@ -167,13 +190,16 @@ def paged_decode(k_pool, v_pool, dtype, q, block_tables, context_lens, scale):
     bt = np.ascontiguousarray(block_tables, dtype=np.int32)
     ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
     out = np.zeros((S, Hq, d), dtype=np.float64)
-    _check(_load().oracle_paged_decode(_ptr(k_pool), _ptr(v_pool), dtype, nb, Hkv, B, d, _ptr(q), Hq,
+    qd = dtype if q_dtype is None else q_dtype
+    _check(_load().oracle_paged_decode(_ptr(k_pool), _ptr(v_pool), dtype, qd, float(k_scale),
+                                       float(v_scale), nb, Hkv, B, d, _ptr(q), Hq,
                                        _ptr(bt), bt.shape[1], _ptr(ctx), S, float(scale), _ptr(out)),
            "paged_decode")
     return out
 
 
-def paged_prefill(k_pool, v_pool, dtype, q, query_start_loc, context_lens, block_tables, scale):
+def paged_prefill(k_pool, v_pool, dtype, q, query_start_loc, context_lens, block_tables, scale,
+                  q_dtype=None, k_scale=1.0, v_scale=1.0):
     """fp64 chunked-prefill output [Tq][Hq][d] (causal over history + chunk)."""
     nb, Hkv, B, d = _geom(k_pool, v_pool, dtype)
     q = np.ascontiguousarray(q)
@@ -183,7 +209,9 @@ def paged_prefill(k_pool, v_pool, dtype, q, query_start_loc, context_lens, block
     bt = np.ascontiguousarray(block_tables, dtype=np.int32)
     assert qsl[-1] == Tq
     out = np.zeros((Tq, Hq, d), dtype=np.float64)
-    _check(_load().oracle_paged_prefill(_ptr(k_pool), _ptr(v_pool), dtype, nb, Hkv, B, d, _ptr(q), Hq,
+    qd = dtype if q_dtype is None else q_dtype
+    _check(_load().oracle_paged_prefill(_ptr(k_pool), _ptr(v_pool), dtype, qd, float(k_scale),
+                                        float(v_scale), nb, Hkv, B, d, _ptr(q), Hq,
                                         _ptr(qsl), _ptr(ctx), _ptr(bt), bt.shape[1], ctx.shape[0],
                                         float(scale), _ptr(out)), "paged_prefill")
     return out
@@ -197,10 +225,19 @@ def bf16_to_double(bits: int) -> float:
     return _load().oracle_bf16_to_double(bits)
 
 
+def fp8_to_double(bits: int) -> float:
+    return _load().oracle_fp8_to_double(bits)
+
+
+def fp8_from_float(x: float) -> int:
+    """E4M3 code of an fp32 value (nearest, ties to even; saturating at +-448)."""
+    return int(_load().oracle_fp8_from_float(x))
+
+
 def decode_values(arr: np.ndarray, dtype: int) -> np.ndarray:
     """fp64 values of a raw-bits array, decoded element by element by the C decoder."""
     flat = np.ascontiguousarray(arr).reshape(-1)
     if dtype == F32:
         return flat.astype(np.float64).reshape(arr.shape)
-    f = f16_to_double if dtype == F16 else bf16_to_double
+    f = {F16: f16_to_double, BF16: bf16_to_double, FP8: fp8_to_double}[dtype]
     return np.array([f(int(b)) for b in flat], dtype=np.float64).reshape(arr.shape)

@@ -19,8 +19,8 @@
  *
  * Pool layout (an interface contract of the library, restated here; the
  * pages fix only "fixed-size blocks of B token slots", [T] step 5):
- *   K pool  [num_blocks][H][d/X][B][X], X = 64 bytes / element size (32
- *           fp16/bf16 values, 16 fp32 values): a key row is cut into 64-byte
+ *   K pool  [num_blocks][H][d/X][B][X], X = 64 bytes / element size (64 E4M3,
+ *           32 fp16/bf16, 16 fp32 values): a key row is cut into 64-byte
  *           pieces and the B pieces of one dimension range are adjacent;
  *           element (blk,h,off,e) at (((blk*H+h)*(d/X)+e/X)*B+off)*X+e%X
  *   V pool  [num_blocks][H][d][B]  element (blk,h,off,e) at ((blk*H+h)*d+e)*B+off
@@ -35,7 +35,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_FP8 = 3 /* OCP FP8 E4M3, 8-bit cache only */ };
 
 enum {
   ORC_OK = 0,
@@ -46,7 +46,7 @@ enum {
 };
 
 static size_t elt_size(int dtype) {
-  return dtype == ORC_F32 ? 4u : 2u;
+  return dtype == ORC_F32 ? 4u : dtype == ORC_FP8 ? 1u : 2u;
 }
 
 /* IEEE-754 binary16 -> fp64, decoded from the bit fields. */
@@ -73,8 +73,48 @@ static double bf16_to_double(uint16_t b) {
   return (double)f;
 }
 
+/*
+ * 8-bit float cache entries.  [W] section "PagedAttention 커널: 비연속 메모리
+ * 접근": write_to_paged_cache passes kv_cache_dtype, k_scale and v_scale on
+ * to reshape_and_cache.  Reading taken: for an 8-bit cache the stored code of
+ * a key element x is the OCP FP8 E4M3 encoding of the fp32 quotient x /
+ * k_scale (values with v_scale), and a read gives code * scale.
+ *
+ * E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0
+ * holds subnormals m * 2^-9; the all-ones pattern S.1111.111 is NaN and there
+ * are no infinities, so the largest magnitude is 1.110b * 2^8 = 448.
+ */
+static double fp8_to_double(uint8_t b) {
+  int sign = b >> 7, expo = (b >> 3) & 15, mant = b & 7;
+  double v;
+  if (expo == 15 && mant == 7) v = NAN;
+  else if (expo == 0) v = ldexp((double)mant, -9);
+  else v = ldexp((double)(8 + mant), expo - 10); /* (1.mant) * 2^(expo-7) */
+  return sign ? -v : v;
+}
+
+/* fp32 -> E4M3: round to nearest, ties to the even code; magnitudes of 448
+ * and beyond (infinities included) saturate to +-448; NaN stays NaN. */
+static uint8_t fp8_from_float(float x) {
+  uint8_t sign = signbit(x) ? 0x80 : 0;
+  if (isnan(x)) return sign | 0x7F;
+  double a = fabs((double)x);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a < ldexp(1.0, -6)) return sign | (uint8_t)rint(a * 512.0); /* subnormal grid 2^-9; 8 = 2^-6 */
+  int e2;
+  frexp(a, &e2);
+  int E = e2 - 1;                      /* a in [2^E, 2^(E+1)) */
+  int n = (int)rint(ldexp(a, 3 - E));  /* 8..16: significand in units of 2^(E-3) */
+  if (n == 16) {
+    E += 1;
+    n = 8;
+  }
+  return sign | (uint8_t)(((E + 7) << 3) | (n - 8));
+}
+
 static double load_elt(const void *base, size_t idx, int dtype) {
   if (dtype == ORC_F32) return (double)((const float *)base)[idx];
+  if (dtype == ORC_FP8) return fp8_to_double(((const uint8_t *)base)[idx]);
   uint16_t bits = ((const uint16_t *)base)[idx];
   return dtype == ORC_F16 ? f16_to_double(bits) : bf16_to_double(bits);
 }
@@ -82,8 +122,23 @@ static double load_elt(const void *base, size_t idx, int dtype) {
 static void copy_elt(void *dst, size_t di, const void *src, size_t si, int dtype) {
   if (dtype == ORC_F32)
     ((uint32_t *)dst)[di] = ((const uint32_t *)src)[si];
+  else if (dtype == ORC_FP8)
+    ((uint8_t *)dst)[di] = ((const uint8_t *)src)[si];
   else
     ((uint16_t *)dst)[di] = ((const uint16_t *)src)[si];
+}
+
+/* One element of a scatter: a bit copy, or for an 8-bit cache the code of
+ * the fp32 quotient (the input value is exact in fp32; the division is one
+ * IEEE single-precision division). */
+static void store_elt(void *dst, size_t di, int kv_dtype, const void *src, size_t si, int in_dtype,
+                      float scale) {
+  if (kv_dtype != ORC_FP8) {
+    copy_elt(dst, di, src, si, kv_dtype);
+    return;
+  }
+  float x = (float)load_elt(src, si, in_dtype);
+  ((uint8_t *)dst)[di] = fp8_from_float(x / scale);
 }
 
 static size_t k_index(int64_t blk, int h, int off, int e, int H, int B, int d, int dtype) {
@@ -96,7 +151,7 @@ static size_t v_index(int64_t blk, int h, int off, int e, int H, int B, int d) {
 }
 
 static int check_geometry(int dtype, int64_t num_blocks, int H, int B, int d) {
-  if (dtype != ORC_F32 && dtype != ORC_F16 && dtype != ORC_BF16) return ORC_ERR_ARG;
+  if (dtype != ORC_F32 && dtype != ORC_F16 && dtype != ORC_BF16 && dtype != ORC_FP8) return ORC_ERR_ARG;
   if (num_blocks <= 0 || H <= 0 || B <= 0 || d <= 0) return ORC_ERR_ARG;
   if (d % (64 / (int)elt_size(dtype)) != 0) return ORC_ERR_ARG; /* whole 64-byte key pieces */
   return ORC_OK;
@@ -112,11 +167,17 @@ static int check_geometry(int dtype, int64_t num_blocks, int H, int B, int d) {
  * slot = blk*B + off.  A negative slot marks a padding token: nothing is
  * written.  key/value are [T][H][d], token-major.
  */
-int oracle_reshape_and_cache(void *k_pool, void *v_pool, int dtype, int64_t num_blocks,
-                             int H, int B, int d, const void *key, const void *value,
-                             const int64_t *slots, int64_t T) {
-  int rc = check_geometry(dtype, num_blocks, H, B, d);
+static int scatter(void *k_pool, void *v_pool, int kv_dtype, int in_dtype, float k_scale,
+                   float v_scale, int64_t num_blocks, int H, int B, int d, const void *key,
+                   const void *value, const int64_t *slots, int64_t T) {
+  int rc = check_geometry(kv_dtype, num_blocks, H, B, d);
   if (rc) return rc;
+  if (kv_dtype == ORC_FP8) {
+    if (in_dtype != ORC_F16 && in_dtype != ORC_BF16) return ORC_ERR_ARG;
+    if (!(k_scale > 0.f) || !(v_scale > 0.f) || isinf(k_scale) || isinf(v_scale)) return ORC_ERR_ARG;
+  } else if (in_dtype != kv_dtype) {
+    return ORC_ERR_ARG;
+  }
   if (T < 0 || (T > 0 && (!key || !value || !slots || !k_pool || !v_pool))) return ORC_ERR_ARG;
   int64_t nslots = num_blocks * B;
   /* Duplicate destinations have no defined winner: refuse them. */
@@ -138,12 +199,27 @@ int oracle_reshape_and_cache(void *k_pool, void *v_pool, int dtype, int64_t num_
     for (int h = 0; h < H; ++h) {
       for (int e = 0; e < d; ++e) {
         size_t src = ((size_t)t * H + h) * d + e;
-        copy_elt(k_pool, k_index(blk, h, off, e, H, B, d, dtype), key, src, dtype);
-        copy_elt(v_pool, v_index(blk, h, off, e, H, B, d), value, src, dtype);
+        store_elt(k_pool, k_index(blk, h, off, e, H, B, d, kv_dtype), kv_dtype, key, src, in_dtype, k_scale);
+        store_elt(v_pool, v_index(blk, h, off, e, H, B, d), kv_dtype, value, src, in_dtype, v_scale);
       }
     }
   }
   return ORC_OK;
+}
+
+int oracle_reshape_and_cache(void *k_pool, void *v_pool, int dtype, int64_t num_blocks,
+                             int H, int B, int d, const void *key, const void *value,
+                             const int64_t *slots, int64_t T) {
+  return scatter(k_pool, v_pool, dtype, dtype, 1.f, 1.f, num_blocks, H, B, d, key, value, slots, T);
+}
+
+/* The same into an 8-bit cache: key/value rows in in_dtype (f16 or bf16). */
+int oracle_reshape_and_cache_fp8(void *k_pool, void *v_pool, int in_dtype, float k_scale,
+                                 float v_scale, int64_t num_blocks, int H, int B, int d,
+                                 const void *key, const void *value, const int64_t *slots,
+                                 int64_t T) {
+  return scatter(k_pool, v_pool, ORC_FP8, in_dtype, k_scale, v_scale, num_blocks, H, B, d, key,
+                 value, slots, T);
 }
 
 /*
@@ -223,9 +299,12 @@ int oracle_gather_kv(const void *k_pool, const void *v_pool, int dtype, int64_t 
   return ORC_OK;
 }
 
-/* fp64 reassembly of positions [0, n) of one sequence: Kc/Vc are [n][H][d]. */
-static int reassemble(const void *k_pool, const void *v_pool, int dtype, int64_t num_blocks, int H,
-                      int B, int d, const int32_t *bt_row, int n, double *Kc, double *Vc) {
+/* fp64 reassembly of positions [0, n) of one sequence: Kc/Vc are [n][H][d].
+ * Entries of an 8-bit cache read as code * scale (exact in fp64). */
+static int reassemble(const void *k_pool, const void *v_pool, int dtype, double k_scale,
+                      double v_scale, int64_t num_blocks, int H, int B, int d,
+                      const int32_t *bt_row, int n, double *Kc, double *Vc) {
+  const double ks = dtype == ORC_FP8 ? k_scale : 1.0, vs = dtype == ORC_FP8 ? v_scale : 1.0;
   for (int j = 0; j < n; ++j) {
     int64_t blk;
     int off;
@@ -234,8 +313,8 @@ static int reassemble(const void *k_pool, const void *v_pool, int dtype, int64_t
     for (int h = 0; h < H; ++h)
       for (int e = 0; e < d; ++e) {
         size_t dst = ((size_t)j * H + h) * d + e;
-        Kc[dst] = load_elt(k_pool, k_index(blk, h, off, e, H, B, d, dtype), dtype);
-        Vc[dst] = load_elt(v_pool, v_index(blk, h, off, e, H, B, d), dtype);
+        Kc[dst] = ks * load_elt(k_pool, k_index(blk, h, off, e, H, B, d, dtype), dtype);
+        Vc[dst] = vs * load_elt(v_pool, v_index(blk, h, off, e, H, B, d), dtype);
       }
   }
   return ORC_OK;
@@ -278,13 +357,14 @@ static void attend_one(const double *q, int p, const double *Kc, const double *V
 /*
  * Attention for a list of query rows.  Row r belongs to sequence row_seq[r]
  * and sits at absolute position row_pos[r]; it attends to cached positions
- * 0..row_pos[r] of that sequence.  q is [n][Hq][d] in the cache dtype, out
+ * 0..row_pos[r] of that sequence.  q is [n][Hq][d] in q_dtype (the cache dtype, or f16/bf16 over an 8-bit cache), out
  * is [n][Hq][d] fp64.  The sequence's K/V are first reassembled into
  * contiguous fp64 arrays through its block table, then each head runs the
  * textbook formula above; consecutive rows of one sequence reuse one
  * reassembly.
  */
-int oracle_paged_attention_rows(const void *k_pool, const void *v_pool, int dtype,
+int oracle_paged_attention_rows(const void *k_pool, const void *v_pool, int dtype, int q_dtype,
+                                double k_scale, double v_scale,
                                 int64_t num_blocks, int Hkv, int B, int d, const void *q, int Hq,
                                 const int32_t *block_tables, int max_blocks_per_seq,
                                 const int32_t *context_lens, int S, const int32_t *row_seq,
@@ -292,6 +372,7 @@ int oracle_paged_attention_rows(const void *k_pool, const void *v_pool, int dtyp
   int rc = check_geometry(dtype, num_blocks, Hkv, B, d);
   if (rc) return rc;
   if (Hq <= 0 || Hq % Hkv != 0 || n < 0 || S <= 0) return ORC_ERR_ARG;
+  if (dtype == ORC_FP8 ? (q_dtype != ORC_F16 && q_dtype != ORC_BF16) : q_dtype != dtype) return ORC_ERR_ARG;
   int G = Hq / Hkv;
   int cap = max_blocks_per_seq * B;
   double *Kc = malloc(sizeof(double) * (size_t)cap * Hkv * d);
@@ -308,13 +389,14 @@ int oracle_paged_attention_rows(const void *k_pool, const void *v_pool, int dtyp
     }
     if (s != cur_seq || p + 1 > cur_len) {
       const int32_t *bt = block_tables + (size_t)s * max_blocks_per_seq;
-      if ((rc = reassemble(k_pool, v_pool, dtype, num_blocks, Hkv, B, d, bt, context_lens[s], Kc, Vc)))
+      if ((rc = reassemble(k_pool, v_pool, dtype, k_scale, v_scale, num_blocks, Hkv, B, d, bt,
+                           context_lens[s], Kc, Vc)))
         goto done;
       cur_seq = s;
       cur_len = context_lens[s];
     }
     for (int hq = 0; hq < Hq; ++hq) {
-      for (int e = 0; e < d; ++e) qv[e] = load_elt(q, ((size_t)r * Hq + hq) * d + e, dtype);
+      for (int e = 0; e < d; ++e) qv[e] = load_elt(q, ((size_t)r * Hq + hq) * d + e, q_dtype);
       attend_one(qv, p, Kc, Vc, Hkv, hq / G, d, (double)scale, z, out + ((size_t)r * Hq + hq) * d);
     }
   }
@@ -334,7 +416,8 @@ done:
  * reads the whole cache every step; [R] eq. (4) is the block-wise form of
  * the same result.  q and out are [S][Hq][d].
  */
-int oracle_paged_decode(const void *k_pool, const void *v_pool, int dtype, int64_t num_blocks,
+int oracle_paged_decode(const void *k_pool, const void *v_pool, int dtype, int q_dtype,
+                        double k_scale, double v_scale, int64_t num_blocks,
                         int Hkv, int B, int d, const void *q, int Hq, const int32_t *block_tables,
                         int max_blocks_per_seq, const int32_t *context_lens, int S, float scale,
                         double *out) {
@@ -346,9 +429,9 @@ int oracle_paged_decode(const void *k_pool, const void *v_pool, int dtype, int64
     rs[s] = s;
     rp[s] = context_lens[s] - 1;
   }
-  int rc = oracle_paged_attention_rows(k_pool, v_pool, dtype, num_blocks, Hkv, B, d, q, Hq,
-                                       block_tables, max_blocks_per_seq, context_lens, S, rs, rp, S,
-                                       scale, out);
+  int rc = oracle_paged_attention_rows(k_pool, v_pool, dtype, q_dtype, k_scale, v_scale, num_blocks,
+                                       Hkv, B, d, q, Hq, block_tables, max_blocks_per_seq,
+                                       context_lens, S, rs, rp, S, scale, out);
   free(rs);
   free(rp);
   return rc;
@@ -364,7 +447,8 @@ int oracle_paged_decode(const void *k_pool, const void *v_pool, int dtype, int64
  * [T] step 6: prefill handles all prompt tokens at once.  q and out are
  * [total rows][Hq][d].
  */
-int oracle_paged_prefill(const void *k_pool, const void *v_pool, int dtype, int64_t num_blocks,
+int oracle_paged_prefill(const void *k_pool, const void *v_pool, int dtype, int q_dtype,
+                         double k_scale, double v_scale, int64_t num_blocks,
                          int Hkv, int B, int d, const void *q, int Hq,
                          const int32_t *query_start_loc, const int32_t *context_lens,
                          const int32_t *block_tables, int max_blocks_per_seq, int S, float scale,
@@ -386,9 +470,9 @@ int oracle_paged_prefill(const void *k_pool, const void *v_pool, int dtype, int6
       rp[query_start_loc[s] + i] = hist + i;
     }
   }
-  int rc = oracle_paged_attention_rows(k_pool, v_pool, dtype, num_blocks, Hkv, B, d, q, Hq,
-                                       block_tables, max_blocks_per_seq, context_lens, S, rs, rp, n,
-                                       scale, out);
+  int rc = oracle_paged_attention_rows(k_pool, v_pool, dtype, q_dtype, k_scale, v_scale, num_blocks,
+                                       Hkv, B, d, q, Hq, block_tables, max_blocks_per_seq,
+                                       context_lens, S, rs, rp, n, scale, out);
   free(rs);
   free(rp);
   return rc;
@@ -397,3 +481,5 @@ int oracle_paged_prefill(const void *k_pool, const void *v_pool, int dtype, int6
 /* Bit decoders exported so that tests can pin them against known encodings. */
 double oracle_f16_to_double(uint16_t h) { return f16_to_double(h); }
 double oracle_bf16_to_double(uint16_t b) { return bf16_to_double(b); }
+double oracle_fp8_to_double(uint8_t b) { return fp8_to_double(b); }
+uint8_t oracle_fp8_from_float(float x) { return fp8_from_float(x); }

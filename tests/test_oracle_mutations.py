@@ -30,6 +30,13 @@ MUTATIONS = [
     ("prefill position", "rp[query_start_loc[s] + i] = hist + i;",
      "rp[query_start_loc[s] + i] = hist + i / 2;", ["test_prefill_causal_range_is_exact"]),
     ("f16 exponent bias", "expo - 25", "expo - 24", ["test_f16_decoder_known_encodings"]),
+    ("fp8 exponent bias", "expo - 10", "expo - 9", ["test_fp8_decoder_known_encodings"]),
+    ("fp8 ties away from zero", "(int)rint(ldexp(a, 3 - E))", "(int)floor(ldexp(a, 3 - E) + 0.5)",
+     ["test_fp8_encoder_is_nearest_even_by_brute_force"]),
+    ("fp8 scale not applied on write", "fp8_from_float(x / scale)", "fp8_from_float(x)",
+     ["test_fp8_scatter_stores_codes_of_fp32_quotients"]),
+    ("fp8 key scale not applied on read", "Kc[dst] = ks *", "Kc[dst] =",
+     ["test_fp8_decode_matches_brute_force_on_dequantised_kv"]),
     ("query dot uses wrong operand", "dot += q[e] * k[e];", "dot += q[e] * q[e];",
      ["test_weights_are_softmax_and_sum_to_one"]),
 ]

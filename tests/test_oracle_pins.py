@@ -416,3 +416,115 @@ def test_sampled_rows_match_full_output():
     full = reference_output(wl, k, v)
     rows = [0, 7, 15, 16, 31]
     assert np.array_equal(sampled_rows(wl, k, v, rows), full[rows])
+
+
+# --------------------------------------------------------------------------
+# 8-bit float cache (E4M3 codes with per-tensor scales)
+# --------------------------------------------------------------------------
+
+FP8 = oracle.FP8
+
+
+def test_fp8_decoder_known_encodings():
+    # Values fixed by the E4M3 format: bias 7, 3 mantissa bits, subnormals
+    # m * 2^-9, S.1111.111 is NaN, no infinities.
+    cases = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+             0x39: 1.125, 0x40: 2.0, 0x7E: 448.0, 0x77: 240.0, 0x80: -0.0, 0xB8: -1.0, 0xFE: -448.0}
+    for b, v in cases.items():
+        got = oracle.fp8_to_double(b)
+        assert got == v and math.copysign(1, got) == math.copysign(1, v), (hex(b), got, v)
+    assert math.isnan(oracle.fp8_to_double(0x7F)) and math.isnan(oracle.fp8_to_double(0xFF))
+
+
+def test_fp8_decoder_matches_torch_on_every_pattern():
+    import torch
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.fp8_to_double(b) for b in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+def _nearest_code_brute_force(x):
+    """E4M3 code nearest to x among all finite codes, ties to the even code (last bit 0)."""
+    vals = np.array([oracle.fp8_to_double(b) for b in range(256)])
+    best = None
+    for b in range(256):
+        if math.isnan(vals[b]) or (vals[b] == 0 and b == 0x80 and x >= 0) or \
+                (vals[b] == 0 and b == 0x00 and math.copysign(1, x) < 0):
+            continue
+        err = abs(vals[b] - x)
+        if best is None or err < best[0] or (err == best[0] and (b & 1) == 0):
+            best = (err, b)
+    return best[1]
+
+
+def test_fp8_encoder_is_nearest_even_by_brute_force():
+    rng = np.random.default_rng(8)
+    xs = list(rng.standard_normal(300).astype(np.float32) * np.float32(40))
+    xs += list((rng.random(100).astype(np.float32) * np.float32(0.03)))      # subnormal range
+    # Exact midpoints between neighbouring codes: ties go to the even code.
+    vals = [oracle.fp8_to_double(b) for b in range(0x7E)]
+    xs += [np.float32((vals[i] + vals[i + 1]) / 2) for i in range(0, 0x7D, 3)]
+    for x in xs:
+        x = float(np.float32(x))
+        assert oracle.fp8_from_float(x) == _nearest_code_brute_force(x), x
+
+
+def test_fp8_encoder_round_trips_and_saturates():
+    for b in range(256):
+        v = oracle.fp8_to_double(b)
+        if not math.isnan(v):
+            assert oracle.fp8_from_float(v) == b, hex(b)
+    for x, code in [(447.9, 0x7E), (448.0, 0x7E), (464.0, 0x7E), (1e30, 0x7E), (math.inf, 0x7E),
+                    (-1e30, 0xFE), (-math.inf, 0xFE), (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02), (5 * 2.0 ** -10, 0x02)]:
+        assert oracle.fp8_from_float(x) == code, (x, hex(code))
+    assert oracle.fp8_from_float(math.nan) & 0x7F == 0x7F
+    import torch   # in range the code is the library's round-to-nearest-even conversion
+    xs = torch.from_numpy(np.random.default_rng(9).uniform(-440, 440, 2000).astype(np.float32))
+    ref = xs.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert [oracle.fp8_from_float(float(x)) for x in xs] == list(ref)
+
+
+def test_fp8_scatter_stores_codes_of_fp32_quotients():
+    # Stored code = E4M3 code of fp32(x) / fp32(scale), one fp32 division.
+    H, d, B = 2, 64, 16
+    k = np.zeros((4, H, d // 64, B, 64), np.uint8)
+    v = np.zeros((4, H, d, B), np.uint8)
+    rng = np.random.default_rng(12)
+    key = W.round_to(rng.standard_normal((3, H, d), dtype=np.float32) * 3, BF16)
+    val = W.round_to(rng.standard_normal((3, H, d), dtype=np.float32) * 3, BF16)
+    ks, vs = np.float32(0.037), np.float32(1.9)
+    oracle.reshape_and_cache(k, v, FP8, key, val, np.array([5, 17, 63]), in_dtype=BF16, k_scale=ks,
+                             v_scale=vs)
+    kf = (key.astype(np.uint32) << 16).view(np.float32)
+    vf = (val.astype(np.uint32) << 16).view(np.float32)
+    for t, slot in enumerate([5, 17, 63]):
+        blk, off = divmod(slot, B)
+        for h in range(H):
+            for e in range(0, d, 7):
+                assert k[blk, h, e // 64, off, e % 64] == _nearest_code_brute_force(float(kf[t, h, e] / ks))
+                assert v[blk, h, e, off] == _nearest_code_brute_force(float(vf[t, h, e] / vs))
+
+
+def test_fp8_decode_matches_brute_force_on_dequantised_kv():
+    wl = W.make_decode("fp8bf", 14, lambda rng: [1, 30, 77], Hq=4, Hkv=2, d=64, B=16, dtype=BF16,
+                       max_context_len=96)
+    ks, vs = np.float32(0.02), np.float32(0.03)
+    nb = wl.num_blocks
+    k = np.zeros((nb, 2, 1, 16, 64), np.uint8)
+    v = np.zeros((nb, 2, 64, 16), np.uint8)
+    for op in wl.setup + [wl.step_scatter]:
+        oracle.reshape_and_cache(k, v, FP8, op.key, op.value, op.slots, in_dtype=BF16, k_scale=ks,
+                                 v_scale=vs)
+    out = oracle.paged_decode(k, v, FP8, wl.q, wl.block_tables, wl.context_lens, wl.scale,
+                              q_dtype=BF16, k_scale=ks, v_scale=vs)
+    gk, gv = oracle.gather_kv(k, v, FP8, wl.block_tables, wl.context_lens)
+    cu = np.concatenate([[0], np.cumsum(wl.context_lens)])
+    for s in range(wl.S):
+        K = oracle.decode_values(gk[cu[s]:cu[s + 1]], FP8) * float(ks)
+        V = oracle.decode_values(gv[cu[s]:cu[s + 1]], FP8) * float(vs)
+        for hq in range(4):
+            q = _vals(wl.q[s, hq], BF16)
+            ref = _numpy_textbook(q, K[:, hq // 2], V[:, hq // 2], wl.scale)
+            np.testing.assert_allclose(out[s, hq], ref, rtol=1e-12, atol=1e-14)
