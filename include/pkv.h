@@ -68,7 +68,9 @@
 extern "C" {
 #endif
 
-typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+/* PKV_FP8_E4M3 is a cache storage type only (OCP FP8 E4M3: 4 exponent bits,
+ * bias 7, 3 mantissa bits, S.1111.111 = NaN, no infinities, |x| <= 448). */
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_FP8_E4M3 = 3 } pkv_dtype;
 
 typedef enum {
   PKV_OK = 0,
@@ -78,15 +80,28 @@ typedef enum {
   PKV_ERR_HIP = 4          /* a HIP launch error (message from the runtime) */
 } pkv_status;
 
-/* Describes caller-owned device memory of one layer's cache. */
+/*
+ * Describes caller-owned device memory of one layer's cache.
+ *
+ * An 8-bit cache ([W] section "PagedAttention 커널: 비연속 메모리 접근":
+ * write_to_paged_cache passes kv_cache_dtype, k_scale and v_scale to
+ * reshape_and_cache): dtype PKV_FP8_E4M3, model_dtype PKV_F16 or PKV_BF16.
+ * A key element x is stored as the E4M3 code of the fp32 quotient x /
+ * k_scale (nearest, ties to even; magnitudes >= 448 saturate to 448; NaN
+ * stays NaN) and read back as code * k_scale; values likewise with v_scale.
+ * Otherwise model_dtype equals dtype and the scales are ignored.
+ */
 typedef struct {
-  void *k_pool;          /* [num_blocks][num_kv_heads][block_size][head_dim] */
+  void *k_pool;          /* [num_blocks][num_kv_heads][head_dim/X][block_size][X] */
   void *v_pool;          /* [num_blocks][num_kv_heads][head_dim][block_size] */
   int64_t num_blocks;
   int32_t num_kv_heads;
   int32_t block_size;    /* 16 or 32 */
   int32_t head_dim;      /* 64 or 128 */
-  int32_t dtype;         /* pkv_dtype */
+  int32_t dtype;         /* pkv_dtype of the pools */
+  int32_t model_dtype;   /* pkv_dtype of key/value inputs, queries and outputs */
+  float k_scale;         /* 8-bit cache only: positive, finite */
+  float v_scale;
 } pkv_cache;
 
 /*
@@ -96,12 +111,13 @@ typedef struct {
  * in the slot named for it; [T] step 6: decode stores the new token's K/V in
  * the next free slot of the request's last block.
  *
- *   key, value     [num_tokens][num_kv_heads][head_dim], cache dtype
+ *   key, value     [num_tokens][num_kv_heads][head_dim], model_dtype
  *   slot_mapping   int64 [num_tokens]; a negative slot skips that token
  *                  (padding); slots >= num_blocks * block_size are skipped too
  *
- * Bit-exact copy (no conversion).  Duplicate non-negative slots are a caller
- * error with no defined winner.  num_tokens == 0 is a no-op.
+ * Bit-exact copy into a 16/32-bit cache; into an 8-bit cache each element
+ * is quantised as described at pkv_cache.  Duplicate non-negative slots are
+ * a caller error with no defined winner.  num_tokens == 0 is a no-op.
  */
 pkv_status pkv_reshape_and_cache(const pkv_cache *cache, const void *key, const void *value,
                                  const int64_t *slot_mapping, int64_t num_tokens,
@@ -146,8 +162,8 @@ size_t pkv_decode_workspace_bytes(const pkv_cache *cache, int32_t num_seqs, int3
  * weighted values.  Query head hq reads KV head hq / (Hq / Hkv) (grouped
  * heads, [S] section "The Hidden Waste of KV Cache").
  *
- *   out, q            [num_seqs][num_q_heads][head_dim]; q in the cache dtype
- *   out_dtype         the cache dtype (out rounded once, to nearest even, from
+ *   out, q            [num_seqs][num_q_heads][head_dim]; q in model_dtype
+ *   out_dtype         model_dtype (out rounded once, to nearest even, from
  *                     the fp32 result) or PKV_F32 (the fp32 result itself)
  *   block_tables      int32 [num_seqs][max_blocks_per_seq]
  *   context_lens      int32 [num_seqs]; L_s counts every cached token,
@@ -170,9 +186,10 @@ size_t pkv_decode_workspace_bytes(const pkv_cache *cache, int32_t num_seqs, int3
  *   workspace         device scratch of >= pkv_decode_workspace_bytes(...)
  *                     bytes, 16-byte aligned; may be NULL when that is 0
  *
- * Grouped heads (num_q_heads > num_kv_heads) with f16/bf16 run on the matrix
- * cores with the group's queries stacked into one tile; other cases run the
- * wavefront dot-product kernel.  Group size must be <= 16.
+ * Grouped heads (num_q_heads > num_kv_heads) over an f16/bf16 cache run on
+ * the matrix cores with the group's queries stacked into one tile (group
+ * size <= 16); other cases, 8-bit caches included, run the wavefront
+ * dot-product kernel (which reads a KV head once per query head).
  */
 pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype, const void *q,
                             int32_t num_q_heads,
@@ -192,7 +209,8 @@ pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype
  * position.  Blocks may be shared between sequences (prefix sharing).
  *
  *   out, q            [total_rows][num_q_heads][head_dim]; cache dtype f16 or
- *                     bf16; out_dtype as for pkv_paged_decode
+ *                     bf16 (8-bit caches: PKV_ERR_UNSUPPORTED); out_dtype as
+ *                     for pkv_paged_decode
  *   query_start_loc   int32 [num_seqs + 1], non-decreasing, starts at 0
  *   context_lens      int32 [num_seqs], >= qlen_s, >= 1
  *   max_query_len     host bound on every qlen_s
@@ -208,7 +226,8 @@ pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, int32_t out_dtyp
  * Debug gather with the kernels' own address arithmetic: the contiguous
  * K and V of every sequence, back to back, token-major.
  *
- *   k_out, v_out      [sum_s L_s][num_kv_heads][head_dim], cache dtype
+ *   k_out, v_out      [sum_s L_s][num_kv_heads][head_dim], cache dtype (the
+ *                     stored codes for an 8-bit cache)
  *   cu_context_lens   int32 [num_seqs + 1], prefix sums of context_lens
  */
 pkv_status pkv_gather_kv(const pkv_cache *cache, void *k_out, void *v_out,

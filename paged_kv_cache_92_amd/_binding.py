@@ -17,8 +17,9 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpkv.so")
 
-PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
-_TORCH_TO_PKV = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
+_TORCH_TO_PKV = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16,
+                 torch.float8_e4m3fn: PKV_FP8_E4M3}
 _STATUS = {0: "OK", 1: "INVALID", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP"}
 
 EXPORTED = ("pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_decode_workspace_bytes",
@@ -36,7 +37,8 @@ class PkvCacheDesc(ctypes.Structure):
     _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
                 ("num_blocks", ctypes.c_int64), ("num_kv_heads", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("model_dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 _lib = None
@@ -96,10 +98,16 @@ class PagedKVCache:
     block's pieces of one dimension range adjacent) and ``v_pool`` is
     [num_blocks][num_kv_heads][head_dim][block_size] (value tile
     dimension-major).
+
+    ``dtype`` is the pools' element type; ``model_dtype`` the type of the
+    key/value rows written, the queries and the outputs (``dtype`` itself,
+    except for a ``torch.float8_e4m3fn`` cache: float16 or bfloat16, with
+    per-tensor ``k_scale`` / ``v_scale``: stored code = x / scale).
     """
 
     def __init__(self, num_blocks, num_kv_heads, block_size, head_dim, dtype=torch.float16,
-                 device="cuda", k_pool=None, v_pool=None):
+                 device="cuda", k_pool=None, v_pool=None, model_dtype=None, k_scale=1.0,
+                 v_scale=1.0):
         self.num_blocks = int(num_blocks)
         self.num_kv_heads = int(num_kv_heads)
         self.block_size = int(block_size)
@@ -107,6 +115,11 @@ class PagedKVCache:
         self.dtype = dtype
         if dtype not in _TORCH_TO_PKV:
             raise ValueError(f"unsupported dtype {dtype}")
+        self.model_dtype = dtype if model_dtype is None else model_dtype
+        if self.model_dtype not in _TORCH_TO_PKV:
+            raise ValueError(f"unsupported model dtype {self.model_dtype}")
+        self.k_scale = float(k_scale)
+        self.v_scale = float(v_scale)
         x = 64 // torch.tensor([], dtype=dtype).element_size()
         if self.head_dim % x:
             raise ValueError(f"head_dim must be a multiple of {x}")
@@ -123,7 +136,8 @@ class PagedKVCache:
     def desc(self) -> PkvCacheDesc:
         return PkvCacheDesc(self.k_pool.data_ptr(), self.v_pool.data_ptr(), self.num_blocks,
                             self.num_kv_heads, self.block_size, self.head_dim,
-                            _TORCH_TO_PKV[self.dtype])
+                            _TORCH_TO_PKV[self.dtype], _TORCH_TO_PKV[self.model_dtype],
+                            self.k_scale, self.v_scale)
 
     def nbytes(self) -> int:
         return self.k_pool.nbytes + self.v_pool.nbytes
@@ -136,8 +150,8 @@ def reshape_and_cache(cache: PagedKVCache, key, value, slot_mapping):
               or tuple(value.shape) != tuple(key.shape)):
         raise ValueError("key/value must be [T][num_kv_heads][head_dim]")
     d = cache.desc()
-    _check(lib().pkv_reshape_and_cache(ctypes.byref(d), _dev_ptr(key, "key", cache.dtype),
-                                       _dev_ptr(value, "value", cache.dtype),
+    _check(lib().pkv_reshape_and_cache(ctypes.byref(d), _dev_ptr(key, "key", cache.model_dtype),
+                                       _dev_ptr(value, "value", cache.model_dtype),
                                        _dev_ptr(slot_mapping, "slot_mapping", torch.int64), T,
                                        _stream()))
 
@@ -176,7 +190,7 @@ def paged_decode(cache: PagedKVCache, q, block_tables, context_lens, max_context
                  partition_size=0, out=None, workspace=None, out_dtype=None):
     """Decode attention: q [S][Hq][d] -> out [S][Hq][d] over each sequence's paged cache.
 
-    ``out_dtype`` is the cache dtype (default: the fp32 result rounded once) or
+    ``out_dtype`` is the model dtype (default: the fp32 result rounded once) or
     torch.float32 (the fp32 result itself)."""
     S, Hq, dq = q.shape
     if dq != cache.head_dim:
@@ -191,7 +205,7 @@ def paged_decode(cache: PagedKVCache, q, block_tables, context_lens, max_context
     ws_bytes = workspace.nbytes if workspace is not None else 0
     d = cache.desc()
     _check(lib().pkv_paged_decode(ctypes.byref(d), _dev_ptr(out, "out"), _TORCH_TO_PKV[out.dtype],
-                                  _dev_ptr(q, "q", cache.dtype), Hq,
+                                  _dev_ptr(q, "q", cache.model_dtype), Hq,
                                   _dev_ptr(block_tables, "block_tables", torch.int32),
                                   block_tables.shape[1],
                                   _dev_ptr(context_lens, "context_lens", torch.int32), S,
@@ -212,7 +226,7 @@ def paged_prefill(cache: PagedKVCache, q, query_start_loc, context_lens, block_t
     S = context_lens.shape[0]
     d = cache.desc()
     _check(lib().pkv_paged_prefill(ctypes.byref(d), _dev_ptr(out, "out"), _TORCH_TO_PKV[out.dtype],
-                                   _dev_ptr(q, "q", cache.dtype), Hq,
+                                   _dev_ptr(q, "q", cache.model_dtype), Hq,
                                    _dev_ptr(query_start_loc, "query_start_loc", torch.int32),
                                    _dev_ptr(context_lens, "context_lens", torch.int32),
                                    _dev_ptr(block_tables, "block_tables", torch.int32),

@@ -79,6 +79,73 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict_
   }
 }
 
+// Slot scatter into an 8-bit cache: as scatter_kernel, but every element of
+// the model-dtype key (value) row is stored as the E4M3 code of the fp32
+// quotient x / k_scale (x / v_scale), one IEEE single division, rounded to
+// nearest even and saturating (the cache-write call's kv_cache_dtype,
+// k_scale and v_scale, [vLLM] PagedAttention, blog.secrett2633.cloud).  Key
+// codes go out 8 at a time into the 64-byte pieces; value codes are
+// transposed through LDS like the 16-bit values.
+template <typename M, int D>
+__global__ __launch_bounds__(256) void scatter_fp8_kernel(const uint16_t *__restrict__ key,
+                                                          const uint16_t *__restrict__ value,
+                                                          const int64_t *__restrict__ slots,
+                                                          uint8_t *__restrict__ kpool,
+                                                          uint8_t *__restrict__ vpool, int64_t T,
+                                                          int H, int B, int64_t nslots,
+                                                          float k_scale, float v_scale) {
+  constexpr int kTok = 16;
+  constexpr int CH = D / 8;          // 8-element groups per (token, head) row
+  constexpr int NC = D / 64;         // 64-byte key pieces per row
+  __shared__ int64_t sslot[kTok];
+  __shared__ uint8_t sv[D][kTok + 4];
+
+  const int h = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * kTok;
+  const int tid = threadIdx.x;
+  if (tid < kTok) {
+    const int64_t t = t0 + tid;
+    int64_t sl = t < T ? slots[t] : -1;
+    if (sl >= nslots) sl = -1;
+    sslot[tid] = sl;
+  }
+  __syncthreads();
+  const int lgB = B == 32 ? 5 : 4;
+  auto quantise8 = [](const u32x4 &c, float scale) -> u32x2 {
+    float f[8];
+    unpack16<M>(c, f);
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i >> 2] |= f32_to_fp8_bits(__fdiv_rn(f[i], scale)) << (8 * (i & 3));
+    return u32x2{w[0], w[1]};
+  };
+  for (int c = tid; c < kTok * CH; c += blockDim.x) {
+    const int tt = c / CH, g = c % CH;
+    const int64_t t = t0 + tt;
+    if (t >= T) continue;
+    const size_t src = ((size_t)t * H + h) * D + (size_t)g * 8;
+    const u32x2 vq = quantise8(load16(value + src), v_scale);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sv[g * 8 + i][tt] = (uint8_t)(vq[i >> 2] >> (8 * (i & 3)));
+    const int64_t sl = sslot[tt];
+    if (sl < 0) continue;
+    const int64_t blk = sl >> lgB;
+    const int off = (int)(sl & (B - 1));
+    const int e0 = g * 8;
+    *(u32x2 *)(kpool + (((size_t)(blk * H + h) * NC + e0 / 64) * B + off) * 64 + e0 % 64) =
+        quantise8(load16(key + src), k_scale);
+  }
+  __syncthreads();
+  for (int c = tid; c < D * kTok; c += blockDim.x) {
+    const int tt = c % kTok, e = c / kTok;
+    const int64_t sl = sslot[tt];
+    if (sl < 0) continue;
+    const int64_t blk = sl >> lgB;
+    const int off = (int)(sl & (B - 1));
+    vpool[((size_t)(blk * H + h) * D + e) * B + off] = sv[e][tt];
+  }
+}
+
 // Copy-on-write block copy ("Sparse Computation and Memory Management...",
 // pyy0715.github.io, section "Copy-on-Write"): both tiles of every head of
 // block src go to block dst.  grid.y walks the pairs, grid.x strides over the
@@ -131,7 +198,16 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t *__restrict__
       kpool + ((((size_t)(blk * (int64_t)H + h) * NC + c / 4) * B + off) * X + (c % 4) * VEC) * EB);
   const size_t vrow = ((size_t)(blk * (int64_t)H + h) * D + (size_t)c * VEC) * B + off;
   u32x4 packed;
-  if constexpr (EB == 4) {
+  if constexpr (EB == 1) {
+    const uint8_t *vp = vpool;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w |= (uint32_t)vp[vrow + (size_t)(4 * i + k) * B] << (8 * k);
+      packed[i] = w;
+    }
+  } else if constexpr (EB == 4) {
     const uint32_t *vp = (const uint32_t *)vpool;
 #pragma unroll
     for (int i = 0; i < 4; ++i) packed[i] = vp[vrow + (size_t)i * B];
@@ -156,7 +232,19 @@ hipError_t launch_reshape_and_cache(const CacheDesc &c, const void *key, const v
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const uint8_t *)key, (const uint8_t *)value,
                        slots, (uint8_t *)c.k, (uint8_t *)c.v, T, c.H, c.B, nslots);
   };
-  if (c.elt_bytes() == 4) {
+  auto go8 = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const uint16_t *)key, (const uint16_t *)value,
+                       slots, (uint8_t *)c.k, (uint8_t *)c.v, T, c.H, c.B, nslots, c.k_scale, c.v_scale);
+  };
+  if (c.fp8()) {
+    if (c.mdtype == 1) {
+      if (c.D == 64) go8(scatter_fp8_kernel<F16, 64>);
+      else go8(scatter_fp8_kernel<F16, 128>);
+    } else {
+      if (c.D == 64) go8(scatter_fp8_kernel<BF16, 64>);
+      else go8(scatter_fp8_kernel<BF16, 128>);
+    }
+  } else if (c.elt_bytes() == 4) {
     if (c.D == 64) go(scatter_kernel<4, 64>);
     else go(scatter_kernel<4, 128>);
   } else {
@@ -183,7 +271,11 @@ hipError_t launch_gather_kv(const CacheDesc &c, void *k_out, void *v_out, const 
   const int EB = c.elt_bytes();
   const int64_t work = (int64_t)max_context_len * c.H * (c.D * EB / 16);
   const dim3 grid((unsigned)((work + 255) / 256), (unsigned)S);
-  if (EB == 4)
+  if (EB == 1)
+    hipLaunchKernelGGL(gather_kernel<1>, grid, dim3(256), 0, stream, (const uint8_t *)c.k,
+                       (const uint8_t *)c.v, (uint8_t *)k_out, (uint8_t *)v_out, bt, mbps, ctx, cu,
+                       c.num_blocks, c.H, c.B, c.D, max_context_len);
+  else if (EB == 4)
     hipLaunchKernelGGL(gather_kernel<4>, grid, dim3(256), 0, stream, (const uint8_t *)c.k,
                        (const uint8_t *)c.v, (uint8_t *)k_out, (uint8_t *)v_out, bt, mbps, ctx, cu,
                        c.num_blocks, c.H, c.B, c.D, max_context_len);

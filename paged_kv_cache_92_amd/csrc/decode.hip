@@ -59,17 +59,21 @@ struct ValuLds {
 };
 
 // One work item: blocks [b0, b1) of sequence s for query head hq; the merged
-// result goes to the output or to a workspace partial row (dest).
-template <typename E, int D, int BS>
+// result goes to the output or to a workspace partial row (dest).  E is the
+// cache's element type, Q the query/output type (E itself, except over an
+// 8-bit cache: there the key scale is folded into scale_log2 and the value
+// scale multiplies the merged sums).
+template <typename E, typename Q, int D, int BS>
 __device__ __forceinline__ void valu_item(
     ValuLds<E, D, BS> &sh, int s, int hq, int b0, int b1, Dest dest, void *__restrict__ out,
-    int out_f32, const typename E::storage *__restrict__ q,
+    int out_f32, const typename Q::storage *__restrict__ q,
     const typename E::storage *__restrict__ kpool, const typename E::storage *__restrict__ vpool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    int64_t num_blocks, int Hkv, int Hq, int mbps, float scale_log2, float *__restrict__ ws_ml,
-    float *__restrict__ ws_acc) {
+    int64_t num_blocks, int Hkv, int Hq, int mbps, float scale_log2, float v_scale,
+    float *__restrict__ ws_ml, float *__restrict__ ws_acc) {
   using C = ValuCfg<E, D, BS>;
   using T = typename E::storage;
+  constexpr bool kFP8 = E::kBytes == 1;
   const int L = min(context_lens[s], mbps * BS);
   const int tok0 = b0 * BS;
   const int tok1 = min(L, b1 * BS);
@@ -89,13 +93,36 @@ __device__ __forceinline__ void valu_item(
   auto &lds_l = sh.l;
   auto &lds_acc = sh.acc;
 
-  // The query dimensions this lane multiplies, kept in the packed input format.
-  u32x4 qc[C::NC];
+  // The query dimensions this lane multiplies: kept in the packed input
+  // format (dot2 products), or as fp32 over an 8-bit cache.
+  u32x4 qc[kFP8 ? 1 : C::NC];
+  float qf[kFP8 ? C::NC : 1][kFP8 ? C::VEC : 1];
   {
-    const T *qrow = q + ((size_t)s * Hq + hq) * D + kq * C::VEC;
+    const typename Q::storage *qrow = q + ((size_t)s * Hq + hq) * D + kq * C::VEC;
+    if constexpr (kFP8) {
 #pragma unroll
-    for (int c = 0; c < C::NC; ++c) qc[c] = load16(qrow + c * C::X);
+      for (int c = 0; c < C::NC; ++c) {
+        unpack16<Q>(load16(qrow + c * C::X), &qf[c][0]);
+        unpack16<Q>(load16(qrow + c * C::X + 8), &qf[c][8]);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) qc[c] = load16(qrow + c * C::X);
+    }
   }
+  // q.k of this lane's slice against one 16-byte key load of piece c.
+  auto dot = [&](const u32x4 &k, int c) -> float {
+    if constexpr (kFP8) {
+      float kf[16];
+      unpack16<FP8>(k, kf);
+      float d = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) d = fmaf(qf[c][i], kf[i], d);
+      return d;
+    } else {
+      return dot16<E>(k, qc[c]);
+    }
+  };
 
   float m = -INFINITY;
   float l = 0.f;
@@ -125,9 +152,9 @@ __device__ __forceinline__ void valu_item(
     float sc[C::TG];
 #pragma unroll
     for (int r = 0; r < C::TG; ++r) {
-      float x = dot16<E>(kr[r], qc[0]);
+      float x = dot(kr[r], 0);
 #pragma unroll
-      for (int c = 1; c < C::NC; ++c) x += dot16<E>(kr[c * C::TG + r], qc[c]);
+      for (int c = 1; c < C::NC; ++c) x += dot(kr[c * C::TG + r], c);
       x = group_sum<4>(x) * scale_log2;
       if (partial && tbase + 16 * r + kt >= tok1) x = -INFINITY;
       sc[r] = x;
@@ -200,8 +227,9 @@ __device__ __forceinline__ void valu_item(
       num = fmaf(f, lds_acc[k][e], num);
       den = fmaf(f, lds_l[k], den);
     }
+    if constexpr (kFP8) num *= v_scale;
     if (dest.base < 0) {
-      store_out<E>(out, ((size_t)s * Hq + hq) * D + e, num / den, out_f32);
+      store_out<Q>(out, ((size_t)s * Hq + hq) * D + e, num / den, out_f32);
     } else {
       const size_t pi = dest.base;
       ws_acc[pi * D + e] = num;
@@ -218,21 +246,23 @@ __device__ __forceinline__ void valu_item(
 // grid schedule asks for 8 waves per SIMD (64 VGPRs) only where one block's
 // loads plus the query slice fit that budget without spills; other variants
 // keep the compiler's choice.
-template <typename E, int D, int BS, int SCHED>
-__global__ __launch_bounds__(256, (SCHED == kSchedGrid && ValuCfg<E, D, BS>::kLoadRegs + 4 * ValuCfg<E, D, BS>::NC <= 24) ? 8 : 1) void
+template <typename E, typename Q, int D, int BS, int SCHED>
+__global__ __launch_bounds__(256, (SCHED == kSchedGrid && E::kBytes >= 2 && ValuCfg<E, D, BS>::kLoadRegs + 4 * ValuCfg<E, D, BS>::NC <= 24) ? 8 : 1) void
 decode_valu_kernel(
-    void *__restrict__ out, int out_f32, const typename E::storage *__restrict__ q,
+    void *__restrict__ out, int out_f32, const typename Q::storage *__restrict__ q,
     const typename E::storage *__restrict__ kpool, const typename E::storage *__restrict__ vpool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    int64_t num_blocks, int Hkv, int Hq, int S, int mbps, float scale_log2, int part_tokens,
-    int nparts, float *__restrict__ ws_ml, float *__restrict__ ws_acc, int *__restrict__ ws_hdr) {
+    int64_t num_blocks, int Hkv, int Hq, int S, int mbps, float scale_log2, float v_scale,
+    int part_tokens, int nparts, float *__restrict__ ws_ml, float *__restrict__ ws_acc,
+    int *__restrict__ ws_hdr) {
   __shared__ ValuLds<E, D, BS> sh;
   extern __shared__ int plan[];
   __shared__ int scan[16];
   run_schedule<SCHED>(
       [&](int s, int hq, int b0, int b1, Dest dest) {
-        valu_item<E, D, BS>(sh, s, hq, b0, b1, dest, out, out_f32, q, kpool, vpool, block_tables,
-                            context_lens, num_blocks, Hkv, Hq, mbps, scale_log2, ws_ml, ws_acc);
+        valu_item<E, Q, D, BS>(sh, s, hq, b0, b1, dest, out, out_f32, q, kpool, vpool, block_tables,
+                               context_lens, num_blocks, Hkv, Hq, mbps, scale_log2, v_scale, ws_ml,
+                               ws_acc);
       },
       plan, scan, context_lens, S, mbps * BS, BS, Hq, 1, part_tokens, nparts, ws_hdr);
 }
@@ -292,16 +322,17 @@ __global__ __launch_bounds__(128) void decode_reduce_flat_kernel(
   }
 }
 
-template <typename E, int D, int BS>
+template <typename E, typename Q, int D, int BS>
 void launch_valu_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
   using T = typename E::storage;
-  const float sl = a.scale * kLog2e;
+  using TQ = typename Q::storage;
+  const float sl = a.scale * kLog2e * c.k_scale;  // k_scale is 1 unless the cache is 8-bit
   const size_t lds = sizeof(int) * (a.S + 1);
   auto go = [&](auto kern, dim3 grid, size_t dyn) {
-    hipLaunchKernelGGL(kern, grid, dim3(256), dyn, stream, a.out, (int)a.out_f32, (const T *)a.q,
+    hipLaunchKernelGGL(kern, grid, dim3(256), dyn, stream, a.out, (int)a.out_f32, (const TQ *)a.q,
                        (const T *)c.k, (const T *)c.v, a.block_tables, a.context_lens,
-                       c.num_blocks, c.H, a.Hq, a.S, a.max_blocks_per_seq, sl, a.partition_tokens,
-                       a.num_partitions, a.ws_ml, a.ws_acc, a.ws_hdr);
+                       c.num_blocks, c.H, a.Hq, a.S, a.max_blocks_per_seq, sl, c.v_scale,
+                       a.partition_tokens, a.num_partitions, a.ws_ml, a.ws_acc, a.ws_hdr);
   };
   // Fixed partitions run a persistent grid over the non-empty cells (a 3-D
   // grid would launch a workgroup for every empty partition); without a split
@@ -310,38 +341,38 @@ void launch_valu_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) 
 #define PKV_GRID_FACTOR 4
 #endif
   if (a.flat) {
-    go(decode_valu_kernel<E, D, BS, kSchedFlat>, dim3(a.flat_grid), lds);
+    go(decode_valu_kernel<E, Q, D, BS, kSchedFlat>, dim3(a.flat_grid), lds);
   } else if (a.num_partitions > 1 && a.S <= kPlanMaxSeqs) {
-    auto kern = decode_valu_kernel<E, D, BS, kSchedPlan>;
+    auto kern = decode_valu_kernel<E, Q, D, BS, kSchedPlan>;
     const int64_t cells = (int64_t)a.S * a.num_partitions * a.Hq;
     const int grid = (int)std::min<int64_t>(cells, PKV_GRID_FACTOR * (int64_t)resident_workgroups((const void *)kern, 256, lds));
     go(kern, dim3(grid), lds);
   } else {
-    go(decode_valu_kernel<E, D, BS, kSchedGrid>,
+    go(decode_valu_kernel<E, Q, D, BS, kSchedGrid>,
        dim3((unsigned)a.num_partitions, (unsigned)a.Hq, (unsigned)a.S), 0);
   }
 }
 
-template <typename E>
+template <typename E, typename Q = E>
 void launch_valu_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
-  if (c.D == 64 && c.B == 16) launch_valu_t<E, 64, 16>(c, a, stream);
-  else if (c.D == 64 && c.B == 32) launch_valu_t<E, 64, 32>(c, a, stream);
-  else if (c.D == 128 && c.B == 16) launch_valu_t<E, 128, 16>(c, a, stream);
-  else launch_valu_t<E, 128, 32>(c, a, stream);
+  if (c.D == 64 && c.B == 16) launch_valu_t<E, Q, 64, 16>(c, a, stream);
+  else if (c.D == 64 && c.B == 32) launch_valu_t<E, Q, 64, 32>(c, a, stream);
+  else if (c.D == 128 && c.B == 16) launch_valu_t<E, Q, 128, 16>(c, a, stream);
+  else launch_valu_t<E, Q, 128, 32>(c, a, stream);
 }
 
-template <typename E, int D, int BS>
+template <typename E, typename Q, int D, int BS>
 int flat_grid_t(int S) {
-  return resident_workgroups((const void *)decode_valu_kernel<E, D, BS, kSchedFlat>, 256,
+  return resident_workgroups((const void *)decode_valu_kernel<E, Q, D, BS, kSchedFlat>, 256,
                              sizeof(int) * (S + 1));
 }
 
-template <typename E>
+template <typename E, typename Q = E>
 int flat_grid_e(const CacheDesc &c, int S) {
-  if (c.D == 64 && c.B == 16) return flat_grid_t<E, 64, 16>(S);
-  if (c.D == 64 && c.B == 32) return flat_grid_t<E, 64, 32>(S);
-  if (c.D == 128 && c.B == 16) return flat_grid_t<E, 128, 16>(S);
-  return flat_grid_t<E, 128, 32>(S);
+  if (c.D == 64 && c.B == 16) return flat_grid_t<E, Q, 64, 16>(S);
+  if (c.D == 64 && c.B == 32) return flat_grid_t<E, Q, 64, 32>(S);
+  if (c.D == 128 && c.B == 16) return flat_grid_t<E, Q, 128, 16>(S);
+  return flat_grid_t<E, Q, 128, 32>(S);
 }
 
 template <typename E>
@@ -349,7 +380,7 @@ void launch_reduce_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream
   const dim3 grid((unsigned)a.Hq, (unsigned)a.S);
   const int mt = a.max_blocks_per_seq * c.B;
   const int G = a.Hq / c.H;
-  const bool mfma = G > 1 && c.dtype != 0;
+  const bool mfma = G > 1 && (c.dtype == 1 || c.dtype == 2);
   const int HU = mfma ? c.H : a.Hq, GU = mfma ? G : 1;
   auto go = [&](auto kern_part, auto kern_flat, int threads) {
     if (a.flat)
@@ -367,21 +398,30 @@ void launch_reduce_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream
 }  // namespace
 
 hipError_t launch_decode_valu(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
-  if (c.dtype == 0) launch_valu_e<F32>(c, a, stream);
-  else if (c.dtype == 1) launch_valu_e<F16>(c, a, stream);
-  else launch_valu_e<BF16>(c, a, stream);
+  if (c.fp8()) {
+    if (c.mdtype == 1) launch_valu_e<FP8, F16>(c, a, stream);
+    else launch_valu_e<FP8, BF16>(c, a, stream);
+  } else if (c.dtype == 0) {
+    launch_valu_e<F32>(c, a, stream);
+  } else if (c.dtype == 1) {
+    launch_valu_e<F16>(c, a, stream);
+  } else {
+    launch_valu_e<BF16>(c, a, stream);
+  }
   return hipGetLastError();
 }
 
 int decode_valu_flat_grid(const CacheDesc &c, int S) {
+  if (c.fp8()) return c.mdtype == 1 ? flat_grid_e<FP8, F16>(c, S) : flat_grid_e<FP8, BF16>(c, S);
   if (c.dtype == 0) return flat_grid_e<F32>(c, S);
   if (c.dtype == 1) return flat_grid_e<F16>(c, S);
   return flat_grid_e<BF16>(c, S);
 }
 
+// The reduce writes the output, so it goes by the model dtype.
 hipError_t launch_decode_reduce(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
-  if (c.dtype == 0) launch_reduce_e<F32>(c, a, stream);
-  else if (c.dtype == 1) launch_reduce_e<F16>(c, a, stream);
+  if (c.mdtype == 0) launch_reduce_e<F32>(c, a, stream);
+  else if (c.mdtype == 1) launch_reduce_e<F16>(c, a, stream);
   else launch_reduce_e<BF16>(c, a, stream);
   return hipGetLastError();
 }

@@ -44,8 +44,16 @@ pkv_status check_cache(const pkv_cache *c, pkv::CacheDesc *d) {
     return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (16 or 32)", c->block_size);
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", c->head_dim);
-  if (c->dtype != PKV_F32 && c->dtype != PKV_F16 && c->dtype != PKV_BF16)
+  if (c->dtype != PKV_F32 && c->dtype != PKV_F16 && c->dtype != PKV_BF16 && c->dtype != PKV_FP8_E4M3)
     return fail(PKV_ERR_INVALID, "unknown dtype %d", c->dtype);
+  if (c->dtype == PKV_FP8_E4M3) {
+    if (c->model_dtype != PKV_F16 && c->model_dtype != PKV_BF16)
+      return fail(PKV_ERR_INVALID, "an 8-bit cache needs model_dtype PKV_F16 or PKV_BF16");
+    if (!(c->k_scale > 0.f) || !(c->k_scale < INFINITY) || !(c->v_scale > 0.f) || !(c->v_scale < INFINITY))
+      return fail(PKV_ERR_INVALID, "k_scale and v_scale must be positive and finite");
+  } else if (c->model_dtype != c->dtype) {
+    return fail(PKV_ERR_INVALID, "model_dtype must equal dtype for a 16/32-bit cache");
+  }
   d->k = c->k_pool;
   d->v = c->v_pool;
   d->num_blocks = c->num_blocks;
@@ -53,6 +61,9 @@ pkv_status check_cache(const pkv_cache *c, pkv::CacheDesc *d) {
   d->B = c->block_size;
   d->D = c->head_dim;
   d->dtype = c->dtype;
+  d->mdtype = c->model_dtype;
+  d->k_scale = c->dtype == PKV_FP8_E4M3 ? c->k_scale : 1.f;
+  d->v_scale = c->dtype == PKV_FP8_E4M3 ? c->v_scale : 1.f;
   return PKV_OK;
 }
 
@@ -95,7 +106,7 @@ DecodePlan plan_decode(const pkv::CacheDesc &c, int S, int Hq, int max_context_l
                        int partition_size) {
   DecodePlan d;
   const int G = Hq / c.H;
-  d.mfma = G > 1 && c.dtype != PKV_F32;
+  d.mfma = G > 1 && (c.dtype == PKV_F16 || c.dtype == PKV_BF16);
   if (partition_size == PKV_PARTITION_AUTO && S <= pkv::kPlanMaxSeqs) {
     d.flat = true;
     d.flat_grid = d.mfma ? pkv::decode_mfma_flat_grid(c, G, S) : pkv::decode_valu_flat_grid(c, S);
@@ -201,8 +212,8 @@ pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype
   if (!out || !q || !block_tables || !context_lens)
     return fail(PKV_ERR_INVALID, "out/q/block_tables/context_lens is NULL");
   if (!aligned16(out) || !aligned16(q)) return fail(PKV_ERR_INVALID, "q/out must be 16-byte aligned");
-  if (out_dtype != c.dtype && out_dtype != PKV_F32)
-    return fail(PKV_ERR_INVALID, "out_dtype must be the cache dtype or PKV_F32");
+  if (out_dtype != c.mdtype && out_dtype != PKV_F32)
+    return fail(PKV_ERR_INVALID, "out_dtype must be the model dtype or PKV_F32");
   if (num_q_heads <= 0 || num_q_heads % c.H != 0)
     return fail(PKV_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                 num_q_heads, c.H);
@@ -217,7 +228,8 @@ pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype
                 "partition_size %d must be PKV_PARTITION_AUTO, 0 or a positive multiple of block_size %d",
                 partition_size, c.B);
   const int G = num_q_heads / c.H;
-  if (G > 1 && c.dtype != PKV_F32 && G > 16) return fail(PKV_ERR_UNSUPPORTED, "group size %d > 16", G);
+  if (G > 16 && (c.dtype == PKV_F16 || c.dtype == PKV_BF16))
+    return fail(PKV_ERR_UNSUPPORTED, "group size %d > 16", G);
   const DecodePlan plan = plan_decode(c, num_seqs, num_q_heads, max_context_len, partition_size);
   const size_t need = plan.bytes;
   if (need > 0) {
@@ -266,7 +278,8 @@ pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, int32_t out_dtyp
   pkv::CacheDesc c;
   pkv_status st = check_cache(cache, &c);
   if (st) return st;
-  if (c.dtype == PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "prefill supports f16 and bf16");
+  if (c.dtype != PKV_F16 && c.dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "prefill supports f16 and bf16 caches");
   if (num_seqs < 0 || max_query_len < 0) return fail(PKV_ERR_INVALID, "negative size");
   if (num_seqs == 0 || max_query_len == 0) return ok();
   if (!out || !q || !query_start_loc || !context_lens || !block_tables)

@@ -13,6 +13,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -33,6 +34,12 @@ struct F16 {
 struct BF16 {
   using storage = uint16_t;
   static constexpr int kBytes = 2;
+};
+// 8-bit cache entries: OCP FP8 E4M3 codes (bias 7, 3 mantissa bits,
+// S.1111.111 NaN, no infinities, largest magnitude 448).
+struct FP8 {
+  using storage = uint8_t;
+  static constexpr int kBytes = 1;
 };
 
 // ---- scalar conversions ---------------------------------------------------
@@ -93,6 +100,42 @@ __device__ __forceinline__ void unpack16<BF16>(const u32x4 &c, float *out) {
   }
 }
 
+template <>
+__device__ __forceinline__ void unpack16<FP8>(const u32x4 &c, float *out) {
+  // 16 codes; v_cvt_pk_f32_fp8 turns the low or high byte pair of a word into
+  // two floats (exact: every E4M3 value is an fp32 value).
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[i], false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[i], true);
+    out[4 * i] = lo[0];
+    out[4 * i + 1] = lo[1];
+    out[4 * i + 2] = hi[0];
+    out[4 * i + 3] = hi[1];
+  }
+}
+
+// fp32 -> E4M3 code: nearest, ties to the even code; magnitudes of 448 and
+// beyond (infinities included) saturate to 448, NaN stays NaN.  Works on the
+// fp32 bit fields: normal results keep the top 3 of the 23 mantissa bits
+// with the dropped 20 rounded to nearest even (a carry out of the mantissa
+// steps the exponent field, which the code's layout makes one add);
+// results below 2^-6 sit on the subnormal grid of 2^-9.
+__device__ __forceinline__ uint32_t f32_to_fp8_bits(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;        // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;       // >= 448 (and inf): saturate
+  if (a < 0x3c800000u)                             // < 2^-6: multiples of 2^-9
+    return sign | (uint32_t)__builtin_rintf(__builtin_bit_cast(float, a) * 512.f);
+  const uint32_t e = (a >> 23) - 127 + 7;          // biased E4M3 exponent, 1..15
+  const uint32_t top = (a >> 20) & 7u;             // kept mantissa bits
+  const uint32_t rest = a & 0xfffffu;              // dropped mantissa bits
+  const uint32_t up = rest > 0x80000u || (rest == 0x80000u && (top & 1u));
+  return sign | (((e << 3) | top) + up);
+}
+
 // q.k over one 16-byte chunk, accumulated in fp32.  For 16-bit inputs each
 // pair product is exact in fp32 (v_dot2_f32_f16 / v_dot2_f32_bf16); q is the
 // matching chunk of the query in the same packed format.
@@ -130,7 +173,6 @@ __device__ __forceinline__ float dot16<BF16>(const u32x4 &k, const u32x4 &q) {
   return d;
 }
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Two floats -> packed bf16 pair (round to nearest even), one instruction.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {

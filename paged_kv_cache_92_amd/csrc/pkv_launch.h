@@ -22,8 +22,11 @@ struct CacheDesc {
   void *v;           // [num_blocks][H][D][B]
   int64_t num_blocks;
   int H, B, D;
-  int dtype;         // 0 f32, 1 f16, 2 bf16
-  int elt_bytes() const { return dtype == 0 ? 4 : 2; }
+  int dtype;         // pools: 0 f32, 1 f16, 2 bf16, 3 fp8 e4m3
+  int mdtype;        // key/value inputs, queries, outputs (== dtype unless fp8)
+  float k_scale, v_scale;  // fp8 cache: stored = x / scale, read = code * scale
+  int elt_bytes() const { return dtype == 0 ? 4 : dtype == 3 ? 1 : 2; }
+  bool fp8() const { return dtype == 3; }
 };
 
 struct DecodeArgs {

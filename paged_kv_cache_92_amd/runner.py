@@ -11,23 +11,28 @@ import torch
 from . import _binding as pkv
 from . import workloads as W
 
-TORCH_DTYPE = {W.F32: torch.float32, W.F16: torch.float16, W.BF16: torch.bfloat16}
-NAN_BITS = {W.F32: None, W.F16: 0x7E00, W.BF16: 0x7FC0}
+TORCH_DTYPE = {W.F32: torch.float32, W.F16: torch.float16, W.BF16: torch.bfloat16,
+               W.FP8: torch.float8_e4m3fn}
+NAN_BITS = {W.F32: None, W.F16: 0x7E00, W.BF16: 0x7FC0, W.FP8: 0x7F}
 
 
 def to_device(bits: np.ndarray, dtype: int, device="cuda") -> torch.Tensor:
     """Raw-bits numpy array -> device tensor of the cache dtype (same bits)."""
     if dtype == W.F32:
         return torch.from_numpy(np.ascontiguousarray(bits)).to(device)
+    if dtype == W.FP8:
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.uint8)).to(device).view(torch.float8_e4m3fn)
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device)
     return t.view(TORCH_DTYPE[dtype])
 
 
 def bits_of(t: torch.Tensor) -> np.ndarray:
-    """Device tensor -> raw-bits numpy array (float32 or uint16)."""
+    """Device tensor -> raw-bits numpy array (float32, uint16, or uint8 for 8-bit floats)."""
     t = t.detach().contiguous().cpu()
     if t.dtype == torch.float32:
         return t.numpy()
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
@@ -36,14 +41,19 @@ def values_of(t: torch.Tensor) -> np.ndarray:
 
 
 def new_cache(wl, device="cuda") -> pkv.PagedKVCache:
+    cd = wl.cache_dtype
     cache = pkv.PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim,
-                             TORCH_DTYPE[wl.dtype], device=device)
-    if wl.dtype == W.F32:
+                             TORCH_DTYPE[cd], device=device, model_dtype=TORCH_DTYPE[wl.dtype],
+                             k_scale=wl.k_scale, v_scale=wl.v_scale)
+    if cd == W.F32:
         cache.k_pool.fill_(float("nan"))
         cache.v_pool.fill_(float("nan"))
+    elif cd == W.FP8:
+        cache.k_pool.view(torch.uint8).fill_(NAN_BITS[cd])
+        cache.v_pool.view(torch.uint8).fill_(NAN_BITS[cd])
     else:
-        cache.k_pool.view(torch.int16).fill_(NAN_BITS[wl.dtype])
-        cache.v_pool.view(torch.int16).fill_(NAN_BITS[wl.dtype])
+        cache.k_pool.view(torch.int16).fill_(NAN_BITS[cd])
+        cache.v_pool.view(torch.int16).fill_(NAN_BITS[cd])
     return cache
 
 

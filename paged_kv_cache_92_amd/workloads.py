@@ -32,9 +32,10 @@ import numpy as np
 
 from .block_manager import BlockManager
 
-F32, F16, BF16 = 0, 1, 2
-DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
-_NAN_BITS = {F32: np.float32(np.nan), F16: np.uint16(0x7E00), BF16: np.uint16(0x7FC0)}
+F32, F16, BF16, FP8 = 0, 1, 2, 3      # FP8 (E4M3 codes) is a cache storage type only
+DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", FP8: "fp8_e4m3"}
+_NAN_BITS = {F32: np.float32(np.nan), F16: np.uint16(0x7E00), BF16: np.uint16(0x7FC0),
+             FP8: np.uint8(0x7F)}
 
 
 def round_to(x: np.ndarray, dtype: int) -> np.ndarray:
@@ -50,7 +51,7 @@ def round_to(x: np.ndarray, dtype: int) -> np.ndarray:
 
 
 def storage_dtype(dtype: int):
-    return np.float32 if dtype == F32 else np.uint16
+    return {F32: np.float32, F16: np.uint16, BF16: np.uint16, FP8: np.uint8}[dtype]
 
 
 @dataclass
@@ -85,6 +86,13 @@ class Workload:
     partition_size: int = 0
     max_context_len: int = 0
     info: dict = field(default_factory=dict)
+    kv_dtype: int = -1            # cache storage dtype (-1: ``dtype``; FP8 for an 8-bit cache)
+    k_scale: float = 1.0          # 8-bit cache: stored code = x / scale
+    v_scale: float = 1.0
+
+    @property
+    def cache_dtype(self) -> int:
+        return self.dtype if self.kv_dtype < 0 else self.kv_dtype
 
     @property
     def S(self) -> int:
@@ -96,15 +104,16 @@ class Workload:
 
     def empty_pools(self):
         nb, H, B, d = self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim
-        st = storage_dtype(self.dtype)
+        cd = self.cache_dtype
+        st = storage_dtype(cd)
         x = 64 // np.dtype(st).itemsize           # key rows in 64-byte pieces
-        k = np.full((nb, H, d // x, B, x), _NAN_BITS[self.dtype], dtype=st)
-        v = np.full((nb, H, d, B), _NAN_BITS[self.dtype], dtype=st)
+        k = np.full((nb, H, d // x, B, x), _NAN_BITS[cd], dtype=st)
+        v = np.full((nb, H, d, B), _NAN_BITS[cd], dtype=st)
         return k, v
 
     def kv_bytes(self) -> int:
         """Bytes of live cached K and V that one attention pass reads once per KV head."""
-        elt = 4 if self.dtype == F32 else 2
+        elt = {F32: 4, F16: 2, BF16: 2, FP8: 1}[self.cache_dtype]
         return int(self.context_lens.astype(np.int64).sum()) * 2 * self.num_kv_heads * self.head_dim * elt
 
 
@@ -127,7 +136,8 @@ def _poison_block(bm: BlockManager) -> int:
 
 
 def make_decode(name, seed, context_lens_fn, Hq, Hkv, d, B, dtype, max_context_len,
-                num_blocks=None, pool_factor=1.1, partition_size=0, placement="shuffled"):
+                num_blocks=None, pool_factor=1.1, partition_size=0, placement="shuffled",
+                kv_dtype=-1, k_scale=1.0, v_scale=1.0):
     """Decode workload: every sequence holds ctx[s]-1 history tokens and appends one.
 
     ``context_lens_fn(rng)`` draws the context lengths (post-append, so they
@@ -135,7 +145,9 @@ def make_decode(name, seed, context_lens_fn, Hq, Hkv, d, B, dtype, max_context_l
     ``placement``: "shuffled" hands out physical blocks in a seeded random
     order; "contiguous" in pool order, so each sequence's blocks are
     consecutive and in logical order (an identity-like block table).  The
-    values drawn are the same either way.
+    values drawn are the same either way.  ``kv_dtype=FP8`` makes the cache
+    8-bit (E4M3 codes of x / k_scale, x / v_scale); ``dtype`` stays the type of
+    the queries and of the key/value rows written.
     """
     rng = np.random.default_rng(seed)
     ctx = np.asarray(context_lens_fn(rng), dtype=np.int32)
@@ -173,7 +185,8 @@ def make_decode(name, seed, context_lens_fn, Hq, Hkv, d, B, dtype, max_context_l
     wl = Workload(name=name, mode="decode", dtype=dtype, num_blocks=nb, num_kv_heads=Hkv,
                   num_q_heads=Hq, head_dim=d, block_size=B, context_lens=ctx, block_tables=bt,
                   q=q, scale=_scale(d), partition_size=partition_size,
-                  max_context_len=int(max_context_len))
+                  max_context_len=int(max_context_len), kv_dtype=kv_dtype,
+                  k_scale=float(np.float32(k_scale)), v_scale=float(np.float32(v_scale)))
     wl.setup.append(Op("scatter", key=np.ascontiguousarray(keys[hist_idx]),
                        value=np.ascontiguousarray(values[hist_idx]),
                        slots=np.concatenate(hist_slots).astype(np.int64)))
@@ -315,6 +328,16 @@ def llama13b_decode_f16(S=64, lo=128, hi=2048, seed=2, partition_size=512, B=16,
                        lambda rng: rng.integers(lo, hi + 1, size=S), Hq=40, Hkv=40, d=128, B=B,
                        dtype=F16, max_context_len=hi, partition_size=partition_size,
                        placement=placement)
+
+
+def llama13b_decode_fp8(S=64, lo=128, hi=2048, seed=2, partition_size=512, B=16,
+                        k_scale=0.0135, v_scale=0.0135):
+    """The LLaMA-2-13B-shaped decode over an 8-bit (E4M3) cache: fp16 queries and inputs,
+    per-tensor scales about 6 sigma / 448 of the N(0, 1) values."""
+    return make_decode(f"llama13b_decode_fp8_S{S}", seed,
+                       lambda rng: rng.integers(lo, hi + 1, size=S), Hq=40, Hkv=40, d=128, B=B,
+                       dtype=F16, max_context_len=hi, partition_size=partition_size,
+                       kv_dtype=FP8, k_scale=k_scale, v_scale=v_scale)
 
 
 def long_context_split_f16(S=16, lo=2048, hi=4096, seed=3, partition_size=512):

@@ -18,18 +18,24 @@ def fill_pools(wl, include_step=True):
     ops = list(wl.setup) + ([wl.step_scatter] if include_step and wl.step_scatter else [])
     for op in ops:
         if op.kind == "scatter":
-            oracle.reshape_and_cache(k, v, wl.dtype, op.key, op.value, op.slots)
+            oracle.reshape_and_cache(k, v, wl.cache_dtype, op.key, op.value, op.slots,
+                                     in_dtype=wl.dtype, k_scale=wl.k_scale, v_scale=wl.v_scale)
         else:
-            oracle.copy_blocks(k, v, wl.dtype, op.pairs)
+            oracle.copy_blocks(k, v, wl.cache_dtype, op.pairs)
     return k, v
+
+
+def _kv(wl):
+    return dict(q_dtype=wl.dtype, k_scale=wl.k_scale, v_scale=wl.v_scale)
 
 
 def reference_output(wl, k, v):
     """fp64 oracle output of the workload's attention step over pools k, v."""
     if wl.mode == "decode":
-        return oracle.paged_decode(k, v, wl.dtype, wl.q, wl.block_tables, wl.context_lens, wl.scale)
-    return oracle.paged_prefill(k, v, wl.dtype, wl.q, wl.query_start_loc, wl.context_lens,
-                                wl.block_tables, wl.scale)
+        return oracle.paged_decode(k, v, wl.cache_dtype, wl.q, wl.block_tables, wl.context_lens,
+                                   wl.scale, **_kv(wl))
+    return oracle.paged_prefill(k, v, wl.cache_dtype, wl.q, wl.query_start_loc, wl.context_lens,
+                                wl.block_tables, wl.scale, **_kv(wl))
 
 
 def sampled_rows(wl, k, v, rows):
@@ -43,5 +49,5 @@ def sampled_rows(wl, k, v, rows):
         seq = np.searchsorted(qsl, rows, side="right") - 1
         qlen = qsl[seq + 1] - qsl[seq]
         pos = wl.context_lens[seq] - qlen + (rows - qsl[seq])
-    return oracle.paged_attention_rows(k, v, wl.dtype, wl.q[rows], wl.block_tables, wl.context_lens,
-                                       seq, pos, wl.scale)
+    return oracle.paged_attention_rows(k, v, wl.cache_dtype, wl.q[rows], wl.block_tables,
+                                       wl.context_lens, seq, pos, wl.scale, **_kv(wl))

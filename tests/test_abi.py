@@ -37,8 +37,9 @@ def test_library_exports_every_declared_symbol():
 
 def _desc(**kw):
     base = dict(k_pool=0x10000, v_pool=0x20000, num_blocks=8, num_kv_heads=2, block_size=16,
-                head_dim=64, dtype=1)
+                head_dim=64, dtype=1, k_scale=1.0, v_scale=1.0)
     base.update(kw)
+    base.setdefault("model_dtype", base["dtype"])
     return PkvCacheDesc(**base)
 
 
@@ -48,13 +49,18 @@ FAKE = ctypes.c_void_p(0x30000)   # never dereferenced: every call below fails v
 @pytest.mark.parametrize("kw,status", [
     (dict(k_pool=None), 1), (dict(block_size=8), 2), (dict(head_dim=96), 2), (dict(dtype=7), 1),
     (dict(num_blocks=0), 1), (dict(k_pool=0x10008), 1),
+    (dict(dtype=1, model_dtype=2), 1),                       # 16-bit cache: model dtype = dtype
+    (dict(dtype=3, model_dtype=3), 1), (dict(dtype=3, model_dtype=0), 1),   # 8-bit: f16/bf16 model
+    (dict(dtype=3, model_dtype=1, k_scale=0.0), 1), (dict(dtype=3, model_dtype=2, v_scale=-1.0), 1),
+    (dict(dtype=3, model_dtype=1, k_scale=float("inf")), 1), (dict(dtype=3, model_dtype=2), 0),
 ])
 def test_cache_descriptor_checks(kw, status):
     lib = pkv.lib()
     d = _desc(**kw)
-    st = lib.pkv_reshape_and_cache(ctypes.byref(d), FAKE, FAKE, FAKE, 4, None)
+    # num_tokens 0: the descriptor is validated, nothing is ever launched.
+    st = lib.pkv_reshape_and_cache(ctypes.byref(d), FAKE, FAKE, FAKE, 0, None)
     assert st == status
-    assert lib.pkv_last_error().decode()
+    assert bool(lib.pkv_last_error().decode()) == (status != 0)
 
 
 def _decode(d, out=FAKE, out_dtype=1, q=FAKE, Hq=2, bt=FAKE, mbps=4, ctx=FAKE, S=2, maxlen=64,

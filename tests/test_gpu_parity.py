@@ -21,25 +21,18 @@ pytestmark = pytest.mark.gpu
 
 
 def _pools_equal(cache, k_ref, v_ref, dtype):
-    kd = to_device(k_ref, dtype)
-    vd = to_device(v_ref, dtype)
-    if dtype == W.F32:
-        same_k = torch.equal(cache.k_pool.view(torch.int32), kd.view(torch.int32))
-        same_v = torch.equal(cache.v_pool.view(torch.int32), vd.view(torch.int32))
-    else:
-        same_k = torch.equal(cache.k_pool.view(torch.int16), kd.view(torch.int16))
-        same_v = torch.equal(cache.v_pool.view(torch.int16), vd.view(torch.int16))
-    assert same_k, "K pool differs from the oracle's"
-    assert same_v, "V pool differs from the oracle's"
+    for name, dev, ref in (("K", cache.k_pool, k_ref), ("V", cache.v_pool, v_ref)):
+        got = bits_of(dev)
+        assert np.array_equal(got.view(np.uint8), np.ascontiguousarray(ref).view(np.uint8)), \
+            f"{name} pool differs from the oracle's"
 
 
-def _check_gather(cache, wl, dw):
+def _check_gather(cache, wl, dw, k_ref, v_ref):
     ctx = wl.context_lens
     cu = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)
     k, v = pkv.gather_kv(cache, dw.block_tables, dw.context_lens, torch.from_numpy(cu).cuda(),
                          int(cu[-1]), wl.max_context_len)
-    ref_k = np.concatenate(wl.seq_tokens_key)
-    ref_v = np.concatenate(wl.seq_tokens_value)
+    ref_k, ref_v = oracle.gather_kv(k_ref, v_ref, wl.cache_dtype, wl.block_tables, wl.context_lens)
     assert np.array_equal(bits_of(k).view(np.uint8), ref_k.view(np.uint8)), "gathered K differs"
     assert np.array_equal(bits_of(v).view(np.uint8), ref_v.view(np.uint8)), "gathered V differs"
 
@@ -53,8 +46,8 @@ def _full_check(wl, partition_size=None):
     out = dw.run(cache, partition_size=partition_size)
     o32 = dw.attend(cache, partition_size=partition_size, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    _pools_equal(cache, k_ref, v_ref, wl.dtype)
-    _check_gather(cache, wl, dw)
+    _pools_equal(cache, k_ref, v_ref, wl.cache_dtype)
+    _check_gather(cache, wl, dw, k_ref, v_ref)
     worst = assert_close(values_of(o32), ref, wl.dtype, wl.name)
     assert_rounded(out, o32, wl.dtype, wl.name)
     return worst, out, cache, dw
@@ -208,7 +201,7 @@ def test_negative_slots_are_skipped_and_copy_blocks_copies():
     dw.fill(cache)
     dw.apply(cache, dw.step)
     torch.cuda.synchronize()
-    _pools_equal(cache, k_ref, v_ref, wl.dtype)
+    _pools_equal(cache, k_ref, v_ref, wl.cache_dtype)
 
 
 # ----------------------------------------------------------------------------
@@ -322,7 +315,7 @@ def _sampled_check(wl, rows, partition_size=None):
     out = dw.run(cache, partition_size=partition_size)
     o32 = dw.attend(cache, partition_size=partition_size, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    _pools_equal(cache, k_ref, v_ref, wl.dtype)
+    _pools_equal(cache, k_ref, v_ref, wl.cache_dtype)
     ref = sampled_rows(wl, k_ref, v_ref, rows)
     got = values_of(o32)
     worst = assert_close(got[rows], ref, wl.dtype, wl.name)
@@ -446,3 +439,68 @@ def test_pool_beyond_4_gib_addresses_correctly(dtype, G):
     torch.cuda.synchronize()
     assert torch.equal(big.k_pool[0].view(torch.int16), big.k_pool[NB - 1].view(torch.int16))
     assert torch.equal(big.v_pool[0].view(torch.int16), big.v_pool[NB - 1].view(torch.int16))
+
+
+# ----------------------------------------------------------------------------
+# 8-bit (E4M3) cache with per-tensor scales
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16], ids=["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B", [16, 32])
+@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("part", [0, 64, -1], ids=["whole", "p64", "auto"])
+def test_fp8_cache_decode_variants(dtype, d, B, G, part):
+    # Scatter codes bit-exact against the oracle's quantisation, gather
+    # bit-exact, attention over the dequantised cache within the tolerance.
+    wl = W.make_decode(f"fp8_{dtype}_{d}_{B}_{G}_{part}", 200 + d + B + G, lambda rng: RAGGED,
+                       Hq=2 * G, Hkv=2, d=d, B=B, dtype=dtype, max_context_len=320,
+                       partition_size=part, kv_dtype=W.FP8, k_scale=0.0123, v_scale=0.0317)
+    _full_check(wl)
+
+
+def test_fp8_cache_reads_every_code_exactly():
+    # With v_scale 1 and the value row of a dominant key holding every finite
+    # E4M3 value (negative zero aside: a sum cannot return it), the fp32
+    # output must be exactly those values: this pins the kernel's code ->
+    # value conversion and its byte order.
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF, 0x80)] + [0x38] * 3, np.uint8)
+    vals = np.array([oracle.fp8_to_double(int(c)) for c in codes], np.float32)   # 256 = 2 heads x 128
+    lens = [5, 40]
+    wl = W.make_decode("fp8codes", 21, lambda rng: lens, Hq=2, Hkv=2, d=128, B=16, dtype=W.F16,
+                       max_context_len=48, kv_dtype=W.FP8, k_scale=1.0, v_scale=1.0)
+    one = W.round_to(np.ones(1, np.float32), W.F16)[0]
+    wl.q[:] = one
+    hist, step = wl.setup[0], wl.step_scatter
+    hist.key[:] = 0
+    step.key[:] = 0
+    row = W.round_to(vals.reshape(2, 128), W.F16)          # exact: E4M3 values are fp16 values
+    cu = np.concatenate([[0], np.cumsum(np.array(lens) - 1)])
+    picks = [2, 39]
+    for s, j in enumerate(picks):
+        tgt = step if j == lens[s] - 1 else hist
+        i = s if tgt is step else cu[s] + j
+        tgt.key[i] = W.round_to(np.full((2, 128), 448.0, np.float32), W.F16)
+        tgt.value[i] = row
+    dw = DeviceWorkload(wl)
+    cache = new_cache(wl)
+    dw.run(cache)
+    o32 = bits_of(dw.attend(cache, out_dtype=torch.float32))
+    for s in range(len(lens)):
+        assert np.array_equal(o32[s].reshape(-1).view(np.uint32), vals.view(np.uint32)), s
+
+
+def test_fp8_cache_llama13b_full():
+    wl = W.llama13b_decode_fp8()
+    worst, *_ = _sampled_check(wl, _decode_rows(wl, 8, 5))
+    print(f"13B fp8-cache decode: worst err/bound {worst:.3f}")
+
+
+def test_fp8_cache_prefill_is_unsupported():
+    wl = W.make_decode("fp8pf", 3, lambda rng: [20], Hq=2, Hkv=2, d=64, B=16, dtype=W.BF16,
+                       max_context_len=32, kv_dtype=W.FP8, k_scale=0.1, v_scale=0.1)
+    dw = DeviceWorkload(wl)
+    cache = new_cache(wl)
+    qsl = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    with pytest.raises(pkv.PkvError, match="UNSUPPORTED"):
+        pkv.paged_prefill(cache, dw.q, qsl, dw.context_lens, dw.block_tables, 1, 32)
