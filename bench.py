@@ -37,6 +37,10 @@ def make_workload(name, partition, block_size=16, placement="shuffled"):
         desc = "llama2-13b-shaped single-layer paged decode, fp16 KV"
         if block_size != 16 or placement != "shuffled":
             desc += f" (block {block_size}, {placement} blocks)"
+    elif name == "llama13b_fp8":
+        wl = W.llama13b_decode_fp8()
+        desc = ("llama2-13b-shaped single-layer paged decode, fp8 e4m3 KV cache "
+                "(per-tensor scales, fp16 queries)")
     elif name == "long_split":
         wl = W.long_context_split_f16()
         desc = "long-context split-KV paged decode, fp16 KV"
@@ -108,17 +112,20 @@ def cpu_baseline(wl, budget_s):
     k, v = wl.empty_pools()
     for op in wl.setup + [wl.step_scatter]:
         if op.kind == "scatter":
-            oracle.reshape_and_cache(k, v, wl.dtype, op.key, op.value, op.slots)
+            oracle.reshape_and_cache(k, v, wl.cache_dtype, op.key, op.value, op.slots,
+                                     in_dtype=wl.dtype, k_scale=wl.k_scale, v_scale=wl.v_scale)
         else:
-            oracle.copy_blocks(k, v, wl.dtype, op.pairs)
-    elt = 4 if wl.dtype == 0 else 2
+            oracle.copy_blocks(k, v, wl.cache_dtype, op.pairs)
+    elt = {0: 4, 1: 2, 2: 2, 3: 1}[wl.cache_dtype]
+    kv = dict(q_dtype=wl.dtype, k_scale=wl.k_scale, v_scale=wl.v_scale)
     t0 = time.perf_counter()
     n = 0
     kv_bytes = 0
     if wl.mode == "decode":
         while n < wl.S and (time.perf_counter() - t0) < budget_s:
-            oracle.paged_attention_rows(k, v, wl.dtype, wl.q[n:n + 1], wl.block_tables,
-                                        wl.context_lens, [n], [int(wl.context_lens[n]) - 1], wl.scale)
+            oracle.paged_attention_rows(k, v, wl.cache_dtype, wl.q[n:n + 1], wl.block_tables,
+                                        wl.context_lens, [n], [int(wl.context_lens[n]) - 1], wl.scale,
+                                        **kv)
             kv_bytes += int(wl.context_lens[n]) * 2 * wl.num_kv_heads * wl.head_dim * elt
             n += 1
         el = time.perf_counter() - t0
@@ -132,8 +139,8 @@ def cpu_baseline(wl, budget_s):
     while n < qsl[-1] and (time.perf_counter() - t0) < budget_s:
         s = int(np.searchsorted(qsl, n, side="right") - 1)
         pos = int(wl.context_lens[s] - (qsl[s + 1] - qsl[s]) + (n - qsl[s]))
-        oracle.paged_attention_rows(k, v, wl.dtype, wl.q[n:n + 1], wl.block_tables, wl.context_lens,
-                                    [s], [pos], wl.scale)
+        oracle.paged_attention_rows(k, v, wl.cache_dtype, wl.q[n:n + 1], wl.block_tables, wl.context_lens,
+                                    [s], [pos], wl.scale, **kv)
         flops += (pos + 1) * wl.num_q_heads * wl.head_dim * 4
         rows.append(n)
         n += 1
@@ -149,7 +156,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="llama13b",
-                    choices=["llama13b", "long_split", "gqa16", "gqa32", "prefill", "tiny"])
+                    choices=["llama13b", "llama13b_fp8", "long_split", "gqa16", "gqa32", "prefill",
+                             "tiny"])
     ap.add_argument("--partition", type=int, default=None,
                     help="split-KV partition size in tokens (default: the workload's)")
     ap.add_argument("--block-size", type=int, default=16, choices=[16, 32],
@@ -241,7 +249,7 @@ def main():
         f"{attn_avg * 1e3:.1f} us avg (median {np.median(attn_ms) * 1e3:.1f}, "
         f"min {np.min(attn_ms) * 1e3:.1f})")
 
-    dt = {0: "f32", 1: "f16", 2: "bf16"}[wl.dtype]
+    dt = {0: "f32", 1: "f16", 2: "bf16", 3: "fp8_e4m3"}[wl.cache_dtype]
     kv = wl.kv_bytes()
     flops = attention_flops(wl)
     res = {
