@@ -186,10 +186,11 @@ size_t pkv_decode_workspace_bytes(const pkv_cache *cache, int32_t num_seqs, int3
  *   workspace         device scratch of >= pkv_decode_workspace_bytes(...)
  *                     bytes, 16-byte aligned; may be NULL when that is 0
  *
- * Grouped heads (num_q_heads > num_kv_heads) over an f16/bf16 cache run on
- * the matrix cores with the group's queries stacked into one tile (group
- * size <= 16); other cases, 8-bit caches included, run the wavefront
- * dot-product kernel (which reads a KV head once per query head).
+ * Grouped heads (num_q_heads > num_kv_heads) over an f16/bf16/8-bit cache
+ * run on the matrix cores with the group's queries stacked into one tile
+ * (group size <= 16; 8-bit codes are widened to the model dtype as they
+ * arrive); fp32 caches and single heads run the wavefront dot-product
+ * kernel.
  */
 pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype, const void *q,
                             int32_t num_q_heads,

@@ -380,7 +380,7 @@ void launch_reduce_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream
   const dim3 grid((unsigned)a.Hq, (unsigned)a.S);
   const int mt = a.max_blocks_per_seq * c.B;
   const int G = a.Hq / c.H;
-  const bool mfma = G > 1 && (c.dtype == 1 || c.dtype == 2);
+  const bool mfma = G > 1 && c.dtype != 0;
   const int HU = mfma ? c.H : a.Hq, GU = mfma ? G : 1;
   auto go = [&](auto kern_part, auto kern_flat, int threads) {
     if (a.flat)

@@ -76,17 +76,29 @@ __device__ __forceinline__ int token_of_row(int sb, int i) {
   else return 16 * sb + i;
 }
 
+// E4M3 codes -> the matrix-core input type, exactly (every E4M3 value is an
+// fp16 and a bf16 value): 4 codes of word w become two packed pairs.
+template <typename E>
+__device__ __forceinline__ u32x2 widen4(uint32_t w) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  return u32x2{Mfma<E>::pack2(lo[0], lo[1]), Mfma<E>::pack2(hi[0], hi[1])};
+}
+
 // One work item: blocks [b0, b1) of sequence s for the G query heads of KV
 // head hkv; head h's merged result goes to the output or to workspace
 // partial row dest.base + h * dest.stride.  `lds_dyn` holds the cross-wave
-// merge buffers.
-template <typename E, int D, int BS>
+// merge buffers.  E is the query / matrix-core type; KV the cache element
+// (E itself, or FP8: codes are widened to E right after the loads, the key
+// scale is folded into scale_log2 and v_scale multiplies the merged sums).
+template <typename E, typename KV, int D, int BS>
 __device__ __forceinline__ void mfma_item(
     float *lds_dyn, int s, int hkv, int b0, int b1, Dest dest, void *__restrict__ out,
-    int out_f32, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kpool,
-    const uint16_t *__restrict__ vpool, const int32_t *__restrict__ block_tables,
+    int out_f32, const uint16_t *__restrict__ q, const typename KV::storage *__restrict__ kpool,
+    const typename KV::storage *__restrict__ vpool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, int64_t num_blocks, int Hkv, int G, int mbps,
-    float scale_log2, float *__restrict__ ws_ml, float *__restrict__ ws_acc) {
+    float scale_log2, float v_scale, float *__restrict__ ws_ml, float *__restrict__ ws_acc) {
+  constexpr bool kFP8 = KV::kBytes == 1;
   constexpr int KS = D / 32;    // k-steps of the score product
   constexpr int NT = D / 16;    // 16-dimension tiles of the output
   constexpr int SUB = BS / 16;  // 16-token sub-tiles per block
@@ -114,15 +126,18 @@ __device__ __forceinline__ void mfma_item(
   float *lds_acc = lds_dyn + 2 * kWaves * 16;
   auto acc_at = [&](int wv, int h, int e) -> float & { return lds_acc[(wv * G + h) * (D + 1) + e]; };
 
-  // Q^T operand: head n16 of the group (zero past G), dimensions 32*ks + 8*g4 .. +8.
+  // Q^T operand: head n16 of the group (zero past G); k-step ks covers
+  // dimensions 32*ks + 8*g4 .. +8 (16-bit cache) or, over an 8-bit cache
+  // whose loads bring 16 dimensions of a 64-dimension piece, 64*(ks/2) +
+  // 16*g4 + 8*(ks%2) .. +8: the contraction order only has to match the
+  // keys'.
+  auto qdim = [&](int ks) { return kFP8 ? 64 * (ks >> 1) + 16 * g4 + 8 * (ks & 1) : 32 * ks + 8 * g4; };
   u32x4 qb[KS];
   {
     const bool valid = n16 < G;
     const uint16_t *qrow = q + ((size_t)s * Hq + hkv * G + (valid ? n16 : 0)) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qb[ks] = valid ? load16(qrow + 32 * ks + 8 * g4) : u32x4{0, 0, 0, 0};
-    }
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = valid ? load16(qrow + qdim(ks)) : u32x4{0, 0, 0, 0};
   }
 
   float m = -INFINITY;  // running max of head n16 (log2 domain)
@@ -136,27 +151,54 @@ __device__ __forceinline__ void mfma_item(
     const int lb = blk0 + b;
     const int64_t phys = uniform(bt[lb]);
     if (phys < 0 || phys >= num_blocks) continue;
-    const uint16_t *kt = kpool + ((size_t)phys * Hkv + hkv) * (BS * D);
-    const uint16_t *vt = vpool + ((size_t)phys * Hkv + hkv) * (D * BS);
+    const typename KV::storage *kt = kpool + ((size_t)phys * Hkv + hkv) * (BS * D);
+    const typename KV::storage *vt = vpool + ((size_t)phys * Hkv + hkv) * (D * BS);
     u32x4 ka[SUB][KS];
+    if constexpr (kFP8) {
+      // One 16-byte load = 16 dimensions (64-byte piece c, quarter g4) of a
+      // token: k-steps 2c and 2c+1.
 #pragma unroll
-    for (int sb = 0; sb < SUB; ++sb)
+      for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        ka[sb][ks] = load16_stream(kt + (ks * BS + token_of_row<BS>(sb, n16)) * 32 + 8 * g4);
+        for (int c = 0; c < KS / 2; ++c) {
+          const u32x4 raw = load16_stream(kt + (c * BS + token_of_row<BS>(sb, n16)) * 64 + 16 * g4);
+          const u32x2 a0 = widen4<E>(raw[0]), a1 = widen4<E>(raw[1]);
+          const u32x2 a2 = widen4<E>(raw[2]), a3 = widen4<E>(raw[3]);
+          ka[sb][2 * c] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+          ka[sb][2 * c + 1] = u32x4{a2[0], a2[1], a3[0], a3[1]};
+        }
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < SUB; ++sb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          ka[sb][ks] = load16_stream(kt + (ks * BS + token_of_row<BS>(sb, n16)) * 32 + 8 * g4);
+    }
     // V^T operand: dimension row 16*nt + n16; tokens 8*g4 .. +8 (wide) or
     // 16*sb + 4*g4 .. +4 of sub-tile sb.
     u32x4 vw[kWide ? NT : 1];
     u32x2 va[kWide ? 1 : SUB][kWide ? 1 : NT];
     if constexpr (kWide) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) vw[nt] = load16_stream(vt + (16 * nt + n16) * BS + 8 * g4);
+      for (int nt = 0; nt < NT; ++nt) {
+        if constexpr (kFP8) {
+          const u32x2 raw = load8_stream(vt + (16 * nt + n16) * BS + 8 * g4);
+          const u32x2 lo = widen4<E>(raw[0]), hi = widen4<E>(raw[1]);
+          vw[nt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+          vw[nt] = load16_stream(vt + (16 * nt + n16) * BS + 8 * g4);
+        }
+      }
     } else {
 #pragma unroll
       for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          va[sb][nt] = load8_stream(vt + (16 * nt + n16) * BS + 16 * sb + 4 * g4);
+        for (int nt = 0; nt < NT; ++nt) {
+          if constexpr (kFP8)
+            va[sb][nt] = widen4<E>(load4_stream(vt + (16 * nt + n16) * BS + 16 * sb + 4 * g4));
+          else
+            va[sb][nt] = load8_stream(vt + (16 * nt + n16) * BS + 16 * sb + 4 * g4);
+        }
     }
 
     const int tbase = lb * BS;
@@ -278,6 +320,7 @@ __device__ __forceinline__ void mfma_item(
       num = fmaf(f, acc_at(k, h, e), num);
       den = fmaf(f, lds_l[k * 16 + h], den);
     }
+    if constexpr (kFP8) num *= v_scale;
     const int hq = hkv * G + h;
     if (dest.base < 0) {
       store_out<E>(out, ((size_t)s * Hq + hq) * D + e, num / den, out_f32);
@@ -297,92 +340,105 @@ __device__ __forceinline__ void mfma_item(
 #ifndef PKV_MFMA_MIN_WAVES
 #define PKV_MFMA_MIN_WAVES 4
 #endif
-template <typename E, int D, int BS, int SCHED>
-__global__ __launch_bounds__(256, PKV_MFMA_MIN_WAVES) void decode_mfma_kernel(
+#ifndef PKV_MFMA_MIN_WAVES_FP8
+#define PKV_MFMA_MIN_WAVES_FP8 3
+#endif
+template <typename E, typename KV, int D, int BS, int SCHED>
+__global__ __launch_bounds__(256, KV::kBytes == 1 ? PKV_MFMA_MIN_WAVES_FP8 : PKV_MFMA_MIN_WAVES) void decode_mfma_kernel(
     void *__restrict__ out, int out_f32, const uint16_t *__restrict__ q,
-    const uint16_t *__restrict__ kpool, const uint16_t *__restrict__ vpool,
+    const typename KV::storage *__restrict__ kpool, const typename KV::storage *__restrict__ vpool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    int64_t num_blocks, int Hkv, int G, int S, int mbps, float scale_log2, int part_tokens,
-    int nparts, float *__restrict__ ws_ml, float *__restrict__ ws_acc, int *__restrict__ ws_hdr) {
+    int64_t num_blocks, int Hkv, int G, int S, int mbps, float scale_log2, float v_scale,
+    int part_tokens, int nparts, float *__restrict__ ws_ml, float *__restrict__ ws_acc,
+    int *__restrict__ ws_hdr) {
   extern __shared__ __attribute__((aligned(16))) int dyn[];
   __shared__ int scan[16];
   int *plan = dyn;
   float *merge = (float *)(dyn + (SCHED == kSchedGrid ? 0 : ((S + 1 + 3) & ~3)));
   run_schedule<SCHED>(
       [&](int s, int hkv, int b0, int b1, Dest dest) {
-        mfma_item<E, D, BS>(merge, s, hkv, b0, b1, dest, out, out_f32, q, kpool, vpool,
-                            block_tables, context_lens, num_blocks, Hkv, G, mbps, scale_log2,
-                            ws_ml, ws_acc);
+        mfma_item<E, KV, D, BS>(merge, s, hkv, b0, b1, dest, out, out_f32, q, kpool, vpool,
+                                block_tables, context_lens, num_blocks, Hkv, G, mbps, scale_log2,
+                                v_scale, ws_ml, ws_acc);
       },
       plan, scan, context_lens, S, mbps * BS, BS, Hkv, G, part_tokens, nparts, ws_hdr);
 }
 
-template <typename E, int D, int BS>
+template <int D>
 size_t merge_bytes(int G) {
   return sizeof(float) * (2 * kWaves * 16 + (size_t)kWaves * G * (D + 1));
 }
 
-template <typename E, int D, int BS>
+template <typename E, typename KV, int D, int BS>
 void launch_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
+  using T = typename KV::storage;
   const int G = a.Hq / c.H;
-  const size_t merge = merge_bytes<E, D, BS>(G);
+  const size_t merge = merge_bytes<D>(G);
   const size_t plan = sizeof(int) * (size_t)((a.S + 1 + 3) & ~3);
-  const float sl = a.scale * kLog2e;
+  const float sl = a.scale * kLog2e * c.k_scale;  // k_scale is 1 unless the cache is 8-bit
   auto go = [&](auto kern, dim3 grid, size_t dyn) {
     hipLaunchKernelGGL(kern, grid, dim3(256), dyn, stream, a.out, (int)a.out_f32,
-                       (const uint16_t *)a.q, (const uint16_t *)c.k, (const uint16_t *)c.v,
-                       a.block_tables, a.context_lens, c.num_blocks, c.H, G, a.S,
-                       a.max_blocks_per_seq, sl, a.partition_tokens, a.num_partitions, a.ws_ml,
-                       a.ws_acc, a.ws_hdr);
+                       (const uint16_t *)a.q, (const T *)c.k, (const T *)c.v, a.block_tables,
+                       a.context_lens, c.num_blocks, c.H, G, a.S, a.max_blocks_per_seq, sl,
+                       c.v_scale, a.partition_tokens, a.num_partitions, a.ws_ml, a.ws_acc,
+                       a.ws_hdr);
   };
   // Schedules as for the wavefront kernel.
 #ifndef PKV_GRID_FACTOR
 #define PKV_GRID_FACTOR 4
 #endif
   if (a.flat) {
-    go(decode_mfma_kernel<E, D, BS, kSchedFlat>, dim3(a.flat_grid), plan + merge);
+    go(decode_mfma_kernel<E, KV, D, BS, kSchedFlat>, dim3(a.flat_grid), plan + merge);
   } else if (a.num_partitions > 1 && a.S <= kPlanMaxSeqs) {
-    auto kern = decode_mfma_kernel<E, D, BS, kSchedPlan>;
+    auto kern = decode_mfma_kernel<E, KV, D, BS, kSchedPlan>;
     const int64_t cells = (int64_t)a.S * a.num_partitions * c.H;
     const int grid = (int)std::min<int64_t>(cells, PKV_GRID_FACTOR * (int64_t)resident_workgroups((const void *)kern, 256, plan + merge));
     go(kern, dim3(grid), plan + merge);
   } else {
-    go(decode_mfma_kernel<E, D, BS, kSchedGrid>,
+    go(decode_mfma_kernel<E, KV, D, BS, kSchedGrid>,
        dim3((unsigned)a.num_partitions, (unsigned)c.H, (unsigned)a.S), merge);
   }
 }
 
-template <typename E>
+template <typename E, typename KV = E>
 void launch_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
-  if (c.D == 64 && c.B == 16) launch_t<E, 64, 16>(c, a, stream);
-  else if (c.D == 64 && c.B == 32) launch_t<E, 64, 32>(c, a, stream);
-  else if (c.D == 128 && c.B == 16) launch_t<E, 128, 16>(c, a, stream);
-  else launch_t<E, 128, 32>(c, a, stream);
+  if (c.D == 64 && c.B == 16) launch_t<E, KV, 64, 16>(c, a, stream);
+  else if (c.D == 64 && c.B == 32) launch_t<E, KV, 64, 32>(c, a, stream);
+  else if (c.D == 128 && c.B == 16) launch_t<E, KV, 128, 16>(c, a, stream);
+  else launch_t<E, KV, 128, 32>(c, a, stream);
 }
 
-template <typename E, int D, int BS>
+template <typename E, typename KV, int D, int BS>
 int flat_grid_t(int G, int S) {
-  const size_t dyn = sizeof(int) * (size_t)((S + 1 + 3) & ~3) + merge_bytes<E, D, BS>(G);
-  return resident_workgroups((const void *)decode_mfma_kernel<E, D, BS, kSchedFlat>, 256, dyn);
+  const size_t dyn = sizeof(int) * (size_t)((S + 1 + 3) & ~3) + merge_bytes<D>(G);
+  return resident_workgroups((const void *)decode_mfma_kernel<E, KV, D, BS, kSchedFlat>, 256, dyn);
 }
 
-template <typename E>
+template <typename E, typename KV = E>
 int flat_grid_e(const CacheDesc &c, int G, int S) {
-  if (c.D == 64 && c.B == 16) return flat_grid_t<E, 64, 16>(G, S);
-  if (c.D == 64 && c.B == 32) return flat_grid_t<E, 64, 32>(G, S);
-  if (c.D == 128 && c.B == 16) return flat_grid_t<E, 128, 16>(G, S);
-  return flat_grid_t<E, 128, 32>(G, S);
+  if (c.D == 64 && c.B == 16) return flat_grid_t<E, KV, 64, 16>(G, S);
+  if (c.D == 64 && c.B == 32) return flat_grid_t<E, KV, 64, 32>(G, S);
+  if (c.D == 128 && c.B == 16) return flat_grid_t<E, KV, 128, 16>(G, S);
+  return flat_grid_t<E, KV, 128, 32>(G, S);
 }
 
 }  // namespace
 
+// Over an 8-bit cache the matrix cores run in the model dtype.
 hipError_t launch_decode_mfma(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
-  if (c.dtype == 1) launch_e<F16>(c, a, stream);
-  else launch_e<BF16>(c, a, stream);
+  if (c.fp8()) {
+    if (c.mdtype == 1) launch_e<F16, FP8>(c, a, stream);
+    else launch_e<BF16, FP8>(c, a, stream);
+  } else if (c.dtype == 1) {
+    launch_e<F16>(c, a, stream);
+  } else {
+    launch_e<BF16>(c, a, stream);
+  }
   return hipGetLastError();
 }
 
 int decode_mfma_flat_grid(const CacheDesc &c, int G, int S) {
+  if (c.fp8()) return c.mdtype == 1 ? flat_grid_e<F16, FP8>(c, G, S) : flat_grid_e<BF16, FP8>(c, G, S);
   return c.dtype == 1 ? flat_grid_e<F16>(c, G, S) : flat_grid_e<BF16>(c, G, S);
 }
 

@@ -106,7 +106,7 @@ DecodePlan plan_decode(const pkv::CacheDesc &c, int S, int Hq, int max_context_l
                        int partition_size) {
   DecodePlan d;
   const int G = Hq / c.H;
-  d.mfma = G > 1 && (c.dtype == PKV_F16 || c.dtype == PKV_BF16);
+  d.mfma = G > 1 && c.dtype != PKV_F32;
   if (partition_size == PKV_PARTITION_AUTO && S <= pkv::kPlanMaxSeqs) {
     d.flat = true;
     d.flat_grid = d.mfma ? pkv::decode_mfma_flat_grid(c, G, S) : pkv::decode_valu_flat_grid(c, S);
@@ -228,8 +228,7 @@ pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype
                 "partition_size %d must be PKV_PARTITION_AUTO, 0 or a positive multiple of block_size %d",
                 partition_size, c.B);
   const int G = num_q_heads / c.H;
-  if (G > 16 && (c.dtype == PKV_F16 || c.dtype == PKV_BF16))
-    return fail(PKV_ERR_UNSUPPORTED, "group size %d > 16", G);
+  if (G > 16 && c.dtype != PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "group size %d > 16", G);
   const DecodePlan plan = plan_decode(c, num_seqs, num_q_heads, max_context_len, partition_size);
   const size_t need = plan.bytes;
   if (need > 0) {

@@ -287,5 +287,8 @@ __device__ __forceinline__ u32x4 load16_stream(const void *p) {
 __device__ __forceinline__ u32x2 load8_stream(const void *p) {
   return __builtin_nontemporal_load((const u32x2 *)p);
 }
+__device__ __forceinline__ uint32_t load4_stream(const void *p) {
+  return __builtin_nontemporal_load((const uint32_t *)p);
+}
 
 }  // namespace pkv
