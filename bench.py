@@ -50,12 +50,16 @@ def make_workload(name, partition, block_size=16, placement="shuffled"):
     elif name == "prefill":
         wl = W.chunked_prefill_bf16()
         desc = "chunked causal prefill over paged cache with shared prefixes, bf16"
+    elif name == "mixed":
+        wl = W.mixed_step_f16()
+        desc = ("llama2-13b-shaped step batching 64 decode rows with two 512-row prefill chunks "
+                "in one call, fp16")
     elif name == "tiny":
         wl = W.tiny_decode_f32()
         desc = "tiny paged decode, fp32"
     else:
         raise SystemExit(f"unknown config {name}")
-    if partition is not None and wl.mode == "decode":
+    if partition is not None and wl.mode in ("decode", "mixed"):
         wl.partition_size = partition
     return wl, desc
 
@@ -145,6 +149,10 @@ def cpu_baseline(wl, budget_s):
         rows.append(n)
         n += 1
     el = time.perf_counter() - t0
+    if wl.mode == "mixed":
+        return {"value": round(n / el, 3), "unit": "rows/s", "cores": 1, "kind": "oracle",
+                "sample": f"first {n} query rows of {int(qsl[-1])} (decode rows first, all "
+                          f"{wl.num_q_heads} heads), {el:.1f} s wall, 1 thread"}
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} query rows of {int(qsl[-1])} (all {wl.num_q_heads} heads), "
                       f"{el:.1f} s wall, 1 thread"}
@@ -157,7 +165,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="llama13b",
                     choices=["llama13b", "llama13b_fp8", "long_split", "gqa16", "gqa32", "prefill",
-                             "tiny"])
+                             "mixed", "tiny"])
     ap.add_argument("--partition", type=int, default=None,
                     help="split-KV partition size in tokens (default: the workload's)")
     ap.add_argument("--block-size", type=int, default=16, choices=[16, 32],
@@ -220,8 +228,9 @@ def main():
     dw0 = copies[0][0]
     out = torch.empty_like(dw0.q)
     ws = None
-    if wl.mode == "decode":
-        need = pkv.decode_workspace_bytes(copies[0][1], wl.S, wl.num_q_heads, wl.max_context_len,
+    if wl.mode in ("decode", "mixed"):
+        nd = wl.S if wl.mode == "decode" else int(wl.info["num_decode_seqs"])
+        need = pkv.decode_workspace_bytes(copies[0][1], nd, wl.num_q_heads, wl.max_context_len,
                                           wl.partition_size)
         if need:
             ws = torch.empty(need, dtype=torch.uint8, device="cuda")
@@ -257,6 +266,24 @@ def main():
         f"{attn_avg * 1e3:.1f} us avg (median {np.median(attn_ms) * 1e3:.1f}, "
         f"min {np.min(attn_ms) * 1e3:.1f})")
 
+    ways = {}
+    if wl.mode == "mixed":
+        # The same step served other ways, attention only, same alternation.
+        for how in ("sequential", "unified", "decode", "prefill"):
+            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(args.steps)]
+            for i in range(args.warmup + args.steps):
+                dw, cache = copies[i % 2]
+                j = i - args.warmup
+                if j >= 0:
+                    pairs[j][0].record()
+                dw.attend_split(cache, how, out, workspace=ws)
+                if j >= 0:
+                    pairs[j][1].record()
+            torch.cuda.synchronize()
+            ways[how] = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+            log(f"[bench] {how}: {ways[how] * 1e3:.1f} us avg")
+
     dt = {0: "f32", 1: "f16", 2: "bf16", 3: "fp8_e4m3"}[wl.cache_dtype]
     kv = wl.kv_bytes()
     flops = attention_flops(wl)
@@ -281,6 +308,41 @@ def main():
                          "algorithmic_bytes_per_launch": kv,
                          "avg_launch_us": round(attn_avg * 1e3, 2)},
         })
+    elif wl.mode == "mixed":
+        nd = int(wl.info["num_decode_seqs"])
+        rows = int(wl.query_start_loc[-1])
+        elt = {0: 4, 1: 2, 2: 2, 3: 1}[wl.cache_dtype]
+        dec_bytes = int(wl.context_lens[:nd].astype(np.int64).sum()) * 2 * wl.num_kv_heads * \
+            wl.head_dim * elt
+        pre_flops = attention_flops(wl) - float(wl.context_lens[:nd].astype(np.int64).sum()) * \
+            wl.num_q_heads * wl.head_dim * 4
+        # Lower bound of the step: decode KV at HBM peak and chunk products at
+        # MFMA peak, overlapped perfectly; the larger of the two names the bound.
+        t_hbm = dec_bytes / (HBM_PEAK_GBS * 1e9)
+        t_mfma = pre_flops / (MFMA_PEAK_TFLOPS[dt] * 1e12)
+        bound = "hbm" if t_hbm >= t_mfma else "mfma"
+        t_attn = attn_avg * 1e-3
+        res["metric"] = "mixed decode + chunked-prefill step: query rows/s (one call)"
+        res.update({
+            "value": round(rows / (ms_step * 1e-3), 1), "unit": "rows/s",
+            "roofline": {"bound": bound,
+                         "achieved": round(dec_bytes / t_attn / 1e9, 2) if bound == "hbm"
+                         else round(pre_flops / t_attn / 1e12, 2),
+                         "peak": HBM_PEAK_GBS if bound == "hbm" else MFMA_PEAK_TFLOPS[dt],
+                         "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+                         "frac": round(max(t_hbm, t_mfma) / t_attn, 4),
+                         "traffic": measured_traffic(args.config),
+                         "kernel": "mixed step (decode kernel and prefill kernel at once)",
+                         "algorithmic_bytes_decode": dec_bytes,
+                         "algorithmic_flops_prefill": pre_flops,
+                         "avg_launch_us": round(attn_avg * 1e3, 2)},
+            "mixed": {"one_call_us": round(attn_avg * 1e3, 2),
+                      "sequential_calls_us": round(ways["sequential"] * 1e3, 2),
+                      "unified_prefill_kernel_us": round(ways["unified"] * 1e3, 2),
+                      "decode_part_alone_us": round(ways["decode"] * 1e3, 2),
+                      "prefill_part_alone_us": round(ways["prefill"] * 1e3, 2),
+                      "decode_rows": nd, "chunk_rows": rows - nd},
+        })
     else:
         tf_step = flops / (ms_step * 1e-3) / 1e12
         tf_attn = flops / (attn_avg * 1e-3) / 1e12
@@ -298,7 +360,7 @@ def main():
                      "block_size": wl.block_size, "pool_blocks": wl.num_blocks,
                      "placement": args.placement,
                      "total_context_tokens": int(wl.context_lens.sum()),
-                     "partition_size": wl.partition_size if wl.mode == "decode" else None,
+                     "partition_size": wl.partition_size if wl.mode != "prefill" else None,
                      "kv_bytes": kv, "attention_flops": flops}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")

@@ -224,6 +224,45 @@ pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, int32_t out_dtyp
                              int32_t max_context_len, float scale, hipStream_t stream);
 
 /*
+ * One step's attention over a batch that mixes decode rows and prefill-chunk
+ * rows.  [S] section "Prefill-Decode Disaggregation": on a single GPU a long
+ * prompt is cut into chunks, and every step batches one chunk together with
+ * the decode tokens of the other requests.  The result is exactly that of
+ * pkv_paged_prefill over all num_seqs sequences (a decode row is a chunk of
+ * one row at position context_lens[s] - 1), computed by two kernels that run
+ * at once: the decode kernel of pkv_paged_decode over the decode sequences
+ * and the prefill kernel over the chunk sequences.  The decode part is
+ * enqueued on a stream the library owns (one per device, default priority,
+ * forked from and joined back into `stream` with events), so work enqueued on
+ * `stream` after this call sees both parts finished.
+ *
+ *   sequences 0 .. num_decode_seqs-1   decode: one query row each, row s
+ *                     (query_start_loc[s] == s for s <= num_decode_seqs; the
+ *                     decode part does not read query_start_loc)
+ *   sequences num_decode_seqs .. num_seqs-1   chunks, as for pkv_paged_prefill
+ *                     (query_start_loc holds absolute row numbers)
+ *   out, q            [total_rows][num_q_heads][head_dim], model dtype; out
+ *                     also PKV_F32.  A cache with chunk sequences must be f16
+ *                     or bf16 (8-bit: PKV_ERR_UNSUPPORTED); decode-only calls
+ *                     take every cache pkv_paged_decode takes
+ *   partition_size, workspace   as for pkv_paged_decode over the decode
+ *                     sequences: pkv_decode_workspace_bytes(cache,
+ *                     num_decode_seqs, num_q_heads, max_context_len,
+ *                     partition_size) bytes
+ *   max_query_len     host bound on the chunk lengths; max_context_len a host
+ *                     bound on every context length
+ * Host-side locking serialises concurrent calls on one device while they
+ * enqueue; the side stream may be captured into a graph with `stream`.
+ */
+pkv_status pkv_paged_mixed(const pkv_cache *cache, void *out, int32_t out_dtype, const void *q,
+                           int32_t num_q_heads, const int32_t *query_start_loc,
+                           const int32_t *context_lens, const int32_t *block_tables,
+                           int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_decode_seqs,
+                           int32_t max_query_len, int32_t max_context_len, float scale,
+                           int32_t partition_size, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
  * Debug gather with the kernels' own address arithmetic: the contiguous
  * K and V of every sequence, back to back, token-major.
  *

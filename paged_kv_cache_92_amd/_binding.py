@@ -23,7 +23,8 @@ _TORCH_TO_PKV = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16:
 _STATUS = {0: "OK", 1: "INVALID", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP"}
 
 EXPORTED = ("pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_decode_workspace_bytes",
-            "pkv_paged_decode", "pkv_paged_prefill", "pkv_gather_kv", "pkv_validate_host",
+            "pkv_paged_decode", "pkv_paged_prefill", "pkv_paged_mixed", "pkv_gather_kv",
+            "pkv_validate_host",
             "pkv_last_error", "pkv_version")
 
 
@@ -58,12 +59,14 @@ def lib() -> ctypes.CDLL:
         L.pkv_decode_workspace_bytes.restype = sz
         L.pkv_paged_decode.argtypes = [cp, vp, i32, vp, i32, vp, i32, vp, i32, i32, f32, i32, vp, sz, vp]
         L.pkv_paged_prefill.argtypes = [cp, vp, i32, vp, i32, vp, vp, vp, i32, i32, i32, i32, f32, vp]
+        L.pkv_paged_mixed.argtypes = [cp, vp, i32, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                      i32, vp, sz, vp]
         L.pkv_gather_kv.argtypes = [cp, vp, vp, vp, i32, vp, vp, i32, i32, vp]
         L.pkv_validate_host.argtypes = [vp, i64, vp, i32, vp, i32, i64, i32]
         L.pkv_last_error.restype = ctypes.c_char_p
         L.pkv_version.restype = ctypes.c_char_p
         for name in ("pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_paged_decode",
-                     "pkv_paged_prefill", "pkv_gather_kv", "pkv_validate_host"):
+                     "pkv_paged_prefill", "pkv_paged_mixed", "pkv_gather_kv", "pkv_validate_host"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -232,6 +235,40 @@ def paged_prefill(cache: PagedKVCache, q, query_start_loc, context_lens, block_t
                                    _dev_ptr(block_tables, "block_tables", torch.int32),
                                    block_tables.shape[1], S, int(max_query_len),
                                    int(max_context_len), float(scale), _stream()))
+    return out
+
+
+def paged_mixed(cache: PagedKVCache, q, query_start_loc, context_lens, block_tables,
+                num_decode_seqs, max_query_len, max_context_len, scale=None, partition_size=0,
+                out=None, workspace=None, out_dtype=None):
+    """One step over decode rows and prefill-chunk rows: q [rows][Hq][d] -> out.
+
+    Sequences ``0 .. num_decode_seqs-1`` hold one query row each (rows
+    ``0 .. num_decode_seqs-1``); the rest are chunks placed by
+    ``query_start_loc`` (absolute rows).  ``partition_size`` and
+    ``workspace`` apply to the decode sequences."""
+    Tq, Hq, dq = q.shape
+    if dq != cache.head_dim:
+        raise ValueError("q head_dim does not match the cache")
+    if scale is None:
+        scale = 1.0 / math.sqrt(cache.head_dim)
+    out = _out(q, out, out_dtype)
+    S = context_lens.shape[0]
+    nd = int(num_decode_seqs)
+    need = decode_workspace_bytes(cache, nd, Hq, max_context_len, partition_size) if nd else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.nbytes if workspace is not None else 0
+    d = cache.desc()
+    _check(lib().pkv_paged_mixed(ctypes.byref(d), _dev_ptr(out, "out"), _TORCH_TO_PKV[out.dtype],
+                                 _dev_ptr(q, "q", cache.model_dtype), Hq,
+                                 _dev_ptr(query_start_loc, "query_start_loc", torch.int32),
+                                 _dev_ptr(context_lens, "context_lens", torch.int32),
+                                 _dev_ptr(block_tables, "block_tables", torch.int32),
+                                 block_tables.shape[1], S, nd, int(max_query_len),
+                                 int(max_context_len), float(scale), int(partition_size), ws_ptr,
+                                 ws_bytes, _stream()))
     return out
 
 

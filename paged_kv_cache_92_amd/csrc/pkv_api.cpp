@@ -126,6 +126,155 @@ DecodePlan plan_decode(const pkv::CacheDesc &c, int S, int Hq, int max_context_l
   return d;
 }
 
+// Validates a decode call and fills `a` and `plan`.
+pkv_status prepare_decode(const pkv::CacheDesc &c, void *out, int32_t out_dtype, const void *q,
+                          int32_t num_q_heads, const int32_t *block_tables,
+                          int32_t max_blocks_per_seq, const int32_t *context_lens,
+                          int32_t num_seqs, int32_t max_context_len, float scale,
+                          int32_t partition_size, void *workspace, size_t ws_bytes,
+                          pkv::DecodeArgs *a, DecodePlan *plan) {
+  if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "at most 65535 sequences per call");
+  if (!out || !q || !block_tables || !context_lens)
+    return fail(PKV_ERR_INVALID, "out/q/block_tables/context_lens is NULL");
+  if (!aligned16(out) || !aligned16(q)) return fail(PKV_ERR_INVALID, "q/out must be 16-byte aligned");
+  if (out_dtype != c.mdtype && out_dtype != PKV_F32)
+    return fail(PKV_ERR_INVALID, "out_dtype must be the model dtype or PKV_F32");
+  if (num_q_heads <= 0 || num_q_heads % c.H != 0)
+    return fail(PKV_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, c.H);
+  if (num_q_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "too many query heads");
+  if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID, "max_blocks_per_seq must be > 0");
+  if (max_context_len <= 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * c.B)
+    return fail(PKV_ERR_INVALID, "max_context_len %d outside [1, max_blocks_per_seq*block_size]",
+                max_context_len);
+  if (!(scale > 0.f) || !(scale < INFINITY)) return fail(PKV_ERR_INVALID, "scale must be positive and finite");
+  if (partition_size != PKV_PARTITION_AUTO && (partition_size < 0 || partition_size % c.B != 0))
+    return fail(PKV_ERR_INVALID,
+                "partition_size %d must be PKV_PARTITION_AUTO, 0 or a positive multiple of block_size %d",
+                partition_size, c.B);
+  const int G = num_q_heads / c.H;
+  if (G > 16 && c.dtype != PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "group size %d > 16", G);
+  *plan = plan_decode(c, num_seqs, num_q_heads, max_context_len, partition_size);
+  const size_t need = plan->bytes;
+  if (need > 0) {
+    if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if (ws_bytes < need)
+      return fail(PKV_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", ws_bytes, need);
+    if (!aligned16(workspace)) return fail(PKV_ERR_INVALID, "workspace must be 16-byte aligned");
+  }
+  a->out = out;
+  a->out_f32 = out_dtype == PKV_F32;
+  a->q = q;
+  a->Hq = num_q_heads;
+  a->block_tables = block_tables;
+  a->max_blocks_per_seq = max_blocks_per_seq;
+  a->context_lens = context_lens;
+  a->S = num_seqs;
+  a->max_context_len = max_context_len;
+  a->scale = scale;
+  a->partition_tokens = plan->part.tokens;
+  a->num_partitions = plan->part.count;
+  a->flat = plan->flat;
+  a->flat_grid = plan->flat_grid;
+  a->ws_ml = nullptr;
+  a->ws_acc = nullptr;
+  a->ws_hdr = nullptr;
+  if (need > 0) {
+    a->ws_hdr = plan->flat ? (int *)workspace : nullptr;
+    a->ws_ml = (float *)((char *)workspace + plan->off_ml);
+    a->ws_acc = (float *)((char *)workspace + plan->off_acc);
+  }
+  return PKV_OK;
+}
+
+pkv_status launch_decode(const pkv::CacheDesc &c, const pkv::DecodeArgs &a, const DecodePlan &plan,
+                         hipStream_t stream) {
+  hipError_t e = plan.mfma ? pkv::launch_decode_mfma(c, a, stream) : pkv::launch_decode_valu(c, a, stream);
+  if (e != hipSuccess) return hip_status(e, "paged_decode launch");
+  if (plan.reduce()) {
+    e = pkv::launch_decode_reduce(c, a, stream);
+    if (e != hipSuccess) return hip_status(e, "paged_decode reduce launch");
+  }
+  return PKV_OK;
+}
+
+// Validates a prefill call over num_seqs > 0 sequences and fills `a`.
+pkv_status prepare_prefill(const pkv::CacheDesc &c, void *out, int32_t out_dtype, const void *q,
+                           int32_t num_q_heads, const int32_t *query_start_loc,
+                           const int32_t *context_lens, const int32_t *block_tables,
+                           int32_t max_blocks_per_seq, int32_t num_seqs, int32_t max_query_len,
+                           int32_t max_context_len, float scale, pkv::PrefillArgs *a) {
+  if (c.dtype != PKV_F16 && c.dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "prefill supports f16 and bf16 caches");
+  if (!out || !q || !query_start_loc || !context_lens || !block_tables)
+    return fail(PKV_ERR_INVALID, "a required pointer is NULL");
+  if (!aligned16(out) || !aligned16(q)) return fail(PKV_ERR_INVALID, "q/out must be 16-byte aligned");
+  if (out_dtype != c.dtype && out_dtype != PKV_F32)
+    return fail(PKV_ERR_INVALID, "out_dtype must be the cache dtype or PKV_F32");
+  if (num_q_heads <= 0 || num_q_heads % c.H != 0)
+    return fail(PKV_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, c.H);
+  if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID, "max_blocks_per_seq must be > 0");
+  if (max_context_len <= 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * c.B)
+    return fail(PKV_ERR_INVALID, "max_context_len %d outside [1, max_blocks_per_seq*block_size]",
+                max_context_len);
+  if (max_query_len > max_context_len) return fail(PKV_ERR_INVALID, "max_query_len > max_context_len");
+  if (!(scale > 0.f) || !(scale < INFINITY)) return fail(PKV_ERR_INVALID, "scale must be positive and finite");
+  const int64_t work = (int64_t)num_seqs * num_q_heads * ((max_query_len + 255) / 256);
+  if (work >= (int64_t)1 << 31) return fail(PKV_ERR_UNSUPPORTED, "launch too large");
+  a->out = out;
+  a->out_f32 = out_dtype == PKV_F32;
+  a->q = q;
+  a->Hq = num_q_heads;
+  a->query_start_loc = query_start_loc;
+  a->context_lens = context_lens;
+  a->block_tables = block_tables;
+  a->max_blocks_per_seq = max_blocks_per_seq;
+  a->S = num_seqs;
+  a->max_query_len = max_query_len;
+  a->max_context_len = max_context_len;
+  a->scale = scale;
+  return PKV_OK;
+}
+
+// A second stream per device, with the events that fork work onto it from a
+// caller's stream and join it back.  Created on first use with the device
+// current; default priority.  `mu` serialises the record/wait sequence of
+// concurrent callers on one device.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+
+pkv_status side_stream(SideStream **out) {
+  static std::mutex mu;
+  static std::map<int, SideStream *> streams;  // lives until the process ends
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = streams.find(dev);
+  if (it != streams.end()) {
+    *out = it->second;
+    return PKV_OK;
+  }
+  SideStream *ss = new SideStream;
+  e = hipStreamCreateWithFlags(&ss->stream, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&ss->join, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    if (ss->join) (void)hipEventDestroy(ss->join);
+    if (ss->fork) (void)hipEventDestroy(ss->fork);
+    if (ss->stream) (void)hipStreamDestroy(ss->stream);
+    delete ss;
+    return hip_status(e, "side stream setup");
+  }
+  streams[dev] = ss;
+  *out = ss;
+  return PKV_OK;
+}
+
 }  // namespace
 
 namespace pkv {
@@ -208,65 +357,14 @@ pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype
   if (st) return st;
   if (num_seqs < 0) return fail(PKV_ERR_INVALID, "num_seqs < 0");
   if (num_seqs == 0) return ok();
-  if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "at most 65535 sequences per call");
-  if (!out || !q || !block_tables || !context_lens)
-    return fail(PKV_ERR_INVALID, "out/q/block_tables/context_lens is NULL");
-  if (!aligned16(out) || !aligned16(q)) return fail(PKV_ERR_INVALID, "q/out must be 16-byte aligned");
-  if (out_dtype != c.mdtype && out_dtype != PKV_F32)
-    return fail(PKV_ERR_INVALID, "out_dtype must be the model dtype or PKV_F32");
-  if (num_q_heads <= 0 || num_q_heads % c.H != 0)
-    return fail(PKV_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
-                num_q_heads, c.H);
-  if (num_q_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "too many query heads");
-  if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID, "max_blocks_per_seq must be > 0");
-  if (max_context_len <= 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * c.B)
-    return fail(PKV_ERR_INVALID, "max_context_len %d outside [1, max_blocks_per_seq*block_size]",
-                max_context_len);
-  if (!(scale > 0.f) || !(scale < INFINITY)) return fail(PKV_ERR_INVALID, "scale must be positive and finite");
-  if (partition_size != PKV_PARTITION_AUTO && (partition_size < 0 || partition_size % c.B != 0))
-    return fail(PKV_ERR_INVALID,
-                "partition_size %d must be PKV_PARTITION_AUTO, 0 or a positive multiple of block_size %d",
-                partition_size, c.B);
-  const int G = num_q_heads / c.H;
-  if (G > 16 && c.dtype != PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "group size %d > 16", G);
-  const DecodePlan plan = plan_decode(c, num_seqs, num_q_heads, max_context_len, partition_size);
-  const size_t need = plan.bytes;
-  if (need > 0) {
-    if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required", need);
-    if (ws_bytes < need)
-      return fail(PKV_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", ws_bytes, need);
-    if (!aligned16(workspace)) return fail(PKV_ERR_INVALID, "workspace must be 16-byte aligned");
-  }
   pkv::DecodeArgs a;
-  a.out = out;
-  a.out_f32 = out_dtype == PKV_F32;
-  a.q = q;
-  a.Hq = num_q_heads;
-  a.block_tables = block_tables;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.context_lens = context_lens;
-  a.S = num_seqs;
-  a.max_context_len = max_context_len;
-  a.scale = scale;
-  a.partition_tokens = plan.part.tokens;
-  a.num_partitions = plan.part.count;
-  a.flat = plan.flat;
-  a.flat_grid = plan.flat_grid;
-  a.ws_ml = nullptr;
-  a.ws_acc = nullptr;
-  a.ws_hdr = nullptr;
-  if (need > 0) {
-    a.ws_hdr = plan.flat ? (int *)workspace : nullptr;
-    a.ws_ml = (float *)((char *)workspace + plan.off_ml);
-    a.ws_acc = (float *)((char *)workspace + plan.off_acc);
-  }
-  hipError_t e = plan.mfma ? pkv::launch_decode_mfma(c, a, stream) : pkv::launch_decode_valu(c, a, stream);
-  if (e != hipSuccess) return hip_status(e, "paged_decode launch");
-  if (plan.reduce()) {
-    e = pkv::launch_decode_reduce(c, a, stream);
-    if (e != hipSuccess) return hip_status(e, "paged_decode reduce launch");
-  }
-  return ok();
+  DecodePlan plan;
+  st = prepare_decode(c, out, out_dtype, q, num_q_heads, block_tables, max_blocks_per_seq,
+                      context_lens, num_seqs, max_context_len, scale, partition_size, workspace,
+                      ws_bytes, &a, &plan);
+  if (st) return st;
+  st = launch_decode(c, a, plan, stream);
+  return st ? st : ok();
 }
 
 pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, int32_t out_dtype, const void *q,
@@ -281,36 +379,74 @@ pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, int32_t out_dtyp
     return fail(PKV_ERR_UNSUPPORTED, "prefill supports f16 and bf16 caches");
   if (num_seqs < 0 || max_query_len < 0) return fail(PKV_ERR_INVALID, "negative size");
   if (num_seqs == 0 || max_query_len == 0) return ok();
-  if (!out || !q || !query_start_loc || !context_lens || !block_tables)
-    return fail(PKV_ERR_INVALID, "a required pointer is NULL");
-  if (!aligned16(out) || !aligned16(q)) return fail(PKV_ERR_INVALID, "q/out must be 16-byte aligned");
-  if (out_dtype != c.dtype && out_dtype != PKV_F32)
-    return fail(PKV_ERR_INVALID, "out_dtype must be the cache dtype or PKV_F32");
-  if (num_q_heads <= 0 || num_q_heads % c.H != 0)
-    return fail(PKV_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
-                num_q_heads, c.H);
-  if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID, "max_blocks_per_seq must be > 0");
-  if (max_context_len <= 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * c.B)
-    return fail(PKV_ERR_INVALID, "max_context_len %d outside [1, max_blocks_per_seq*block_size]",
-                max_context_len);
-  if (max_query_len > max_context_len) return fail(PKV_ERR_INVALID, "max_query_len > max_context_len");
-  if (!(scale > 0.f) || !(scale < INFINITY)) return fail(PKV_ERR_INVALID, "scale must be positive and finite");
-  const int64_t work = (int64_t)num_seqs * num_q_heads * ((max_query_len + 255) / 256);
-  if (work >= (int64_t)1 << 31) return fail(PKV_ERR_UNSUPPORTED, "launch too large");
   pkv::PrefillArgs a;
-  a.out = out;
-  a.out_f32 = out_dtype == PKV_F32;
-  a.q = q;
-  a.Hq = num_q_heads;
-  a.query_start_loc = query_start_loc;
-  a.context_lens = context_lens;
-  a.block_tables = block_tables;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.S = num_seqs;
-  a.max_query_len = max_query_len;
-  a.max_context_len = max_context_len;
-  a.scale = scale;
+  st = prepare_prefill(c, out, out_dtype, q, num_q_heads, query_start_loc, context_lens,
+                       block_tables, max_blocks_per_seq, num_seqs, max_query_len, max_context_len,
+                       scale, &a);
+  if (st) return st;
   return hip_status(pkv::launch_prefill(c, a, stream), "paged_prefill launch");
+}
+
+pkv_status pkv_paged_mixed(const pkv_cache *cache, void *out, int32_t out_dtype, const void *q,
+                           int32_t num_q_heads, const int32_t *query_start_loc,
+                           const int32_t *context_lens, const int32_t *block_tables,
+                           int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_decode_seqs,
+                           int32_t max_query_len, int32_t max_context_len, float scale,
+                           int32_t partition_size, void *workspace, size_t ws_bytes,
+                           hipStream_t stream) {
+  pkv::CacheDesc c;
+  pkv_status st = check_cache(cache, &c);
+  if (st) return st;
+  if (num_seqs < 0 || num_decode_seqs < 0 || max_query_len < 0)
+    return fail(PKV_ERR_INVALID, "negative size");
+  if (num_decode_seqs > num_seqs) return fail(PKV_ERR_INVALID, "num_decode_seqs > num_seqs");
+  const int32_t np = num_seqs - num_decode_seqs;
+  const bool has_prefill = np > 0 && max_query_len > 0;
+  const bool has_decode = num_decode_seqs > 0;
+  if (!query_start_loc && np > 0) return fail(PKV_ERR_INVALID, "query_start_loc is NULL");
+  pkv::DecodeArgs da;
+  DecodePlan plan;
+  if (has_decode) {
+    st = prepare_decode(c, out, out_dtype, q, num_q_heads, block_tables, max_blocks_per_seq,
+                        context_lens, num_decode_seqs, max_context_len, scale, partition_size,
+                        workspace, ws_bytes, &da, &plan);
+    if (st) return st;
+  }
+  pkv::PrefillArgs pa;
+  if (has_prefill) {
+    // The chunk sequences' own rows of the integer inputs; query_start_loc
+    // keeps absolute row numbers, so q and out stay the whole step's.
+    st = prepare_prefill(c, out, out_dtype, q, num_q_heads, query_start_loc + num_decode_seqs,
+                         context_lens + num_decode_seqs,
+                         block_tables + (size_t)num_decode_seqs * max_blocks_per_seq,
+                         max_blocks_per_seq, np, max_query_len, max_context_len, scale, &pa);
+    if (st) return st;
+  }
+  if (!has_decode && !has_prefill) return ok();
+  if (!has_decode) return hip_status(pkv::launch_prefill(c, pa, stream), "paged_mixed prefill launch");
+  if (!has_prefill) {
+    st = launch_decode(c, da, plan, stream);
+    return st ? st : ok();
+  }
+  // Both kinds: the chunk rows go on the caller's stream first, the decode
+  // rows on the side stream, so the matrix-core prefill and the HBM-bound
+  // decode share the chip; the caller's stream then waits for both.
+  SideStream *ss = nullptr;
+  st = side_stream(&ss);
+  if (st) return st;
+  std::lock_guard<std::mutex> lock(ss->mu);
+  hipError_t e = hipEventRecord(ss->fork, stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->fork, 0);
+  if (e != hipSuccess) return hip_status(e, "paged_mixed fork");
+  e = pkv::launch_prefill(c, pa, stream);
+  if (e != hipSuccess) return hip_status(e, "paged_mixed prefill launch");
+  st = launch_decode(c, da, plan, ss->stream);
+  // Join even after a failed decode launch: the side stream must not run
+  // ahead of later work on the caller's stream.
+  e = hipEventRecord(ss->join, ss->stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(stream, ss->join, 0);
+  if (st) return st;
+  return hip_status(e, "paged_mixed join");
 }
 
 pkv_status pkv_gather_kv(const pkv_cache *cache, void *k_out, void *v_out,

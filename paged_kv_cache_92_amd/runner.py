@@ -66,6 +66,7 @@ class DeviceWorkload:
         self.context_lens = torch.from_numpy(wl.context_lens).to(device)
         self.q = to_device(wl.q, wl.dtype, device)
         self.qsl = None if wl.query_start_loc is None else torch.from_numpy(wl.query_start_loc).to(device)
+        self._qsl_tail = None
         self.ops = []
         for op in wl.setup:
             self.ops.append(self._dev_op(op, device))
@@ -95,9 +96,42 @@ class DeviceWorkload:
                                     wl.max_context_len, scale=wl.scale, partition_size=ps, out=out,
                                     workspace=workspace, out_dtype=out_dtype)
         qlens = np.diff(wl.query_start_loc)
+        if wl.mode == "mixed":
+            nd = int(wl.info["num_decode_seqs"])
+            ps = wl.partition_size if partition_size is None else partition_size
+            return pkv.paged_mixed(cache, self.q, self.qsl, self.context_lens, self.block_tables,
+                                   nd, int(qlens[nd:].max(initial=0)), wl.max_context_len,
+                                   scale=wl.scale, partition_size=ps, out=out,
+                                   workspace=workspace, out_dtype=out_dtype)
         return pkv.paged_prefill(cache, self.q, self.qsl, self.context_lens, self.block_tables,
                                  int(qlens.max()), wl.max_context_len, scale=wl.scale, out=out,
                                  out_dtype=out_dtype)
+
+    def attend_split(self, cache, how, out, workspace=None):
+        """A mixed step served another way, for comparison: ``"sequential"`` is
+        a decode call then a prefill call on one stream, ``"unified"`` one
+        prefill call over every row (a decode row as a chunk of one);
+        ``"decode"`` and ``"prefill"`` run one part alone."""
+        wl = self.wl
+        assert wl.mode == "mixed"
+        nd = int(wl.info["num_decode_seqs"])
+        qlens = np.diff(wl.query_start_loc)
+        if how == "unified":
+            return pkv.paged_prefill(cache, self.q, self.qsl, self.context_lens, self.block_tables,
+                                     int(qlens.max()), wl.max_context_len, scale=wl.scale, out=out)
+        assert how in ("sequential", "decode", "prefill")
+        if how != "prefill":
+            pkv.paged_decode(cache, self.q[:nd], self.block_tables[:nd], self.context_lens[:nd],
+                             wl.max_context_len, scale=wl.scale, partition_size=wl.partition_size,
+                             out=out[:nd], workspace=workspace)
+        if how != "decode":
+            base = int(wl.query_start_loc[nd])
+            if self._qsl_tail is None:
+                self._qsl_tail = self.qsl[nd:] - base
+            pkv.paged_prefill(cache, self.q[base:], self._qsl_tail, self.context_lens[nd:],
+                              self.block_tables[nd:], int(qlens[nd:].max()), wl.max_context_len,
+                              scale=wl.scale, out=out[base:])
+        return out
 
     def run(self, cache, partition_size=None):
         """Setup, then one step: scatter the new tokens and attend."""

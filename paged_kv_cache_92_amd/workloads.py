@@ -311,6 +311,70 @@ def make_prefill(name, seed, S, chunk, hist_fn, shared_prefix, Hq, Hkv, d, B, dt
     return wl
 
 
+def make_mixed(name, seed, decode_lens_fn, chunk_hist_fn, chunk_lens, Hq, Hkv, d, B, dtype,
+               max_context_len, pool_factor=1.1, partition_size=0):
+    """One step that batches decode rows with prefill chunks, decode sequences first.
+
+    ``decode_lens_fn(rng)`` draws the decode sequences' context lengths
+    (post-append); ``chunk_hist_fn(rng)`` the history of each chunk sequence,
+    which then appends ``chunk_lens[i]`` new tokens.  Setup scatters every
+    history; the step scatters the decode tokens and the chunk tokens, then
+    attends.  query_start_loc is [0, 1, ..., nd, nd + c0, ...]; blocks are
+    handed out in a seeded random order.
+    """
+    rng = np.random.default_rng(seed)
+    dctx = np.asarray(decode_lens_fn(rng), dtype=np.int64)
+    hist = np.asarray(chunk_hist_fn(rng), dtype=np.int64)
+    clen = np.asarray(chunk_lens, dtype=np.int64)
+    assert hist.shape == clen.shape
+    nd = dctx.shape[0]
+    ctx = np.concatenate([dctx, hist + clen]).astype(np.int32)
+    qlen = np.concatenate([np.ones(nd, dtype=np.int64), clen])
+    if (ctx < 1).any() or (ctx > max_context_len).any() or (clen < 1).any():
+        raise ValueError("context lengths must lie in [1, max_context_len], chunks non-empty")
+    S = ctx.shape[0]
+    need = int(sum(-(-int(L) // B) for L in ctx))
+    nb = int(math.ceil(pool_factor * need)) + 1
+    perm = rng.permutation(nb)
+    bm = BlockManager(nb, B, free_order=perm)
+    qsl = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32)
+    q = _draw_values(rng, (int(qsl[-1]), Hq, d), dtype)
+    total = int(ctx.astype(np.int64).sum())
+    keys = _draw_values(rng, (total, Hkv, d), dtype)
+    values = _draw_values(rng, (total, Hkv, d), dtype)
+    cu = np.concatenate([[0], np.cumsum(ctx.astype(np.int64))])
+    sids, hist_idx, hist_slots, new_idx, new_slots = [], [], [], [], []
+    for s in range(S):
+        sid = bm.new_sequence()
+        sids.append(sid)
+        slots, copies = bm.append_tokens(sid, int(ctx[s]))
+        assert not copies
+        h = int(ctx[s] - qlen[s])
+        hist_idx.append(np.arange(cu[s], cu[s] + h))
+        hist_slots.append(slots[:h])
+        new_idx.append(np.arange(cu[s] + h, cu[s + 1]))
+        new_slots.append(slots[h:])
+    hist_idx = np.concatenate(hist_idx)
+    new_idx = np.concatenate(new_idx)
+    mbps = -(-max_context_len // B)
+    bt = bm.block_table_array(sids, mbps, pad=_poison_block(bm))
+    wl = Workload(name=name, mode="mixed", dtype=dtype, num_blocks=nb, num_kv_heads=Hkv,
+                  num_q_heads=Hq, head_dim=d, block_size=B, context_lens=ctx, block_tables=bt,
+                  q=q, scale=_scale(d), query_start_loc=qsl, partition_size=partition_size,
+                  max_context_len=int(max_context_len))
+    wl.setup.append(Op("scatter", key=np.ascontiguousarray(keys[hist_idx]),
+                       value=np.ascontiguousarray(values[hist_idx]),
+                       slots=np.concatenate(hist_slots).astype(np.int64)))
+    wl.step_scatter = Op("scatter", key=np.ascontiguousarray(keys[new_idx]),
+                         value=np.ascontiguousarray(values[new_idx]),
+                         slots=np.concatenate(new_slots).astype(np.int64))
+    wl.seq_tokens_key = [keys[cu[s]:cu[s + 1]] for s in range(S)]
+    wl.seq_tokens_value = [values[cu[s]:cu[s + 1]] for s in range(S)]
+    wl.info = {"blocks_needed": need, "num_decode_seqs": nd, "chunk_rows": int(clen.sum()),
+               "tokens": total}
+    return wl
+
+
 # ---------------------------------------------------------------------------
 # The five workloads (sizes as stated for each), plus small variants for tests.
 # ---------------------------------------------------------------------------
@@ -368,3 +432,14 @@ def chunked_prefill_bf16(S=8, chunk=512, hist_lo=1024, hist_hi=3584, shared_pref
     return make_prefill(f"chunked_prefill_bf16_S{S}", seed, S, chunk, fn, shared_prefix, Hq=Hq,
                         Hkv=Hkv, d=128, B=16, dtype=BF16, max_context_len=max_context_len,
                         pair_sharing=pair_sharing)
+
+
+def mixed_step_f16(nd=64, n_chunks=2, chunk=512, lo=128, hi=2048, hist_lo=1024, hist_hi=1536,
+                   seed=6, partition_size=512, Hq=40, Hkv=40, dtype=F16):
+    """One LLaMA-2-13B-shaped step: nd decode rows (L ~ U[lo, hi]) batched with n_chunks
+    prefill chunks of ``chunk`` rows over histories ~ U[hist_lo, hist_hi]; d 128, B 16."""
+    return make_mixed(f"mixed_step_f16_D{nd}_C{n_chunks}x{chunk}", seed,
+                      lambda rng: rng.integers(lo, hi + 1, size=nd),
+                      lambda rng: rng.integers(hist_lo, hist_hi + 1, size=n_chunks),
+                      [chunk] * n_chunks, Hq=Hq, Hkv=Hkv, d=128, B=16, dtype=dtype,
+                      max_context_len=max(hi, hist_hi + chunk), partition_size=partition_size)

@@ -227,6 +227,32 @@ def test_decode_matches_brute_force_on_unpaged_kv(dtype, G):
             np.testing.assert_allclose(out[s, hq], ref, rtol=1e-12, atol=1e-13)
 
 
+def test_mixed_step_matches_brute_force_on_unpaged_kv():
+    # A step batching decode rows with prefill chunks: every decode row sees
+    # its whole context, chunk row i of a chunk after h history tokens sees
+    # positions 0..h+i.  Textbook attention on the never-paged token lists.
+    G, Hkv = 2, 2
+    wl = W.make_mixed("mix", 23, lambda rng: [1, 17, 40], lambda rng: [20, 33], [7, 16],
+                      Hq=Hkv * G, Hkv=Hkv, d=64, B=16, dtype=BF16, max_context_len=64)
+    nd = wl.info["num_decode_seqs"]
+    assert list(wl.query_start_loc[:nd + 1]) == list(range(nd + 1))
+    k, v = fill_pools(wl)
+    out = reference_output(wl, k, v)
+    qsl = wl.query_start_loc
+    for s in range(wl.S):
+        L = int(wl.context_lens[s])
+        K = _vals(wl.seq_tokens_key[s], BF16)
+        V = _vals(wl.seq_tokens_value[s], BF16)
+        qlen = int(qsl[s + 1] - qsl[s])
+        for i in range(qlen):
+            p = L - qlen + i
+            row = int(qsl[s]) + i
+            for hq in range(wl.num_q_heads):
+                q = _vals(wl.q[row, hq], BF16)
+                ref = _numpy_textbook(q, K[:p + 1, hq // G], V[:p + 1, hq // G], wl.scale)
+                np.testing.assert_allclose(out[row, hq], ref, rtol=1e-12, atol=1e-13)
+
+
 def _onehot_case(L, d, B=16, seed=0, q_scale=1):
     """One sequence whose V rows are one-hot (V[j] = e_j): the output is the weight vector."""
     rng = np.random.default_rng(seed)
