@@ -50,6 +50,10 @@ def make_workload(name, partition, block_size=16, placement="shuffled"):
     elif name == "prefill":
         wl = W.chunked_prefill_bf16()
         desc = "chunked causal prefill over paged cache with shared prefixes, bf16"
+    elif name == "sliding":
+        wl = W.sliding_window_gqa_bf16()
+        desc = ("mistral-7b-shaped sliding-window paged decode (window 4096, 32q/8kv heads, "
+                "L ~ U[1024, 16384], blocks before each window released), bf16")
     elif name == "mixed":
         wl = W.mixed_step_f16()
         desc = ("llama2-13b-shaped step batching 64 decode rows with two 512-row prefill chunks "
@@ -68,7 +72,10 @@ def attention_flops(wl):
     import numpy as np
     d, Hq = wl.head_dim, wl.num_q_heads
     if wl.mode == "decode":
-        return float(wl.context_lens.astype(np.int64).sum()) * Hq * d * 4
+        L = wl.context_lens.astype(np.int64)
+        if wl.window > 0:
+            L = np.minimum(L, wl.window)
+        return float(L.sum()) * Hq * d * 4
     qsl = wl.query_start_loc
     total = 0
     for s in range(wl.S):
@@ -129,8 +136,9 @@ def cpu_baseline(wl, budget_s):
         while n < wl.S and (time.perf_counter() - t0) < budget_s:
             oracle.paged_attention_rows(k, v, wl.cache_dtype, wl.q[n:n + 1], wl.block_tables,
                                         wl.context_lens, [n], [int(wl.context_lens[n]) - 1], wl.scale,
-                                        **kv)
-            kv_bytes += int(wl.context_lens[n]) * 2 * wl.num_kv_heads * wl.head_dim * elt
+                                        window=wl.window, **kv)
+            L = int(wl.context_lens[n])
+            kv_bytes += (min(L, wl.window) if wl.window else L) * 2 * wl.num_kv_heads * wl.head_dim * elt
             n += 1
         el = time.perf_counter() - t0
         return {"value": round(kv_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
@@ -165,7 +173,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="llama13b",
                     choices=["llama13b", "llama13b_fp8", "long_split", "gqa16", "gqa32", "prefill",
-                             "mixed", "tiny"])
+                             "mixed", "sliding", "tiny"])
     ap.add_argument("--partition", type=int, default=None,
                     help="split-KV partition size in tokens (default: the workload's)")
     ap.add_argument("--block-size", type=int, default=16, choices=[16, 32],
@@ -300,7 +308,6 @@ def main():
             "value": round(gbs_step, 2), "unit": "GB/s",
             "pct_hbm_peak": round(100 * gbs_step / HBM_PEAK_GBS, 2),
             "decode_tokens_per_s": round(wl.S / (ms_step * 1e-3), 1),
-            "decode_tokens_per_s_40_layer_attention_only": round(wl.S / (40 * ms_step * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs_attn, 2), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs_attn / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic(args.config),
@@ -308,6 +315,10 @@ def main():
                          "algorithmic_bytes_per_launch": kv,
                          "avg_launch_us": round(attn_avg * 1e3, 2)},
         })
+        if args.config.startswith("llama13b"):
+            res["decode_tokens_per_s_40_layer_attention_only"] = round(wl.S / (40 * ms_step * 1e-3), 1)
+        if wl.window:
+            res["metric"] = "sliding-window paged decode effective KV GB/s (window tokens only)"
     elif wl.mode == "mixed":
         nd = int(wl.info["num_decode_seqs"])
         rows = int(wl.query_start_loc[-1])
@@ -360,6 +371,7 @@ def main():
                      "block_size": wl.block_size, "pool_blocks": wl.num_blocks,
                      "placement": args.placement,
                      "total_context_tokens": int(wl.context_lens.sum()),
+                     "sliding_window": wl.window or None,
                      "partition_size": wl.partition_size if wl.mode != "prefill" else None,
                      "kv_bytes": kv, "attention_flops": flops}
     if not args.no_cpu_baseline:

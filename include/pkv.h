@@ -200,6 +200,28 @@ pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype
                             void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Sliding-window decode.  [W] section "블록 할당: allocate_slots" (under
+ * "KVCacheManager: 블록 단위 할당의 중심"): before a step's allocation the
+ * cache manager releases the blocks that fell out of the sliding window, as
+ * an OS pages out frames, then allocates new ones.  Reading
+ * taken: the query at position L-1 attends to positions max(0, L - W) .. L-1
+ * (the W most recent tokens, itself included); a block holding only earlier
+ * positions may have been released, so its table entry may name any block
+ * or none, and is never read.  Everything else as for pkv_paged_decode,
+ * which is this call with sliding_window 0 (no window); the same workspace
+ * size applies.
+ *
+ *   sliding_window    W in tokens, >= 0 (0: the whole context)
+ */
+pkv_status pkv_paged_decode_window(const pkv_cache *cache, void *out, int32_t out_dtype,
+                                   const void *q, int32_t num_q_heads,
+                                   const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t *context_lens, int32_t num_seqs,
+                                   int32_t max_context_len, int32_t sliding_window, float scale,
+                                   int32_t partition_size, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Causal chunked prefill over the paged cache.  [S] section "Prefill-Decode
  * Disaggregation": a long prompt is processed in chunks over several steps;
  * [T] step 6 and [R] section 01: prefill processes all prompt tokens at once

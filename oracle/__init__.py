@@ -73,9 +73,9 @@ def _load(path: str | None = None) -> ctypes.CDLL:
         lib.oracle_copy_blocks.argtypes = [vp, vp, i32, i64, i32, i32, i32, vp, i64]
         lib.oracle_gather_kv.argtypes = [vp, vp, i32, i64, i32, i32, i32, vp, i32, vp, i32, vp, vp]
         lib.oracle_paged_attention_rows.argtypes = [vp, vp, i32, i32, f64, f64, i64, i32, i32, i32, vp,
-                                                   i32, vp, i32, vp, i32, vp, vp, i64, f32, vp]
+                                                   i32, vp, i32, vp, i32, vp, vp, i64, i32, f32, vp]
         lib.oracle_paged_decode.argtypes = [vp, vp, i32, i32, f64, f64, i64, i32, i32, i32, vp, i32, vp,
-                                            i32, vp, i32, f32, vp]
+                                            i32, vp, i32, i32, f32, vp]
         lib.oracle_paged_prefill.argtypes = [vp, vp, i32, i32, f64, f64, i64, i32, i32, i32, vp, i32, vp,
                                              vp, vp, i32, i32, f32, vp]
         lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
@@ -158,11 +158,12 @@ def gather_kv(k_pool, v_pool, dtype, block_tables, context_lens):
 
 
 def paged_attention_rows(k_pool, v_pool, dtype, q, block_tables, context_lens, row_seq, row_pos,
-                         scale, q_dtype=None, k_scale=1.0, v_scale=1.0):
+                         scale, q_dtype=None, k_scale=1.0, v_scale=1.0, window=0):
     """fp64 attention for query rows q [n][Hq][d] at (row_seq[r], row_pos[r]); returns [n][Hq][d].
 
     q is in ``q_dtype`` (default: the cache dtype; F16/BF16 over an FP8 cache,
-    whose entries read as code * k_scale / code * v_scale)."""
+    whose entries read as code * k_scale / code * v_scale).  ``window`` > 0:
+    each row attends to its last ``window`` positions only."""
     nb, Hkv, B, d = _geom(k_pool, v_pool, dtype)
     q = np.ascontiguousarray(q)
     n, Hq, dq = q.shape
@@ -176,14 +177,15 @@ def paged_attention_rows(k_pool, v_pool, dtype, q, block_tables, context_lens, r
     _check(_load().oracle_paged_attention_rows(_ptr(k_pool), _ptr(v_pool), dtype, qd, float(k_scale),
                                                float(v_scale), nb, Hkv, B, d,
                                                _ptr(q), Hq, _ptr(bt), bt.shape[1], _ptr(ctx),
-                                               ctx.shape[0], _ptr(rs), _ptr(rp), n, float(scale),
-                                               _ptr(out)), "paged_attention_rows")
+                                               ctx.shape[0], _ptr(rs), _ptr(rp), n, int(window),
+                                               float(scale), _ptr(out)), "paged_attention_rows")
     return out
 
 
 def paged_decode(k_pool, v_pool, dtype, q, block_tables, context_lens, scale, q_dtype=None,
-                 k_scale=1.0, v_scale=1.0):
-    """fp64 decode output [S][Hq][d]: each sequence's query over all its ctx tokens."""
+                 k_scale=1.0, v_scale=1.0, window=0):
+    """fp64 decode output [S][Hq][d]: each sequence's query over all its ctx tokens (its
+    last ``window`` tokens when ``window`` > 0)."""
     nb, Hkv, B, d = _geom(k_pool, v_pool, dtype)
     q = np.ascontiguousarray(q)
     S, Hq, _ = q.shape
@@ -193,8 +195,8 @@ def paged_decode(k_pool, v_pool, dtype, q, block_tables, context_lens, scale, q_
     qd = dtype if q_dtype is None else q_dtype
     _check(_load().oracle_paged_decode(_ptr(k_pool), _ptr(v_pool), dtype, qd, float(k_scale),
                                        float(v_scale), nb, Hkv, B, d, _ptr(q), Hq,
-                                       _ptr(bt), bt.shape[1], _ptr(ctx), S, float(scale), _ptr(out)),
-           "paged_decode")
+                                       _ptr(bt), bt.shape[1], _ptr(ctx), S, int(window), float(scale),
+                                       _ptr(out)), "paged_decode")
     return out
 
 

@@ -299,13 +299,15 @@ int oracle_gather_kv(const void *k_pool, const void *v_pool, int dtype, int64_t 
   return ORC_OK;
 }
 
-/* fp64 reassembly of positions [0, n) of one sequence: Kc/Vc are [n][H][d].
- * Entries of an 8-bit cache read as code * scale (exact in fp64). */
+/* fp64 reassembly of positions [j0, n) of one sequence into Kc/Vc, which are
+ * indexed by absolute position: [n][H][d] (rows before j0 untouched; the
+ * table entries of their blocks are not read).  Entries of an 8-bit cache
+ * read as code * scale (exact in fp64). */
 static int reassemble(const void *k_pool, const void *v_pool, int dtype, double k_scale,
                       double v_scale, int64_t num_blocks, int H, int B, int d,
-                      const int32_t *bt_row, int n, double *Kc, double *Vc) {
+                      const int32_t *bt_row, int j0, int n, double *Kc, double *Vc) {
   const double ks = dtype == ORC_FP8 ? k_scale : 1.0, vs = dtype == ORC_FP8 ? v_scale : 1.0;
-  for (int j = 0; j < n; ++j) {
+  for (int j = j0; j < n; ++j) {
     int64_t blk;
     int off;
     int rc = lookup(bt_row, j, B, num_blocks, &blk, &off);
@@ -329,12 +331,13 @@ static int reassemble(const void *k_pool, const void *v_pool, int dtype, double 
  * The maximum is subtracted before exponentiation, which leaves the softmax
  * unchanged in exact arithmetic.  Grouped heads (GQA, [S] section "The
  * Hidden Waste of KV Cache": 32 query heads share 8 KV heads) read KV head
- * hkv = hq / (Hq / Hkv).
+ * hkv = hq / (Hq / Hkv).  Keys lo..p are used: lo = 0, or the first position
+ * of a sliding window.
  */
-static void attend_one(const double *q, int p, const double *Kc, const double *Vc, int Hkv, int hkv,
-                       int d, double scale, double *z, double *o) {
+static void attend_one(const double *q, int lo, int p, const double *Kc, const double *Vc, int Hkv,
+                       int hkv, int d, double scale, double *z, double *o) {
   double m = -INFINITY;
-  for (int j = 0; j <= p; ++j) {
+  for (int j = lo; j <= p; ++j) {
     const double *k = Kc + ((size_t)j * Hkv + hkv) * d;
     double dot = 0.0;
     for (int e = 0; e < d; ++e) dot += q[e] * k[e];
@@ -342,12 +345,12 @@ static void attend_one(const double *q, int p, const double *Kc, const double *V
     if (z[j] > m) m = z[j];
   }
   double Z = 0.0;
-  for (int j = 0; j <= p; ++j) {
+  for (int j = lo; j <= p; ++j) {
     z[j] = exp(z[j] - m);
     Z += z[j];
   }
   for (int e = 0; e < d; ++e) o[e] = 0.0;
-  for (int j = 0; j <= p; ++j) {
+  for (int j = lo; j <= p; ++j) {
     const double *v = Vc + ((size_t)j * Hkv + hkv) * d;
     double w = z[j] / Z;
     for (int e = 0; e < d; ++e) o[e] += w * v[e];
@@ -357,7 +360,10 @@ static void attend_one(const double *q, int p, const double *Kc, const double *V
 /*
  * Attention for a list of query rows.  Row r belongs to sequence row_seq[r]
  * and sits at absolute position row_pos[r]; it attends to cached positions
- * 0..row_pos[r] of that sequence.  q is [n][Hq][d] in q_dtype (the cache dtype, or f16/bf16 over an 8-bit cache), out
+ * 0..row_pos[r] of that sequence, or, with window > 0, to the window's
+ * positions max(0, row_pos[r] - window + 1)..row_pos[r]: [W] section "블록
+ * 할당: allocate_slots" releases the blocks that fall out of a sliding
+ * window, read here as the W most recent positions, the row's own included.  q is [n][Hq][d] in q_dtype (the cache dtype, or f16/bf16 over an 8-bit cache), out
  * is [n][Hq][d] fp64.  The sequence's K/V are first reassembled into
  * contiguous fp64 arrays through its block table, then each head runs the
  * textbook formula above; consecutive rows of one sequence reuse one
@@ -368,10 +374,11 @@ int oracle_paged_attention_rows(const void *k_pool, const void *v_pool, int dtyp
                                 int64_t num_blocks, int Hkv, int B, int d, const void *q, int Hq,
                                 const int32_t *block_tables, int max_blocks_per_seq,
                                 const int32_t *context_lens, int S, const int32_t *row_seq,
-                                const int32_t *row_pos, int64_t n, float scale, double *out) {
+                                const int32_t *row_pos, int64_t n, int window, float scale,
+                                double *out) {
   int rc = check_geometry(dtype, num_blocks, Hkv, B, d);
   if (rc) return rc;
-  if (Hq <= 0 || Hq % Hkv != 0 || n < 0 || S <= 0) return ORC_ERR_ARG;
+  if (Hq <= 0 || Hq % Hkv != 0 || n < 0 || S <= 0 || window < 0) return ORC_ERR_ARG;
   if (dtype == ORC_FP8 ? (q_dtype != ORC_F16 && q_dtype != ORC_BF16) : q_dtype != dtype) return ORC_ERR_ARG;
   int G = Hq / Hkv;
   int cap = max_blocks_per_seq * B;
@@ -380,24 +387,26 @@ int oracle_paged_attention_rows(const void *k_pool, const void *v_pool, int dtyp
   double *z = malloc(sizeof(double) * (size_t)cap);
   double *qv = malloc(sizeof(double) * (size_t)d);
   if (!Kc || !Vc || !z || !qv) { rc = ORC_ERR_NOMEM; goto done; }
-  int cur_seq = -1, cur_len = 0;
+  int cur_seq = -1, cur_lo = 0;
   for (int64_t r = 0; r < n; ++r) {
     int s = row_seq[r], p = row_pos[r];
     if (s < 0 || s >= S || p < 0 || p >= context_lens[s] || context_lens[s] > cap) {
       rc = ORC_ERR_RANGE;
       goto done;
     }
-    if (s != cur_seq || p + 1 > cur_len) {
+    int lo = window > 0 && p - window + 1 > 0 ? p - window + 1 : 0;
+    if (s != cur_seq || lo < cur_lo) {
       const int32_t *bt = block_tables + (size_t)s * max_blocks_per_seq;
-      if ((rc = reassemble(k_pool, v_pool, dtype, k_scale, v_scale, num_blocks, Hkv, B, d, bt,
+      if ((rc = reassemble(k_pool, v_pool, dtype, k_scale, v_scale, num_blocks, Hkv, B, d, bt, lo,
                            context_lens[s], Kc, Vc)))
         goto done;
       cur_seq = s;
-      cur_len = context_lens[s];
+      cur_lo = lo;
     }
     for (int hq = 0; hq < Hq; ++hq) {
       for (int e = 0; e < d; ++e) qv[e] = load_elt(q, ((size_t)r * Hq + hq) * d + e, q_dtype);
-      attend_one(qv, p, Kc, Vc, Hkv, hq / G, d, (double)scale, z, out + ((size_t)r * Hq + hq) * d);
+      attend_one(qv, lo, p, Kc, Vc, Hkv, hq / G, d, (double)scale, z,
+                 out + ((size_t)r * Hq + hq) * d);
     }
   }
   rc = ORC_OK;
@@ -414,13 +423,14 @@ done:
  * all ctx[s] cached tokens (the new token's K/V already scattered, so the
  * query sees itself as the equation's j <= i requires).  [T] step 6: decode
  * reads the whole cache every step; [R] eq. (4) is the block-wise form of
- * the same result.  q and out are [S][Hq][d].
+ * the same result.  With window > 0 only the last `window` positions are
+ * attended (see oracle_paged_attention_rows).  q and out are [S][Hq][d].
  */
 int oracle_paged_decode(const void *k_pool, const void *v_pool, int dtype, int q_dtype,
                         double k_scale, double v_scale, int64_t num_blocks,
                         int Hkv, int B, int d, const void *q, int Hq, const int32_t *block_tables,
-                        int max_blocks_per_seq, const int32_t *context_lens, int S, float scale,
-                        double *out) {
+                        int max_blocks_per_seq, const int32_t *context_lens, int S, int window,
+                        float scale, double *out) {
   if (S <= 0) return ORC_ERR_ARG;
   int32_t *rs = malloc(sizeof(int32_t) * (size_t)S);
   int32_t *rp = malloc(sizeof(int32_t) * (size_t)S);
@@ -431,7 +441,7 @@ int oracle_paged_decode(const void *k_pool, const void *v_pool, int dtype, int q
   }
   int rc = oracle_paged_attention_rows(k_pool, v_pool, dtype, q_dtype, k_scale, v_scale, num_blocks,
                                        Hkv, B, d, q, Hq, block_tables, max_blocks_per_seq,
-                                       context_lens, S, rs, rp, S, scale, out);
+                                       context_lens, S, rs, rp, S, window, scale, out);
   free(rs);
   free(rp);
   return rc;
@@ -472,7 +482,7 @@ int oracle_paged_prefill(const void *k_pool, const void *v_pool, int dtype, int 
   }
   int rc = oracle_paged_attention_rows(k_pool, v_pool, dtype, q_dtype, k_scale, v_scale, num_blocks,
                                        Hkv, B, d, q, Hq, block_tables, max_blocks_per_seq,
-                                       context_lens, S, rs, rp, n, scale, out);
+                                       context_lens, S, rs, rp, n, 0, scale, out);
   free(rs);
   free(rp);
   return rc;

@@ -23,7 +23,8 @@ _TORCH_TO_PKV = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16:
 _STATUS = {0: "OK", 1: "INVALID", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP"}
 
 EXPORTED = ("pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_decode_workspace_bytes",
-            "pkv_paged_decode", "pkv_paged_prefill", "pkv_paged_mixed", "pkv_gather_kv",
+            "pkv_paged_decode", "pkv_paged_decode_window", "pkv_paged_prefill", "pkv_paged_mixed",
+            "pkv_gather_kv",
             "pkv_validate_host",
             "pkv_last_error", "pkv_version")
 
@@ -58,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.pkv_decode_workspace_bytes.argtypes = [cp, i32, i32, i32, i32]
         L.pkv_decode_workspace_bytes.restype = sz
         L.pkv_paged_decode.argtypes = [cp, vp, i32, vp, i32, vp, i32, vp, i32, i32, f32, i32, vp, sz, vp]
+        L.pkv_paged_decode_window.argtypes = [cp, vp, i32, vp, i32, vp, i32, vp, i32, i32, i32, f32, i32,
+                                              vp, sz, vp]
         L.pkv_paged_prefill.argtypes = [cp, vp, i32, vp, i32, vp, vp, vp, i32, i32, i32, i32, f32, vp]
         L.pkv_paged_mixed.argtypes = [cp, vp, i32, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                       i32, vp, sz, vp]
@@ -66,6 +69,7 @@ def lib() -> ctypes.CDLL:
         L.pkv_last_error.restype = ctypes.c_char_p
         L.pkv_version.restype = ctypes.c_char_p
         for name in ("pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_paged_decode",
+                     "pkv_paged_decode_window",
                      "pkv_paged_prefill", "pkv_paged_mixed", "pkv_gather_kv", "pkv_validate_host"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -190,11 +194,12 @@ def _out(q, out, out_dtype):
 
 
 def paged_decode(cache: PagedKVCache, q, block_tables, context_lens, max_context_len, scale=None,
-                 partition_size=0, out=None, workspace=None, out_dtype=None):
+                 partition_size=0, out=None, workspace=None, out_dtype=None, sliding_window=0):
     """Decode attention: q [S][Hq][d] -> out [S][Hq][d] over each sequence's paged cache.
 
     ``out_dtype`` is the model dtype (default: the fp32 result rounded once) or
-    torch.float32 (the fp32 result itself)."""
+    torch.float32 (the fp32 result itself).  ``sliding_window`` > 0 attends to
+    each sequence's last ``sliding_window`` tokens only (pkv_paged_decode_window)."""
     S, Hq, dq = q.shape
     if dq != cache.head_dim:
         raise ValueError("q head_dim does not match the cache")
@@ -207,13 +212,15 @@ def paged_decode(cache: PagedKVCache, q, block_tables, context_lens, max_context
     ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.nbytes if workspace is not None else 0
     d = cache.desc()
-    _check(lib().pkv_paged_decode(ctypes.byref(d), _dev_ptr(out, "out"), _TORCH_TO_PKV[out.dtype],
-                                  _dev_ptr(q, "q", cache.model_dtype), Hq,
-                                  _dev_ptr(block_tables, "block_tables", torch.int32),
-                                  block_tables.shape[1],
-                                  _dev_ptr(context_lens, "context_lens", torch.int32), S,
-                                  int(max_context_len), float(scale), int(partition_size), ws_ptr,
-                                  ws_bytes, _stream()))
+    args = [ctypes.byref(d), _dev_ptr(out, "out"), _TORCH_TO_PKV[out.dtype],
+            _dev_ptr(q, "q", cache.model_dtype), Hq,
+            _dev_ptr(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+            _dev_ptr(context_lens, "context_lens", torch.int32), S, int(max_context_len)]
+    tail = [float(scale), int(partition_size), ws_ptr, ws_bytes, _stream()]
+    if sliding_window:
+        _check(lib().pkv_paged_decode_window(*args, int(sliding_window), *tail))
+    else:
+        _check(lib().pkv_paged_decode(*args, *tail))
     return out
 
 

@@ -23,6 +23,11 @@ Behaviour follows the pages:
   repoints the writer's table (same pyy0715.github.io page, section
   "Copy-on-Write"; hrletsgo.me step 9).
 * A finished sequence returns its blocks (hrletsgo.me step 7.7).
+* Under a sliding window of W tokens, blocks that hold only positions before
+  the window of the sequence's newest token are released before new ones are
+  taken, as an OS pages out frames (blog.secrett2633.cloud, section "블록
+  할당: allocate_slots", remove_skipped_blocks); their table entries become
+  ``NULL_BLOCK``.
 
 A slot number is ``physical_block * block_size + offset``.
 """
@@ -32,6 +37,9 @@ from collections import deque
 from dataclasses import dataclass, field
 
 import numpy as np
+
+
+NULL_BLOCK = -1   # table entry of a block released from before a sliding window
 
 
 class OutOfBlocks(RuntimeError):
@@ -74,6 +82,8 @@ class BlockManager:
         return b
 
     def _release(self, b: int):
+        if b == NULL_BLOCK:
+            return
         self.ref_count[b] -= 1
         if self.ref_count[b] < 0:
             raise AssertionError(f"block {b} released more times than it was held")
@@ -98,7 +108,8 @@ class BlockManager:
         child.block_table = list(p.block_table)
         child.num_tokens = p.num_tokens
         for b in p.block_table:
-            self.ref_count[b] += 1
+            if b != NULL_BLOCK:
+                self.ref_count[b] += 1
         return sid
 
     def blocks_needed(self, sid: int, n: int) -> int:
@@ -129,24 +140,47 @@ class BlockManager:
                               f"{self.num_free} free")
         copies = []
         slots = np.empty(n, dtype=np.int64)
-        for i in range(n):
-            pos = s.num_tokens
-            logical = pos // B
-            off = pos % B
-            if off == 0:
-                # The last block is full (or there is none): take a new one.
-                s.block_table.append(self._take())
-            else:
-                phys = s.block_table[logical]
-                if self.ref_count[phys] > 1:
-                    # Copy-on-write: this sequence gets a private copy.
-                    new_phys = self._take()
-                    copies.append((phys, new_phys))
-                    self.ref_count[phys] -= 1
-                    s.block_table[logical] = new_phys
-            slots[i] = s.block_table[logical] * B + off
-            s.num_tokens += 1
+        i = 0
+        off = s.num_tokens % B
+        if n > 0 and off != 0:
+            # Tokens that fill the partially used last block.  Only the first of
+            # them can meet a shared block: copy-on-write makes it private.
+            logical = s.num_tokens // B
+            phys = s.block_table[logical]
+            if self.ref_count[phys] > 1:
+                new_phys = self._take()
+                copies.append((phys, new_phys))
+                self.ref_count[phys] -= 1
+                s.block_table[logical] = new_phys
+            k = min(n, B - off)
+            slots[:k] = s.block_table[logical] * B + off + np.arange(k)
+            s.num_tokens += k
+            i = k
+        while i < n:
+            # The last block is full (or there is none): take a new one.
+            b = self._take()
+            s.block_table.append(b)
+            k = min(B, n - i)
+            slots[i:i + k] = b * B + np.arange(k)
+            s.num_tokens += k
+            i += k
         return slots, copies
+
+    def remove_skipped_blocks(self, sid: int, window: int) -> int:
+        """Release the blocks of ``sid`` that hold only positions before
+        ``num_tokens - window`` (outside the window of the newest token and of
+        every later one); returns how many were released."""
+        s = self._seqs[sid]
+        if window <= 0:
+            return 0
+        first = max(0, s.num_tokens - window) // self.block_size
+        n = 0
+        for i in range(min(first, len(s.block_table))):
+            if s.block_table[i] != NULL_BLOCK:
+                self._release(s.block_table[i])
+                s.block_table[i] = NULL_BLOCK
+                n += 1
+        return n
 
     def free_sequence(self, sid: int):
         s = self._seqs.pop(sid)
@@ -165,10 +199,12 @@ class BlockManager:
 
     def wasted_slots(self) -> int:
         """Allocated-but-empty token slots over live sequences (each block counted once)."""
-        held = {b for s in self._seqs.values() for b in s.block_table}
+        held = {b for s in self._seqs.values() for b in s.block_table if b != NULL_BLOCK}
         used = np.zeros(self.num_blocks, dtype=np.int64)
         for s in self._seqs.values():
             for i, b in enumerate(s.block_table):
+                if b == NULL_BLOCK:
+                    continue
                 fill = min(self.block_size, s.num_tokens - i * self.block_size)
                 used[b] = max(used[b], fill)
         return int(sum(self.block_size - used[b] for b in held))

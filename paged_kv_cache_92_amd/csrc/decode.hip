@@ -58,8 +58,9 @@ struct ValuLds {
   float acc[kWaves][D];
 };
 
-// One work item: blocks [b0, b1) of sequence s for query head hq; the merged
-// result goes to the output or to a workspace partial row (dest).  E is the
+// One work item: blocks [b0, b1) of sequence s for query head hq, positions
+// before the sliding window's start (window > 0) masked; the merged result
+// goes to the output or to a workspace partial row (dest).  E is the
 // cache's element type, Q the query/output type (E itself, except over an
 // 8-bit cache: there the key scale is folded into scale_log2 and the value
 // scale multiplies the merged sums).
@@ -69,14 +70,15 @@ __device__ __forceinline__ void valu_item(
     int out_f32, const typename Q::storage *__restrict__ q,
     const typename E::storage *__restrict__ kpool, const typename E::storage *__restrict__ vpool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    int64_t num_blocks, int Hkv, int Hq, int mbps, float scale_log2, float v_scale,
+    int64_t num_blocks, int Hkv, int Hq, int mbps, int window, float scale_log2, float v_scale,
     float *__restrict__ ws_ml, float *__restrict__ ws_acc) {
   using C = ValuCfg<E, D, BS>;
   using T = typename E::storage;
   constexpr bool kFP8 = E::kBytes == 1;
-  const int L = min(context_lens[s], mbps * BS);
-  const int tok0 = b0 * BS;
-  const int tok1 = min(L, b1 * BS);
+  const Span sp = seq_span(context_lens, s, mbps * BS, window);
+  const int lo = sp.lo;                      // first attended position
+  const int tok0 = max(b0 * BS, lo);
+  const int tok1 = min(sp.hi, b1 * BS);
   if (tok0 >= tok1) return;
   const int blk0 = b0;
   const int nblk = b1 - b0;
@@ -148,7 +150,9 @@ __device__ __forceinline__ void valu_item(
     for (int i = 0; i < C::VL; ++i) vr[i] = load16_stream(vtile + (size_t)(kWave * i + lane) * C::VEC);
 
     const int tbase = lb * BS;
-    const bool partial = tbase + BS > tok1;
+    // Only the last block can end past the length, only the first start
+    // before the window.
+    const bool partial = tbase + BS > tok1 || tbase < lo;
     float sc[C::TG];
 #pragma unroll
     for (int r = 0; r < C::TG; ++r) {
@@ -156,7 +160,7 @@ __device__ __forceinline__ void valu_item(
 #pragma unroll
       for (int c = 1; c < C::NC; ++c) x += dot(kr[c * C::TG + r], c);
       x = group_sum<4>(x) * scale_log2;
-      if (partial && tbase + 16 * r + kt >= tok1) x = -INFINITY;
+      if (partial && (unsigned)(tbase + 16 * r + kt - lo) >= (unsigned)(tok1 - lo)) x = -INFINITY;
       sc[r] = x;
     }
     float mb = sc[0];
@@ -187,10 +191,11 @@ __device__ __forceinline__ void valu_item(
       unpack16<E>(vr[i], vf);
       float a = acc[i] * alpha;
       if (partial) {
-        // Unfilled slots may hold anything (NaN included): their values count as 0.
+        // Slots outside [lo, tok1) may hold anything (NaN included): their values count as 0.
 #pragma unroll
         for (int e = 0; e < C::VEC; ++e) {
-          const float ve = (tbase + cp * C::VEC + e < tok1) ? vf[e] : 0.f;
+          const float ve =
+              ((unsigned)(tbase + cp * C::VEC + e - lo) < (unsigned)(tok1 - lo)) ? vf[e] : 0.f;
           a = fmaf(p[e], ve, a);
         }
       } else {
@@ -252,33 +257,35 @@ decode_valu_kernel(
     void *__restrict__ out, int out_f32, const typename Q::storage *__restrict__ q,
     const typename E::storage *__restrict__ kpool, const typename E::storage *__restrict__ vpool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    int64_t num_blocks, int Hkv, int Hq, int S, int mbps, float scale_log2, float v_scale,
-    int part_tokens, int nparts, float *__restrict__ ws_ml, float *__restrict__ ws_acc,
-    int *__restrict__ ws_hdr) {
+    int64_t num_blocks, int Hkv, int Hq, int S, int mbps, int window, float scale_log2,
+    float v_scale, int part_tokens, int nparts, float *__restrict__ ws_ml,
+    float *__restrict__ ws_acc, int *__restrict__ ws_hdr) {
   __shared__ ValuLds<E, D, BS> sh;
   extern __shared__ int plan[];
   __shared__ int scan[16];
   run_schedule<SCHED>(
       [&](int s, int hq, int b0, int b1, Dest dest) {
         valu_item<E, Q, D, BS>(sh, s, hq, b0, b1, dest, out, out_f32, q, kpool, vpool, block_tables,
-                               context_lens, num_blocks, Hkv, Hq, mbps, scale_log2, v_scale, ws_ml,
-                               ws_acc);
+                               context_lens, num_blocks, Hkv, Hq, mbps, window, scale_log2, v_scale,
+                               ws_ml, ws_acc);
       },
-      plan, scan, context_lens, S, mbps * BS, BS, Hq, 1, part_tokens, nparts, ws_hdr);
+      plan, scan, context_lens, S, mbps * BS, window, BS, Hq, 1, part_tokens, nparts, ws_hdr);
 }
 
-// Cross-partition reduce: o = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+// Cross-partition reduce over the partitions of the sequence's span:
+// o = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
 template <typename E, int D>
 __global__ __launch_bounds__(128) void decode_reduce_kernel(
     void *__restrict__ out, int out_f32, const int32_t *__restrict__ context_lens, int Hq,
-    int mbps_tokens, int part_tokens, int nparts, const float *__restrict__ ws_ml,
+    int mbps_tokens, int window, int part_tokens, int nparts, const float *__restrict__ ws_ml,
     const float *__restrict__ ws_acc) {
   const int hq = blockIdx.x;
   const int s = blockIdx.y;
-  const int L = min(context_lens[s], mbps_tokens);
-  const int np = min((L + part_tokens - 1) / part_tokens, nparts);
+  const Span sp = seq_span(context_lens, s, mbps_tokens, window);
+  const int p0 = first_part(sp, part_tokens);
+  const int np = min(parts_in(sp, part_tokens), nparts - p0);
   if (np <= 1) return;
-  const size_t base = ((size_t)s * Hq + hq) * nparts;
+  const size_t base = ((size_t)s * Hq + hq) * nparts + p0;
   float M = -INFINITY;
   for (int p = 0; p < np; ++p) M = fmaxf(M, ws_ml[2 * (base + p)]);
   for (int e = threadIdx.x; e < D; e += blockDim.x) {
@@ -331,7 +338,7 @@ void launch_valu_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) 
   auto go = [&](auto kern, dim3 grid, size_t dyn) {
     hipLaunchKernelGGL(kern, grid, dim3(256), dyn, stream, a.out, (int)a.out_f32, (const TQ *)a.q,
                        (const T *)c.k, (const T *)c.v, a.block_tables, a.context_lens,
-                       c.num_blocks, c.H, a.Hq, a.S, a.max_blocks_per_seq, sl, c.v_scale,
+                       c.num_blocks, c.H, a.Hq, a.S, a.max_blocks_per_seq, a.window, sl, c.v_scale,
                        a.partition_tokens, a.num_partitions, a.ws_ml, a.ws_acc, a.ws_hdr);
   };
   // Fixed partitions run a persistent grid over the non-empty cells (a 3-D
@@ -388,8 +395,8 @@ void launch_reduce_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream
                          (const int *)a.ws_hdr, a.Hq, HU, GU, a.ws_ml, a.ws_acc);
     else
       hipLaunchKernelGGL(kern_part, grid, dim3(threads), 0, stream, a.out, (int)a.out_f32,
-                         a.context_lens, a.Hq, mt, a.partition_tokens, a.num_partitions, a.ws_ml,
-                         a.ws_acc);
+                         a.context_lens, a.Hq, mt, a.window, a.partition_tokens, a.num_partitions,
+                         a.ws_ml, a.ws_acc);
   };
   if (c.D == 64) go(decode_reduce_kernel<E, 64>, decode_reduce_flat_kernel<E, 64>, 64);
   else go(decode_reduce_kernel<E, 128>, decode_reduce_flat_kernel<E, 128>, 128);

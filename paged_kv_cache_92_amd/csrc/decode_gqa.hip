@@ -86,7 +86,8 @@ __device__ __forceinline__ u32x2 widen4(uint32_t w) {
 }
 
 // One work item: blocks [b0, b1) of sequence s for the G query heads of KV
-// head hkv; head h's merged result goes to the output or to workspace
+// head hkv, positions before the sliding window's start (window > 0)
+// masked; head h's merged result goes to the output or to workspace
 // partial row dest.base + h * dest.stride.  `lds_dyn` holds the cross-wave
 // merge buffers.  E is the query / matrix-core type; KV the cache element
 // (E itself, or FP8: codes are widened to E right after the loads, the key
@@ -97,7 +98,8 @@ __device__ __forceinline__ void mfma_item(
     int out_f32, const uint16_t *__restrict__ q, const typename KV::storage *__restrict__ kpool,
     const typename KV::storage *__restrict__ vpool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, int64_t num_blocks, int Hkv, int G, int mbps,
-    float scale_log2, float v_scale, float *__restrict__ ws_ml, float *__restrict__ ws_acc) {
+    int window, float scale_log2, float v_scale, float *__restrict__ ws_ml,
+    float *__restrict__ ws_acc) {
   constexpr bool kFP8 = KV::kBytes == 1;
   constexpr int KS = D / 32;    // k-steps of the score product
   constexpr int NT = D / 16;    // 16-dimension tiles of the output
@@ -106,9 +108,10 @@ __device__ __forceinline__ void mfma_item(
   // lane ends up with 8 consecutive tokens, and P.V runs as 16x16x32 products
   // over 16-byte V^T operands.
   constexpr bool kWide = BS == 32;
-  const int L = min(context_lens[s], mbps * BS);
-  const int tok0 = b0 * BS;
-  const int tok1 = min(L, b1 * BS);
+  const Span sp = seq_span(context_lens, s, mbps * BS, window);
+  const int lo = sp.lo;                      // first attended position
+  const int tok0 = max(b0 * BS, lo);
+  const int tok1 = min(sp.hi, b1 * BS);
   if (tok0 >= tok1) return;
   const int blk0 = b0;
   const int nblk = b1 - b0;
@@ -202,7 +205,11 @@ __device__ __forceinline__ void mfma_item(
     }
 
     const int tbase = lb * BS;
-    const bool partial = tbase + BS > tok1;
+    // Only the last block can end past the length, only the first start
+    // before the window.
+    const bool partial = tbase + BS > tok1 || tbase < lo;
+    const unsigned span = (unsigned)(tok1 - lo);
+    auto keep = [&](int t) { return (unsigned)(t - lo) < span; };
     f32x4 st[SUB];
 #pragma unroll
     for (int sb = 0; sb < SUB; ++sb) {
@@ -212,7 +219,7 @@ __device__ __forceinline__ void mfma_item(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float v = x[j] * scale_log2;
-        if (partial && tbase + token_of_row<BS>(sb, 4 * g4 + j) >= tok1) v = -INFINITY;
+        if (partial && !keep(tbase + token_of_row<BS>(sb, 4 * g4 + j))) v = -INFINITY;
         x[j] = v;
       }
       st[sb] = x;
@@ -250,22 +257,22 @@ __device__ __forceinline__ void mfma_item(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
     if (partial) {
-      // Unfilled slots may hold anything (NaN included): zero their values.
+      // Slots outside [lo, tok1) may hold anything (NaN included): zero their values.
       if constexpr (kWide) {
         const int t0 = tbase + 8 * g4;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const uint32_t keep = (t0 + 2 * k < tok1 ? 0x0000ffffu : 0u) |
-                                (t0 + 2 * k + 1 < tok1 ? 0xffff0000u : 0u);
+          const uint32_t mask = (keep(t0 + 2 * k) ? 0x0000ffffu : 0u) |
+                                (keep(t0 + 2 * k + 1) ? 0xffff0000u : 0u);
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) vw[nt][k] &= keep;
+          for (int nt = 0; nt < NT; ++nt) vw[nt][k] &= mask;
         }
       } else {
 #pragma unroll
         for (int sb = 0; sb < SUB; ++sb) {
           const int t0 = tbase + 16 * sb + 4 * g4;
-          const uint32_t keep01 = (t0 < tok1 ? 0x0000ffffu : 0u) | (t0 + 1 < tok1 ? 0xffff0000u : 0u);
-          const uint32_t keep23 = (t0 + 2 < tok1 ? 0x0000ffffu : 0u) | (t0 + 3 < tok1 ? 0xffff0000u : 0u);
+          const uint32_t keep01 = (keep(t0) ? 0x0000ffffu : 0u) | (keep(t0 + 1) ? 0xffff0000u : 0u);
+          const uint32_t keep23 = (keep(t0 + 2) ? 0x0000ffffu : 0u) | (keep(t0 + 3) ? 0xffff0000u : 0u);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
             va[sb][nt][0] &= keep01;
@@ -348,9 +355,9 @@ __global__ __launch_bounds__(256, KV::kBytes == 1 ? PKV_MFMA_MIN_WAVES_FP8 : PKV
     void *__restrict__ out, int out_f32, const uint16_t *__restrict__ q,
     const typename KV::storage *__restrict__ kpool, const typename KV::storage *__restrict__ vpool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    int64_t num_blocks, int Hkv, int G, int S, int mbps, float scale_log2, float v_scale,
-    int part_tokens, int nparts, float *__restrict__ ws_ml, float *__restrict__ ws_acc,
-    int *__restrict__ ws_hdr) {
+    int64_t num_blocks, int Hkv, int G, int S, int mbps, int window, float scale_log2,
+    float v_scale, int part_tokens, int nparts, float *__restrict__ ws_ml,
+    float *__restrict__ ws_acc, int *__restrict__ ws_hdr) {
   extern __shared__ __attribute__((aligned(16))) int dyn[];
   __shared__ int scan[16];
   int *plan = dyn;
@@ -358,10 +365,10 @@ __global__ __launch_bounds__(256, KV::kBytes == 1 ? PKV_MFMA_MIN_WAVES_FP8 : PKV
   run_schedule<SCHED>(
       [&](int s, int hkv, int b0, int b1, Dest dest) {
         mfma_item<E, KV, D, BS>(merge, s, hkv, b0, b1, dest, out, out_f32, q, kpool, vpool,
-                                block_tables, context_lens, num_blocks, Hkv, G, mbps, scale_log2,
-                                v_scale, ws_ml, ws_acc);
+                                block_tables, context_lens, num_blocks, Hkv, G, mbps, window,
+                                scale_log2, v_scale, ws_ml, ws_acc);
       },
-      plan, scan, context_lens, S, mbps * BS, BS, Hkv, G, part_tokens, nparts, ws_hdr);
+      plan, scan, context_lens, S, mbps * BS, window, BS, Hkv, G, part_tokens, nparts, ws_hdr);
 }
 
 template <int D>
@@ -379,8 +386,8 @@ void launch_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
   auto go = [&](auto kern, dim3 grid, size_t dyn) {
     hipLaunchKernelGGL(kern, grid, dim3(256), dyn, stream, a.out, (int)a.out_f32,
                        (const uint16_t *)a.q, (const T *)c.k, (const T *)c.v, a.block_tables,
-                       a.context_lens, c.num_blocks, c.H, G, a.S, a.max_blocks_per_seq, sl,
-                       c.v_scale, a.partition_tokens, a.num_partitions, a.ws_ml, a.ws_acc,
+                       a.context_lens, c.num_blocks, c.H, G, a.S, a.max_blocks_per_seq, a.window,
+                       sl, c.v_scale, a.partition_tokens, a.num_partitions, a.ws_ml, a.ws_acc,
                        a.ws_hdr);
   };
   // Schedules as for the wavefront kernel.

@@ -130,7 +130,7 @@ DecodePlan plan_decode(const pkv::CacheDesc &c, int S, int Hq, int max_context_l
 pkv_status prepare_decode(const pkv::CacheDesc &c, void *out, int32_t out_dtype, const void *q,
                           int32_t num_q_heads, const int32_t *block_tables,
                           int32_t max_blocks_per_seq, const int32_t *context_lens,
-                          int32_t num_seqs, int32_t max_context_len, float scale,
+                          int32_t num_seqs, int32_t max_context_len, int32_t window, float scale,
                           int32_t partition_size, void *workspace, size_t ws_bytes,
                           pkv::DecodeArgs *a, DecodePlan *plan) {
   if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "at most 65535 sequences per call");
@@ -148,6 +148,7 @@ pkv_status prepare_decode(const pkv::CacheDesc &c, void *out, int32_t out_dtype,
     return fail(PKV_ERR_INVALID, "max_context_len %d outside [1, max_blocks_per_seq*block_size]",
                 max_context_len);
   if (!(scale > 0.f) || !(scale < INFINITY)) return fail(PKV_ERR_INVALID, "scale must be positive and finite");
+  if (window < 0) return fail(PKV_ERR_INVALID, "sliding_window %d < 0", window);
   if (partition_size != PKV_PARTITION_AUTO && (partition_size < 0 || partition_size % c.B != 0))
     return fail(PKV_ERR_INVALID,
                 "partition_size %d must be PKV_PARTITION_AUTO, 0 or a positive multiple of block_size %d",
@@ -171,6 +172,7 @@ pkv_status prepare_decode(const pkv::CacheDesc &c, void *out, int32_t out_dtype,
   a->context_lens = context_lens;
   a->S = num_seqs;
   a->max_context_len = max_context_len;
+  a->window = window;
   a->scale = scale;
   a->partition_tokens = plan->part.tokens;
   a->num_partitions = plan->part.count;
@@ -346,12 +348,13 @@ size_t pkv_decode_workspace_bytes(const pkv_cache *cache, int32_t num_seqs, int3
   return plan_decode(c, num_seqs, num_q_heads, max_context_len, partition_size).bytes;
 }
 
-pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype, const void *q,
-                            int32_t num_q_heads,
-                            const int32_t *block_tables, int32_t max_blocks_per_seq,
-                            const int32_t *context_lens, int32_t num_seqs,
-                            int32_t max_context_len, float scale, int32_t partition_size,
-                            void *workspace, size_t ws_bytes, hipStream_t stream) {
+pkv_status pkv_paged_decode_window(const pkv_cache *cache, void *out, int32_t out_dtype,
+                                   const void *q, int32_t num_q_heads,
+                                   const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t *context_lens, int32_t num_seqs,
+                                   int32_t max_context_len, int32_t sliding_window, float scale,
+                                   int32_t partition_size, void *workspace, size_t ws_bytes,
+                                   hipStream_t stream) {
   pkv::CacheDesc c;
   pkv_status st = check_cache(cache, &c);
   if (st) return st;
@@ -360,11 +363,22 @@ pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype
   pkv::DecodeArgs a;
   DecodePlan plan;
   st = prepare_decode(c, out, out_dtype, q, num_q_heads, block_tables, max_blocks_per_seq,
-                      context_lens, num_seqs, max_context_len, scale, partition_size, workspace,
-                      ws_bytes, &a, &plan);
+                      context_lens, num_seqs, max_context_len, sliding_window, scale,
+                      partition_size, workspace, ws_bytes, &a, &plan);
   if (st) return st;
   st = launch_decode(c, a, plan, stream);
   return st ? st : ok();
+}
+
+pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype, const void *q,
+                            int32_t num_q_heads,
+                            const int32_t *block_tables, int32_t max_blocks_per_seq,
+                            const int32_t *context_lens, int32_t num_seqs,
+                            int32_t max_context_len, float scale, int32_t partition_size,
+                            void *workspace, size_t ws_bytes, hipStream_t stream) {
+  return pkv_paged_decode_window(cache, out, out_dtype, q, num_q_heads, block_tables,
+                                 max_blocks_per_seq, context_lens, num_seqs, max_context_len, 0,
+                                 scale, partition_size, workspace, ws_bytes, stream);
 }
 
 pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, int32_t out_dtype, const void *q,
@@ -408,7 +422,7 @@ pkv_status pkv_paged_mixed(const pkv_cache *cache, void *out, int32_t out_dtype,
   DecodePlan plan;
   if (has_decode) {
     st = prepare_decode(c, out, out_dtype, q, num_q_heads, block_tables, max_blocks_per_seq,
-                        context_lens, num_decode_seqs, max_context_len, scale, partition_size,
+                        context_lens, num_decode_seqs, max_context_len, 0, scale, partition_size,
                         workspace, ws_bytes, &da, &plan);
     if (st) return st;
   }

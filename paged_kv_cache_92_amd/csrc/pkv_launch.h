@@ -39,6 +39,7 @@ struct DecodeArgs {
   const int32_t *context_lens;
   int S;
   int max_context_len;
+  int window;             // sliding window in tokens (0: attend to the whole context)
   float scale;
   int partition_tokens;   // > 0, multiple of B
   int num_partitions;     // ceil(max_context_len / partition_tokens)

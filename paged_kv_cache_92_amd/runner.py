@@ -94,7 +94,8 @@ class DeviceWorkload:
             ps = wl.partition_size if partition_size is None else partition_size
             return pkv.paged_decode(cache, self.q, self.block_tables, self.context_lens,
                                     wl.max_context_len, scale=wl.scale, partition_size=ps, out=out,
-                                    workspace=workspace, out_dtype=out_dtype)
+                                    workspace=workspace, out_dtype=out_dtype,
+                                    sliding_window=wl.window)
         qlens = np.diff(wl.query_start_loc)
         if wl.mode == "mixed":
             nd = int(wl.info["num_decode_seqs"])

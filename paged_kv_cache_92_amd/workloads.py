@@ -30,7 +30,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from .block_manager import BlockManager
+from .block_manager import NULL_BLOCK, BlockManager
 
 F32, F16, BF16, FP8 = 0, 1, 2, 3      # FP8 (E4M3 codes) is a cache storage type only
 DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", FP8: "fp8_e4m3"}
@@ -86,6 +86,7 @@ class Workload:
     partition_size: int = 0
     max_context_len: int = 0
     info: dict = field(default_factory=dict)
+    window: int = 0               # sliding window in tokens (0: whole context)
     kv_dtype: int = -1            # cache storage dtype (-1: ``dtype``; FP8 for an 8-bit cache)
     k_scale: float = 1.0          # 8-bit cache: stored code = x / scale
     v_scale: float = 1.0
@@ -112,9 +113,13 @@ class Workload:
         return k, v
 
     def kv_bytes(self) -> int:
-        """Bytes of live cached K and V that one attention pass reads once per KV head."""
+        """Bytes of live cached K and V that one attention pass reads once per KV head
+        (under a sliding window, only the window's tokens)."""
         elt = {F32: 4, F16: 2, BF16: 2, FP8: 1}[self.cache_dtype]
-        return int(self.context_lens.astype(np.int64).sum()) * 2 * self.num_kv_heads * self.head_dim * elt
+        L = self.context_lens.astype(np.int64)
+        if self.window > 0:
+            L = np.minimum(L, self.window)
+        return int(L.sum()) * 2 * self.num_kv_heads * self.head_dim * elt
 
 
 def _scale(d: int) -> float:
@@ -311,6 +316,82 @@ def make_prefill(name, seed, S, chunk, hist_fn, shared_prefix, Hq, Hkv, d, B, dt
     return wl
 
 
+def make_sliding_decode(name, seed, context_lens_fn, window, Hq, Hkv, d, B, dtype, max_context_len,
+                        partition_size=0, pool_factor=1.1, chunk=None):
+    """Decode under a sliding window of ``window`` tokens, with block release.
+
+    Each sequence's history is appended in chunks (default: ``window`` tokens),
+    and after every chunk the blocks outside the window of the newest token are
+    released (``remove_skipped_blocks``) and return to the free list, where
+    later chunks and other sequences take them again; then the new token is
+    appended and the release runs once more.  Only the positions still held
+    at the end, [first_pos[s], L), carry drawn values: they are scattered by
+    the setup (the new token by the step).  Table entries of released blocks
+    point at a NaN-filled block no sequence holds, so reading one would show.
+    """
+    rng = np.random.default_rng(seed)
+    ctx = np.asarray(context_lens_fn(rng), dtype=np.int64)
+    S = ctx.shape[0]
+    if (ctx < 1).any() or (ctx > max_context_len).any() or window < 1:
+        raise ValueError("context lengths must lie in [1, max_context_len], window >= 1")
+    chunk = int(chunk or window)
+    first_blk = np.maximum(0, ctx - window) // B
+    held = -(-ctx // B) - first_blk
+    need = int(held.sum())
+    nb = int(math.ceil(pool_factor * need)) + -(-chunk // B) + 3
+    perm = rng.permutation(nb)
+    bm = BlockManager(nb, B, free_order=perm)
+    q = _draw_values(rng, (S, Hq, d), dtype)
+    kept = (ctx - first_blk * B).astype(np.int64)          # positions [first_pos, L)
+    total = int(kept.sum())
+    keys = _draw_values(rng, (total, Hkv, d), dtype)
+    values = _draw_values(rng, (total, Hkv, d), dtype)
+    sids, released = [], 0
+    for s in range(S):
+        sid = bm.new_sequence()
+        sids.append(sid)
+        pos, L = 0, int(ctx[s])
+        while pos < L - 1:
+            n = min(chunk, L - 1 - pos)
+            bm.append_tokens(sid, n)
+            pos += n
+            released += bm.remove_skipped_blocks(sid, window)
+        bm.append_tokens(sid, 1)                           # the step's token
+        released += bm.remove_skipped_blocks(sid, window)
+        tbl = bm.seq(sid).block_table
+        assert all(b == NULL_BLOCK for b in tbl[:first_blk[s]])
+        assert all(b != NULL_BLOCK for b in tbl[first_blk[s]:])
+    mbps = -(-max_context_len // B)
+    poison = _poison_block(bm)
+    bt = bm.block_table_array(sids, mbps, pad=poison)
+    bt[bt == NULL_BLOCK] = poison
+    cu = np.concatenate([[0], np.cumsum(kept)])
+    hist_idx, hist_slots, new_idx, new_slots = [], [], [], []
+    for s in range(S):
+        p0, L = int(first_blk[s] * B), int(ctx[s])
+        pos = np.arange(p0, L)
+        slots = bt[s, pos // B].astype(np.int64) * B + pos % B
+        hist_idx.append(np.arange(cu[s], cu[s + 1] - 1))
+        hist_slots.append(slots[:-1])
+        new_idx.append(cu[s + 1] - 1)
+        new_slots.append(slots[-1])
+    wl = Workload(name=name, mode="decode", dtype=dtype, num_blocks=nb, num_kv_heads=Hkv,
+                  num_q_heads=Hq, head_dim=d, block_size=B, context_lens=ctx.astype(np.int32),
+                  block_tables=bt, q=q, scale=_scale(d), partition_size=partition_size,
+                  max_context_len=int(max_context_len), window=int(window))
+    wl.setup.append(Op("scatter", key=np.ascontiguousarray(keys[np.concatenate(hist_idx)]),
+                       value=np.ascontiguousarray(values[np.concatenate(hist_idx)]),
+                       slots=np.concatenate(hist_slots).astype(np.int64)))
+    wl.step_scatter = Op("scatter", key=np.ascontiguousarray(keys[new_idx]),
+                         value=np.ascontiguousarray(values[new_idx]),
+                         slots=np.asarray(new_slots, dtype=np.int64))
+    wl.seq_tokens_key = [keys[cu[s]:cu[s + 1]] for s in range(S)]
+    wl.seq_tokens_value = [values[cu[s]:cu[s + 1]] for s in range(S)]
+    wl.info = {"blocks_needed": need, "released_blocks": released,
+               "first_pos": (first_blk * B).tolist(), "window_tokens": int(np.minimum(ctx, window).sum())}
+    return wl
+
+
 def make_mixed(name, seed, decode_lens_fn, chunk_hist_fn, chunk_lens, Hq, Hkv, d, B, dtype,
                max_context_len, pool_factor=1.1, partition_size=0):
     """One step that batches decode rows with prefill chunks, decode sequences first.
@@ -443,3 +524,12 @@ def mixed_step_f16(nd=64, n_chunks=2, chunk=512, lo=128, hi=2048, hist_lo=1024, 
                       lambda rng: rng.integers(hist_lo, hist_hi + 1, size=n_chunks),
                       [chunk] * n_chunks, Hq=Hq, Hkv=Hkv, d=128, B=16, dtype=dtype,
                       max_context_len=max(hi, hist_hi + chunk), partition_size=partition_size)
+
+
+def sliding_window_gqa_bf16(S=64, lo=1024, hi=16384, window=4096, seed=7, partition_size=512, B=16):
+    """Mistral-7B-shaped sliding-window decode: 32 q / 8 kv heads, d 128, window 4096,
+    L ~ U[lo, hi], bf16; blocks before each window released."""
+    return make_sliding_decode(f"sliding_window_gqa_bf16_S{S}_W{window}", seed,
+                               lambda rng: rng.integers(lo, hi + 1, size=S), window, Hq=32, Hkv=8,
+                               d=128, B=B, dtype=BF16, max_context_len=hi,
+                               partition_size=partition_size)

@@ -33,7 +33,7 @@ def reference_output(wl, k, v):
     """fp64 oracle output of the workload's attention step over pools k, v."""
     if wl.mode == "decode":
         return oracle.paged_decode(k, v, wl.cache_dtype, wl.q, wl.block_tables, wl.context_lens,
-                                   wl.scale, **_kv(wl))
+                                   wl.scale, window=wl.window, **_kv(wl))
     return oracle.paged_prefill(k, v, wl.cache_dtype, wl.q, wl.query_start_loc, wl.context_lens,
                                 wl.block_tables, wl.scale, **_kv(wl))
 
@@ -50,4 +50,5 @@ def sampled_rows(wl, k, v, rows):
         qlen = qsl[seq + 1] - qsl[seq]
         pos = wl.context_lens[seq] - qlen + (rows - qsl[seq])
     return oracle.paged_attention_rows(k, v, wl.cache_dtype, wl.q[rows], wl.block_tables,
-                                       wl.context_lens, seq, pos, wl.scale, **_kv(wl))
+                                       wl.context_lens, seq, pos, wl.scale, window=wl.window,
+                                       **_kv(wl))

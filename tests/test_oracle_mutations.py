@@ -39,6 +39,10 @@ MUTATIONS = [
      ["test_fp8_decode_matches_brute_force_on_dequantised_kv"]),
     ("query dot uses wrong operand", "dot += q[e] * k[e];", "dot += q[e] * q[e];",
      ["test_weights_are_softmax_and_sum_to_one"]),
+    ("window start off by one", "p - window + 1 > 0 ? p - window + 1 : 0",
+     "p - window > 0 ? p - window : 0", ["test_sliding_window_range_is_exact"]),
+    ("window ignored", "int lo = window > 0 &&", "int lo = 0 &&",
+     ["test_sliding_window_range_is_exact"]),
 ]
 
 

@@ -379,6 +379,61 @@ def test_prefill_causal_range_is_exact():
         np.testing.assert_allclose(out[i, 0], expect, rtol=1e-14, atol=1e-15)
 
 
+def test_sliding_window_range_is_exact():
+    # q = 0 and one-hot V by position: a row at position p under window W must
+    # average exactly positions max(0, p - W + 1)..p.
+    L, d = 45, 64
+    k, v, bt, K, _ = _onehot_case(L, d)
+    ctx = np.array([L], np.int32)
+    for W in (1, 2, 16, 17, 44, 45, 100):
+        for p in (0, 7, 30, L - 1):
+            q = np.zeros((1, 1, d), np.float32)
+            out = oracle.paged_attention_rows(k, v, F32, q, bt, ctx, [0], [p], 0.125, window=W)
+            lo = max(0, p - W + 1)
+            expect = np.zeros(d)
+            expect[lo:p + 1] = 1.0 / (p + 1 - lo)
+            np.testing.assert_allclose(out[0, 0], expect, rtol=1e-14, atol=1e-15)
+
+
+def test_sliding_window_matches_brute_force_and_skips_released_blocks():
+    # Decode under window 40 with blocks released on the way (chunks of 24
+    # tokens): textbook attention over the last 40 never-paged tokens, and the
+    # table entries of released blocks are never read (set to -1 they would
+    # make the oracle fail).
+    wl = W.make_sliding_decode("sw", 31, lambda rng: [1, 20, 40, 47, 64, 100, 129], 40, Hq=4, Hkv=2,
+                               d=64, B=16, dtype=BF16, max_context_len=160, chunk=24)
+    assert wl.info["released_blocks"] > 0
+    k, v = fill_pools(wl)
+    out = reference_output(wl, k, v)
+    Wn = wl.window
+    for s, L in enumerate(wl.context_lens):
+        fp = wl.info["first_pos"][s]
+        lo = max(0, int(L) - Wn)
+        K = _vals(wl.seq_tokens_key[s], BF16)[lo - fp:]
+        V = _vals(wl.seq_tokens_value[s], BF16)[lo - fp:]
+        assert K.shape[0] == min(int(L), Wn)
+        for hq in range(wl.num_q_heads):
+            q = _vals(wl.q[s, hq], BF16)
+            ref = _numpy_textbook(q, K[:, hq // 2], V[:, hq // 2], wl.scale)
+            np.testing.assert_allclose(out[s, hq], ref, rtol=1e-12, atol=1e-13)
+    bt = wl.block_tables.copy()
+    for s in range(wl.S):
+        bt[s, :wl.info["first_pos"][s] // wl.block_size] = -1
+    out2 = oracle.paged_decode(k, v, BF16, wl.q, bt, wl.context_lens, wl.scale, window=Wn)
+    assert np.array_equal(out, out2)
+
+
+def test_window_covering_the_context_changes_nothing():
+    wl = W.make_decode("cover", 33, lambda rng: [1, 9, 16, 31, 50], Hq=2, Hkv=2, d=64, B=16,
+                       dtype=F16, max_context_len=64)
+    k, v = fill_pools(wl)
+    full = oracle.paged_decode(k, v, F16, wl.q, wl.block_tables, wl.context_lens, wl.scale)
+    for Wn in (50, 51, 1000):
+        win = oracle.paged_decode(k, v, F16, wl.q, wl.block_tables, wl.context_lens, wl.scale,
+                                  window=Wn)
+        assert np.array_equal(full, win)
+
+
 def test_prefill_ignores_future_positions():
     wl = W.chunked_prefill_bf16(S=2, chunk=24, shared_prefix=16, Hq=2, Hkv=2, max_context_len=128,
                                 hist_fn=lambda rng: np.array([40, 57]))
