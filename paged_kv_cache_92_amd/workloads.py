@@ -526,7 +526,7 @@ def mixed_step_f16(nd=64, n_chunks=2, chunk=512, lo=128, hi=2048, hist_lo=1024, 
                       max_context_len=max(hi, hist_hi + chunk), partition_size=partition_size)
 
 
-def sliding_window_gqa_bf16(S=64, lo=1024, hi=16384, window=4096, seed=7, partition_size=512, B=16):
+def sliding_window_gqa_bf16(S=64, lo=1024, hi=16384, window=4096, seed=7, partition_size=-1, B=16):
     """Mistral-7B-shaped sliding-window decode: 32 q / 8 kv heads, d 128, window 4096,
     L ~ U[lo, hi], bf16; blocks before each window released."""
     return make_sliding_decode(f"sliding_window_gqa_bf16_S{S}_W{window}", seed,
