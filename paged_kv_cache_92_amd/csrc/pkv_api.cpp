@@ -236,6 +236,15 @@ pkv_status prepare_prefill(const pkv::CacheDesc &c, void *out, int32_t out_dtype
   a->max_query_len = max_query_len;
   a->max_context_len = max_context_len;
   a->scale = scale;
+  int dev = 0, lds_max = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    return fail(PKV_ERR_HIP, "cannot query the device's LDS size");
+  const size_t lds = pkv::prefill_lds_bytes(c, *a);
+  if (lds > (size_t)lds_max)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "max_context_len %d needs %zu bytes of LDS per workgroup, the device has %d",
+                max_context_len, lds, lds_max);
   return PKV_OK;
 }
 

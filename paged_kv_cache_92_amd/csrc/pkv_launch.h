@@ -93,5 +93,8 @@ int decode_mfma_flat_grid(const CacheDesc &c, int G, int S);
 hipError_t launch_decode_reduce(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream);
 // Matrix-core causal chunked prefill (f16/bf16).
 hipError_t launch_prefill(const CacheDesc &c, const PrefillArgs &a, hipStream_t stream);
+// LDS one prefill workgroup takes for these arguments (static tiles + the
+// staged block table); SIZE_MAX if the kernel's attributes are unavailable.
+size_t prefill_lds_bytes(const CacheDesc &c, const PrefillArgs &a);
 
 }  // namespace pkv

@@ -8,11 +8,12 @@
 //
 // Workgroup = 8 waves = one (sequence, query head, 256-row query tile); wave
 // w owns 32 rows.  The key/value positions 0..last row's position are walked
-// in 32-token tiles gathered through the block table into LDS (the next
-// tile's global loads are in flight while the current one is computed):
+// in 64-token tiles gathered through the block table into LDS (the next
+// tile's global loads are in flight while the current one is computed); each
+// tile is two 32-token halves:
 //
-//   S^T (32 tokens x 32 rows) = K (32 x D) . Q^T (D x 32)     32x16 k-steps
-//   O^T (D x 32 rows)        += V^T (D x 32) . P^T (32 x 32)   2 k-steps/tile
+//   S^T (32 tokens x 32 rows) = K (32 x D) . Q^T (D x 32)     D/16 k-steps per half
+//   O^T (D x 32 rows)        += V^T (D x 32) . P^T (32 x 32)   2 k-steps per half
 //
 // with 32x32x16 MFMAs.  The key rows are fed to the first product in a
 // permuted order chosen so that each lane's 16 result rows are, per 16-token
@@ -20,6 +21,9 @@
 // then built from the lane's own registers and the A operand V^T is one
 // 16-byte LDS read from the dimension-major value tile.  Online softmax per
 // row, log2 domain.  Tiles entirely in a wave's future are skipped.
+#include <stdint.h>
+
+#include <algorithm>
 #include <type_traits>
 
 #include "pkv_device.h"
@@ -86,7 +90,9 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void prefill_kernel(
     const uint16_t *__restrict__ kpool, const uint16_t *__restrict__ vpool,
     const int32_t *__restrict__ query_start_loc, const int32_t *__restrict__ context_lens,
     const int32_t *__restrict__ block_tables, int64_t num_blocks, int Hkv, int Hq, int mbps,
-    int nqt, float scale_log2) {
+    int staged, int nqt, float scale_log2) {
+  // staged: block-table entries per sequence that fit the dynamic LDS
+  // (enough for max_context_len); positions beyond them are never walked.
   constexpr int KS = D / 16;          // k-steps of the score product
   constexpr int DT = D / 32;          // 32-dimension tiles of the output
   constexpr int KCH = kKT * D / 8;    // 16-byte chunks of a key tile
@@ -109,7 +115,7 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void prefill_kernel(
   const int qs = query_start_loc[s];
   const int qlen = query_start_loc[s + 1] - qs;
   if (qt * kQT >= qlen) return;
-  const int ctx = min(context_lens[s], mbps * BS);
+  const int ctx = min(context_lens[s], staged * BS);
   const int hist = ctx - qlen;
   if (hist < 0) return;
   const int hkv = hq / (Hq / Hkv);
@@ -138,7 +144,7 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void prefill_kernel(
   if (tid == 0) sOvf = 0;
   {
     const int32_t *bt = block_tables + (size_t)s * mbps;
-    const int nbt = min((ntiles * kKT + BS - 1) / BS, mbps);
+    const int nbt = min((ntiles * kKT + BS - 1) / BS, staged);
     for (int i = tid; i < nbt; i += kThreads) {
       const int32_t b = bt[i];
       sBT[i] = (b >= 0 && b < num_blocks) ? b : -1;
@@ -357,15 +363,37 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void prefill_kernel(
   }
 }
 
+// Block-table entries staged per workgroup: the table's width, or fewer when
+// max_context_len needs fewer.
+int staged_entries(const PrefillArgs &a, int B) {
+  return std::min(a.max_blocks_per_seq, (a.max_context_len + B - 1) / B);
+}
+
+template <typename E, int D, int BS>
+size_t lds_bytes_t(const PrefillArgs &a) {
+  hipFuncAttributes fa{};
+  if (hipFuncGetAttributes(&fa, (const void *)prefill_kernel<E, D, BS>) != hipSuccess) return SIZE_MAX;
+  return fa.sharedSizeBytes + sizeof(int) * (size_t)staged_entries(a, BS);
+}
+
+template <typename E>
+size_t lds_bytes_e(const CacheDesc &c, const PrefillArgs &a) {
+  if (c.D == 64 && c.B == 16) return lds_bytes_t<E, 64, 16>(a);
+  if (c.D == 64 && c.B == 32) return lds_bytes_t<E, 64, 32>(a);
+  if (c.D == 128 && c.B == 16) return lds_bytes_t<E, 128, 16>(a);
+  return lds_bytes_t<E, 128, 32>(a);
+}
+
 template <typename E, int D, int BS>
 void launch_t(const CacheDesc &c, const PrefillArgs &a, hipStream_t stream) {
   const int nqt = (a.max_query_len + kQT - 1) / kQT;
   const int64_t nwork = (int64_t)a.S * a.Hq * nqt;
-  const size_t lds = sizeof(int) * (size_t)a.max_blocks_per_seq;   // staged block table
+  const int staged = staged_entries(a, BS);
+  const size_t lds = sizeof(int) * (size_t)staged;   // staged block table
   hipLaunchKernelGGL((prefill_kernel<E, D, BS>), dim3((unsigned)nwork), dim3(kThreads), lds, stream,
                      a.out, (int)a.out_f32, (const uint16_t *)a.q, (const uint16_t *)c.k,
                      (const uint16_t *)c.v, a.query_start_loc, a.context_lens, a.block_tables,
-                     c.num_blocks, c.H, a.Hq, a.max_blocks_per_seq, nqt, a.scale * kLog2e);
+                     c.num_blocks, c.H, a.Hq, a.max_blocks_per_seq, staged, nqt, a.scale * kLog2e);
 }
 
 template <typename E>
@@ -377,6 +405,10 @@ void launch_e(const CacheDesc &c, const PrefillArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+size_t prefill_lds_bytes(const CacheDesc &c, const PrefillArgs &a) {
+  return c.dtype == 1 ? lds_bytes_e<F16>(c, a) : lds_bytes_e<BF16>(c, a);
+}
 
 hipError_t launch_prefill(const CacheDesc &c, const PrefillArgs &a, hipStream_t stream) {
   if (a.max_query_len == 0 || a.S == 0) return hipSuccess;
