@@ -22,6 +22,8 @@
 // 완전 해부" (hrletsgo.me), "부록".  Scores are kept in the log2 domain.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_launch.h"
 #include "pkv_plan.h"
@@ -80,9 +82,14 @@ __device__ __forceinline__ int token_of_row(int sb, int i) {
 // fp16 and a bf16 value): 4 codes of word w become two packed pairs.
 template <typename E>
 __device__ __forceinline__ u32x2 widen4(uint32_t w) {
-  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  return u32x2{Mfma<E>::pack2(lo[0], lo[1]), Mfma<E>::pack2(hi[0], hi[1])};
+  // One scaled conversion (scale 1, so exact) per code pair, bytes 0-1 then 2-3.
+  if constexpr (std::is_same<E, F16>::value) {
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, true))};
+  } else {
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true))};
+  }
 }
 
 // One work item: blocks [b0, b1) of sequence s for the G query heads of KV

@@ -459,35 +459,39 @@ def test_fp8_cache_decode_variants(dtype, d, B, G, part):
     _full_check(wl)
 
 
-def test_fp8_cache_reads_every_code_exactly():
+@pytest.mark.parametrize("dtype,G,B", [(W.F16, 1, 16), (W.F16, 2, 16), (W.BF16, 2, 16),
+                                       (W.F16, 4, 32), (W.BF16, 2, 32)])
+def test_fp8_cache_reads_every_code_exactly(dtype, G, B):
     # With v_scale 1 and the value row of a dominant key holding every finite
     # E4M3 value (negative zero aside: a sum cannot return it), the fp32
-    # output must be exactly those values: this pins the kernel's code ->
-    # value conversion and its byte order.
+    # output must be exactly those values: this pins the kernels' code ->
+    # value conversions (to fp32 on the wavefront path, to the 16-bit type on
+    # the matrix cores) and their byte order.
     codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF, 0x80)] + [0x38] * 3, np.uint8)
     vals = np.array([oracle.fp8_to_double(int(c)) for c in codes], np.float32)   # 256 = 2 heads x 128
     lens = [5, 40]
-    wl = W.make_decode("fp8codes", 21, lambda rng: lens, Hq=2, Hkv=2, d=128, B=16, dtype=W.F16,
-                       max_context_len=48, kv_dtype=W.FP8, k_scale=1.0, v_scale=1.0)
-    one = W.round_to(np.ones(1, np.float32), W.F16)[0]
+    wl = W.make_decode("fp8codes", 21, lambda rng: lens, Hq=2 * G, Hkv=2, d=128, B=B, dtype=dtype,
+                       max_context_len=64, kv_dtype=W.FP8, k_scale=1.0, v_scale=1.0)
+    one = W.round_to(np.ones(1, np.float32), dtype)[0]
     wl.q[:] = one
     hist, step = wl.setup[0], wl.step_scatter
     hist.key[:] = 0
     step.key[:] = 0
-    row = W.round_to(vals.reshape(2, 128), W.F16)          # exact: E4M3 values are fp16 values
+    row = W.round_to(vals.reshape(2, 128), dtype)          # exact: E4M3 values are fp16 and bf16 values
     cu = np.concatenate([[0], np.cumsum(np.array(lens) - 1)])
     picks = [2, 39]
     for s, j in enumerate(picks):
         tgt = step if j == lens[s] - 1 else hist
         i = s if tgt is step else cu[s] + j
-        tgt.key[i] = W.round_to(np.full((2, 128), 448.0, np.float32), W.F16)
+        tgt.key[i] = W.round_to(np.full((2, 128), 448.0, np.float32), dtype)
         tgt.value[i] = row
     dw = DeviceWorkload(wl)
     cache = new_cache(wl)
     dw.run(cache)
     o32 = bits_of(dw.attend(cache, out_dtype=torch.float32))
+    want = np.repeat(vals.reshape(2, 128), G, axis=0)      # query head hq reads KV head hq // G
     for s in range(len(lens)):
-        assert np.array_equal(o32[s].reshape(-1).view(np.uint32), vals.view(np.uint32)), s
+        assert np.array_equal(o32[s].view(np.uint32), want.view(np.uint32)), s
 
 
 def test_fp8_cache_llama13b_full():
