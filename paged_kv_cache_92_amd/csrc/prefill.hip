@@ -72,6 +72,11 @@ struct Mfma32<BF16> {
 #define PKV_PREFILL_CONV_V 1
 #endif
 
+// Operand reads issued a whole product ahead (1) or next to each product (0).
+#ifndef PKV_PREFILL_EARLY_LDS
+#define PKV_PREFILL_EARLY_LDS 1
+#endif
+
 // Row i of a 32-token score product (i = 8a + 4h + b) holds token perm(i) of
 // its half-tile.
 __device__ __forceinline__ int perm_row(int i) {
@@ -171,8 +176,7 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void prefill_kernel(
   constexpr int VDR = kThreads / 8;   // value dimensions per chunk round
   static_assert(KPT * KPR == D / KX, "whole key pieces per chunk round");
   const int ktok = (tid >> 2) & (kKT - 1), ksub = tid & 3, kpc = tid >> 8;
-  u32x4 kreg[KPT], vreg[VPT];
-  auto load_tile = [&](int t) {
+  auto load_tile = [&](int t, u32x4 (&kreg)[KPT], u32x4 (&vreg)[VPT]) {
     const int t0 = t * kKT;
     const bool full = t0 + kKT <= ctx;
     {
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void prefill_kernel(
   };
   // Staging of one tile into LDS buffer buf.  CONV: values re-encoded to fp16;
   // returns (through sOvf) whether any of them lay outside fp16's range.
-  auto store_tile = [&](auto conv, int buf) {
+  auto store_tile = [&](auto conv, int buf, const u32x4 (&kreg)[KPT], const u32x4 (&vreg)[VPT]) {
     constexpr bool CONV = decltype(conv)::value;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) *(u32x4 *)&sK[buf][ktok * KROW + KX * (kpc + KPR * i) + 8 * ksub] = kreg[i];
@@ -241,93 +245,124 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void prefill_kernel(
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
-    load_tile(0);
-    store_tile(conv, 0);
+    // One tile's scores, softmax update and P.V: tile t, staged in LDS buffer cur.
+    auto tile = [&](int t, int cur) {
+      constexpr int HALVES = kKT / 32;
+      f32x16 st[HALVES];  // raw scores q.k
+      const uint16_t *krp = &sK[cur][krow * KROW + 8 * h];
+#if PKV_PREFILL_EARLY_LDS
+      // All key operands of the tile are read before the first product, so
+      // the LDS latency is paid once rather than before every product; the
+      // fence keeps the compiler from sinking the reads back.
+      u32x4 kop[HALVES][KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int hf = 0; hf < HALVES; ++hf)
+          kop[hf][ks] = *(const u32x4 *)(krp + 32 * hf * KROW + 16 * ks);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int hf = 0; hf < HALVES; ++hf) st[hf] = Mfma32<E>::mma(kop[hf][0], qb[0], zero16);
+#pragma unroll
+      for (int ks = 1; ks < KS; ++ks)
+#pragma unroll
+        for (int hf = 0; hf < HALVES; ++hf)  // independent chains back to back
+          st[hf] = Mfma32<E>::mma(kop[hf][ks], qb[ks], st[hf]);
+      // The value operands of the whole tile, in flight during the softmax.
+      u32x4 vop[2 * HALVES][DT];
+#pragma unroll
+      for (int c = 0; c < 2 * HALVES; ++c)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          vop[c][dt] = *(const u32x4 *)&sV[cur][(32 * dt + j32) * VROW + 16 * c + 8 * h];
+      __builtin_amdgcn_sched_barrier(0);
+#else
+#pragma unroll
+      for (int hf = 0; hf < HALVES; ++hf)
+        st[hf] = Mfma32<E>::mma(*(const u32x4 *)(krp + 32 * hf * KROW), qb[0], zero16);
+#pragma unroll
+      for (int ks = 1; ks < KS; ++ks)
+#pragma unroll
+        for (int hf = 0; hf < HALVES; ++hf)  // independent chains back to back
+          st[hf] = Mfma32<E>::mma(*(const u32x4 *)(krp + 32 * hf * KROW + 16 * ks), qb[ks], st[hf]);
+#endif
+      // Item 4a+b of half hf is tile token 32*hf + perm(8a+4h+b).  Only a
+      // tile that crosses this wave's diagonal needs the causal mask (the
+      // hint keeps the compiler from turning the branch into selects that
+      // every tile would pay for).
+      if (__builtin_expect(t * kKT + kKT - 1 > wave_min_pos, 0)) {
+#pragma unroll
+        for (int hf = 0; hf < HALVES; ++hf)
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              const int pos = t * kKT + 32 * hf + 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
+              if (pos > qpos) st[hf][4 * a + b] = -INFINITY;
+            }
+      }
+      float mraw = -INFINITY;
+#pragma unroll
+      for (int hf = 0; hf < HALVES; ++hf)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, st[hf][i]);
+      mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+      const float mb = mraw * scale_log2;  // scale > 0: the max commutes with scaling
+      if (__any(mb > m + kRescaleLog2)) {
+        const float mnew = fmaxf(m, mb);
+        const float alpha = fast_exp2(m - mnew);  // 1 for rows that keep their reference
+        m = mnew;
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+      }
+      float psum = 0.f;
+#pragma unroll
+      for (int c = 0; c < 2 * HALVES; ++c) {
+        // This lane's 8 weights of k-step c (16 tokens) against the value
+        // rows 32dt + j32, tokens 16c + 8h .. +8 of the staged tile.
+        const int hf = c >> 1, c2 = c & 1;
+        float p[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          p[k] = fast_exp2(fmaf(st[hf][8 * c2 + k], scale_log2, -m));
+          psum += p[k];
+        }
+        u32x4 pb, pl;
+        if constexpr (PV::kSplitP) {
+          uint32_t hi[4], lo[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) split_bf16x2(p[2 * k], p[2 * k + 1], hi[k], lo[k]);
+          pb = u32x4{hi[0], hi[1], hi[2], hi[3]};
+          pl = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        } else {
+          pb = u32x4{PV::pack2(p[0], p[1]), PV::pack2(p[2], p[3]), PV::pack2(p[4], p[5]),
+                     PV::pack2(p[6], p[7])};
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#if PKV_PREFILL_EARLY_LDS
+          const u32x4 a = vop[c][dt];
+#else
+          const u32x4 a = *(const u32x4 *)&sV[cur][(32 * dt + j32) * VROW + 16 * c + 8 * h];
+#endif
+          acc[dt] = PV::mma(a, pb, acc[dt]);
+          if constexpr (PV::kSplitP) acc[dt] = PV::mma(a, pl, acc[dt]);
+        }
+      }
+      l += psum;
+    };
+    u32x4 kreg[KPT], vreg[VPT];
+    load_tile(0, kreg, vreg);
+    store_tile(conv, 0, kreg, vreg);
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
       const int cur = t & 1;
-      if (t + 1 < ntiles) load_tile(t + 1);  // in flight while this tile is computed
-      // One tile's scores, softmax update and P.V.
-      auto tile = [&]() {
-        constexpr int HALVES = kKT / 32;
-        f32x16 st[HALVES];  // raw scores q.k
-        const uint16_t *krp = &sK[cur][krow * KROW + 8 * h];
-#pragma unroll
-        for (int hf = 0; hf < HALVES; ++hf)
-          st[hf] = Mfma32<E>::mma(*(const u32x4 *)(krp + 32 * hf * KROW), qb[0], zero16);
-#pragma unroll
-        for (int ks = 1; ks < KS; ++ks)
-#pragma unroll
-          for (int hf = 0; hf < HALVES; ++hf)  // independent chains back to back
-            st[hf] = Mfma32<E>::mma(*(const u32x4 *)(krp + 32 * hf * KROW + 16 * ks), qb[ks], st[hf]);
-        // Item 4a+b of half hf is tile token 32*hf + perm(8a+4h+b).  Only a
-        // tile that crosses this wave's diagonal needs the causal mask (the
-        // hint keeps the compiler from turning the branch into selects that
-        // every tile would pay for).
-        if (__builtin_expect(t * kKT + kKT - 1 > wave_min_pos, 0)) {
-#pragma unroll
-          for (int hf = 0; hf < HALVES; ++hf)
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-              for (int b = 0; b < 4; ++b) {
-                const int pos = t * kKT + 32 * hf + 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
-                if (pos > qpos) st[hf][4 * a + b] = -INFINITY;
-              }
-        }
-        float mraw = -INFINITY;
-#pragma unroll
-        for (int hf = 0; hf < HALVES; ++hf)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, st[hf][i]);
-        mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
-        const float mb = mraw * scale_log2;  // scale > 0: the max commutes with scaling
-        if (__any(mb > m + kRescaleLog2)) {
-          const float mnew = fmaxf(m, mb);
-          const float alpha = fast_exp2(m - mnew);  // 1 for rows that keep their reference
-          m = mnew;
-          l *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-        }
-        float psum = 0.f;
-#pragma unroll
-        for (int c = 0; c < 2 * HALVES; ++c) {
-          // This lane's 8 weights of k-step c (16 tokens) against the value
-          // rows 32dt + j32, tokens 16c + 8h .. +8 of the staged tile.
-          const int hf = c >> 1, c2 = c & 1;
-          float p[8];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            p[k] = fast_exp2(fmaf(st[hf][8 * c2 + k], scale_log2, -m));
-            psum += p[k];
-          }
-          u32x4 pb, pl;
-          if constexpr (PV::kSplitP) {
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) split_bf16x2(p[2 * k], p[2 * k + 1], hi[k], lo[k]);
-            pb = u32x4{hi[0], hi[1], hi[2], hi[3]};
-            pl = u32x4{lo[0], lo[1], lo[2], lo[3]};
-          } else {
-            pb = u32x4{PV::pack2(p[0], p[1]), PV::pack2(p[2], p[3]), PV::pack2(p[4], p[5]),
-                       PV::pack2(p[6], p[7])};
-          }
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const u32x4 a = *(const u32x4 *)&sV[cur][(32 * dt + j32) * VROW + 16 * c + 8 * h];
-            acc[dt] = PV::mma(a, pb, acc[dt]);
-            if constexpr (PV::kSplitP) acc[dt] = PV::mma(a, pl, acc[dt]);
-          }
-        }
-        l += psum;
-      };
-      if (t * kKT <= wave_max_pos) {  // else entirely in this wave's future
-        tile();
-      }
+      if (t + 1 < ntiles) load_tile(t + 1, kreg, vreg);  // in flight while this tile is computed
+      if (t * kKT <= wave_max_pos) tile(t, cur);  // else entirely in this wave's future
       // The other buffer was last read in the previous iteration, before the
       // barrier that ended it; the barrier below publishes tile t+1.
-      if (t + 1 < ntiles) store_tile(conv, cur ^ 1);
+      if (t + 1 < ntiles) store_tile(conv, cur ^ 1, kreg, vreg);
       __syncthreads();
     }
     return !CONV || uniform(sOvf) == 0;
