@@ -176,7 +176,7 @@ def main():
                              "mixed", "sliding", "tiny"])
     ap.add_argument("--partition", type=int, default=None,
                     help="split-KV partition size in tokens (default: the workload's)")
-    ap.add_argument("--block-size", type=int, default=16, choices=[16, 32],
+    ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
                     help="block size of the llama13b workload (paging-overhead sweep)")
     ap.add_argument("--placement", default="shuffled", choices=["shuffled", "contiguous"],
                     help="physical block order of the llama13b workload (paging-overhead sweep)")

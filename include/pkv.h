@@ -44,16 +44,17 @@
  * A (block, head) tile of either pool is B*d contiguous elements.
  * q, out, key and value rows are [tokens][heads][head_dim], contiguous.
  * Query/output and cache share one dtype.  Supported: dtype f32/f16/bf16,
- * head_dim 64 or 128, block_size 16 or 32.  Base pointers must be 16-byte
- * aligned.
+ * head_dim 64 or 128, block_size 8, 16 or 32.  Base pointers must be
+ * 16-byte aligned.
  *
  * Device-side contract (not checked on the device; pkv_validate_host checks
  * it on host copies): block ids in the first ceil(L/B) table entries of a
  * sequence lie in [0, num_blocks); 1 <= L <= max_blocks_per_seq * block_size;
  * L <= max_context_len; no two tokens of one scatter share a slot.  The
  * kernels never touch memory outside the pool for a block id out of range
- * (that block is skipped) and clamp lengths to the table, so a broken
- * contract gives wrong numbers, not a fault.
+ * (that block is skipped, or with block_size 8 read as block 0 by decode)
+ * and clamp lengths to the table, so a broken contract gives wrong numbers,
+ * not a fault.
  * ----------------------------------------------------------------------------
  */
 #ifndef PKV_H
@@ -96,7 +97,7 @@ typedef struct {
   void *v_pool;          /* [num_blocks][num_kv_heads][head_dim][block_size] */
   int64_t num_blocks;
   int32_t num_kv_heads;
-  int32_t block_size;    /* 16 or 32 */
+  int32_t block_size;    /* 8, 16 or 32 */
   int32_t head_dim;      /* 64 or 128 */
   int32_t dtype;         /* pkv_dtype of the pools */
   int32_t model_dtype;   /* pkv_dtype of key/value inputs, queries and outputs */

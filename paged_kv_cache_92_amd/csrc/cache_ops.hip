@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict_
     sslot[tid] = sl;
   }
   __syncthreads();
-  const int lgB = B == 32 ? 5 : 4;   // block_size is 16 or 32
+  const int lgB = 31 - __builtin_clz(B);   // block_size is a power of two
   for (int c = tid; c < kTok * CH; c += blockDim.x) {
     const int tt = c / CH, ch = c % CH;
     const int64_t t = t0 + tt;
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void scatter_fp8_kernel(const uint16_t *__rest
     sslot[tid] = sl;
   }
   __syncthreads();
-  const int lgB = B == 32 ? 5 : 4;
+  const int lgB = 31 - __builtin_clz(B);
   auto quantise8 = [](const u32x4 &c, float scale) -> u32x2 {
     float f[8];
     unpack16<M>(c, f);

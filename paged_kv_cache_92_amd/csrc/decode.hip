@@ -34,6 +34,11 @@ namespace {
 
 constexpr int kWaves = 4;
 
+// Tokens one wave step covers: a whole block, or for 8-token blocks a pair of
+// consecutive logical blocks (16 tokens), so the wave mapping below always
+// sees groups of 16 tokens.
+constexpr int group_tokens(int BS) { return BS == 8 ? 16 : BS; }
+
 template <typename E, int D, int BS>
 struct ValuCfg {
   static constexpr int EB = E::kBytes;
@@ -66,13 +71,16 @@ struct ValuLds {
 // scale multiplies the merged sums).
 template <typename E, typename Q, int D, int BS>
 __device__ __forceinline__ void valu_item(
-    ValuLds<E, D, BS> &sh, int s, int hq, int b0, int b1, Dest dest, void *__restrict__ out,
+    ValuLds<E, D, group_tokens(BS)> &sh, int s, int hq, int b0, int b1, Dest dest,
+    void *__restrict__ out,
     int out_f32, const typename Q::storage *__restrict__ q,
     const typename E::storage *__restrict__ kpool, const typename E::storage *__restrict__ vpool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
     int64_t num_blocks, int Hkv, int Hq, int mbps, int window, float scale_log2, float v_scale,
     float *__restrict__ ws_ml, float *__restrict__ ws_acc) {
-  using C = ValuCfg<E, D, BS>;
+  constexpr bool kPair = BS == 8;           // two 8-token blocks per step
+  constexpr int GB = group_tokens(BS);
+  using C = ValuCfg<E, D, GB>;
   using T = typename E::storage;
   constexpr bool kFP8 = E::kBytes == 1;
   const Span sp = seq_span(context_lens, s, mbps * BS, window);
@@ -133,26 +141,55 @@ __device__ __forceinline__ void valu_item(
   for (int i = 0; i < C::VL; ++i) acc[i] = 0.f;
 
   const int32_t *bt = block_tables + (size_t)s * mbps;
-  for (int b = w; b < nblk; b += kWaves) {
+  constexpr int STEP = kPair ? 2 : 1;
+  for (int b = STEP * w; b < nblk; b += STEP * kWaves) {
     const int lb = blk0 + b;
-    const int64_t phys = uniform(bt[lb]);
-    if (phys < 0 || phys >= num_blocks) continue;
-    const T *ktile = kpool + ((size_t)phys * Hkv + hkv) * (BS * D);
-    const T *vtile = vpool + ((size_t)phys * Hkv + hkv) * (D * BS);
+    int64_t phys = uniform(bt[lb]);
     u32x4 kr[C::KL];
     u32x4 vr[C::VL];
+    if constexpr (!kPair) {
+      if (phys < 0 || phys >= num_blocks) continue;
+      const T *ktile = kpool + ((size_t)phys * Hkv + hkv) * (BS * D);
+      const T *vtile = vpool + ((size_t)phys * Hkv + hkv) * (D * BS);
 #pragma unroll
-    for (int c = 0; c < C::NC; ++c)
+      for (int c = 0; c < C::NC; ++c)
 #pragma unroll
-      for (int r = 0; r < C::TG; ++r)
-        kr[c * C::TG + r] = load16_stream(ktile + (c * BS + 16 * r + kt) * C::X + kq * C::VEC);
+        for (int r = 0; r < C::TG; ++r)
+          kr[c * C::TG + r] = load16_stream(ktile + (c * BS + 16 * r + kt) * C::X + kq * C::VEC);
 #pragma unroll
-    for (int i = 0; i < C::VL; ++i) vr[i] = load16_stream(vtile + (size_t)(kWave * i + lane) * C::VEC);
+      for (int i = 0; i < C::VL; ++i) vr[i] = load16_stream(vtile + (size_t)(kWave * i + lane) * C::VEC);
+    } else {
+      // Blocks lb and lb+1 (the second only if the item covers it; past the
+      // item its tokens are masked and block lb is read in its place).  An
+      // out-of-range id reads block 0 instead of faulting.
+      int64_t phys2 = b + 1 < nblk ? uniform(bt[lb + 1]) : phys;
+      if (phys < 0 || phys >= num_blocks) phys = 0;
+      if (phys2 < 0 || phys2 >= num_blocks) phys2 = 0;
+      const T *kt0 = kpool + ((size_t)phys * Hkv + hkv) * (BS * D);
+      const T *kt1 = kpool + ((size_t)phys2 * Hkv + hkv) * (BS * D);
+      const T *vt0 = vpool + ((size_t)phys * Hkv + hkv) * (D * BS);
+      const T *vt1 = vpool + ((size_t)phys2 * Hkv + hkv) * (D * BS);
+      const T *kmine = kt < 8 ? kt0 : kt1;   // token kt of the 16 lies in block kt / 8
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) kr[c] = load16_stream(kmine + (c * BS + (kt & 7)) * C::X + kq * C::VEC);
+#pragma unroll
+      for (int i = 0; i < C::VL; ++i) {
+        const int idx = kWave * i + lane;           // chunk: dimension idx / CPR, tokens VEC*(idx % CPR)..
+        const int dim = idx / C::CPR, tok = (idx % C::CPR) * C::VEC;
+        if constexpr (C::VEC <= 8) {
+          vr[i] = load16_stream((tok < 8 ? vt0 : vt1) + dim * BS + (tok & 7));
+        } else {
+          // 16 codes of one dimension: 8 from each block's row.
+          const u32x2 a = load8_stream(vt0 + dim * BS), c2 = load8_stream(vt1 + dim * BS);
+          vr[i] = u32x4{a[0], a[1], c2[0], c2[1]};
+        }
+      }
+    }
 
     const int tbase = lb * BS;
-    // Only the last block can end past the length, only the first start
+    // Only the last step can end past the length, only the first start
     // before the window.
-    const bool partial = tbase + BS > tok1 || tbase < lo;
+    const bool partial = tbase + GB > tok1 || tbase < lo;
     float sc[C::TG];
 #pragma unroll
     for (int r = 0; r < C::TG; ++r) {
@@ -252,7 +289,7 @@ __device__ __forceinline__ void valu_item(
 // loads plus the query slice fit that budget without spills; other variants
 // keep the compiler's choice.
 template <typename E, typename Q, int D, int BS, int SCHED>
-__global__ __launch_bounds__(256, (SCHED == kSchedGrid && E::kBytes >= 2 && ValuCfg<E, D, BS>::kLoadRegs + 4 * ValuCfg<E, D, BS>::NC <= 24) ? 8 : 1) void
+__global__ __launch_bounds__(256, (SCHED == kSchedGrid && E::kBytes >= 2 && ValuCfg<E, D, group_tokens(BS)>::kLoadRegs + 4 * ValuCfg<E, D, group_tokens(BS)>::NC <= 24) ? 8 : 1) void
 decode_valu_kernel(
     void *__restrict__ out, int out_f32, const typename Q::storage *__restrict__ q,
     const typename E::storage *__restrict__ kpool, const typename E::storage *__restrict__ vpool,
@@ -260,7 +297,7 @@ decode_valu_kernel(
     int64_t num_blocks, int Hkv, int Hq, int S, int mbps, int window, float scale_log2,
     float v_scale, int part_tokens, int nparts, float *__restrict__ ws_ml,
     float *__restrict__ ws_acc, int *__restrict__ ws_hdr) {
-  __shared__ ValuLds<E, D, BS> sh;
+  __shared__ ValuLds<E, D, group_tokens(BS)> sh;
   extern __shared__ int plan[];
   __shared__ int scan[16];
   run_schedule<SCHED>(
@@ -362,7 +399,9 @@ void launch_valu_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) 
 
 template <typename E, typename Q = E>
 void launch_valu_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
-  if (c.D == 64 && c.B == 16) launch_valu_t<E, Q, 64, 16>(c, a, stream);
+  if (c.D == 64 && c.B == 8) launch_valu_t<E, Q, 64, 8>(c, a, stream);
+  else if (c.D == 128 && c.B == 8) launch_valu_t<E, Q, 128, 8>(c, a, stream);
+  else if (c.D == 64 && c.B == 16) launch_valu_t<E, Q, 64, 16>(c, a, stream);
   else if (c.D == 64 && c.B == 32) launch_valu_t<E, Q, 64, 32>(c, a, stream);
   else if (c.D == 128 && c.B == 16) launch_valu_t<E, Q, 128, 16>(c, a, stream);
   else launch_valu_t<E, Q, 128, 32>(c, a, stream);
@@ -376,6 +415,8 @@ int flat_grid_t(int S) {
 
 template <typename E, typename Q = E>
 int flat_grid_e(const CacheDesc &c, int S) {
+  if (c.D == 64 && c.B == 8) return flat_grid_t<E, Q, 64, 8>(S);
+  if (c.D == 128 && c.B == 8) return flat_grid_t<E, Q, 128, 8>(S);
   if (c.D == 64 && c.B == 16) return flat_grid_t<E, Q, 64, 16>(S);
   if (c.D == 64 && c.B == 32) return flat_grid_t<E, Q, 64, 32>(S);
   if (c.D == 128 && c.B == 16) return flat_grid_t<E, Q, 128, 16>(S);

@@ -110,11 +110,14 @@ __device__ __forceinline__ void mfma_item(
   constexpr bool kFP8 = KV::kBytes == 1;
   constexpr int KS = D / 32;    // k-steps of the score product
   constexpr int NT = D / 16;    // 16-dimension tiles of the output
-  constexpr int SUB = BS / 16;  // 16-token sub-tiles per block
+  // 8-token blocks are taken two at a time: a step always covers GB tokens.
+  constexpr bool kPair = BS == 8;
+  constexpr int GB = kPair ? 16 : BS;
+  constexpr int SUB = GB / 16;  // 16-token sub-tiles per step
   // 32-token blocks: the two sub-tiles' score rows are interleaved so each
   // lane ends up with 8 consecutive tokens, and P.V runs as 16x16x32 products
   // over 16-byte V^T operands.
-  constexpr bool kWide = BS == 32;
+  constexpr bool kWide = GB == 32;
   const Span sp = seq_span(context_lens, s, mbps * BS, window);
   const int lo = sp.lo;                      // first attended position
   const int tok0 = max(b0 * BS, lo);
@@ -157,12 +160,36 @@ __device__ __forceinline__ void mfma_item(
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int32_t *bt = block_tables + (size_t)s * mbps;
-  for (int b = w; b < nblk; b += kWaves) {
+  constexpr int STEP = kPair ? 2 : 1;
+  using TS = typename KV::storage;
+  for (int b = STEP * w; b < nblk; b += STEP * kWaves) {
     const int lb = blk0 + b;
-    const int64_t phys = uniform(bt[lb]);
-    if (phys < 0 || phys >= num_blocks) continue;
-    const typename KV::storage *kt = kpool + ((size_t)phys * Hkv + hkv) * (BS * D);
-    const typename KV::storage *vt = vpool + ((size_t)phys * Hkv + hkv) * (D * BS);
+    int64_t phys = uniform(bt[lb]);
+    // Key and value tiles this lane reads: one block's, or for 8-token blocks
+    // those of block lb + t/8 for the lane's token t of the 16 (key row n16,
+    // value tokens 4*g4..+4).  The second block of a pair is read only if the
+    // item covers it (past the item its tokens are masked and block lb is
+    // read in its place); there an out-of-range id reads block 0 instead of
+    // faulting, while a single block with such an id is skipped.
+    const TS *kt, *vt;
+    int krow;   // key row of this lane within its tile
+    int vtok;   // first value token of this lane within its tile (non-wide)
+    if constexpr (!kPair) {
+      if (phys < 0 || phys >= num_blocks) continue;
+      kt = kpool + ((size_t)phys * Hkv + hkv) * (BS * D);
+      vt = vpool + ((size_t)phys * Hkv + hkv) * (D * BS);
+      krow = 0;
+      vtok = 0;
+    } else {
+      int64_t phys2 = b + 1 < nblk ? uniform(bt[lb + 1]) : phys;
+      if (phys < 0 || phys >= num_blocks) phys = 0;
+      if (phys2 < 0 || phys2 >= num_blocks) phys2 = 0;
+      const int64_t pk = n16 < 8 ? phys : phys2, pv = g4 < 2 ? phys : phys2;
+      kt = kpool + ((size_t)pk * Hkv + hkv) * (BS * D);
+      vt = vpool + ((size_t)pv * Hkv + hkv) * (D * BS);
+      krow = (n16 & 7) - n16;        // token_of_row gives n16; the tile holds it at n16 % 8
+      vtok = 4 * (g4 & 1) - 4 * g4;  // tokens 4*g4.. sit at 4*(g4 % 2).. of their tile
+    }
     u32x4 ka[SUB][KS];
     if constexpr (kFP8) {
       // One 16-byte load = 16 dimensions (64-byte piece c, quarter g4) of a
@@ -171,7 +198,7 @@ __device__ __forceinline__ void mfma_item(
       for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
         for (int c = 0; c < KS / 2; ++c) {
-          const u32x4 raw = load16_stream(kt + (c * BS + token_of_row<BS>(sb, n16)) * 64 + 16 * g4);
+          const u32x4 raw = load16_stream(kt + (c * BS + token_of_row<GB>(sb, n16) + krow) * 64 + 16 * g4);
           const u32x2 a0 = widen4<E>(raw[0]), a1 = widen4<E>(raw[1]);
           const u32x2 a2 = widen4<E>(raw[2]), a3 = widen4<E>(raw[3]);
           ka[sb][2 * c] = u32x4{a0[0], a0[1], a1[0], a1[1]};
@@ -182,7 +209,7 @@ __device__ __forceinline__ void mfma_item(
       for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          ka[sb][ks] = load16_stream(kt + (ks * BS + token_of_row<BS>(sb, n16)) * 32 + 8 * g4);
+          ka[sb][ks] = load16_stream(kt + (ks * BS + token_of_row<GB>(sb, n16) + krow) * 32 + 8 * g4);
     }
     // V^T operand: dimension row 16*nt + n16; tokens 8*g4 .. +8 (wide) or
     // 16*sb + 4*g4 .. +4 of sub-tile sb.
@@ -205,16 +232,16 @@ __device__ __forceinline__ void mfma_item(
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           if constexpr (kFP8)
-            va[sb][nt] = widen4<E>(load4_stream(vt + (16 * nt + n16) * BS + 16 * sb + 4 * g4));
+            va[sb][nt] = widen4<E>(load4_stream(vt + (16 * nt + n16) * BS + 16 * sb + 4 * g4 + vtok));
           else
-            va[sb][nt] = load8_stream(vt + (16 * nt + n16) * BS + 16 * sb + 4 * g4);
+            va[sb][nt] = load8_stream(vt + (16 * nt + n16) * BS + 16 * sb + 4 * g4 + vtok);
         }
     }
 
     const int tbase = lb * BS;
     // Only the last block can end past the length, only the first start
     // before the window.
-    const bool partial = tbase + BS > tok1 || tbase < lo;
+    const bool partial = tbase + GB > tok1 || tbase < lo;
     const unsigned span = (unsigned)(tok1 - lo);
     auto keep = [&](int t) { return (unsigned)(t - lo) < span; };
     f32x4 st[SUB];
@@ -226,7 +253,7 @@ __device__ __forceinline__ void mfma_item(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float v = x[j] * scale_log2;
-        if (partial && !keep(tbase + token_of_row<BS>(sb, 4 * g4 + j))) v = -INFINITY;
+        if (partial && !keep(tbase + token_of_row<GB>(sb, 4 * g4 + j))) v = -INFINITY;
         x[j] = v;
       }
       st[sb] = x;
@@ -416,7 +443,9 @@ void launch_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
 
 template <typename E, typename KV = E>
 void launch_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
-  if (c.D == 64 && c.B == 16) launch_t<E, KV, 64, 16>(c, a, stream);
+  if (c.D == 64 && c.B == 8) launch_t<E, KV, 64, 8>(c, a, stream);
+  else if (c.D == 128 && c.B == 8) launch_t<E, KV, 128, 8>(c, a, stream);
+  else if (c.D == 64 && c.B == 16) launch_t<E, KV, 64, 16>(c, a, stream);
   else if (c.D == 64 && c.B == 32) launch_t<E, KV, 64, 32>(c, a, stream);
   else if (c.D == 128 && c.B == 16) launch_t<E, KV, 128, 16>(c, a, stream);
   else launch_t<E, KV, 128, 32>(c, a, stream);
@@ -430,6 +459,8 @@ int flat_grid_t(int G, int S) {
 
 template <typename E, typename KV = E>
 int flat_grid_e(const CacheDesc &c, int G, int S) {
+  if (c.D == 64 && c.B == 8) return flat_grid_t<E, KV, 64, 8>(G, S);
+  if (c.D == 128 && c.B == 8) return flat_grid_t<E, KV, 128, 8>(G, S);
   if (c.D == 64 && c.B == 16) return flat_grid_t<E, KV, 64, 16>(G, S);
   if (c.D == 64 && c.B == 32) return flat_grid_t<E, KV, 64, 32>(G, S);
   if (c.D == 128 && c.B == 16) return flat_grid_t<E, KV, 128, 16>(G, S);

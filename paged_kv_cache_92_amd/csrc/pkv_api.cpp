@@ -40,8 +40,8 @@ pkv_status check_cache(const pkv_cache *c, pkv::CacheDesc *d) {
     return fail(PKV_ERR_INVALID, "k_pool/v_pool must be 16-byte aligned");
   if (c->num_blocks <= 0) return fail(PKV_ERR_INVALID, "num_blocks must be > 0");
   if (c->num_kv_heads <= 0) return fail(PKV_ERR_INVALID, "num_kv_heads must be > 0");
-  if (c->block_size != 16 && c->block_size != 32)
-    return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (16 or 32)", c->block_size);
+  if (c->block_size != 8 && c->block_size != 16 && c->block_size != 32)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (8, 16 or 32)", c->block_size);
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", c->head_dim);
   if (c->dtype != PKV_F32 && c->dtype != PKV_F16 && c->dtype != PKV_BF16 && c->dtype != PKV_FP8_E4M3)

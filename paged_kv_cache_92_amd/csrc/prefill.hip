@@ -413,6 +413,8 @@ size_t lds_bytes_t(const PrefillArgs &a) {
 
 template <typename E>
 size_t lds_bytes_e(const CacheDesc &c, const PrefillArgs &a) {
+  if (c.D == 64 && c.B == 8) return lds_bytes_t<E, 64, 8>(a);
+  if (c.D == 128 && c.B == 8) return lds_bytes_t<E, 128, 8>(a);
   if (c.D == 64 && c.B == 16) return lds_bytes_t<E, 64, 16>(a);
   if (c.D == 64 && c.B == 32) return lds_bytes_t<E, 64, 32>(a);
   if (c.D == 128 && c.B == 16) return lds_bytes_t<E, 128, 16>(a);
@@ -433,7 +435,9 @@ void launch_t(const CacheDesc &c, const PrefillArgs &a, hipStream_t stream) {
 
 template <typename E>
 void launch_e(const CacheDesc &c, const PrefillArgs &a, hipStream_t stream) {
-  if (c.D == 64 && c.B == 16) launch_t<E, 64, 16>(c, a, stream);
+  if (c.D == 64 && c.B == 8) launch_t<E, 64, 8>(c, a, stream);
+  else if (c.D == 128 && c.B == 8) launch_t<E, 128, 8>(c, a, stream);
+  else if (c.D == 64 && c.B == 16) launch_t<E, 64, 16>(c, a, stream);
   else if (c.D == 64 && c.B == 32) launch_t<E, 64, 32>(c, a, stream);
   else if (c.D == 128 && c.B == 16) launch_t<E, 128, 16>(c, a, stream);
   else launch_t<E, 128, 32>(c, a, stream);

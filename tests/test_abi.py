@@ -47,7 +47,7 @@ FAKE = ctypes.c_void_p(0x30000)   # never dereferenced: every call below fails v
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(k_pool=None), 1), (dict(block_size=8), 2), (dict(head_dim=96), 2), (dict(dtype=7), 1),
+    (dict(k_pool=None), 1), (dict(block_size=4), 2), (dict(head_dim=96), 2), (dict(dtype=7), 1),
     (dict(num_blocks=0), 1), (dict(k_pool=0x10008), 1),
     (dict(dtype=1, model_dtype=2), 1),                       # 16-bit cache: model dtype = dtype
     (dict(dtype=3, model_dtype=3), 1), (dict(dtype=3, model_dtype=0), 1),   # 8-bit: f16/bf16 model

@@ -29,7 +29,7 @@ def _mixed(dtype, d, B, G, seed=91, decode_lens=DECODE_LENS, hist=CHUNK_HIST, ch
 
 
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16], ids=["f16", "bf16"])
-@pytest.mark.parametrize("d,B,G", [(128, 16, 1), (128, 32, 4), (64, 16, 2), (64, 32, 1)])
+@pytest.mark.parametrize("d,B,G", [(128, 16, 1), (128, 32, 4), (64, 16, 2), (64, 32, 1), (128, 8, 2)])
 @pytest.mark.parametrize("part", [0, 64, -1], ids=["whole", "p64", "auto"])
 def test_mixed_step_variants(dtype, d, B, G, part):
     wl = _mixed(dtype, d, B, G, partition_size=part)

@@ -72,7 +72,7 @@ RAGGED = [1, 15, 16, 17, 31, 32, 33, 100, 255, 256, 257]
 
 @pytest.mark.parametrize("dtype", [W.F32, W.F16, W.BF16], ids=["f32", "f16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("B", [16, 32])
+@pytest.mark.parametrize("B", [8, 16, 32])
 @pytest.mark.parametrize("G", [1, 4])
 @pytest.mark.parametrize("part", [0, 64, -1], ids=["whole", "p64", "auto"])
 def test_decode_variants(dtype, d, B, G, part):
@@ -209,7 +209,8 @@ def test_negative_slots_are_skipped_and_copy_blocks_copies():
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16], ids=["f16", "bf16"])
-@pytest.mark.parametrize("d,B,G", [(128, 16, 1), (128, 32, 4), (64, 16, 2), (64, 32, 1)])
+@pytest.mark.parametrize("d,B,G", [(128, 16, 1), (128, 32, 4), (64, 16, 2), (64, 32, 1), (128, 8, 2),
+                                    (64, 8, 1)])
 def test_prefill_variants(dtype, d, B, G):
     # Ragged chunks (1 row up to more than one 128-row tile), histories from 0.
     hist = np.array([0, 5, 16, 33, 200, 7])
@@ -339,6 +340,13 @@ def test_llama13b_decode_full(part):
     print(f"13B decode partition {part}: worst err/bound {worst:.3f}")
 
 
+def test_llama13b_decode_block8_full():
+    # 8-token blocks: each wave step takes two consecutive logical blocks.
+    wl = W.llama13b_decode_f16(B=8)
+    worst, *_ = _sampled_check(wl, _decode_rows(wl, 12, 9))
+    print(f"13B B=8 worst err/bound {worst:.3f}")
+
+
 def test_long_context_split_full():
     wl = W.long_context_split_f16()
     worst, out, cache, dw = _sampled_check(wl, _decode_rows(wl, 6, 2))
@@ -349,7 +357,7 @@ def test_long_context_split_full():
     print(f"split decode worst err/bound {worst:.3f}")
 
 
-@pytest.mark.parametrize("B,part", [(16, 1024), (32, 1024), (16, -1), (32, -1)])
+@pytest.mark.parametrize("B,part", [(16, 1024), (32, 1024), (16, -1), (32, -1), (8, 1024), (8, -1)])
 def test_gqa_decode_full(B, part):
     wl = W.gqa_decode_bf16(B=B)
     worst, *_ = _sampled_check(wl, _decode_rows(wl, 14, 3), partition_size=part)
@@ -447,7 +455,7 @@ def test_pool_beyond_4_gib_addresses_correctly(dtype, G):
 
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16], ids=["f16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("B", [16, 32])
+@pytest.mark.parametrize("B", [8, 16, 32])
 @pytest.mark.parametrize("G", [1, 4])
 @pytest.mark.parametrize("part", [0, 64, -1], ids=["whole", "p64", "auto"])
 def test_fp8_cache_decode_variants(dtype, d, B, G, part):
@@ -460,7 +468,8 @@ def test_fp8_cache_decode_variants(dtype, d, B, G, part):
 
 
 @pytest.mark.parametrize("dtype,G,B", [(W.F16, 1, 16), (W.F16, 2, 16), (W.BF16, 2, 16),
-                                       (W.F16, 4, 32), (W.BF16, 2, 32)])
+                                       (W.F16, 4, 32), (W.BF16, 2, 32), (W.F16, 1, 8),
+                                       (W.BF16, 4, 8)])
 def test_fp8_cache_reads_every_code_exactly(dtype, G, B):
     # With v_scale 1 and the value row of a dominant key holding every finite
     # E4M3 value (negative zero aside: a sum cannot return it), the fp32

@@ -29,7 +29,8 @@ def _sliding(dtype, d, B, G, window=40, lens=LENS, partition_size=0, seed=51, ch
 
 
 @pytest.mark.parametrize("dtype", [W.F32, W.F16, W.BF16], ids=["f32", "f16", "bf16"])
-@pytest.mark.parametrize("d,B,G", [(128, 16, 1), (128, 32, 4), (64, 16, 2), (64, 32, 1)])
+@pytest.mark.parametrize("d,B,G", [(128, 16, 1), (128, 32, 4), (64, 16, 2), (64, 32, 1), (128, 8, 4),
+                                   (64, 8, 1)])
 @pytest.mark.parametrize("part", [0, 32, -1], ids=["whole", "p32", "auto"])
 def test_sliding_window_variants(dtype, d, B, G, part):
     wl = _sliding(dtype, d, B, G, partition_size=part)
