@@ -78,8 +78,8 @@ __device__ __forceinline__ void valu_item(
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
     int64_t num_blocks, int Hkv, int Hq, int mbps, int window, float scale_log2, float v_scale,
     float *__restrict__ ws_ml, float *__restrict__ ws_acc) {
-  constexpr bool kPair = BS == 8;           // two 8-token blocks per step
   constexpr int GB = group_tokens(BS);
+  constexpr bool kPair = GB == 2 * BS;      // two blocks per step
   using C = ValuCfg<E, D, GB>;
   using T = typename E::storage;
   constexpr bool kFP8 = E::kBytes == 1;
@@ -169,15 +169,21 @@ __device__ __forceinline__ void valu_item(
       const T *kt1 = kpool + ((size_t)phys2 * Hkv + hkv) * (BS * D);
       const T *vt0 = vpool + ((size_t)phys * Hkv + hkv) * (D * BS);
       const T *vt1 = vpool + ((size_t)phys2 * Hkv + hkv) * (D * BS);
-      const T *kmine = kt < 8 ? kt0 : kt1;   // token kt of the 16 lies in block kt / 8
+      // Token t of the step lies in block t / BS of the pair.
 #pragma unroll
-      for (int c = 0; c < C::NC; ++c) kr[c] = load16_stream(kmine + (c * BS + (kt & 7)) * C::X + kq * C::VEC);
+      for (int c = 0; c < C::NC; ++c)
+#pragma unroll
+        for (int r = 0; r < C::TG; ++r) {
+          const int t = 16 * r + kt;
+          kr[c * C::TG + r] =
+              load16_stream((t < BS ? kt0 : kt1) + (c * BS + t % BS) * C::X + kq * C::VEC);
+        }
 #pragma unroll
       for (int i = 0; i < C::VL; ++i) {
         const int idx = kWave * i + lane;           // chunk: dimension idx / CPR, tokens VEC*(idx % CPR)..
         const int dim = idx / C::CPR, tok = (idx % C::CPR) * C::VEC;
-        if constexpr (C::VEC <= 8) {
-          vr[i] = load16_stream((tok < 8 ? vt0 : vt1) + dim * BS + (tok & 7));
+        if constexpr (C::VEC <= BS) {
+          vr[i] = load16_stream((tok < BS ? vt0 : vt1) + dim * BS + tok % BS);
         } else {
           // 16 codes of one dimension: 8 from each block's row.
           const u32x2 a = load8_stream(vt0 + dim * BS), c2 = load8_stream(vt1 + dim * BS);

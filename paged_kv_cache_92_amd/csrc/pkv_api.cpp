@@ -200,6 +200,23 @@ pkv_status launch_decode(const pkv::CacheDesc &c, const pkv::DecodeArgs &a, cons
   return PKV_OK;
 }
 
+// LDS one workgroup may allocate on the current device (0 if unknown),
+// asked once per device.
+int device_lds_bytes() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int bytes = 0;
+  if (hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    return 0;
+  cache[dev] = bytes;
+  return bytes;
+}
+
 // Validates a prefill call over num_seqs > 0 sequences and fills `a`.
 pkv_status prepare_prefill(const pkv::CacheDesc &c, void *out, int32_t out_dtype, const void *q,
                            int32_t num_q_heads, const int32_t *query_start_loc,
@@ -236,10 +253,8 @@ pkv_status prepare_prefill(const pkv::CacheDesc &c, void *out, int32_t out_dtype
   a->max_query_len = max_query_len;
   a->max_context_len = max_context_len;
   a->scale = scale;
-  int dev = 0, lds_max = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-    return fail(PKV_ERR_HIP, "cannot query the device's LDS size");
+  const int lds_max = device_lds_bytes();
+  if (lds_max <= 0) return fail(PKV_ERR_HIP, "cannot query the device's LDS size");
   const size_t lds = pkv::prefill_lds_bytes(c, *a);
   if (lds > (size_t)lds_max)
     return fail(PKV_ERR_UNSUPPORTED,

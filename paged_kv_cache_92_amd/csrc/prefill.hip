@@ -406,9 +406,15 @@ int staged_entries(const PrefillArgs &a, int B) {
 
 template <typename E, int D, int BS>
 size_t lds_bytes_t(const PrefillArgs &a) {
-  hipFuncAttributes fa{};
-  if (hipFuncGetAttributes(&fa, (const void *)prefill_kernel<E, D, BS>) != hipSuccess) return SIZE_MAX;
-  return fa.sharedSizeBytes + sizeof(int) * (size_t)staged_entries(a, BS);
+  // The kernel's static LDS is a property of its code: asked once.
+  static const size_t static_bytes = [] {
+    hipFuncAttributes fa{};
+    return hipFuncGetAttributes(&fa, (const void *)prefill_kernel<E, D, BS>) == hipSuccess
+               ? fa.sharedSizeBytes
+               : SIZE_MAX;
+  }();
+  if (static_bytes == SIZE_MAX) return SIZE_MAX;
+  return static_bytes + sizeof(int) * (size_t)staged_entries(a, BS);
 }
 
 template <typename E>
