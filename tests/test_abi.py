@@ -96,6 +96,27 @@ def test_prefill_argument_checks():
     assert _prefill(_desc(), S=0) == 0
 
 
+def test_window_and_mixed_argument_checks():
+    lib = pkv.lib()
+    d = _desc()
+    win = lambda w, **kw: lib.pkv_paged_decode_window(  # noqa: E731
+        ctypes.byref(d), kw.get("out", FAKE), 1, FAKE, 2, FAKE, 4, FAKE, kw.get("S", 2), 64, w, 0.125,
+        0, None, 0, None)
+    assert win(-1) == 1                               # negative window
+    assert "sliding_window" in lib.pkv_last_error().decode()
+    assert win(16, out=None) == 1                     # null pointer
+    assert win(16, out=None, S=0) == 0                # zero sequences: no-op
+    mixed = lambda S, nd, maxq=16, qsl=FAKE, dd=d: lib.pkv_paged_mixed(  # noqa: E731
+        ctypes.byref(dd), FAKE, 1, FAKE, 2, qsl, FAKE, FAKE, 4, S, nd, maxq, 64, 0.125, 0, None, 0,
+        None)
+    assert mixed(2, 3) == 1                           # more decode sequences than sequences
+    assert mixed(-1, 0) == 1
+    assert mixed(3, 1, qsl=None) == 1                 # chunk sequences need query_start_loc
+    assert mixed(3, 1, maxq=65) == 1                  # chunk longer than max_context_len
+    assert mixed(2, 1, dd=_desc(dtype=3, model_dtype=1)) == 2   # chunks over an 8-bit cache
+    assert mixed(0, 0) == 0                           # nothing to do
+
+
 def test_empty_scatter_and_copy_are_no_ops():
     lib = pkv.lib()
     d = _desc()
