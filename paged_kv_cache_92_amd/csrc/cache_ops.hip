@@ -35,6 +35,32 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict_
   const int h = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * kTok;
   const int tid = threadIdx.x;
+  // The rows' loads do not depend on the slots: they are issued together with
+  // the slot loads, and only the stores wait for the barrier.
+  constexpr int NCH = kTok * CH;           // 16-byte chunks of the 16 rows
+  constexpr int PER = (NCH + 255) / 256;   // per thread (256 threads)
+  u32x4 kc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = tid + 256 * i;
+    const int tt = c / CH, ch = c % CH;
+    const int64_t t = t0 + tt;
+    if (c >= NCH || t >= T) continue;
+    const size_t src = ((size_t)t * H + h) * D + (size_t)ch * VEC;
+    const u32x4 vc = load16(value + src * EB);
+    kc[i] = load16(key + src * EB);
+    // value chunk -> LDS, dimension-major
+    if constexpr (EB == 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sv[ch * VEC + k][tt] = vc[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        sv[ch * VEC + 2 * k][tt] = (uint16_t)(vc[k] & 0xffffu);
+        sv[ch * VEC + 2 * k + 1][tt] = (uint16_t)(vc[k] >> 16);
+      }
+    }
+  }
   if (tid < kTok) {
     const int64_t t = t0 + tid;
     int64_t sl = t < T ? slots[t] : -1;
@@ -43,31 +69,18 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict_
   }
   __syncthreads();
   const int lgB = 31 - __builtin_clz(B);   // block_size is a power of two
-  for (int c = tid; c < kTok * CH; c += blockDim.x) {
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = tid + 256 * i;
     const int tt = c / CH, ch = c % CH;
-    const int64_t t = t0 + tt;
-    if (t >= T) continue;
-    const size_t src = ((size_t)t * H + h) * D + (size_t)ch * VEC;
-    const u32x4 vc = load16(value + src * EB);
-    // value chunk -> LDS, dimension-major
-    if constexpr (EB == 4) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sv[ch * VEC + i][tt] = vc[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[ch * VEC + 2 * i][tt] = (uint16_t)(vc[i] & 0xffffu);
-        sv[ch * VEC + 2 * i + 1][tt] = (uint16_t)(vc[i] >> 16);
-      }
-    }
+    if (c >= NCH || t0 + tt >= T) continue;
     const int64_t sl = sslot[tt];
     if (sl < 0) continue;
     const int64_t blk = sl >> lgB;
     const int off = (int)(sl & (B - 1));
     *(u32x4 *)(kpool + ((((size_t)(blk * H + h) * NC + ch / 4) * B + off) * X + (ch % 4) * VEC) * EB) =
-        load16(key + src * EB);
+        kc[i];
   }
-  __syncthreads();
   Elem *vp = (Elem *)vpool;
   for (int c = tid; c < D * kTok; c += blockDim.x) {
     const int tt = c % kTok, e = c / kTok;
@@ -103,14 +116,6 @@ __global__ __launch_bounds__(256) void scatter_fp8_kernel(const uint16_t *__rest
   const int h = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * kTok;
   const int tid = threadIdx.x;
-  if (tid < kTok) {
-    const int64_t t = t0 + tid;
-    int64_t sl = t < T ? slots[t] : -1;
-    if (sl >= nslots) sl = -1;
-    sslot[tid] = sl;
-  }
-  __syncthreads();
-  const int lgB = 31 - __builtin_clz(B);
   auto quantise8 = [](const u32x4 &c, float scale) -> u32x2 {
     float f[8];
     unpack16<M>(c, f);
@@ -119,23 +124,44 @@ __global__ __launch_bounds__(256) void scatter_fp8_kernel(const uint16_t *__rest
     for (int i = 0; i < 8; ++i) w[i >> 2] |= f32_to_fp8_bits(__fdiv_rn(f[i], scale)) << (8 * (i & 3));
     return u32x2{w[0], w[1]};
   };
-  for (int c = tid; c < kTok * CH; c += blockDim.x) {
+  // The rows' loads and their quantisation do not depend on the slots: only
+  // the stores wait for the barrier.
+  constexpr int NCH = kTok * CH;           // 8-element groups of the 16 rows
+  constexpr int PER = (NCH + 255) / 256;   // per thread (256 threads)
+  u32x2 kq[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = tid + 256 * i;
     const int tt = c / CH, g = c % CH;
     const int64_t t = t0 + tt;
-    if (t >= T) continue;
+    if (c >= NCH || t >= T) continue;
     const size_t src = ((size_t)t * H + h) * D + (size_t)g * 8;
-    const u32x2 vq = quantise8(load16(value + src), v_scale);
+    const u32x4 vraw = load16(value + src), kraw = load16(key + src);
+    const u32x2 vq = quantise8(vraw, v_scale);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sv[g * 8 + i][tt] = (uint8_t)(vq[i >> 2] >> (8 * (i & 3)));
+    for (int k = 0; k < 8; ++k) sv[g * 8 + k][tt] = (uint8_t)(vq[k >> 2] >> (8 * (k & 3)));
+    kq[i] = quantise8(kraw, k_scale);
+  }
+  if (tid < kTok) {
+    const int64_t t = t0 + tid;
+    int64_t sl = t < T ? slots[t] : -1;
+    if (sl >= nslots) sl = -1;
+    sslot[tid] = sl;
+  }
+  __syncthreads();
+  const int lgB = 31 - __builtin_clz(B);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = tid + 256 * i;
+    const int tt = c / CH, g = c % CH;
+    if (c >= NCH || t0 + tt >= T) continue;
     const int64_t sl = sslot[tt];
     if (sl < 0) continue;
     const int64_t blk = sl >> lgB;
     const int off = (int)(sl & (B - 1));
     const int e0 = g * 8;
-    *(u32x2 *)(kpool + (((size_t)(blk * H + h) * NC + e0 / 64) * B + off) * 64 + e0 % 64) =
-        quantise8(load16(key + src), k_scale);
+    *(u32x2 *)(kpool + (((size_t)(blk * H + h) * NC + e0 / 64) * B + off) * 64 + e0 % 64) = kq[i];
   }
-  __syncthreads();
   for (int c = tid; c < D * kTok; c += blockDim.x) {
     const int tt = c % kTok, e = c / kTok;
     const int64_t sl = sslot[tt];
