@@ -188,7 +188,7 @@ def main():
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build",
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported",
               file=sys.stderr)
         sys.exit(2)
 

@@ -76,7 +76,7 @@ typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_FP8_E4M3 = 3 } pkv_dt
 typedef enum {
   PKV_OK = 0,
   PKV_ERR_INVALID = 1,     /* null pointer, bad size, misalignment, Hq % Hkv != 0, ... */
-  PKV_ERR_UNSUPPORTED = 2, /* a valid request this build has no kernel for */
+  PKV_ERR_UNSUPPORTED = 2, /* a valid request the library has no kernel for */
   PKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
   PKV_ERR_HIP = 4          /* a HIP launch error (message from the runtime) */
 } pkv_status;
