@@ -182,6 +182,9 @@ def main():
                     help="physical block order of the llama13b workload (paging-overhead sweep)")
     ap.add_argument("--kv-cache", default="model", choices=["model", "fp8"],
                     help="fp8: store the decode workload's cache as E4M3 codes (scales 0.0135)")
+    ap.add_argument("--step", default="scatter+decode", choices=["scatter+decode", "fused"],
+                    help="decode workloads: fused = one appending call that writes the new "
+                         "tokens' K/V and attends (timed as the attention launch)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -220,6 +223,9 @@ def main():
         from paged_kv_cache_92_amd import workloads as W
         wl.kv_dtype, wl.k_scale, wl.v_scale = W.FP8, 0.0135, 0.0135
         desc += ", stored as fp8 e4m3 codes (per-tensor scales)"
+    fused = args.step == "fused"
+    if fused and wl.mode != "decode":
+        raise SystemExit("--step fused applies to decode workloads")
     log(f"[bench] generated {wl.name} in {time.time() - t0:.1f}s "
         f"(pool {wl.num_blocks} blocks, KV {wl.kv_bytes() / 1e9:.3f} GB)")
 
@@ -245,10 +251,14 @@ def main():
 
     def step(i, ev=None):
         dw, cache = copies[i % 2]
-        dw.apply(cache, dw.step)
+        if not fused:
+            dw.apply(cache, dw.step)
         if ev is not None:
             ev[0].record()
-        dw.attend(cache, out=out, workspace=ws)
+        if fused:
+            dw.append_attend(cache, out=out, workspace=ws)
+        else:
+            dw.attend(cache, out=out, workspace=ws)
         if ev is not None:
             ev[1].record()
 
@@ -311,7 +321,8 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbs_attn, 2), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs_attn / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic(args.config),
-                         "kernel": "paged decode (partial + reduce when split)",
+                         "kernel": "paged decode (partial + reduce when split)" if not fused
+                         else "appending paged decode (partial + reduce when split)",
                          "algorithmic_bytes_per_launch": kv,
                          "avg_launch_us": round(attn_avg * 1e3, 2)},
         })
@@ -370,6 +381,7 @@ def main():
                      "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                      "block_size": wl.block_size, "pool_blocks": wl.num_blocks,
                      "placement": args.placement,
+                     "step": args.step if wl.mode == "decode" else None,
                      "total_context_tokens": int(wl.context_lens.sum()),
                      "sliding_window": wl.window or None,
                      "partition_size": wl.partition_size if wl.mode != "prefill" else None,

@@ -223,6 +223,36 @@ pkv_status pkv_paged_decode_window(const pkv_cache *cache, void *out, int32_t ou
                                    size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Append and attend in one call: for every sequence, the new token's key and
+ * value rows are written into the cache at the slot its block table gives
+ * for position L-1 (physical block table[s][(L-1)/B], offset (L-1) mod B),
+ * and the decode of pkv_paged_decode_window runs over the cache with that
+ * token in place.  The result, cache and output, is bit for bit that of
+ * pkv_reshape_and_cache with those slots followed by
+ * pkv_paged_decode_window: [T] step 6 (decode stores the new token's K/V,
+ * then attends).  The decode kernel takes the new token from the input rows
+ * instead of the cache, and the short kernel that follows it (the split
+ * reduce, launched for this call also when nothing is split) stores the
+ * rows, which saves the scatter's launch and keeps stores out of the decode
+ * kernel's read stream.
+ *
+ *   key, value        [num_seqs][num_kv_heads][head_dim], model dtype
+ *                     (8-bit cache: quantised with k_scale / v_scale as the
+ *                     scatter does)
+ *   other arguments   as for pkv_paged_decode_window (same workspace size)
+ * The block holding position L-1 must belong to sequence s alone (copy on
+ * write done), as for any append.  A table entry for position L-1 that is
+ * out of range receives nothing.
+ */
+pkv_status pkv_paged_decode_append(const pkv_cache *cache, const void *key, const void *value,
+                                   void *out, int32_t out_dtype, const void *q,
+                                   int32_t num_q_heads, const int32_t *block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                   int32_t num_seqs, int32_t max_context_len,
+                                   int32_t sliding_window, float scale, int32_t partition_size,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Causal chunked prefill over the paged cache.  [S] section "Prefill-Decode
  * Disaggregation": a long prompt is processed in chunks over several steps;
  * [T] step 6 and [R] section 01: prefill processes all prompt tokens at once

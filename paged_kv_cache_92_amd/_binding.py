@@ -23,7 +23,8 @@ _TORCH_TO_PKV = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16:
 _STATUS = {0: "OK", 1: "INVALID", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP"}
 
 EXPORTED = ("pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_decode_workspace_bytes",
-            "pkv_paged_decode", "pkv_paged_decode_window", "pkv_paged_prefill", "pkv_paged_mixed",
+            "pkv_paged_decode", "pkv_paged_decode_window", "pkv_paged_decode_append",
+            "pkv_paged_prefill", "pkv_paged_mixed",
             "pkv_gather_kv",
             "pkv_validate_host",
             "pkv_last_error", "pkv_version")
@@ -61,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.pkv_paged_decode.argtypes = [cp, vp, i32, vp, i32, vp, i32, vp, i32, i32, f32, i32, vp, sz, vp]
         L.pkv_paged_decode_window.argtypes = [cp, vp, i32, vp, i32, vp, i32, vp, i32, i32, i32, f32, i32,
                                               vp, sz, vp]
+        L.pkv_paged_decode_append.argtypes = [cp, vp, vp, vp, i32, vp, i32, vp, i32, vp, i32, i32, i32,
+                                              f32, i32, vp, sz, vp]
         L.pkv_paged_prefill.argtypes = [cp, vp, i32, vp, i32, vp, vp, vp, i32, i32, i32, i32, f32, vp]
         L.pkv_paged_mixed.argtypes = [cp, vp, i32, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                       i32, vp, sz, vp]
@@ -69,7 +72,7 @@ def lib() -> ctypes.CDLL:
         L.pkv_last_error.restype = ctypes.c_char_p
         L.pkv_version.restype = ctypes.c_char_p
         for name in ("pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_paged_decode",
-                     "pkv_paged_decode_window",
+                     "pkv_paged_decode_window", "pkv_paged_decode_append",
                      "pkv_paged_prefill", "pkv_paged_mixed", "pkv_gather_kv", "pkv_validate_host"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -221,6 +224,37 @@ def paged_decode(cache: PagedKVCache, q, block_tables, context_lens, max_context
         _check(lib().pkv_paged_decode_window(*args, int(sliding_window), *tail))
     else:
         _check(lib().pkv_paged_decode(*args, *tail))
+    return out
+
+
+def paged_decode_append(cache: PagedKVCache, key, value, q, block_tables, context_lens,
+                        max_context_len, scale=None, partition_size=0, out=None, workspace=None,
+                        out_dtype=None, sliding_window=0):
+    """Append each sequence's new token (key/value [S][Hkv][d]) at position L-1 of its block
+    table and decode, in one launch: the same cache and output as ``reshape_and_cache`` with
+    those slots followed by ``paged_decode``."""
+    S, Hq, dq = q.shape
+    if dq != cache.head_dim:
+        raise ValueError("q head_dim does not match the cache")
+    if (tuple(key.shape) != (S, cache.num_kv_heads, cache.head_dim)
+            or tuple(value.shape) != tuple(key.shape)):
+        raise ValueError("key/value must be [S][num_kv_heads][head_dim]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(cache.head_dim)
+    out = _out(q, out, out_dtype)
+    need = decode_workspace_bytes(cache, S, Hq, max_context_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.nbytes if workspace is not None else 0
+    d = cache.desc()
+    _check(lib().pkv_paged_decode_append(
+        ctypes.byref(d), _dev_ptr(key, "key", cache.model_dtype),
+        _dev_ptr(value, "value", cache.model_dtype), _dev_ptr(out, "out"), _TORCH_TO_PKV[out.dtype],
+        _dev_ptr(q, "q", cache.model_dtype), Hq, _dev_ptr(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev_ptr(context_lens, "context_lens", torch.int32), S,
+        int(max_context_len), int(sliding_window), float(scale), int(partition_size), ws_ptr,
+        ws_bytes, _stream()))
     return out
 
 

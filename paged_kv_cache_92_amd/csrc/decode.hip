@@ -68,8 +68,10 @@ struct ValuLds {
 // goes to the output or to a workspace partial row (dest).  E is the
 // cache's element type, Q the query/output type (E itself, except over an
 // 8-bit cache: there the key scale is folded into scale_log2 and the value
-// scale multiplies the merged sums).
-template <typename E, typename Q, int D, int BS>
+// scale multiplies the merged sums).  APPEND: the sequence's new token
+// (position L-1) is taken from the input rows ap.k / ap.v, in cache format,
+// instead of the pool, whose slot is written by the reduce kernel.
+template <typename E, typename Q, int D, int BS, bool APPEND>
 __device__ __forceinline__ void valu_item(
     ValuLds<E, D, group_tokens(BS)> &sh, int s, int hq, int b0, int b1, Dest dest,
     void *__restrict__ out,
@@ -77,7 +79,7 @@ __device__ __forceinline__ void valu_item(
     const typename E::storage *__restrict__ kpool, const typename E::storage *__restrict__ vpool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
     int64_t num_blocks, int Hkv, int Hq, int mbps, int window, float scale_log2, float v_scale,
-    float *__restrict__ ws_ml, float *__restrict__ ws_acc) {
+    float *__restrict__ ws_ml, float *__restrict__ ws_acc, const Append<Q> &ap) {
   constexpr int GB = group_tokens(BS);
   constexpr bool kPair = GB == 2 * BS;      // two blocks per step
   using C = ValuCfg<E, D, GB>;
@@ -92,11 +94,11 @@ __device__ __forceinline__ void valu_item(
   const int nblk = b1 - b0;
   const int hkv = hq / (Hq / Hkv);
 
-  const int lane = threadIdx.x & (kWave - 1);
+  int lane = threadIdx.x & (kWave - 1);
   const int w = uniform(threadIdx.x >> 6);
-  const int kq = lane & 3;         // 16-byte piece within a 64-byte key slice
-  const int kt = lane >> 2;        // token within a 16-token group
-  const int cp = lane % C::CPR;    // token chunk of the value row
+  int kq = lane & 3;         // 16-byte piece within a 64-byte key slice
+  int kt = lane >> 2;        // token within a 16-token group
+  int cp = lane % C::CPR;    // token chunk of the value row
 
   auto &lds_p = sh.p;
   auto &lds_m = sh.m;
@@ -142,29 +144,48 @@ __device__ __forceinline__ void valu_item(
 
   const int32_t *bt = block_tables + (size_t)s * mbps;
   constexpr int STEP = kPair ? 2 : 1;
-  for (int b = STEP * w; b < nblk; b += STEP * kWaves) {
+  // One step of a wave: block b of the item (and b+1 for a pair).  `app`
+  // (std::true_type) marks the step that appends the new token.
+  auto step = [&](const int b, auto app) {
+    constexpr bool kApp = decltype(app)::value;
     const int lb = blk0 + b;
+    // Appending step: the new token's index in the step, and (cache in the
+    // model dtype) its key row, which the lanes holding that token load in
+    // place of the pool's slot.
+    const int j = kApp ? sp.hi - 1 - lb * BS : -1;
+    const T *knew = nullptr;
+    if constexpr (kApp && !kFP8) knew = (const T *)ap.k + ((size_t)s * Hkv + hkv) * D + kq * C::VEC;
+    auto kld = [&](const T *p, int t, int c) -> u32x4 {
+      if constexpr (kApp && !kFP8) {
+        if (t == j) p = knew + c * C::X;
+      }
+      return load16_stream(p);
+    };
     int64_t phys = uniform(bt[lb]);
+    int64_t phys2 = phys;
+    bool ok1 = true, ok2 = true;   // table entries in range (a pair's second: if covered)
     u32x4 kr[C::KL];
     u32x4 vr[C::VL];
     if constexpr (!kPair) {
-      if (phys < 0 || phys >= num_blocks) continue;
+      if (phys < 0 || phys >= num_blocks) return;
       const T *ktile = kpool + ((size_t)phys * Hkv + hkv) * (BS * D);
       const T *vtile = vpool + ((size_t)phys * Hkv + hkv) * (D * BS);
 #pragma unroll
       for (int c = 0; c < C::NC; ++c)
 #pragma unroll
         for (int r = 0; r < C::TG; ++r)
-          kr[c * C::TG + r] = load16_stream(ktile + (c * BS + 16 * r + kt) * C::X + kq * C::VEC);
+          kr[c * C::TG + r] = kld(ktile + (c * BS + 16 * r + kt) * C::X + kq * C::VEC, 16 * r + kt, c);
 #pragma unroll
       for (int i = 0; i < C::VL; ++i) vr[i] = load16_stream(vtile + (size_t)(kWave * i + lane) * C::VEC);
     } else {
       // Blocks lb and lb+1 (the second only if the item covers it; past the
       // item its tokens are masked and block lb is read in its place).  An
       // out-of-range id reads block 0 instead of faulting.
-      int64_t phys2 = b + 1 < nblk ? uniform(bt[lb + 1]) : phys;
-      if (phys < 0 || phys >= num_blocks) phys = 0;
-      if (phys2 < 0 || phys2 >= num_blocks) phys2 = 0;
+      phys2 = b + 1 < nblk ? uniform(bt[lb + 1]) : phys;
+      ok1 = phys >= 0 && phys < num_blocks;
+      ok2 = phys2 >= 0 && phys2 < num_blocks;
+      if (!ok1) phys = 0;
+      if (!ok2) phys2 = 0;
       const T *kt0 = kpool + ((size_t)phys * Hkv + hkv) * (BS * D);
       const T *kt1 = kpool + ((size_t)phys2 * Hkv + hkv) * (BS * D);
       const T *vt0 = vpool + ((size_t)phys * Hkv + hkv) * (D * BS);
@@ -175,8 +196,7 @@ __device__ __forceinline__ void valu_item(
 #pragma unroll
         for (int r = 0; r < C::TG; ++r) {
           const int t = 16 * r + kt;
-          kr[c * C::TG + r] =
-              load16_stream((t < BS ? kt0 : kt1) + (c * BS + t % BS) * C::X + kq * C::VEC);
+          kr[c * C::TG + r] = kld((t < BS ? kt0 : kt1) + (c * BS + t % BS) * C::X + kq * C::VEC, t, c);
         }
 #pragma unroll
       for (int i = 0; i < C::VL; ++i) {
@@ -188,6 +208,38 @@ __device__ __forceinline__ void valu_item(
           // 16 codes of one dimension: 8 from each block's row.
           const u32x2 a = load8_stream(vt0 + dim * BS), c2 = load8_stream(vt1 + dim * BS);
           vr[i] = u32x4{a[0], a[1], c2[0], c2[1]};
+        }
+      }
+    }
+
+    // The new token in cache format: its key pieces replace the pool's (an
+    // 8-bit cache quantises them here; otherwise they were loaded from the
+    // input row above) and its value element replaces the pool's as the
+    // values are unpacked.  The pool's slot is never read; the reduce kernel
+    // that follows stores the rows into it.
+    uint32_t vnew[C::VL];   // the new token's value bits, one per chunk of this lane
+    int vj = -1;            // its element within this lane's chunks (-1: none)
+    const size_t row = ((size_t)s * Hkv + hkv) * D;
+    if constexpr (kApp) {
+#pragma unroll
+      for (int i = 0; i < C::VL; ++i) vnew[i] = 0u;
+      if (j >= 0 && j < GB) {
+        if constexpr (kFP8) {
+#pragma unroll
+          for (int r = 0; r < C::TG; ++r) {
+            if (16 * r + kt != j) continue;
+#pragma unroll
+            for (int c = 0; c < C::NC; ++c)
+              kr[c * C::TG + r] = cache_piece<E, Q>(ap.k + row + c * C::X + kq * C::VEC, ap.k_scale);
+          }
+        }
+        // A lane's value chunks all start at token (lane % CPR) * VEC.
+        const int t0 = (lane % C::CPR) * C::VEC;
+        if (j >= t0 && j < t0 + C::VEC) {
+          vj = j - t0;
+#pragma unroll
+          for (int i = 0; i < C::VL; ++i)
+            vnew[i] = cache_elem<E, Q>(ap.v[row + (kWave * i + lane) / C::CPR], ap.v_scale);
         }
       }
     }
@@ -232,6 +284,14 @@ __device__ __forceinline__ void valu_item(
     for (int i = 0; i < C::VL; ++i) {
       float vf[C::VEC];
       unpack16<E>(vr[i], vf);
+      if constexpr (kApp) {
+        if (vj >= 0) {
+          const float nv = elem_value<E>(vnew[i]);
+#pragma unroll
+          for (int e = 0; e < C::VEC; ++e)
+            if (e == vj) vf[e] = nv;
+        }
+      }
       float a = acc[i] * alpha;
       if (partial) {
         // Slots outside [lo, tok1) may hold anything (NaN included): their values count as 0.
@@ -248,6 +308,25 @@ __device__ __forceinline__ void valu_item(
       acc[i] = a;
     }
     __builtin_amdgcn_wave_barrier();
+  };
+  // An appending item that ends the sequence takes its last step (the one
+  // holding position L-1) out of the loop, so that the loop itself is the
+  // plain decode's.
+  int bmain = nblk, blast = -1;
+  if constexpr (APPEND) {
+    if (tok1 == sp.hi) {
+      blast = (nblk - 1) / STEP * STEP;
+      bmain = blast;
+    }
+  }
+  for (int b = STEP * w; b < bmain; b += STEP * kWaves) step(b, std::false_type{});
+  if constexpr (APPEND) {
+    if (blast >= 0 && (blast / STEP) % kWaves == w) {
+      // Opaque copies of the lane indices: the step recomputes its per-lane
+      // addresses instead of keeping them live through the loop.
+      asm volatile("" : "+v"(lane), "+v"(kq), "+v"(kt), "+v"(cp));
+      step(blast, std::true_type{});
+    }
   }
 
   // Sum each dimension over the CPR lanes that share it, and l over the same lanes.
@@ -293,37 +372,92 @@ __device__ __forceinline__ void valu_item(
 // partitions over a persistent grid) or kSchedFlat (balanced ranges).  The
 // grid schedule asks for 8 waves per SIMD (64 VGPRs) only where one block's
 // loads plus the query slice fit that budget without spills; other variants
-// keep the compiler's choice.
-template <typename E, typename Q, int D, int BS, int SCHED>
-__global__ __launch_bounds__(256, (SCHED == kSchedGrid && E::kBytes >= 2 && ValuCfg<E, D, group_tokens(BS)>::kLoadRegs + 4 * ValuCfg<E, D, group_tokens(BS)>::NC <= 24) ? 8 : 1) void
+// keep the compiler's choice.  Appending variants of 16-bit caches with
+// head_dim 128 and 16-token blocks ask for the 5 waves per SIMD their plain
+// versions reach.
+template <typename E, int D, int BS, int SCHED, bool APPEND>
+constexpr int valu_min_waves() {
+  if constexpr (APPEND) return E::kBytes == 2 && D == 128 && BS == 16 ? 5 : 1;
+  return SCHED == kSchedGrid && E::kBytes >= 2 &&
+                 ValuCfg<E, D, group_tokens(BS)>::kLoadRegs + 4 * ValuCfg<E, D, group_tokens(BS)>::NC <= 24
+             ? 8
+             : 1;
+}
+template <typename E, typename Q, int D, int BS, int SCHED, bool APPEND>
+__global__ __launch_bounds__(256, (valu_min_waves<E, D, BS, SCHED, APPEND>())) void
 decode_valu_kernel(
     void *__restrict__ out, int out_f32, const typename Q::storage *__restrict__ q,
     const typename E::storage *__restrict__ kpool, const typename E::storage *__restrict__ vpool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
     int64_t num_blocks, int Hkv, int Hq, int S, int mbps, int window, float scale_log2,
     float v_scale, int part_tokens, int nparts, float *__restrict__ ws_ml,
-    float *__restrict__ ws_acc, int *__restrict__ ws_hdr) {
+    float *__restrict__ ws_acc, int *__restrict__ ws_hdr, Append<Q> ap) {
   __shared__ ValuLds<E, D, group_tokens(BS)> sh;
   extern __shared__ int plan[];
   __shared__ int scan[16];
   run_schedule<SCHED>(
       [&](int s, int hq, int b0, int b1, Dest dest) {
-        valu_item<E, Q, D, BS>(sh, s, hq, b0, b1, dest, out, out_f32, q, kpool, vpool, block_tables,
+        valu_item<E, Q, D, BS, APPEND>(sh, s, hq, b0, b1, dest, out, out_f32, q, kpool, vpool, block_tables,
                                context_lens, num_blocks, Hkv, Hq, mbps, window, scale_log2, v_scale,
-                               ws_ml, ws_acc);
+                               ws_ml, ws_acc, ap);
       },
       plan, scan, context_lens, S, mbps * BS, window, BS, Hq, 1, part_tokens, nparts, ws_hdr);
 }
 
+// Appending call: the reduce kernel (launched after the decode kernel, also
+// when there is nothing to reduce) stores each sequence's new key and value
+// rows into the cache slot of position L-1; the decode kernel took them from
+// the input rows and never read that slot.  Stores in the middle of the
+// decode kernel's read stream cost it far more than the bytes they move.
+struct NewToken {
+  const void *k = nullptr;   // [S][Hkv][D] model dtype; nullptr: nothing to store
+  const void *v = nullptr;
+  float k_scale = 1.f, v_scale = 1.f;
+  void *kpool = nullptr;
+  void *vpool = nullptr;
+  const int32_t *block_tables = nullptr;
+  int64_t num_blocks = 0;
+  int Hkv = 1, BS = 16, mbps = 0;
+};
+
+// Rows of sequence s, KV head hkv, into the slot of position L-1 (none if
+// the table entry is out of range), each element as pkv_reshape_and_cache
+// stores it.  KV is the cache element, Q the model dtype.
+template <typename KV, typename Q, int D>
+__device__ __forceinline__ void store_new_token(const NewToken &nt,
+                                                const int32_t *__restrict__ context_lens, int s,
+                                                int hkv) {
+  const int L = min(context_lens[s], nt.mbps * nt.BS);
+  if (L <= 0) return;
+  const int64_t phys = nt.block_tables[(size_t)s * nt.mbps + (L - 1) / nt.BS];
+  if (phys < 0 || phys >= nt.num_blocks) return;
+  const int off = (L - 1) % nt.BS;
+  constexpr int X = 64 / KV::kBytes;   // elements per 64-byte key piece
+  using T = typename KV::storage;
+  using TQ = typename Q::storage;
+  const size_t row = ((size_t)s * nt.Hkv + hkv) * D;
+  const size_t tile = ((size_t)phys * nt.Hkv + hkv) * ((size_t)nt.BS * D);
+  T *kt = (T *)nt.kpool + tile;
+  T *vt = (T *)nt.vpool + tile;
+  for (int e = threadIdx.x; e < D; e += blockDim.x) {
+    store_bits<KV::kBytes>(kt + (e / X) * (nt.BS * X) + off * X + e % X,
+                           cache_elem<KV, Q>(((const TQ *)nt.k)[row + e], nt.k_scale));
+    store_bits<KV::kBytes>(vt + (size_t)e * nt.BS + off,
+                           cache_elem<KV, Q>(((const TQ *)nt.v)[row + e], nt.v_scale));
+  }
+}
+
 // Cross-partition reduce over the partitions of the sequence's span:
 // o = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
-template <typename E, int D>
+template <typename E, typename KV, int D>
 __global__ __launch_bounds__(128) void decode_reduce_kernel(
     void *__restrict__ out, int out_f32, const int32_t *__restrict__ context_lens, int Hq,
     int mbps_tokens, int window, int part_tokens, int nparts, const float *__restrict__ ws_ml,
-    const float *__restrict__ ws_acc) {
+    const float *__restrict__ ws_acc, NewToken nt) {
   const int hq = blockIdx.x;
   const int s = blockIdx.y;
+  const int G = Hq / nt.Hkv;
+  if (nt.k != nullptr && hq % G == 0) store_new_token<KV, E, D>(nt, context_lens, s, hq / G);
   const Span sp = seq_span(context_lens, s, mbps_tokens, window);
   const int p0 = first_part(sp, part_tokens);
   const int np = min(parts_in(sp, part_tokens), nparts - p0);
@@ -345,12 +479,15 @@ __global__ __launch_bounds__(128) void decode_reduce_kernel(
 // Balanced-schedule reduce: the partial rows of every segment that spans
 // several workgroup ranges (see run_schedule), combined as above.  HU head
 // units per sequence, G query heads per unit.
-template <typename E, int D>
+template <typename E, typename KV, int D>
 __global__ __launch_bounds__(128) void decode_reduce_flat_kernel(
     void *__restrict__ out, int out_f32, const int *__restrict__ ws_hdr, int Hq, int HU, int G,
-    const float *__restrict__ ws_ml, const float *__restrict__ ws_acc) {
+    const float *__restrict__ ws_ml, const float *__restrict__ ws_acc,
+    const int32_t *__restrict__ context_lens, NewToken nt) {
   const int hq = blockIdx.x;
   const int s = blockIdx.y;
+  if (nt.k != nullptr && hq % (Hq / nt.Hkv) == 0)
+    store_new_token<KV, E, D>(nt, context_lens, s, hq / (Hq / nt.Hkv));
   const int g = hq % G;
   const FlatSegment f = flat_segment(ws_hdr, s, hq / G, HU);
   if (f.w1 <= f.w0) return;
@@ -372,8 +509,8 @@ __global__ __launch_bounds__(128) void decode_reduce_flat_kernel(
   }
 }
 
-template <typename E, typename Q, int D, int BS>
-void launch_valu_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
+template <typename E, typename Q, int D, int BS, bool APPEND>
+void launch_valu_ta(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
   using T = typename E::storage;
   using TQ = typename Q::storage;
   const float sl = a.scale * kLog2e * c.k_scale;  // k_scale is 1 unless the cache is 8-bit
@@ -382,7 +519,8 @@ void launch_valu_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) 
     hipLaunchKernelGGL(kern, grid, dim3(256), dyn, stream, a.out, (int)a.out_f32, (const TQ *)a.q,
                        (const T *)c.k, (const T *)c.v, a.block_tables, a.context_lens,
                        c.num_blocks, c.H, a.Hq, a.S, a.max_blocks_per_seq, a.window, sl, c.v_scale,
-                       a.partition_tokens, a.num_partitions, a.ws_ml, a.ws_acc, a.ws_hdr);
+                       a.partition_tokens, a.num_partitions, a.ws_ml, a.ws_acc, a.ws_hdr,
+                       Append<Q>{(const TQ *)a.new_k, (const TQ *)a.new_v, c.k_scale, c.v_scale});
   };
   // Fixed partitions run a persistent grid over the non-empty cells (a 3-D
   // grid would launch a workgroup for every empty partition); without a split
@@ -391,16 +529,24 @@ void launch_valu_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) 
 #define PKV_GRID_FACTOR 4
 #endif
   if (a.flat) {
-    go(decode_valu_kernel<E, Q, D, BS, kSchedFlat>, dim3(a.flat_grid), lds);
+    go(decode_valu_kernel<E, Q, D, BS, kSchedFlat, APPEND>, dim3(a.flat_grid), lds);
   } else if (a.num_partitions > 1 && a.S <= kPlanMaxSeqs) {
-    auto kern = decode_valu_kernel<E, Q, D, BS, kSchedPlan>;
+    auto kern = decode_valu_kernel<E, Q, D, BS, kSchedPlan, APPEND>;
     const int64_t cells = (int64_t)a.S * a.num_partitions * a.Hq;
     const int grid = (int)std::min<int64_t>(cells, PKV_GRID_FACTOR * (int64_t)resident_workgroups((const void *)kern, 256, lds));
     go(kern, dim3(grid), lds);
   } else {
-    go(decode_valu_kernel<E, Q, D, BS, kSchedGrid>,
+    go(decode_valu_kernel<E, Q, D, BS, kSchedGrid, APPEND>,
        dim3((unsigned)a.num_partitions, (unsigned)a.Hq, (unsigned)a.S), 0);
   }
+}
+
+// Appending calls run their own instantiations, so that plain decode keeps
+// its register budget.
+template <typename E, typename Q, int D, int BS>
+void launch_valu_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
+  if (a.new_k != nullptr) launch_valu_ta<E, Q, D, BS, true>(c, a, stream);
+  else launch_valu_ta<E, Q, D, BS, false>(c, a, stream);
 }
 
 template <typename E, typename Q = E>
@@ -415,7 +561,7 @@ void launch_valu_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) 
 
 template <typename E, typename Q, int D, int BS>
 int flat_grid_t(int S) {
-  return resident_workgroups((const void *)decode_valu_kernel<E, Q, D, BS, kSchedFlat>, 256,
+  return resident_workgroups((const void *)decode_valu_kernel<E, Q, D, BS, kSchedFlat, false>, 256,
                              sizeof(int) * (S + 1));
 }
 
@@ -429,24 +575,38 @@ int flat_grid_e(const CacheDesc &c, int S) {
   return flat_grid_t<E, Q, 128, 32>(S);
 }
 
-template <typename E>
+template <typename E, typename KV>
 void launch_reduce_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
   const dim3 grid((unsigned)a.Hq, (unsigned)a.S);
   const int mt = a.max_blocks_per_seq * c.B;
   const int G = a.Hq / c.H;
   const bool mfma = G > 1 && c.dtype != 0;
   const int HU = mfma ? c.H : a.Hq, GU = mfma ? G : 1;
+  NewToken nt;
+  if (a.new_k != nullptr) {
+    nt.k = a.new_k;
+    nt.v = a.new_v;
+    nt.k_scale = c.k_scale;
+    nt.v_scale = c.v_scale;
+    nt.kpool = c.k;
+    nt.vpool = c.v;
+    nt.block_tables = a.block_tables;
+    nt.num_blocks = c.num_blocks;
+    nt.BS = c.B;
+    nt.mbps = a.max_blocks_per_seq;
+  }
+  nt.Hkv = c.H;
   auto go = [&](auto kern_part, auto kern_flat, int threads) {
     if (a.flat)
       hipLaunchKernelGGL(kern_flat, grid, dim3(threads), 0, stream, a.out, (int)a.out_f32,
-                         (const int *)a.ws_hdr, a.Hq, HU, GU, a.ws_ml, a.ws_acc);
+                         (const int *)a.ws_hdr, a.Hq, HU, GU, a.ws_ml, a.ws_acc, a.context_lens, nt);
     else
       hipLaunchKernelGGL(kern_part, grid, dim3(threads), 0, stream, a.out, (int)a.out_f32,
                          a.context_lens, a.Hq, mt, a.window, a.partition_tokens, a.num_partitions,
-                         a.ws_ml, a.ws_acc);
+                         a.ws_ml, a.ws_acc, nt);
   };
-  if (c.D == 64) go(decode_reduce_kernel<E, 64>, decode_reduce_flat_kernel<E, 64>, 64);
-  else go(decode_reduce_kernel<E, 128>, decode_reduce_flat_kernel<E, 128>, 128);
+  if (c.D == 64) go(decode_reduce_kernel<E, KV, 64>, decode_reduce_flat_kernel<E, KV, 64>, 64);
+  else go(decode_reduce_kernel<E, KV, 128>, decode_reduce_flat_kernel<E, KV, 128>, 128);
 }
 
 }  // namespace
@@ -472,11 +632,12 @@ int decode_valu_flat_grid(const CacheDesc &c, int S) {
   return flat_grid_e<BF16>(c, S);
 }
 
-// The reduce writes the output, so it goes by the model dtype.
+// The reduce writes the output, so it goes by the model dtype; an appending
+// call's stores go by the cache's.
 hipError_t launch_decode_reduce(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
-  if (c.mdtype == 0) launch_reduce_e<F32>(c, a, stream);
-  else if (c.mdtype == 1) launch_reduce_e<F16>(c, a, stream);
-  else launch_reduce_e<BF16>(c, a, stream);
+  if (c.mdtype == 0) launch_reduce_e<F32, F32>(c, a, stream);
+  else if (c.mdtype == 1) c.fp8() ? launch_reduce_e<F16, FP8>(c, a, stream) : launch_reduce_e<F16, F16>(c, a, stream);
+  else c.fp8() ? launch_reduce_e<BF16, FP8>(c, a, stream) : launch_reduce_e<BF16, BF16>(c, a, stream);
   return hipGetLastError();
 }
 

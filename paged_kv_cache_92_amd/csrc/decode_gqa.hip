@@ -99,14 +99,14 @@ __device__ __forceinline__ u32x2 widen4(uint32_t w) {
 // merge buffers.  E is the query / matrix-core type; KV the cache element
 // (E itself, or FP8: codes are widened to E right after the loads, the key
 // scale is folded into scale_log2 and v_scale multiplies the merged sums).
-template <typename E, typename KV, int D, int BS>
+template <typename E, typename KV, int D, int BS, bool APPEND>
 __device__ __forceinline__ void mfma_item(
     float *lds_dyn, int s, int hkv, int b0, int b1, Dest dest, void *__restrict__ out,
     int out_f32, const uint16_t *__restrict__ q, const typename KV::storage *__restrict__ kpool,
     const typename KV::storage *__restrict__ vpool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, int64_t num_blocks, int Hkv, int G, int mbps,
     int window, float scale_log2, float v_scale, float *__restrict__ ws_ml,
-    float *__restrict__ ws_acc) {
+    float *__restrict__ ws_acc, const Append<E> &ap) {
   constexpr bool kFP8 = KV::kBytes == 1;
   constexpr int KS = D / 32;    // k-steps of the score product
   constexpr int NT = D / 16;    // 16-dimension tiles of the output
@@ -127,10 +127,10 @@ __device__ __forceinline__ void mfma_item(
   const int nblk = b1 - b0;
   const int Hq = Hkv * G;
 
-  const int lane = threadIdx.x & (kWave - 1);
+  int lane = threadIdx.x & (kWave - 1);
   const int w = uniform(threadIdx.x >> 6);
-  const int n16 = lane & 15;   // query head (column) / token row / dimension row
-  const int g4 = lane >> 4;    // k-group of the operands, row group of the result
+  int n16 = lane & 15;   // query head (column) / token row / dimension row
+  int g4 = lane >> 4;    // k-group of the operands, row group of the result
 
   // Cross-wave merge buffers, sized for the G live heads:
   // m[kWaves][16], l[kWaves][16], acc[kWaves][G][D + 1].
@@ -162,8 +162,17 @@ __device__ __forceinline__ void mfma_item(
   const int32_t *bt = block_tables + (size_t)s * mbps;
   constexpr int STEP = kPair ? 2 : 1;
   using TS = typename KV::storage;
-  for (int b = STEP * w; b < nblk; b += STEP * kWaves) {
+  // One step of a wave: block b of the item (and b+1 for a pair).  `app`
+  // (std::true_type) marks the step that appends the new token.
+  auto step = [&](const int b, auto app) {
+    constexpr bool kApp = decltype(app)::value;
     const int lb = blk0 + b;
+    // Appending step: the new token's index in the step; over a 16-bit cache
+    // the lanes holding its key rows load them from the input row in place
+    // of the pool's slot.
+    const int j = kApp ? sp.hi - 1 - lb * BS : -1;
+    const TS *knew = nullptr;
+    if constexpr (kApp && !kFP8) knew = (const TS *)ap.k + ((size_t)s * Hkv + hkv) * D + 8 * g4;
     int64_t phys = uniform(bt[lb]);
     // Key and value tiles this lane reads: one block's, or for 8-token blocks
     // those of block lb + t/8 for the lane's token t of the 16 (key row n16,
@@ -172,18 +181,22 @@ __device__ __forceinline__ void mfma_item(
     // read in its place); there an out-of-range id reads block 0 instead of
     // faulting, while a single block with such an id is skipped.
     const TS *kt, *vt;
+    int64_t phys2 = phys;
+    bool ok1 = true, ok2 = true;   // table entries in range (a pair's second: if covered)
     int krow;   // key row of this lane within its tile
     int vtok;   // first value token of this lane within its tile (non-wide)
     if constexpr (!kPair) {
-      if (phys < 0 || phys >= num_blocks) continue;
+      if (phys < 0 || phys >= num_blocks) return;
       kt = kpool + ((size_t)phys * Hkv + hkv) * (BS * D);
       vt = vpool + ((size_t)phys * Hkv + hkv) * (D * BS);
       krow = 0;
       vtok = 0;
     } else {
-      int64_t phys2 = b + 1 < nblk ? uniform(bt[lb + 1]) : phys;
-      if (phys < 0 || phys >= num_blocks) phys = 0;
-      if (phys2 < 0 || phys2 >= num_blocks) phys2 = 0;
+      phys2 = b + 1 < nblk ? uniform(bt[lb + 1]) : phys;
+      ok1 = phys >= 0 && phys < num_blocks;
+      ok2 = phys2 >= 0 && phys2 < num_blocks;
+      if (!ok1) phys = 0;
+      if (!ok2) phys2 = 0;
       const int64_t pk = n16 < 8 ? phys : phys2, pv = g4 < 2 ? phys : phys2;
       kt = kpool + ((size_t)pk * Hkv + hkv) * (BS * D);
       vt = vpool + ((size_t)pv * Hkv + hkv) * (D * BS);
@@ -208,8 +221,13 @@ __device__ __forceinline__ void mfma_item(
 #pragma unroll
       for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          ka[sb][ks] = load16_stream(kt + (ks * BS + token_of_row<GB>(sb, n16) + krow) * 32 + 8 * g4);
+        for (int ks = 0; ks < KS; ++ks) {
+          const TS *p = kt + (ks * BS + token_of_row<GB>(sb, n16) + krow) * 32 + 8 * g4;
+          if constexpr (kApp) {
+            if (token_of_row<GB>(sb, n16) == j) p = knew + 32 * ks;
+          }
+          ka[sb][ks] = load16_stream(p);
+        }
     }
     // V^T operand: dimension row 16*nt + n16; tokens 8*g4 .. +8 (wide) or
     // 16*sb + 4*g4 .. +4 of sub-tile sb.
@@ -236,6 +254,50 @@ __device__ __forceinline__ void mfma_item(
           else
             va[sb][nt] = load8_stream(vt + (16 * nt + n16) * BS + 16 * sb + 4 * g4 + vtok);
         }
+    }
+
+    // The new token in cache format: over an 8-bit cache its key codes are
+    // quantised here (a 16-bit cache loaded the key rows from the input
+    // above); its value element is read here and patched into the V^T
+    // operand just before the product.  The pool's slot is never read; the
+    // reduce kernel that follows stores the rows into it.
+    const bool has_new = kApp && j >= 0 && j < GB;
+    const size_t row = ((size_t)s * Hkv + hkv) * D;
+    uint32_t vnew[NT];   // cache bits of the new value, dimensions 16*nt + n16
+    int vj = -1;         // its element in this lane's V^T operand (-1: none)
+    int vsb = 0;         // ... and that operand's sub-tile (non-wide)
+    if constexpr (kApp) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) vnew[nt] = 0u;
+      if (has_new) {
+        if constexpr (kFP8) {
+#pragma unroll
+          for (int sb = 0; sb < SUB; ++sb) {
+            if (token_of_row<GB>(sb, n16) != j) continue;
+#pragma unroll
+            for (int c = 0; c < KS / 2; ++c) {
+              const u32x4 codes = cache_piece<KV, E>(ap.k + row + 64 * c + 16 * g4, ap.k_scale);
+              const u32x2 a0 = widen4<E>(codes[0]), a1 = widen4<E>(codes[1]);
+              const u32x2 a2 = widen4<E>(codes[2]), a3 = widen4<E>(codes[3]);
+              ka[sb][2 * c] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+              ka[sb][2 * c + 1] = u32x4{a2[0], a2[1], a3[0], a3[1]};
+            }
+          }
+        }
+        // This lane's value tokens: 8*g4 .. +8 (wide) or 16*sb + 4*g4 .. +4.
+#pragma unroll
+        for (int sb = 0; sb < (kWide ? 1 : SUB); ++sb) {
+          const int t0 = kWide ? 8 * g4 : 16 * sb + 4 * g4;
+          if (j >= t0 && j < t0 + (kWide ? 8 : 4)) {
+            vj = j - t0;
+            vsb = sb;
+          }
+        }
+        if (vj >= 0) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) vnew[nt] = cache_elem<KV, E>(ap.v[row + 16 * nt + n16], ap.v_scale);
+        }
+      }
     }
 
     const int tbase = lb * BS;
@@ -315,6 +377,26 @@ __device__ __forceinline__ void mfma_item(
         }
       }
     }
+    if constexpr (kApp) {
+      if (vj >= 0) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          // The element as the product reads it: an 8-bit code widened to E.
+          uint32_t e = vnew[nt];
+          if constexpr (kFP8) e = widen4<E>(e)[0] & 0xffffu;
+          if constexpr (kWide) {
+            vw[nt] = put_elem<2>(vw[nt], vj, e);
+          } else {
+#pragma unroll
+            for (int sb = 0; sb < SUB; ++sb) {
+              if (sb != vsb) continue;
+              const u32x4 w4 = put_elem<2>(u32x4{va[sb][nt][0], va[sb][nt][1], 0u, 0u}, vj, e);
+              va[sb][nt] = u32x2{w4[0], w4[1]};
+            }
+          }
+        }
+      }
+    }
     if constexpr (kWide) {
       const u32x4 pw = {ph[0], ph[1], ph[2], ph[3]};
 #pragma unroll
@@ -331,6 +413,25 @@ __device__ __forceinline__ void mfma_item(
           if constexpr (Mfma<E>::kSplitP)
             acc[nt] = Mfma<E>::pv(va[sb][nt], u32x2{plo[2 * sb], plo[2 * sb + 1]}, acc[nt]);
         }
+    }
+  };
+  // An appending item that ends the sequence takes its last step (the one
+  // holding position L-1) out of the loop, so that the loop itself is the
+  // plain decode's.
+  int bmain = nblk, blast = -1;
+  if constexpr (APPEND) {
+    if (tok1 == sp.hi) {
+      blast = (nblk - 1) / STEP * STEP;
+      bmain = blast;
+    }
+  }
+  for (int b = STEP * w; b < bmain; b += STEP * kWaves) step(b, std::false_type{});
+  if constexpr (APPEND) {
+    if (blast >= 0 && (blast / STEP) % kWaves == w) {
+      // Opaque copies of the lane indices: the step recomputes its per-lane
+      // addresses instead of keeping them live through the loop.
+      asm volatile("" : "+v"(lane), "+v"(n16), "+v"(g4));
+      step(blast, std::true_type{});
     }
   }
 
@@ -384,23 +485,25 @@ __device__ __forceinline__ void mfma_item(
 #ifndef PKV_MFMA_MIN_WAVES_FP8
 #define PKV_MFMA_MIN_WAVES_FP8 3
 #endif
-template <typename E, typename KV, int D, int BS, int SCHED>
-__global__ __launch_bounds__(256, KV::kBytes == 1 ? PKV_MFMA_MIN_WAVES_FP8 : PKV_MFMA_MIN_WAVES) void decode_mfma_kernel(
+// The appending variant over 32-token blocks gives up one wave per SIMD rather
+// than spill the new token's staging.
+template <typename E, typename KV, int D, int BS, int SCHED, bool APPEND>
+__global__ __launch_bounds__(256, KV::kBytes == 1 ? PKV_MFMA_MIN_WAVES_FP8 : (APPEND && BS == 32 ? 3 : PKV_MFMA_MIN_WAVES)) void decode_mfma_kernel(
     void *__restrict__ out, int out_f32, const uint16_t *__restrict__ q,
     const typename KV::storage *__restrict__ kpool, const typename KV::storage *__restrict__ vpool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
     int64_t num_blocks, int Hkv, int G, int S, int mbps, int window, float scale_log2,
     float v_scale, int part_tokens, int nparts, float *__restrict__ ws_ml,
-    float *__restrict__ ws_acc, int *__restrict__ ws_hdr) {
+    float *__restrict__ ws_acc, int *__restrict__ ws_hdr, Append<E> ap) {
   extern __shared__ __attribute__((aligned(16))) int dyn[];
   __shared__ int scan[16];
   int *plan = dyn;
   float *merge = (float *)(dyn + (SCHED == kSchedGrid ? 0 : ((S + 1 + 3) & ~3)));
   run_schedule<SCHED>(
       [&](int s, int hkv, int b0, int b1, Dest dest) {
-        mfma_item<E, KV, D, BS>(merge, s, hkv, b0, b1, dest, out, out_f32, q, kpool, vpool,
+        mfma_item<E, KV, D, BS, APPEND>(merge, s, hkv, b0, b1, dest, out, out_f32, q, kpool, vpool,
                                 block_tables, context_lens, num_blocks, Hkv, G, mbps, window,
-                                scale_log2, v_scale, ws_ml, ws_acc);
+                                scale_log2, v_scale, ws_ml, ws_acc, ap);
       },
       plan, scan, context_lens, S, mbps * BS, window, BS, Hkv, G, part_tokens, nparts, ws_hdr);
 }
@@ -410,8 +513,8 @@ size_t merge_bytes(int G) {
   return sizeof(float) * (2 * kWaves * 16 + (size_t)kWaves * G * (D + 1));
 }
 
-template <typename E, typename KV, int D, int BS>
-void launch_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
+template <typename E, typename KV, int D, int BS, bool APPEND>
+void launch_ta(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
   using T = typename KV::storage;
   const int G = a.Hq / c.H;
   const size_t merge = merge_bytes<D>(G);
@@ -422,23 +525,33 @@ void launch_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
                        (const uint16_t *)a.q, (const T *)c.k, (const T *)c.v, a.block_tables,
                        a.context_lens, c.num_blocks, c.H, G, a.S, a.max_blocks_per_seq, a.window,
                        sl, c.v_scale, a.partition_tokens, a.num_partitions, a.ws_ml, a.ws_acc,
-                       a.ws_hdr);
+                       a.ws_hdr,
+                       Append<E>{(const uint16_t *)a.new_k, (const uint16_t *)a.new_v, c.k_scale,
+                                 c.v_scale});
   };
   // Schedules as for the wavefront kernel.
 #ifndef PKV_GRID_FACTOR
 #define PKV_GRID_FACTOR 4
 #endif
   if (a.flat) {
-    go(decode_mfma_kernel<E, KV, D, BS, kSchedFlat>, dim3(a.flat_grid), plan + merge);
+    go(decode_mfma_kernel<E, KV, D, BS, kSchedFlat, APPEND>, dim3(a.flat_grid), plan + merge);
   } else if (a.num_partitions > 1 && a.S <= kPlanMaxSeqs) {
-    auto kern = decode_mfma_kernel<E, KV, D, BS, kSchedPlan>;
+    auto kern = decode_mfma_kernel<E, KV, D, BS, kSchedPlan, APPEND>;
     const int64_t cells = (int64_t)a.S * a.num_partitions * c.H;
     const int grid = (int)std::min<int64_t>(cells, PKV_GRID_FACTOR * (int64_t)resident_workgroups((const void *)kern, 256, plan + merge));
     go(kern, dim3(grid), plan + merge);
   } else {
-    go(decode_mfma_kernel<E, KV, D, BS, kSchedGrid>,
+    go(decode_mfma_kernel<E, KV, D, BS, kSchedGrid, APPEND>,
        dim3((unsigned)a.num_partitions, (unsigned)c.H, (unsigned)a.S), merge);
   }
+}
+
+// Appending calls run their own instantiations, so that plain decode keeps
+// its register budget.
+template <typename E, typename KV, int D, int BS>
+void launch_t(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
+  if (a.new_k != nullptr) launch_ta<E, KV, D, BS, true>(c, a, stream);
+  else launch_ta<E, KV, D, BS, false>(c, a, stream);
 }
 
 template <typename E, typename KV = E>
@@ -454,7 +567,7 @@ void launch_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
 template <typename E, typename KV, int D, int BS>
 int flat_grid_t(int G, int S) {
   const size_t dyn = sizeof(int) * (size_t)((S + 1 + 3) & ~3) + merge_bytes<D>(G);
-  return resident_workgroups((const void *)decode_mfma_kernel<E, KV, D, BS, kSchedFlat>, 256, dyn);
+  return resident_workgroups((const void *)decode_mfma_kernel<E, KV, D, BS, kSchedFlat, false>, 256, dyn);
 }
 
 template <typename E, typename KV = E>

@@ -193,7 +193,9 @@ pkv_status launch_decode(const pkv::CacheDesc &c, const pkv::DecodeArgs &a, cons
                          hipStream_t stream) {
   hipError_t e = plan.mfma ? pkv::launch_decode_mfma(c, a, stream) : pkv::launch_decode_valu(c, a, stream);
   if (e != hipSuccess) return hip_status(e, "paged_decode launch");
-  if (plan.reduce()) {
+  // An appending call's reduce kernel also stores the new tokens: it runs
+  // even when there is nothing to reduce.
+  if (plan.reduce() || a.new_k != nullptr) {
     e = pkv::launch_decode_reduce(c, a, stream);
     if (e != hipSuccess) return hip_status(e, "paged_decode reduce launch");
   }
@@ -390,6 +392,32 @@ pkv_status pkv_paged_decode_window(const pkv_cache *cache, void *out, int32_t ou
                       context_lens, num_seqs, max_context_len, sliding_window, scale,
                       partition_size, workspace, ws_bytes, &a, &plan);
   if (st) return st;
+  st = launch_decode(c, a, plan, stream);
+  return st ? st : ok();
+}
+
+pkv_status pkv_paged_decode_append(const pkv_cache *cache, const void *key, const void *value,
+                                   void *out, int32_t out_dtype, const void *q,
+                                   int32_t num_q_heads, const int32_t *block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                   int32_t num_seqs, int32_t max_context_len,
+                                   int32_t sliding_window, float scale, int32_t partition_size,
+                                   void *workspace, size_t ws_bytes, hipStream_t stream) {
+  pkv::CacheDesc c;
+  pkv_status st = check_cache(cache, &c);
+  if (st) return st;
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID, "num_seqs < 0");
+  if (num_seqs == 0) return ok();
+  if (!key || !value) return fail(PKV_ERR_INVALID, "key/value is NULL");
+  if (!aligned16(key) || !aligned16(value)) return fail(PKV_ERR_INVALID, "key/value must be 16-byte aligned");
+  pkv::DecodeArgs a;
+  DecodePlan plan;
+  st = prepare_decode(c, out, out_dtype, q, num_q_heads, block_tables, max_blocks_per_seq,
+                      context_lens, num_seqs, max_context_len, sliding_window, scale,
+                      partition_size, workspace, ws_bytes, &a, &plan);
+  if (st) return st;
+  a.new_k = key;
+  a.new_v = value;
   st = launch_decode(c, a, plan, stream);
   return st ? st : ok();
 }

@@ -1,6 +1,8 @@
 // Device-side helpers shared by the pkv HIP kernels (gfx950, wave64).
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -289,6 +291,78 @@ __device__ __forceinline__ u32x2 load8_stream(const void *p) {
 }
 __device__ __forceinline__ uint32_t load4_stream(const void *p) {
   return __builtin_nontemporal_load((const uint32_t *)p);
+}
+
+// ---- the new token of an appending decode call ----------------------------
+// The new token's key and value rows (model dtype Q, [seq][kv head][D]) and,
+// for an 8-bit cache, the scales its codes are quantised with; read by the
+// appending instantiations of the decode kernels.
+template <typename Q>
+struct Append {
+  const typename Q::storage *k;
+  const typename Q::storage *v;
+  float k_scale, v_scale;
+};
+
+// 16 bytes of cache-format key data from the input row at src: the same bits
+// for a 16/32-bit cache; for an 8-bit cache the E4M3 codes of 16 inputs
+// (x / scale, one fp32 division each, as the scatter stores them).
+template <typename E, typename Q>
+__device__ __forceinline__ u32x4 cache_piece(const typename Q::storage *src, float scale) {
+  if constexpr (E::kBytes == 1) {
+    float f[16];
+    unpack16<Q>(*(const u32x4 *)src, f);
+    unpack16<Q>(*(const u32x4 *)(src + 8), f + 8);
+    u32x4 w = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i >> 2] |= f32_to_fp8_bits(__fdiv_rn(f[i], scale)) << (8 * (i & 3));
+    return w;
+  } else {
+    return *(const u32x4 *)src;
+  }
+}
+
+// One cache-format element (its bits, in the low E::kBytes bytes) of input x.
+template <typename E, typename Q>
+__device__ __forceinline__ uint32_t cache_elem(typename Q::storage x, float scale) {
+  if constexpr (E::kBytes == 1) {
+    float f;
+    if constexpr (std::is_same<Q, F16>::value) f = f16_bits_to_f32(x);
+    else f = bf16_bits_to_f32(x);
+    return f32_to_fp8_bits(__fdiv_rn(f, scale));
+  } else if constexpr (E::kBytes == 2) {
+    return (uint32_t)x;
+  } else {
+    return __builtin_bit_cast(uint32_t, x);
+  }
+}
+
+// The value of one cache element from its bits (low E::kBytes bytes), as
+// unpack16 decodes it.
+template <typename E>
+__device__ __forceinline__ float elem_value(uint32_t bits) {
+  float f[16];
+  unpack16<E>(u32x4{bits, 0u, 0u, 0u}, f);
+  return f[0];
+}
+
+// Stores the low EB bytes of bits at p.
+template <int EB>
+__device__ __forceinline__ void store_bits(void *p, uint32_t bits) {
+  if constexpr (EB == 1) *(uint8_t *)p = (uint8_t)bits;
+  else if constexpr (EB == 2) *(uint16_t *)p = (uint16_t)bits;
+  else *(uint32_t *)p = bits;
+}
+
+// v with element e (of EB bytes each) replaced by the low EB bytes of bits.
+template <int EB>
+__device__ __forceinline__ u32x4 put_elem(u32x4 v, int e, uint32_t bits) {
+  const int word = e * EB / 4, sh = (e * EB % 4) * 8;
+  const uint32_t mask = (EB == 4 ? 0xffffffffu : ((1u << (8 * EB)) - 1u)) << sh;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    if (w == word) v[w] = (v[w] & ~mask) | ((bits << sh) & mask);
+  return v;
 }
 
 }  // namespace pkv

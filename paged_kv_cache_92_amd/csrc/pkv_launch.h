@@ -51,6 +51,10 @@ struct DecodeArgs {
   float *ws_ml;
   float *ws_acc;
   int *ws_hdr;
+  // Appending call: the new token's key and value rows, [S][Hkv][D] in the
+  // model dtype (nullptr: plain decode).
+  const void *new_k = nullptr;
+  const void *new_v = nullptr;
 };
 
 struct PrefillArgs {

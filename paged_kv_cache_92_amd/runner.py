@@ -108,6 +108,18 @@ class DeviceWorkload:
                                  int(qlens.max()), wl.max_context_len, scale=wl.scale, out=out,
                                  out_dtype=out_dtype)
 
+    def append_attend(self, cache, partition_size=None, out=None, workspace=None, out_dtype=None):
+        """The decode step's scatter and attention as one appending call (the
+        step's key/value rows are one per sequence, for position L-1)."""
+        wl = self.wl
+        assert wl.mode == "decode"
+        _, key, value, _ = self.step
+        ps = wl.partition_size if partition_size is None else partition_size
+        return pkv.paged_decode_append(cache, key, value, self.q, self.block_tables,
+                                       self.context_lens, wl.max_context_len, scale=wl.scale,
+                                       partition_size=ps, out=out, workspace=workspace,
+                                       out_dtype=out_dtype, sliding_window=wl.window)
+
     def attend_split(self, cache, how, out, workspace=None):
         """A mixed step served another way, for comparison: ``"sequential"`` is
         a decode call then a prefill call on one stream, ``"unified"`` one

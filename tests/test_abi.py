@@ -117,6 +117,21 @@ def test_window_and_mixed_argument_checks():
     assert mixed(0, 0) == 0                           # nothing to do
 
 
+def test_append_argument_checks():
+    lib = pkv.lib()
+    d = _desc()
+    app = lambda key=FAKE, value=FAKE, S=2, w=0, out=FAKE: lib.pkv_paged_decode_append(  # noqa: E731
+        ctypes.byref(d), key, value, out, 1, FAKE, 2, FAKE, 4, FAKE, S, 64, w, 0.125, 0, None, 0,
+        None)
+    assert app(key=None) == 1                         # no key rows
+    assert "key" in lib.pkv_last_error().decode()
+    assert app(value=ctypes.c_void_p(0x30008)) == 1   # misaligned value rows
+    assert app(w=-1) == 1                             # as for the windowed decode
+    assert app(out=None) == 1
+    assert app(S=-1) == 1
+    assert app(key=None, value=None, out=None, S=0) == 0   # zero sequences: no-op
+
+
 def test_empty_scatter_and_copy_are_no_ops():
     lib = pkv.lib()
     d = _desc()
