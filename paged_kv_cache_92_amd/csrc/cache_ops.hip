@@ -9,21 +9,21 @@ namespace pkv {
 namespace {
 
 // Slot scatter ("reshape_and_cache", [vLLM] PagedAttention, blog.secrett2633.cloud,
-// section "PagedAttention 커널: 비연속 메모리 접근").  One workgroup moves 16
-// consecutive tokens of one head.  Key rows are copied 16 bytes at a time into
+// section "PagedAttention 커널: 비연속 메모리 접근").  One workgroup moves kTok
+// (16, or 64 for large batches: more loads in flight per thread) consecutive
+// tokens of one head.  Key rows are copied 16 bytes at a time into
 // the key tiles, whose rows are cut into 64-byte pieces ([D/X][B][X]).  Value rows are transposed through LDS so that
 // lanes write consecutive tokens of one dimension: when the 16 slots are
 // consecutive (a prompt chunk) each dimension row of a value tile receives
 // contiguous runs.  Any slot mapping is handled (negative or out-of-range
 // slots are skipped).
-template <int EB, int D>
+template <int EB, int D, int kTok>
 __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict__ key,
                                                       const uint8_t *__restrict__ value,
                                                       const int64_t *__restrict__ slots,
                                                       uint8_t *__restrict__ kpool,
                                                       uint8_t *__restrict__ vpool, int64_t T, int H,
                                                       int B, int64_t nslots) {
-  constexpr int kTok = 16;
   constexpr int VEC = 16 / EB;       // elements per 16-byte chunk
   constexpr int CH = D / VEC;        // chunks per (token, head) row
   constexpr int X = 64 / EB;         // elements per 64-byte key piece (4 chunks)
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict_
   const int tid = threadIdx.x;
   // The rows' loads do not depend on the slots: they are issued together with
   // the slot loads, and only the stores wait for the barrier.
-  constexpr int NCH = kTok * CH;           // 16-byte chunks of the 16 rows
+  constexpr int NCH = kTok * CH;           // 16-byte chunks of the kTok rows
   constexpr int PER = (NCH + 255) / 256;   // per thread (256 threads)
   u32x4 kc[PER];
 #pragma unroll
@@ -82,8 +82,10 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict_
         kc[i];
   }
   Elem *vp = (Elem *)vpool;
+  // 16-token groups: a wave writes 4 dimensions x 16 tokens.
   for (int c = tid; c < D * kTok; c += blockDim.x) {
-    const int tt = c % kTok, e = c / kTok;
+    const int r = c % (D * 16);
+    const int tt = c / (D * 16) * 16 + r % 16, e = r / 16;
     const int64_t sl = sslot[tt];
     if (sl < 0) continue;
     const int64_t blk = sl >> lgB;
@@ -254,8 +256,16 @@ hipError_t launch_reshape_and_cache(const CacheDesc &c, const void *key, const v
   if (T == 0) return hipSuccess;
   const dim3 grid((unsigned)((T + 15) / 16), (unsigned)c.H);
   const int64_t nslots = c.num_blocks * c.B;
-  auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const uint8_t *)key, (const uint8_t *)value,
+  // Large batches of 16-bit rows (prompt chunks) take 64 tokens per workgroup.
+  const bool wide = T >= 2048 && c.elt_bytes() == 2;
+  const dim3 grid64((unsigned)((T + 63) / 64), (unsigned)c.H);
+  auto go = [&](auto kern16, auto kern64) {
+    if (wide)
+      hipLaunchKernelGGL(kern64, grid64, dim3(256), 0, stream, (const uint8_t *)key,
+                         (const uint8_t *)value, slots, (uint8_t *)c.k, (uint8_t *)c.v, T, c.H, c.B,
+                         nslots);
+    else
+      hipLaunchKernelGGL(kern16, grid, dim3(256), 0, stream, (const uint8_t *)key, (const uint8_t *)value,
                        slots, (uint8_t *)c.k, (uint8_t *)c.v, T, c.H, c.B, nslots);
   };
   auto go8 = [&](auto kern) {
@@ -271,11 +281,12 @@ hipError_t launch_reshape_and_cache(const CacheDesc &c, const void *key, const v
       else go8(scatter_fp8_kernel<BF16, 128>);
     }
   } else if (c.elt_bytes() == 4) {
-    if (c.D == 64) go(scatter_kernel<4, 64>);
-    else go(scatter_kernel<4, 128>);
+    // fp32 rows: 16 tokens already fill a thread's loads (prefill takes no fp32 cache).
+    if (c.D == 64) go(scatter_kernel<4, 64, 16>, scatter_kernel<4, 64, 16>);
+    else go(scatter_kernel<4, 128, 16>, scatter_kernel<4, 128, 16>);
   } else {
-    if (c.D == 64) go(scatter_kernel<2, 64>);
-    else go(scatter_kernel<2, 128>);
+    if (c.D == 64) go(scatter_kernel<2, 64, 16>, scatter_kernel<2, 64, 64>);
+    else go(scatter_kernel<2, 128, 16>, scatter_kernel<2, 128, 64>);
   }
   return hipGetLastError();
 }
