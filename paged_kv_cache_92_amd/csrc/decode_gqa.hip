@@ -110,11 +110,16 @@ __device__ __forceinline__ void mfma_item(
   constexpr bool kFP8 = KV::kBytes == 1;
   constexpr int KS = D / 32;    // k-steps of the score product
   constexpr int NT = D / 16;    // 16-dimension tiles of the output
-  // 8-token blocks are taken two at a time: a step always covers GB tokens.
-  constexpr bool kPair = BS == 8;
-  constexpr int GB = kPair ? 16 : BS;
+  // 8-token blocks, and 16-token blocks of an 8-bit cache, are taken two at a
+  // time: a step covers GB tokens (the 8-bit cache's fixed work per token
+  // weighs twice as much per byte, and a 32-token step halves it).
+#ifndef PKV_MFMA_PAIR16_FP8
+#define PKV_MFMA_PAIR16_FP8 1
+#endif
+  constexpr bool kPair = BS == 8 || (BS == 16 && kFP8 && PKV_MFMA_PAIR16_FP8);
+  constexpr int GB = kPair ? 2 * BS : BS;
   constexpr int SUB = GB / 16;  // 16-token sub-tiles per step
-  // 32-token blocks: the two sub-tiles' score rows are interleaved so each
+  // 32-token steps: the two sub-tiles' score rows are interleaved so each
   // lane ends up with 8 consecutive tokens, and P.V runs as 16x16x32 products
   // over 16-byte V^T operands.
   constexpr bool kWide = GB == 32;
@@ -174,9 +179,10 @@ __device__ __forceinline__ void mfma_item(
     const TS *knew = nullptr;
     if constexpr (kApp && !kFP8) knew = (const TS *)ap.k + ((size_t)s * Hkv + hkv) * D + 8 * g4;
     int64_t phys = uniform(bt[lb]);
-    // Key and value tiles this lane reads: one block's, or for 8-token blocks
-    // those of block lb + t/8 for the lane's token t of the 16 (key row n16,
-    // value tokens 4*g4..+4).  The second block of a pair is read only if the
+    // Key and value tiles this lane reads: one block's, or for a pair those of
+    // block lb + t/BS for the lane's tokens t (key rows: block n16 / 8 of the
+    // pair for every sub-tile; value tokens 4*g4..+4 or, 32-token steps,
+    // 8*g4..+8: block g4 / 2).  The second block of a pair is read only if the
     // item covers it (past the item its tokens are masked and block lb is
     // read in its place); there an out-of-range id reads block 0 instead of
     // faulting, while a single block with such an id is skipped.
@@ -200,8 +206,8 @@ __device__ __forceinline__ void mfma_item(
       const int64_t pk = n16 < 8 ? phys : phys2, pv = g4 < 2 ? phys : phys2;
       kt = kpool + ((size_t)pk * Hkv + hkv) * (BS * D);
       vt = vpool + ((size_t)pv * Hkv + hkv) * (D * BS);
-      krow = (n16 & 7) - n16;        // token_of_row gives n16; the tile holds it at n16 % 8
-      vtok = 4 * (g4 & 1) - 4 * g4;  // tokens 4*g4.. sit at 4*(g4 % 2).. of their tile
+      krow = -BS * (n16 >> 3);   // the lane's key rows sit BS*(n16/8) earlier in their tile
+      vtok = -BS * (g4 >> 1);    // and its value tokens BS*(g4/2) earlier
     }
     u32x4 ka[SUB][KS];
     if constexpr (kFP8) {
@@ -237,11 +243,11 @@ __device__ __forceinline__ void mfma_item(
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         if constexpr (kFP8) {
-          const u32x2 raw = load8_stream(vt + (16 * nt + n16) * BS + 8 * g4);
+          const u32x2 raw = load8_stream(vt + (16 * nt + n16) * BS + 8 * g4 + vtok);
           const u32x2 lo = widen4<E>(raw[0]), hi = widen4<E>(raw[1]);
           vw[nt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         } else {
-          vw[nt] = load16_stream(vt + (16 * nt + n16) * BS + 8 * g4);
+          vw[nt] = load16_stream(vt + (16 * nt + n16) * BS + 8 * g4 + vtok);
         }
       }
     } else {
