@@ -99,3 +99,18 @@ def test_append_llama13b():
         assert np.array_equal(bits_of(dev).view(np.uint8), np.ascontiguousarray(ref).view(np.uint8))
     rows = sorted({0, int(np.argmin(wl.context_lens)), int(np.argmax(wl.context_lens)), wl.S - 1})
     assert_close(values_of(o32)[rows], sampled_rows(wl, k_ref, v_ref, rows), wl.dtype, wl.name)
+
+
+@pytest.mark.parametrize("G,part", [(1, 16), (4, 0)])
+def test_append_beyond_plan_limit(G, part):
+    # More sequences than the device-built plan takes: the grid schedule runs,
+    # and the reduce kernel stores 8200 new tokens.
+    lens = list(np.random.default_rng(5).integers(1, 49, size=8200))
+    wl = W.make_decode(f"app_many_{G}_{part}", 91 + G + part, lambda rng: lens, Hq=2 * G, Hkv=2,
+                       d=64, B=16, dtype=W.F16, max_context_len=48, partition_size=part)
+    cache, o32 = _both_ways(wl)
+    k_ref, v_ref = fill_pools(wl)
+    for dev, ref in ((cache.k_pool, k_ref), (cache.v_pool, v_ref)):
+        assert np.array_equal(bits_of(dev).view(np.uint8), np.ascontiguousarray(ref).view(np.uint8))
+    rows = sorted(set(np.random.default_rng(6).choice(wl.S, size=24, replace=False).tolist()) | {8199})
+    assert_close(values_of(o32)[rows], sampled_rows(wl, k_ref, v_ref, rows), wl.dtype, wl.name)
