@@ -115,8 +115,30 @@ def measured_traffic(config):
     return int(round(e["fetch_bytes"] + e["write_bytes"]))
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _all_cores(calls, cores):
+    """Wall time of the same oracle calls spread over `cores` threads (the oracle's C
+    entry points run without the interpreter lock and keep no shared state)."""
+    from concurrent.futures import ThreadPoolExecutor
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=cores) as pool:
+        list(pool.map(lambda f: f(), calls))
+    return time.perf_counter() - t0
+
+
 def cpu_baseline(wl, budget_s):
-    """The oracle as it stands, single-threaded, on a bounded sample of the same input."""
+    """The oracle as it stands on a bounded sample of the same input: one thread, then the
+    same sample over all host cores (up to 16 threads)."""
     import numpy as np
 
     import oracle
@@ -129,41 +151,57 @@ def cpu_baseline(wl, budget_s):
             oracle.copy_blocks(k, v, wl.cache_dtype, op.pairs)
     elt = {0: 4, 1: 2, 2: 2, 3: 1}[wl.cache_dtype]
     kv = dict(q_dtype=wl.dtype, k_scale=wl.k_scale, v_scale=wl.v_scale)
+    cores = max(1, min(16, os.cpu_count() or 1))
     t0 = time.perf_counter()
     n = 0
     kv_bytes = 0
     if wl.mode == "decode":
+        def seq(i):
+            return lambda: oracle.paged_attention_rows(
+                k, v, wl.cache_dtype, wl.q[i:i + 1], wl.block_tables, wl.context_lens, [i],
+                [int(wl.context_lens[i]) - 1], wl.scale, window=wl.window, **kv)
         while n < wl.S and (time.perf_counter() - t0) < budget_s:
-            oracle.paged_attention_rows(k, v, wl.cache_dtype, wl.q[n:n + 1], wl.block_tables,
-                                        wl.context_lens, [n], [int(wl.context_lens[n]) - 1], wl.scale,
-                                        window=wl.window, **kv)
+            seq(n)()
             L = int(wl.context_lens[n])
             kv_bytes += (min(L, wl.window) if wl.window else L) * 2 * wl.num_kv_heads * wl.head_dim * elt
             n += 1
         el = time.perf_counter() - t0
+        el_all = _all_cores([seq(i) for i in range(n)], cores)
         return {"value": round(kv_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                 "tokens_per_s": round(n / el, 3),
+                "all_cores": {"value": round(kv_bytes / el_all / 1e9, 4), "cores": cores,
+                              "tokens_per_s": round(n / el_all, 3)},
+                "cpu_model": _cpu_model(),
                 "sample": f"decode of the first {n} of {wl.S} sequences (all {wl.num_q_heads} heads): "
-                          f"block-table reassembly + fp64 softmax attention, {el:.1f} s wall, 1 thread"}
+                          f"block-table reassembly + fp64 softmax attention, {el:.1f} s wall on 1 "
+                          f"thread, {el_all:.1f} s on {cores}"}
     qsl = wl.query_start_loc
     flops = 0.0
-    rows = []
+
+    def row(r):
+        s_ = int(np.searchsorted(qsl, r, side="right") - 1)
+        pos = int(wl.context_lens[s_] - (qsl[s_ + 1] - qsl[s_]) + (r - qsl[s_]))
+        return pos, lambda: oracle.paged_attention_rows(
+            k, v, wl.cache_dtype, wl.q[r:r + 1], wl.block_tables, wl.context_lens, [s_], [pos],
+            wl.scale, **kv)
     while n < qsl[-1] and (time.perf_counter() - t0) < budget_s:
-        s = int(np.searchsorted(qsl, n, side="right") - 1)
-        pos = int(wl.context_lens[s] - (qsl[s + 1] - qsl[s]) + (n - qsl[s]))
-        oracle.paged_attention_rows(k, v, wl.cache_dtype, wl.q[n:n + 1], wl.block_tables, wl.context_lens,
-                                    [s], [pos], wl.scale, **kv)
+        pos, call = row(n)
+        call()
         flops += (pos + 1) * wl.num_q_heads * wl.head_dim * 4
-        rows.append(n)
         n += 1
     el = time.perf_counter() - t0
+    el_all = _all_cores([row(r)[1] for r in range(n)], cores)
+    common = {"kind": "oracle", "cores": 1, "cpu_model": _cpu_model()}
     if wl.mode == "mixed":
-        return {"value": round(n / el, 3), "unit": "rows/s", "cores": 1, "kind": "oracle",
+        return {"value": round(n / el, 3), "unit": "rows/s", **common,
+                "all_cores": {"value": round(n / el_all, 3), "cores": cores},
                 "sample": f"first {n} query rows of {int(qsl[-1])} (decode rows first, all "
-                          f"{wl.num_q_heads} heads), {el:.1f} s wall, 1 thread"}
-    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+                          f"{wl.num_q_heads} heads), {el:.1f} s wall on 1 thread, {el_all:.1f} s on "
+                          f"{cores}"}
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", **common,
+            "all_cores": {"value": round(flops / el_all / 1e12, 6), "cores": cores},
             "sample": f"first {n} query rows of {int(qsl[-1])} (all {wl.num_q_heads} heads), "
-                      f"{el:.1f} s wall, 1 thread"}
+                      f"{el:.1f} s wall on 1 thread, {el_all:.1f} s on {cores}"}
 
 
 def main():
