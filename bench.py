@@ -115,6 +115,46 @@ def measured_traffic(config):
     return int(round(e["fetch_bytes"] + e["write_bytes"]))
 
 
+def read_probe_gbps(torch, gib=4, reps=5, tile=4096, waves=65536):
+    """Read ceiling of the memory system for the decode kernels' access pattern: 4 KiB tiles in
+    random order, non-temporal 16-byte loads (paged_kv_cache_92_amd/probe).  GB/s."""
+    import ctypes
+
+    import numpy as np
+
+    from paged_kv_cache_92_amd.build import PROBE_LIB
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is not built: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.pkv_probe_read_tiles.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = gib << 30
+    ntiles = nbytes // tile
+    tpw = ntiles // waves
+    used = waves * tpw
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    perm = np.random.default_rng(0).permutation(used).astype(np.int32)
+    assert 0 <= perm.min() and perm.max() < ntiles
+    idx = torch.from_numpy(perm).cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def run():
+        rc = lib.pkv_probe_read_tiles(ctypes.c_void_p(buf.data_ptr()), ctypes.c_void_p(idx.data_ptr()),
+                                      tile, waves, tpw, ctypes.c_void_p(sink.data_ptr()), stream)
+        if rc != 0:
+            raise RuntimeError(f"read probe launch failed ({rc})")
+    run()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    return used * tile / (a.elapsed_time(b) * 1e-3 / reps) / 1e9
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as fh:
@@ -227,6 +267,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--read-probe-gib", type=int, default=0,
+                    help="only run the HBM read-ceiling probe over this many GiB of random 4 KiB tiles")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="decode workloads: skip the read-ceiling probe after the timed steps")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported",
@@ -249,6 +293,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "launches": args.steps}), flush=True)
+        return
+    if args.read_probe_gib:
+        g = read_probe_gbps(torch, gib=args.read_probe_gib, reps=args.steps)
+        print(json.dumps({"read_probe_GBps": round(g, 1), "tile_bytes": 4096,
+                          "bytes": args.read_probe_gib << 30, "launches": args.steps}), flush=True)
         return
     pkv.lib()
     t0 = time.time()
@@ -364,6 +413,12 @@ def main():
                          "algorithmic_bytes_per_launch": kv,
                          "avg_launch_us": round(attn_avg * 1e3, 2)},
         })
+        if not args.no_read_probe:
+            probe = read_probe_gbps(torch)
+            res["roofline"]["read_probe_GBps"] = round(probe, 1)
+            res["roofline"]["frac_of_read_probe"] = round(gbs_attn / probe, 4)
+            log(f"[bench] read-ceiling probe: {probe:.0f} GB/s (decode call at "
+                f"{100 * gbs_attn / probe:.1f}% of it)")
         if args.config.startswith("llama13b"):
             res["decode_tokens_per_s_40_layer_attention_only"] = round(wl.S / (40 * ms_step * 1e-3), 1)
         if wl.window:

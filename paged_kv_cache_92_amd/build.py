@@ -39,6 +39,22 @@ def build(verbose: bool = False, out: str = LIB, extra: tuple[str, ...] = ()) ->
     return out
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "hbm_read_probe.hip")
+PROBE_LIB = os.path.join(PKG, "probe", "libpkv_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The HBM read-ceiling probe bench.py runs (not part of libpkv.so)."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_probe(verbose=True)
     sys.exit(0)

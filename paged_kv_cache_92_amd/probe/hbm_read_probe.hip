@@ -1,0 +1,50 @@
+// HBM read-ceiling probe: how fast the memory system delivers 4 KiB tiles in
+// random order to waves that read them with non-temporal 16-byte loads, the
+// access pattern of the paged decode kernels (one 4 KiB key or value tile per
+// (block, head) at 16-token blocks of head_dim 128, fp16).  Measurement
+// infrastructure only: the attention library does not use it.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Wave w reads tiles idx[w * tiles_per_wave + i], i < tiles_per_wave, each
+// TILE bytes as TILE/1024 loads of 16 bytes per lane.  The xor of everything
+// read goes to sink only if it equals a value no input produces, so the
+// loads stay live and nothing is stored.
+template <int TILE>
+__global__ __launch_bounds__(256) void read_tiles(const uint8_t *__restrict__ buf,
+                                                  const int32_t *__restrict__ idx,
+                                                  int tiles_per_wave, uint32_t *__restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int i = 0; i < tiles_per_wave; ++i) {
+    const uint8_t *tile = buf + (size_t)idx[wave * tiles_per_wave + i] * TILE;
+#pragma unroll
+    for (int c = 0; c < TILE / 1024; ++c)
+      acc ^= __builtin_nontemporal_load((const u32x4 *)(tile + c * 1024 + lane * 16));
+  }
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9e3779b9u && lane == 0) sink[0] = 1u;
+}
+
+}  // namespace
+
+// waves must be a multiple of 4; every idx entry must lie in [0, ntiles) for a
+// buffer of ntiles * tile_bytes bytes (checked by the caller on the host).
+extern "C" int pkv_probe_read_tiles(const void *buf, const int32_t *idx, int tile_bytes, int waves,
+                                    int tiles_per_wave, uint32_t *sink, hipStream_t stream) {
+  if (waves <= 0 || waves % 4 != 0 || tiles_per_wave <= 0) return 1;
+  const dim3 grid((unsigned)(waves / 4)), block(256);
+  if (tile_bytes == 4096)
+    hipLaunchKernelGGL(read_tiles<4096>, grid, block, 0, stream, (const uint8_t *)buf, idx,
+                       tiles_per_wave, sink);
+  else if (tile_bytes == 8192)
+    hipLaunchKernelGGL(read_tiles<8192>, grid, block, 0, stream, (const uint8_t *)buf, idx,
+                       tiles_per_wave, sink);
+  else
+    return 1;
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
