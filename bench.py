@@ -155,6 +155,62 @@ def read_probe_gbps(torch, gib=4, reps=5, tile=4096, waves=65536):
     return used * tile / (a.elapsed_time(b) * 1e-3 / reps) / 1e9
 
 
+def cache_ops(torch, pkv, steps):
+    """Block copy (copy-on-write) and slot scatter timed alone, at the chunked-prefill pool shape
+    (32 KV heads, block 16, head_dim 128, bf16: 128 KiB per block and tensor).  Bytes moved count
+    every element read and written once."""
+    import numpy as np
+    H, B, d, nb = 32, 16, 128, 4096
+    cache = pkv.PagedKVCache(nb, H, B, d, torch.bfloat16)
+    cache.k_pool.view(torch.int16).random_()
+    cache.v_pool.view(torch.int16).random_()
+    rng = np.random.default_rng(11)
+    res = {}
+
+    def timed(fn):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / steps
+
+    blk = H * B * d * 2
+    for n in (64, 1024):
+        ids = rng.permutation(nb)[:2 * n].astype(np.int32)
+        pairs = torch.from_numpy(np.stack([ids[:n], ids[n:]], axis=1).copy()).cuda()
+        us = timed(lambda: pkv.copy_blocks(cache, pairs))
+        moved = n * 2 * blk * 2
+        res[f"copy_blocks_{n}_pairs"] = {"us": round(us, 2), "bytes": moved,
+                                         "GBps": round(moved / us / 1e3, 1),
+                                         "frac": round(moved / us / 1e3 / HBM_PEAK_GBS, 4)}
+    # A plain device copy of 2 GiB for comparison (reads and writes 2 GiB each).
+    src = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    us = timed(lambda: dst.copy_(src))
+    res["device_copy_2GiB"] = {"us": round(us, 2), "bytes": 2 * (2 << 30),
+                               "GBps": round(2 * (2 << 30) / us / 1e3, 1),
+                               "frac": round(2 * (2 << 30) / us / 1e3 / HBM_PEAK_GBS, 4)}
+    del src, dst
+    for T, kind in ((4096, "chunk"), (64, "decode")):
+        key = torch.randn(T, H, d, device="cuda").to(torch.bfloat16)
+        value = torch.randn(T, H, d, device="cuda").to(torch.bfloat16)
+        if kind == "chunk":      # one 4096-token run of consecutive slots
+            slots = np.arange(T, dtype=np.int64) + 7 * B
+        else:                    # one token in each of 64 scattered blocks
+            slots = rng.permutation(nb)[:T].astype(np.int64) * B + rng.integers(0, B, size=T)
+        sl = torch.from_numpy(slots).cuda()
+        us = timed(lambda: pkv.reshape_and_cache(cache, key, value, sl))
+        moved = T * H * d * 2 * 2 * 2
+        res[f"scatter_{T}_{kind}"] = {"us": round(us, 2), "bytes": moved,
+                                      "GBps": round(moved / us / 1e3, 1),
+                                      "frac": round(moved / us / 1e3 / HBM_PEAK_GBS, 4)}
+    return res
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as fh:
@@ -269,6 +325,8 @@ def main():
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--read-probe-gib", type=int, default=0,
                     help="only run the HBM read-ceiling probe over this many GiB of random 4 KiB tiles")
+    ap.add_argument("--cache-ops", action="store_true",
+                    help="only time the block copy and the slot scatter alone (prefill pool shape)")
     ap.add_argument("--no-read-probe", action="store_true",
                     help="decode workloads: skip the read-ceiling probe after the timed steps")
     args = ap.parse_args()
@@ -293,6 +351,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "launches": args.steps}), flush=True)
+        return
+    if args.cache_ops:
+        print(json.dumps({"cache_ops": cache_ops(torch, pkv, args.steps), "steps": args.steps,
+                          "peak_GBps": HBM_PEAK_GBS}), flush=True)
         return
     if args.read_probe_gib:
         g = read_probe_gbps(torch, gib=args.read_probe_gib, reps=args.steps)
