@@ -2,8 +2,10 @@
  * pkv — paged KV-cache attention for AMD Instinct MI355X (gfx950).
  *
  * C ABI of libpkv.so.  Every pointer argument is device memory owned by the
- * caller unless a comment says "host"; the library allocates nothing, frees
- * nothing and keeps no handles between calls.  Every call validates its
+ * caller unless a comment says "host"; the library allocates no device
+ * memory, and the only handles it keeps between calls are, per device, the
+ * side stream and two events that pkv_paged_mixed creates on first use
+ * (default priority, kept until the process ends).  Every call validates its
  * scalar arguments on the host, returns a status code (nothing is thrown
  * across the ABI), and on PKV_OK has queued its kernels asynchronously on
  * `stream`.  On any other status nothing was launched and pkv_last_error()
@@ -43,9 +45,10 @@
  *
  * A (block, head) tile of either pool is B*d contiguous elements.
  * q, out, key and value rows are [tokens][heads][head_dim], contiguous.
- * Query/output and cache share one dtype.  Supported: dtype f32/f16/bf16,
- * head_dim 64 or 128, block_size 8, 16 or 32.  Base pointers must be
- * 16-byte aligned.
+ * Query/output and cache share one dtype, except over an 8-bit (E4M3)
+ * cache, whose queries, outputs and key/value rows are f16 or bf16.
+ * Supported: dtype f32/f16/bf16/fp8-e4m3, head_dim 64 or 128, block_size 8,
+ * 16 or 32.  Base pointers must be 16-byte aligned.
  *
  * Device-side contract (not checked on the device; pkv_validate_host checks
  * it on host copies): block ids in the first ceil(L/B) table entries of a
