@@ -1,4 +1,5 @@
-// Grouped-query paged decode on the matrix cores (f16/bf16).
+// Grouped-query paged decode on the matrix cores (f16/bf16 queries over an
+// f16, bf16 or 8-bit E4M3 cache).
 //
 // G query heads share one KV head ("Sparse Computation and Memory Management
 // for Efficient LLM Inference", pyy0715.github.io, section "The Hidden Waste
@@ -99,6 +100,9 @@ __device__ __forceinline__ u32x2 widen4(uint32_t w) {
 // merge buffers.  E is the query / matrix-core type; KV the cache element
 // (E itself, or FP8: codes are widened to E right after the loads, the key
 // scale is folded into scale_log2 and v_scale multiplies the merged sums).
+// APPEND: the sequence's new token (position L-1) is taken from the input
+// rows ap.k / ap.v, in cache format, instead of the pool, whose slot is
+// written by the reduce kernel.
 template <typename E, typename KV, int D, int BS, bool APPEND>
 __device__ __forceinline__ void mfma_item(
     float *lds_dyn, int s, int hkv, int b0, int b1, Dest dest, void *__restrict__ out,
