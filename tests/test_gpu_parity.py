@@ -89,6 +89,16 @@ def test_decode_group_sizes_on_matrix_cores():
         _full_check(wl)
 
 
+@pytest.mark.parametrize("B", [8, 16, 32])
+@pytest.mark.parametrize("G", [8, 16])
+def test_fp8_cache_group_sizes_on_matrix_cores(B, G):
+    # Wide groups over an 8-bit cache (16-token blocks run as 32-token pairs).
+    wl = W.make_decode(f"g8_{G}_{B}", 9 + G + B, lambda rng: [1, 16, 17, 47, 200, 255], Hq=2 * G, Hkv=2,
+                       d=128, B=B, dtype=W.F16, max_context_len=256, partition_size=-1)
+    wl.kv_dtype, wl.k_scale, wl.v_scale = W.FP8, float(np.float32(0.02)), float(np.float32(0.03))
+    _full_check(wl)
+
+
 # ----------------------------------------------------------------------------
 # Exactness pins on the GPU path
 # ----------------------------------------------------------------------------
