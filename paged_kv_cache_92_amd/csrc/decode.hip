@@ -580,8 +580,7 @@ void launch_reduce_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream
   const dim3 grid((unsigned)a.Hq, (unsigned)a.S);
   const int mt = a.max_blocks_per_seq * c.B;
   const int G = a.Hq / c.H;
-  const bool mfma = G > 1 && c.dtype != 0;
-  const int HU = mfma ? c.H : a.Hq, GU = mfma ? G : 1;
+  const int HU = a.mfma ? c.H : a.Hq, GU = a.mfma ? G : 1;   // the decode kernel's work units
   NewToken nt;
   if (a.new_k != nullptr) {
     nt.k = a.new_k;

@@ -177,6 +177,7 @@ pkv_status prepare_decode(const pkv::CacheDesc &c, void *out, int32_t out_dtype,
   a->partition_tokens = plan->part.tokens;
   a->num_partitions = plan->part.count;
   a->flat = plan->flat;
+  a->mfma = plan->mfma;
   a->flat_grid = plan->flat_grid;
   a->ws_ml = nullptr;
   a->ws_acc = nullptr;

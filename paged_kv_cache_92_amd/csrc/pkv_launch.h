@@ -44,6 +44,8 @@ struct DecodeArgs {
   int partition_tokens;   // > 0, multiple of B
   int num_partitions;     // ceil(max_context_len / partition_tokens)
   bool flat;              // balanced schedule (partition fields unused)
+  bool mfma = false;      // grouped heads on the matrix cores: one work unit per KV head
+                          // (the decode and the reduce kernels must agree on it)
   int flat_grid;          // its workgroup count
   // Partial rows (running max and denominator in the log2 domain, weighted
   // sums): fixed partitions [S][Hq][num_partitions], balanced schedule
