@@ -473,7 +473,8 @@ def main():
                          "kernel": "paged decode (partial + reduce when split)" if not fused
                          else "appending paged decode (partial + reduce when split)",
                          "algorithmic_bytes_per_launch": kv,
-                         "avg_launch_us": round(attn_avg * 1e3, 2)},
+                         "avg_launch_us": round(attn_avg * 1e3, 2),
+                         "median_launch_us": round(float(np.median(attn_ms)) * 1e3, 2)},
         })
         if not args.no_read_probe:
             probe = read_probe_gbps(torch)
