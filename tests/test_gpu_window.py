@@ -11,7 +11,7 @@ import torch
 
 from paged_kv_cache_92_amd import workloads as W
 from tests.gpu_run import DeviceWorkload, assert_close, bits_of, new_cache, values_of
-from tests.oracle_run import fill_pools, reference_output, sampled_rows
+from tests.oracle_run import fill_pools, sampled_rows
 from tests.test_gpu_parity import _full_check, _pools_equal
 
 pytestmark = pytest.mark.gpu

@@ -4,7 +4,6 @@ Every mutation below is a one-token slip of the kind a hand-written oracle
 could contain; each must make at least one pin in test_oracle_pins fail.
 """
 import os
-import shutil
 
 import pytest
 
