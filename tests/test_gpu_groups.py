@@ -1,0 +1,88 @@
+"""GPU parity for query-head groups that are not powers of two.
+
+Grouped-query attention maps query head hq to KV head hq // G
+("Sparse Computation and Memory Management for Efficient LLM Inference",
+pyy0715.github.io, GQA section; the pages give only the 32-query / 8-KV
+example).  Models also ship groups of 3, 5, 6, 7 and 12.  The matrix-core
+decode stacks a group's G queries into a 16-row operand and leaves the rows
+past G zero, so these sizes exercise the padding and the merge of a partly
+filled tile.  Every case compares whole pools bit for bit and every output
+with the oracle, at the tolerances of the other parity tests.
+"""
+import numpy as np
+import pytest
+
+from paged_kv_cache_92_amd import workloads as W
+from tests.test_gpu_append import _full_check as _append_check
+from tests.test_gpu_mixed import _mixed
+from tests.test_gpu_parity import _full_check, _ragged_prefill
+from tests.test_gpu_window import _sliding
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [1, 15, 16, 17, 31, 32, 33, 100, 255, 256, 257]
+GROUPS = [(3, 128), (5, 64), (6, 64), (7, 128), (12, 128)]   # (G, head_dim)
+KV = {"f16": (W.F16, None), "bf16": (W.BF16, None), "fp8": (W.BF16, W.FP8)}
+
+
+def _fp8(wl):
+    wl.kv_dtype, wl.k_scale, wl.v_scale = W.FP8, float(np.float32(0.02)), float(np.float32(0.03))
+    return wl
+
+
+@pytest.mark.parametrize("G,d", GROUPS, ids=[f"G{g}_d{d}" for g, d in GROUPS])
+@pytest.mark.parametrize("B", [8, 16, 32])
+@pytest.mark.parametrize("kv", list(KV))
+def test_decode_odd_groups(G, d, B, kv):
+    dtype, cache = KV[kv]
+    for part in (0, 64, -1):   # one partition, fixed 64-token partitions, balanced
+        wl = W.make_decode(f"odd_{G}_{d}_{B}_{kv}", 300 + 7 * G + B + d, lambda rng: RAGGED,
+                           Hq=2 * G, Hkv=2, d=d, B=B, dtype=dtype, max_context_len=320,
+                           partition_size=part)
+        if cache == W.FP8:
+            _fp8(wl)
+        _full_check(wl)
+
+
+def test_decode_odd_group_f32_cache():
+    # A 32-bit cache runs grouped heads on the wavefront kernel.
+    for part in (0, 64, -1):
+        wl = W.make_decode("odd_f32", 331, lambda rng: RAGGED, Hq=14, Hkv=2, d=64, B=16,
+                           dtype=W.F32, max_context_len=320, partition_size=part)
+        _full_check(wl)
+
+
+@pytest.mark.parametrize("G", [3, 6, 7])
+@pytest.mark.parametrize("B", [8, 16, 32])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_append_odd_groups(G, B, kv):
+    dtype, cache = KV[kv]
+    for part in (0, -1):
+        wl = W.make_decode(f"oddapp_{G}_{B}_{kv}", 340 + G + B, lambda rng: RAGGED, Hq=2 * G, Hkv=2,
+                           d=128, B=B, dtype=dtype, max_context_len=320, partition_size=part)
+        if cache == W.FP8:
+            _fp8(wl)
+        _append_check(wl)
+
+
+@pytest.mark.parametrize("G,part", [(6, 32), (7, -1), (3, 0)])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_sliding_window_odd_groups(G, part, kv):
+    wl = _sliding(W.BF16, 128, 16, G, partition_size=part, seed=361)
+    assert wl.info["released_blocks"] > 0
+    if kv == "fp8":
+        _fp8(wl)
+    _full_check(wl)
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16], ids=["f16", "bf16"])
+@pytest.mark.parametrize("d,B,G", [(128, 16, 7), (64, 8, 3), (128, 32, 6)])
+def test_prefill_odd_groups(dtype, d, B, G):
+    hist = np.array([0, 5, 16, 33, 200, 7])
+    chunks = [1, 37, 128, 130, 64, 256]
+    _full_check(_ragged_prefill(dtype, d, B, G, hist, chunks))
+
+
+@pytest.mark.parametrize("G,part", [(7, -1), (5, 64)])
+def test_mixed_step_odd_groups(G, part):
+    _full_check(_mixed(W.BF16, 128, 16, G, partition_size=part, seed=371))
