@@ -1,0 +1,76 @@
+"""GPU parity when the running maximum of the online softmax keeps moving.
+
+The block-wise softmax rescales its running sums whenever a later block holds
+a larger score ("vLLM — KV Cache와 PagedAttention 완전 해부", hrletsgo.me,
+"부록"; the aggregation of "vLLM: LLM 서빙 메모리 최적화의 교과서", velog.io,
+section 02).  Random inputs rarely move the maximum after the first few
+blocks.  Here every key is a ramp in its position, so the scores rise (or
+fall) by about 5 log2 units per 16-token block and by about 20 per 64-key
+prefill tile: rising, the maximum grows at every block and passes the
+prefill kernel's lazy-rescale threshold at every tile; falling, it never
+moves after the first block (over an fp32 cache the slope is a quarter of
+that; see test_decode_moving_maximum).  The queries are all ones, so a score is
+sqrt(d) times the key's value.  Pools, gathers and outputs are compared with
+the oracle as in the other parity tests.
+"""
+import numpy as np
+import pytest
+
+from paged_kv_cache_92_amd import workloads as W
+from tests.test_gpu_parity import _full_check, _ragged_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+def _ramp_keys(key, positions, slope, dtype):
+    # key[t][h][e] = slope*pos_t + 0.4 sin(pos_t / 5), the same for every head and dimension.
+    r = (slope * positions + 0.4 * np.sin(positions / 5.0)).astype(np.float32)
+    key[:] = W.round_to(np.broadcast_to(r[:, None, None], key.shape).astype(np.float32), dtype)
+
+
+def _decode(dtype, G, part, slope, lens, kv=None, d=128, B=16):
+    wl = W.make_decode(f"ramp_{G}_{part}_{slope}", 421 + G, lambda rng: lens, Hq=2 * G, Hkv=2, d=d,
+                       B=B, dtype=dtype, max_context_len=1024, partition_size=part)
+    wl.q[:] = W.round_to(np.ones(1, np.float32), dtype)[0]
+    hist, step = wl.setup[0], wl.step_scatter
+    hpos = np.concatenate([np.arange(L - 1) for L in lens]).astype(np.float32)
+    _ramp_keys(hist.key, hpos, slope, dtype)
+    _ramp_keys(step.key, np.asarray(lens, np.float32) - 1, slope, dtype)
+    if kv == W.FP8:
+        # Codes of key / 0.05: a ramp up to ~20 stays inside E4M3's range (448).
+        wl.kv_dtype, wl.k_scale, wl.v_scale = W.FP8, float(np.float32(0.05)), float(np.float32(0.03))
+    return wl
+
+
+@pytest.mark.parametrize("sign", [1, -1], ids=["rising", "falling"])
+@pytest.mark.parametrize("dtype,G,part,B", [(W.F32, 1, 0, 16), (W.F32, 1, 64, 16), (W.F16, 1, 64, 16),
+                                            (W.F16, 1, -1, 8), (W.BF16, 4, 0, 16), (W.BF16, 4, 64, 32),
+                                            (W.BF16, 4, -1, 16), (W.F16, 7, -1, 8)])
+def test_decode_moving_maximum(dtype, G, part, B, sign):
+    # fp32 cache: a quarter of the slope (scores up to ~80 log2 units, still
+    # rising by ~1.3 per block).  At the full slope they reach ~330, where one
+    # fp32 ulp of a score (3e-5) already moves a weight by ~1e-5 relative: no
+    # fp32 computation of the scores meets the 1e-5 bound against fp64 there.
+    slope = sign * (0.005 if dtype == W.F32 else 0.02)
+    _full_check(_decode(dtype, G, part, slope, [300, 513, 1000, 17], B=B))
+
+
+@pytest.mark.parametrize("slope", [0.02, -0.02], ids=["rising", "falling"])
+@pytest.mark.parametrize("G,B", [(1, 16), (4, 16), (4, 32)])
+def test_decode_moving_maximum_fp8_cache(G, B, slope):
+    _full_check(_decode(W.BF16, G, -1, slope, [300, 513, 1000, 17], kv=W.FP8, B=B))
+
+
+@pytest.mark.parametrize("slope", [0.02, -0.02], ids=["rising", "falling"])
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16], ids=["f16", "bf16"])
+@pytest.mark.parametrize("d,B,G", [(128, 16, 1), (64, 8, 4)])
+def test_prefill_moving_maximum(dtype, d, B, G, slope):
+    hist = np.array([0, 5, 200, 33])
+    chunks = [256, 37, 130, 200]
+    wl = _ragged_prefill(dtype, d, B, G, hist, chunks)
+    wl.q[:] = W.round_to(np.ones(1, np.float32), dtype)[0]
+    hpos = np.concatenate([np.arange(h) for h in hist]).astype(np.float32)
+    cpos = np.concatenate([h + np.arange(c) for h, c in zip(hist, chunks)]).astype(np.float32)
+    _ramp_keys(wl.setup[0].key, hpos, slope, dtype)
+    _ramp_keys(wl.step_scatter.key, cpos, slope, dtype)
+    _full_check(wl)
