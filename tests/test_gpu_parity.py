@@ -183,6 +183,19 @@ def test_repeated_runs_are_bit_identical():
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("dtype,G", [(W.F16, 1), (W.BF16, 4), (W.F32, 2)])
+@pytest.mark.parametrize("part", [64, -1], ids=["p64", "auto"])
+def test_short_contexts_under_a_large_max_context_len(dtype, G, part):
+    # A 32K-token limit with 64-token partitions gives 512 partitions per
+    # sequence, almost all empty: the plan must skip them, and the workspace
+    # and reduce must size and index by the limit, not by the lengths.
+    wl = W.make_decode(f"wide_{G}_{part}", 431 + G, lambda rng: [1, 17, 300, 65],
+                       Hq=2 * G, Hkv=2, d=128, B=16, dtype=dtype, max_context_len=32768,
+                       partition_size=part)
+    assert wl.block_tables.shape[1] == 32768 // 16
+    _full_check(wl)
+
+
 def test_empty_calls_are_no_ops():
     wl = W.tiny_decode_f32()
     cache = new_cache(wl)
