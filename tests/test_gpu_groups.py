@@ -6,7 +6,8 @@ pyy0715.github.io, GQA section; the pages give only the 32-query / 8-KV
 example).  Models also ship groups of 3, 5, 6, 7 and 12.  The matrix-core
 decode stacks a group's G queries into a 16-row operand and leaves the rows
 past G zero, so these sizes exercise the padding and the merge of a partly
-filled tile.  Every case compares whole pools bit for bit and every output
+filled tile; prefill and the mixed step also run the largest group the
+library takes (16).  Every case compares whole pools bit for bit and every output
 with the oracle, at the tolerances of the other parity tests.
 """
 import numpy as np
@@ -76,13 +77,13 @@ def test_sliding_window_odd_groups(G, part, kv):
 
 
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16], ids=["f16", "bf16"])
-@pytest.mark.parametrize("d,B,G", [(128, 16, 7), (64, 8, 3), (128, 32, 6)])
+@pytest.mark.parametrize("d,B,G", [(128, 16, 7), (64, 8, 3), (128, 32, 6), (128, 16, 16)])
 def test_prefill_odd_groups(dtype, d, B, G):
     hist = np.array([0, 5, 16, 33, 200, 7])
     chunks = [1, 37, 128, 130, 64, 256]
     _full_check(_ragged_prefill(dtype, d, B, G, hist, chunks))
 
 
-@pytest.mark.parametrize("G,part", [(7, -1), (5, 64)])
+@pytest.mark.parametrize("G,part", [(7, -1), (5, 64), (16, -1)])
 def test_mixed_step_odd_groups(G, part):
     _full_check(_mixed(W.BF16, 128, 16, G, partition_size=part, seed=371))
