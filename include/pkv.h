@@ -319,8 +319,13 @@ pkv_status pkv_paged_mixed(const pkv_cache *cache, void *out, int32_t out_dtype,
                            hipStream_t stream);
 
 /*
- * Debug gather with the kernels' own address arithmetic: the contiguous
- * K and V of every sequence, back to back, token-major.
+ * Gather with the kernels' own address arithmetic: the contiguous K and V of
+ * every sequence, back to back, token-major.  [T] step 5: the block table
+ * maps a request's logical blocks, in order, to physical blocks, so logical
+ * position j of sequence s is slot table[s][j / B] * B + j mod B; this call
+ * writes those slots out in logical order, the contiguous cache a
+ * non-paged system would hold.  Positions past context_lens[s] are not
+ * written; a table entry out of range leaves its rows unwritten.
  *
  *   k_out, v_out      [sum_s L_s][num_kv_heads][head_dim], cache dtype (the
  *                     stored codes for an 8-bit cache)
@@ -334,14 +339,19 @@ pkv_status pkv_gather_kv(const pkv_cache *cache, void *k_out, void *v_out,
 /*
  * Host-side check of the device-side contract, on HOST copies of the
  * integer inputs (any pointer may be NULL with its count 0 to skip that
- * part): slots in range and unique, every L in [1, max_blocks*B], every
- * table entry a sequence uses in [0, num_blocks).  Returns PKV_OK or
- * PKV_ERR_INVALID with pkv_last_error() naming the first violation.
+ * part): slots in range and unique, every L in [1, max_blocks*B] and, when
+ * max_context_len > 0, L <= max_context_len, every table entry a sequence
+ * uses in [0, num_blocks).  The slot rule is the one the scatter passage
+ * defines ([W] section "PagedAttention 커널: 비연속 메모리 접근": each
+ * token's slot_mapping entry names one slot); the table rule is [T] step 5
+ * (a block table entry names a physical block of the pool).  Returns PKV_OK
+ * or PKV_ERR_INVALID with pkv_last_error() naming the first violation.
+ * Reads only the host arrays; launches nothing.
  */
 pkv_status pkv_validate_host(const int64_t *slot_mapping, int64_t num_tokens,
                              const int32_t *block_tables, int32_t max_blocks_per_seq,
                              const int32_t *context_lens, int32_t num_seqs, int64_t num_blocks,
-                             int32_t block_size);
+                             int32_t block_size, int32_t max_context_len);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *pkv_last_error(void);

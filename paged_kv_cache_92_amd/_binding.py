@@ -68,7 +68,7 @@ def lib() -> ctypes.CDLL:
         L.pkv_paged_mixed.argtypes = [cp, vp, i32, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                       i32, vp, sz, vp]
         L.pkv_gather_kv.argtypes = [cp, vp, vp, vp, i32, vp, vp, i32, i32, vp]
-        L.pkv_validate_host.argtypes = [vp, i64, vp, i32, vp, i32, i64, i32]
+        L.pkv_validate_host.argtypes = [vp, i64, vp, i32, vp, i32, i64, i32, i32]
         L.pkv_last_error.restype = ctypes.c_char_p
         L.pkv_version.restype = ctypes.c_char_p
         for name in ("pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_paged_decode",
@@ -98,6 +98,15 @@ def _dev_ptr(t: torch.Tensor | None, name: str, dtype=None):
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _need_rows(t, rows: int, name: str, width: int | None = None):
+    """The kernels read ``rows`` rows of ``t`` (and ``width`` columns per row when given):
+    a shorter tensor would be read past its end, so it is refused here."""
+    if t.dim() < 1 or t.shape[0] < rows:
+        raise ValueError(f"{name} has {t.shape[0] if t.dim() else 0} rows, the call reads {rows}")
+    if width is not None and (t.dim() != 2 or t.shape[1] != width):
+        raise ValueError(f"{name} must be [n][{width}], got {tuple(t.shape)}")
 
 
 class PagedKVCache:
@@ -169,6 +178,7 @@ def reshape_and_cache(cache: PagedKVCache, key, value, slot_mapping):
 def copy_blocks(cache: PagedKVCache, src_dst):
     """Copy whole blocks: src_dst int32 [n][2] of (src, dst)."""
     n = src_dst.shape[0]
+    _need_rows(src_dst, n, "src_dst", width=2)
     d = cache.desc()
     _check(lib().pkv_copy_blocks(ctypes.byref(d), _dev_ptr(src_dst, "src_dst", torch.int32), n,
                                  _stream()))
@@ -206,6 +216,8 @@ def paged_decode(cache: PagedKVCache, q, block_tables, context_lens, max_context
     S, Hq, dq = q.shape
     if dq != cache.head_dim:
         raise ValueError("q head_dim does not match the cache")
+    _need_rows(block_tables, S, "block_tables")
+    _need_rows(context_lens, S, "context_lens")
     if scale is None:
         scale = 1.0 / math.sqrt(cache.head_dim)
     out = _out(q, out, out_dtype)
@@ -239,6 +251,8 @@ def paged_decode_append(cache: PagedKVCache, key, value, q, block_tables, contex
     if (tuple(key.shape) != (S, cache.num_kv_heads, cache.head_dim)
             or tuple(value.shape) != tuple(key.shape)):
         raise ValueError("key/value must be [S][num_kv_heads][head_dim]")
+    _need_rows(block_tables, S, "block_tables")
+    _need_rows(context_lens, S, "context_lens")
     if scale is None:
         scale = 1.0 / math.sqrt(cache.head_dim)
     out = _out(q, out, out_dtype)
@@ -268,6 +282,8 @@ def paged_prefill(cache: PagedKVCache, q, query_start_loc, context_lens, block_t
         scale = 1.0 / math.sqrt(cache.head_dim)
     out = _out(q, out, out_dtype)
     S = context_lens.shape[0]
+    _need_rows(block_tables, S, "block_tables")
+    _need_rows(query_start_loc, S + 1, "query_start_loc")
     d = cache.desc()
     _check(lib().pkv_paged_prefill(ctypes.byref(d), _dev_ptr(out, "out"), _TORCH_TO_PKV[out.dtype],
                                    _dev_ptr(q, "q", cache.model_dtype), Hq,
@@ -296,6 +312,9 @@ def paged_mixed(cache: PagedKVCache, q, query_start_loc, context_lens, block_tab
     out = _out(q, out, out_dtype)
     S = context_lens.shape[0]
     nd = int(num_decode_seqs)
+    _need_rows(block_tables, S, "block_tables")
+    if S > nd:
+        _need_rows(query_start_loc, S + 1, "query_start_loc")
     need = decode_workspace_bytes(cache, nd, Hq, max_context_len, partition_size) if nd else 0
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -316,6 +335,9 @@ def paged_mixed(cache: PagedKVCache, q, query_start_loc, context_lens, block_tab
 def gather_kv(cache: PagedKVCache, block_tables, context_lens, cu_context_lens, total_tokens,
               max_context_len):
     """Debug gather: contiguous token-major (K, V), each [sum L][Hkv][d]."""
+    S = context_lens.shape[0]
+    _need_rows(block_tables, S, "block_tables")
+    _need_rows(cu_context_lens, S + 1, "cu_context_lens")
     shape = (int(total_tokens), cache.num_kv_heads, cache.head_dim)
     dev = cache.k_pool.device
     k = torch.empty(shape, dtype=cache.dtype, device=dev)
@@ -334,15 +356,17 @@ def _host_ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def validate_host(num_blocks, block_size, slot_mapping=None, block_tables=None, context_lens=None):
-    """Check the device-side contract on host (numpy) copies; raises PkvError on a violation."""
+def validate_host(num_blocks, block_size, slot_mapping=None, block_tables=None, context_lens=None,
+                  max_context_len=0):
+    """Check the device-side contract on host (numpy) copies; raises PkvError on a violation.
+    ``max_context_len`` > 0 also checks every length against it."""
     sm = None if slot_mapping is None else np.ascontiguousarray(slot_mapping, dtype=np.int64)
     bt = None if block_tables is None else np.ascontiguousarray(block_tables, dtype=np.int32)
     cl = None if context_lens is None else np.ascontiguousarray(context_lens, dtype=np.int32)
     _check(lib().pkv_validate_host(_host_ptr(sm), 0 if sm is None else sm.shape[0], _host_ptr(bt),
                                    0 if bt is None else bt.shape[1], _host_ptr(cl),
                                    0 if cl is None else cl.shape[0], int(num_blocks),
-                                   int(block_size)))
+                                   int(block_size), int(max_context_len)))
 
 
 def version() -> str:

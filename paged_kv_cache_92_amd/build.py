@@ -28,10 +28,32 @@ FLAGS = [
 ]
 
 
+OBJ_DIR = os.path.join(ROOT, "_build")
+
+
 def build(verbose: bool = False, out: str = LIB, extra: tuple[str, ...] = ()) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compile every source to an object (in parallel: each translation unit
+    carries its own gfx950 code object), then link them into one library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    tag = os.path.splitext(os.path.basename(out))[0]
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+
+    def compile_one(src: str) -> str:
+        obj = os.path.join(OBJ_DIR, f"{tag}_{os.path.splitext(src)[0]}.o")
+        cmd = [HIPCC, *compile_flags, *extra, "-I", INCLUDE, "-I", CSRC, "-c",
+               os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        return obj
+
+    jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(max_workers=jobs) as pool:
+        objs = list(pool.map(compile_one, SOURCES))
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -78,14 +78,14 @@ __device__ __forceinline__ void valu_item(
     int out_f32, const typename Q::storage *__restrict__ q,
     const typename E::storage *__restrict__ kpool, const typename E::storage *__restrict__ vpool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    int64_t num_blocks, int Hkv, int Hq, int mbps, int window, float scale_log2, float v_scale,
-    float *__restrict__ ws_ml, float *__restrict__ ws_acc, const Append<Q> &ap) {
+    int64_t num_blocks, int Hkv, int Hq, int mbps, int cap, int window, float scale_log2,
+    float v_scale, float *__restrict__ ws_ml, float *__restrict__ ws_acc, const Append<Q> &ap) {
   constexpr int GB = group_tokens(BS);
   constexpr bool kPair = GB == 2 * BS;      // two blocks per step
   using C = ValuCfg<E, D, GB>;
   using T = typename E::storage;
   constexpr bool kFP8 = E::kBytes == 1;
-  const Span sp = seq_span(context_lens, s, mbps * BS, window);
+  const Span sp = seq_span(context_lens, s, cap, window);
   const int lo = sp.lo;                      // first attended position
   const int tok0 = max(b0 * BS, lo);
   const int tok1 = min(sp.hi, b1 * BS);
@@ -389,7 +389,7 @@ decode_valu_kernel(
     void *__restrict__ out, int out_f32, const typename Q::storage *__restrict__ q,
     const typename E::storage *__restrict__ kpool, const typename E::storage *__restrict__ vpool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    int64_t num_blocks, int Hkv, int Hq, int S, int mbps, int window, float scale_log2,
+    int64_t num_blocks, int Hkv, int Hq, int S, int mbps, int cap, int window, float scale_log2,
     float v_scale, int part_tokens, int nparts, float *__restrict__ ws_ml,
     float *__restrict__ ws_acc, int *__restrict__ ws_hdr, Append<Q> ap) {
   __shared__ ValuLds<E, D, group_tokens(BS)> sh;
@@ -398,10 +398,10 @@ decode_valu_kernel(
   run_schedule<SCHED>(
       [&](int s, int hq, int b0, int b1, Dest dest) {
         valu_item<E, Q, D, BS, APPEND>(sh, s, hq, b0, b1, dest, out, out_f32, q, kpool, vpool, block_tables,
-                               context_lens, num_blocks, Hkv, Hq, mbps, window, scale_log2, v_scale,
-                               ws_ml, ws_acc, ap);
+                               context_lens, num_blocks, Hkv, Hq, mbps, cap, window, scale_log2,
+                               v_scale, ws_ml, ws_acc, ap);
       },
-      plan, scan, context_lens, S, mbps * BS, window, BS, Hq, 1, part_tokens, nparts, ws_hdr);
+      plan, scan, context_lens, S, cap, window, BS, Hq, 1, part_tokens, nparts, ws_hdr);
 }
 
 // Appending call: the reduce kernel (launched after the decode kernel, also
@@ -418,6 +418,7 @@ struct NewToken {
   const int32_t *block_tables = nullptr;
   int64_t num_blocks = 0;
   int Hkv = 1, BS = 16, mbps = 0;
+  int cap = 0;   // lengths are clamped to it, as the decode kernel clamps them
 };
 
 // Rows of sequence s, KV head hkv, into the slot of position L-1 (none if
@@ -427,7 +428,7 @@ template <typename KV, typename Q, int D>
 __device__ __forceinline__ void store_new_token(const NewToken &nt,
                                                 const int32_t *__restrict__ context_lens, int s,
                                                 int hkv) {
-  const int L = min(context_lens[s], nt.mbps * nt.BS);
+  const int L = min(context_lens[s], nt.cap);
   if (L <= 0) return;
   const int64_t phys = nt.block_tables[(size_t)s * nt.mbps + (L - 1) / nt.BS];
   if (phys < 0 || phys >= nt.num_blocks) return;
@@ -518,7 +519,8 @@ void launch_valu_ta(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream)
   auto go = [&](auto kern, dim3 grid, size_t dyn) {
     hipLaunchKernelGGL(kern, grid, dim3(256), dyn, stream, a.out, (int)a.out_f32, (const TQ *)a.q,
                        (const T *)c.k, (const T *)c.v, a.block_tables, a.context_lens,
-                       c.num_blocks, c.H, a.Hq, a.S, a.max_blocks_per_seq, a.window, sl, c.v_scale,
+                       c.num_blocks, c.H, a.Hq, a.S, a.max_blocks_per_seq, a.cap_tokens, a.window,
+                       sl, c.v_scale,
                        a.partition_tokens, a.num_partitions, a.ws_ml, a.ws_acc, a.ws_hdr,
                        Append<Q>{(const TQ *)a.new_k, (const TQ *)a.new_v, c.k_scale, c.v_scale});
   };
@@ -578,7 +580,7 @@ int flat_grid_e(const CacheDesc &c, int S) {
 template <typename E, typename KV>
 void launch_reduce_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
   const dim3 grid((unsigned)a.Hq, (unsigned)a.S);
-  const int mt = a.max_blocks_per_seq * c.B;
+  const int mt = a.cap_tokens;
   const int G = a.Hq / c.H;
   const int HU = a.mfma ? c.H : a.Hq, GU = a.mfma ? G : 1;   // the decode kernel's work units
   NewToken nt;
@@ -593,6 +595,7 @@ void launch_reduce_e(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream
     nt.num_blocks = c.num_blocks;
     nt.BS = c.B;
     nt.mbps = a.max_blocks_per_seq;
+    nt.cap = a.cap_tokens;
   }
   nt.Hkv = c.H;
   auto go = [&](auto kern_part, auto kern_flat, int threads) {

@@ -109,7 +109,7 @@ __device__ __forceinline__ void mfma_item(
     int out_f32, const uint16_t *__restrict__ q, const typename KV::storage *__restrict__ kpool,
     const typename KV::storage *__restrict__ vpool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, int64_t num_blocks, int Hkv, int G, int mbps,
-    int window, float scale_log2, float v_scale, float *__restrict__ ws_ml,
+    int cap, int window, float scale_log2, float v_scale, float *__restrict__ ws_ml,
     float *__restrict__ ws_acc, const Append<E> &ap) {
   constexpr bool kFP8 = KV::kBytes == 1;
   constexpr int KS = D / 32;    // k-steps of the score product
@@ -127,7 +127,7 @@ __device__ __forceinline__ void mfma_item(
   // lane ends up with 8 consecutive tokens, and P.V runs as 16x16x32 products
   // over 16-byte V^T operands.
   constexpr bool kWide = GB == 32;
-  const Span sp = seq_span(context_lens, s, mbps * BS, window);
+  const Span sp = seq_span(context_lens, s, cap, window);
   const int lo = sp.lo;                      // first attended position
   const int tok0 = max(b0 * BS, lo);
   const int tok1 = min(sp.hi, b1 * BS);
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(256, KV::kBytes == 1 ? PKV_MFMA_MIN_WAVES_FP8 : (AP
     void *__restrict__ out, int out_f32, const uint16_t *__restrict__ q,
     const typename KV::storage *__restrict__ kpool, const typename KV::storage *__restrict__ vpool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    int64_t num_blocks, int Hkv, int G, int S, int mbps, int window, float scale_log2,
+    int64_t num_blocks, int Hkv, int G, int S, int mbps, int cap, int window, float scale_log2,
     float v_scale, int part_tokens, int nparts, float *__restrict__ ws_ml,
     float *__restrict__ ws_acc, int *__restrict__ ws_hdr, Append<E> ap) {
   extern __shared__ __attribute__((aligned(16))) int dyn[];
@@ -512,10 +512,10 @@ __global__ __launch_bounds__(256, KV::kBytes == 1 ? PKV_MFMA_MIN_WAVES_FP8 : (AP
   run_schedule<SCHED>(
       [&](int s, int hkv, int b0, int b1, Dest dest) {
         mfma_item<E, KV, D, BS, APPEND>(merge, s, hkv, b0, b1, dest, out, out_f32, q, kpool, vpool,
-                                block_tables, context_lens, num_blocks, Hkv, G, mbps, window,
+                                block_tables, context_lens, num_blocks, Hkv, G, mbps, cap, window,
                                 scale_log2, v_scale, ws_ml, ws_acc, ap);
       },
-      plan, scan, context_lens, S, mbps * BS, window, BS, Hkv, G, part_tokens, nparts, ws_hdr);
+      plan, scan, context_lens, S, cap, window, BS, Hkv, G, part_tokens, nparts, ws_hdr);
 }
 
 template <int D>
@@ -533,7 +533,8 @@ void launch_ta(const CacheDesc &c, const DecodeArgs &a, hipStream_t stream) {
   auto go = [&](auto kern, dim3 grid, size_t dyn) {
     hipLaunchKernelGGL(kern, grid, dim3(256), dyn, stream, a.out, (int)a.out_f32,
                        (const uint16_t *)a.q, (const T *)c.k, (const T *)c.v, a.block_tables,
-                       a.context_lens, c.num_blocks, c.H, G, a.S, a.max_blocks_per_seq, a.window,
+                       a.context_lens, c.num_blocks, c.H, G, a.S, a.max_blocks_per_seq, a.cap_tokens,
+                       a.window,
                        sl, c.v_scale, a.partition_tokens, a.num_partitions, a.ws_ml, a.ws_acc,
                        a.ws_hdr,
                        Append<E>{(const uint16_t *)a.new_k, (const uint16_t *)a.new_v, c.k_scale,

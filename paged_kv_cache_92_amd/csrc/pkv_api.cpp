@@ -6,6 +6,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -172,6 +173,11 @@ pkv_status prepare_decode(const pkv::CacheDesc &c, void *out, int32_t out_dtype,
   a->context_lens = context_lens;
   a->S = num_seqs;
   a->max_context_len = max_context_len;
+  {
+    const int64_t reach = (int64_t)max_blocks_per_seq * c.B;
+    const int64_t parts = plan->flat ? reach : (int64_t)plan->part.count * plan->part.tokens;
+    a->cap_tokens = (int)std::min<int64_t>(std::min(reach, parts), INT32_MAX);
+  }
   a->window = window;
   a->scale = scale;
   a->partition_tokens = plan->part.tokens;
@@ -541,7 +547,7 @@ pkv_status pkv_gather_kv(const pkv_cache *cache, void *k_out, void *v_out,
 pkv_status pkv_validate_host(const int64_t *slot_mapping, int64_t num_tokens,
                              const int32_t *block_tables, int32_t max_blocks_per_seq,
                              const int32_t *context_lens, int32_t num_seqs, int64_t num_blocks,
-                             int32_t block_size) {
+                             int32_t block_size, int32_t max_context_len) {
   if (num_blocks <= 0 || block_size <= 0) return fail(PKV_ERR_INVALID, "bad pool geometry");
   if (slot_mapping && num_tokens > 0) {
     std::unordered_set<int64_t> seen;
@@ -565,6 +571,9 @@ pkv_status pkv_validate_host(const int64_t *slot_mapping, int64_t num_tokens,
       if (L < 1 || (int64_t)L > (int64_t)max_blocks_per_seq * block_size)
         return fail(PKV_ERR_INVALID, "context_lens[%d] = %d outside [1, %lld]", s, L,
                     (long long)max_blocks_per_seq * block_size);
+      if (max_context_len > 0 && L > max_context_len)
+        return fail(PKV_ERR_INVALID, "context_lens[%d] = %d > max_context_len %d", s, L,
+                    max_context_len);
       const int32_t nb = (L + block_size - 1) / block_size;
       for (int32_t i = 0; i < nb; ++i) {
         const int32_t b = block_tables[(size_t)s * max_blocks_per_seq + i];

@@ -39,6 +39,11 @@ struct DecodeArgs {
   const int32_t *context_lens;
   int S;
   int max_context_len;
+  // Every length is clamped to cap_tokens: the table's reach, and for the
+  // partitioned schedules also num_partitions * partition_tokens, so that a
+  // length beyond max_context_len (a broken contract) can never name a
+  // partition the workspace has no row for.
+  int cap_tokens;
   int window;             // sliding window in tokens (0: attend to the whole context)
   float scale;
   int partition_tokens;   // > 0, multiple of B

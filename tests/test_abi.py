@@ -179,6 +179,23 @@ def test_validate_host():
         pkv.validate_host(8, B, block_tables=bt, context_lens=np.array([0, 16]))
     with pytest.raises(pkv.PkvError, match="context_lens"):
         pkv.validate_host(8, B, block_tables=bt, context_lens=np.array([49, 16]))
+    # The max_context_len clause (0: not checked).
+    pkv.validate_host(8, B, block_tables=bt, context_lens=np.array([20, 16]), max_context_len=20)
+    with pytest.raises(pkv.PkvError, match="max_context_len"):
+        pkv.validate_host(8, B, block_tables=bt, context_lens=np.array([20, 16]), max_context_len=19)
+
+
+def test_binding_refuses_short_integer_inputs():
+    # A table or length vector shorter than the call's sequence count would be
+    # read past its end by the kernels: the binding refuses it first.
+    from paged_kv_cache_92_amd._binding import _need_rows
+    _need_rows(torch.zeros(3, 4), 3, "block_tables")
+    with pytest.raises(ValueError, match="block_tables"):
+        _need_rows(torch.zeros(2, 4), 3, "block_tables")
+    with pytest.raises(ValueError, match="src_dst"):
+        _need_rows(torch.zeros(4, 3), 4, "src_dst", width=2)
+    with pytest.raises(ValueError, match="query_start_loc"):
+        _need_rows(torch.zeros(3), 4, "query_start_loc")
 
 
 def test_workloads_satisfy_the_device_contract():
@@ -189,7 +206,8 @@ def test_workloads_satisfy_the_device_contract():
                W.chunked_prefill_bf16(S=2, chunk=16, shared_prefix=20, Hq=2, Hkv=2,
                                       max_context_len=128, hist_fn=lambda rng: np.array([30, 41]))):
         pkv.validate_host(wl.num_blocks, wl.block_size, block_tables=wl.block_tables,
-                          context_lens=wl.context_lens)
+                          context_lens=wl.context_lens, max_context_len=wl.max_context_len)
         for op in wl.setup + [wl.step_scatter]:
             if op.kind == "scatter":
                 pkv.validate_host(wl.num_blocks, wl.block_size, slot_mapping=op.slots)
+
