@@ -204,6 +204,26 @@ pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype
                             void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pkv_paged_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The call allocates nothing; the split
+ * partials go to a static device array of 64 MiB that the library holds on
+ * every GPU it runs on until the process ends.  A call that would need more
+ * (pkv_decode_workspace_bytes above 64 MiB) returns PKV_ERR_WORKSPACE and
+ * launches nothing.  Every call on one GPU shares that GPU's array; nothing
+ * in it has to start at zero (each call writes every partial it later
+ * reads), but calls that may run at the same time on one GPU (other streams
+ * or threads) race on it and must be serialised by the caller.  Arguments
+ * and result as for pkv_paged_decode.
+ */
+pkv_status pkv_paged_decode_noalloc(const pkv_cache *cache, void *out, int32_t out_dtype,
+                                    const void *q, int32_t num_q_heads,
+                                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t *context_lens, int32_t num_seqs,
+                                    int32_t max_context_len, float scale, int32_t partition_size,
+                                    hipStream_t stream);
+
+/*
  * Sliding-window decode.  [W] section "블록 할당: allocate_slots" (under
  * "KVCacheManager: 블록 단위 할당의 중심"): before a step's allocation the
  * cache manager releases the blocks that fell out of the sliding window, as

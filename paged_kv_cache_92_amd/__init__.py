@@ -8,9 +8,10 @@ binding over that library (ctypes + torch device memory and streams), plus
 the host-side block manager and the seeded synthetic workloads.
 """
 from ._binding import (PARTITION_AUTO, PagedKVCache, PkvError, copy_blocks, decode_workspace_bytes,
-                       gather_kv, lib, paged_decode, paged_decode_append, paged_mixed,
-                       paged_prefill, reshape_and_cache, validate_host, version)
+                       gather_kv, lib, paged_decode, paged_decode_append, paged_decode_noalloc,
+                       paged_mixed, paged_prefill, reshape_and_cache, validate_host, version)
 
 __all__ = ["PARTITION_AUTO", "PagedKVCache", "PkvError", "copy_blocks", "decode_workspace_bytes",
-           "gather_kv", "lib", "paged_decode", "paged_decode_append", "paged_mixed",
+           "gather_kv", "lib", "paged_decode", "paged_decode_append", "paged_decode_noalloc",
+           "paged_mixed",
            "paged_prefill", "reshape_and_cache", "validate_host", "version"]

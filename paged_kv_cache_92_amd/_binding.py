@@ -24,6 +24,7 @@ _STATUS = {0: "OK", 1: "INVALID", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP"}
 
 EXPORTED = ("pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_decode_workspace_bytes",
             "pkv_paged_decode", "pkv_paged_decode_window", "pkv_paged_decode_append",
+            "pkv_paged_decode_noalloc",
             "pkv_paged_prefill", "pkv_paged_mixed",
             "pkv_gather_kv",
             "pkv_validate_host",
@@ -60,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.pkv_decode_workspace_bytes.argtypes = [cp, i32, i32, i32, i32]
         L.pkv_decode_workspace_bytes.restype = sz
         L.pkv_paged_decode.argtypes = [cp, vp, i32, vp, i32, vp, i32, vp, i32, i32, f32, i32, vp, sz, vp]
+        L.pkv_paged_decode_noalloc.argtypes = [cp, vp, i32, vp, i32, vp, i32, vp, i32, i32, f32, i32,
+                                               vp]
         L.pkv_paged_decode_window.argtypes = [cp, vp, i32, vp, i32, vp, i32, vp, i32, i32, i32, f32, i32,
                                               vp, sz, vp]
         L.pkv_paged_decode_append.argtypes = [cp, vp, vp, vp, i32, vp, i32, vp, i32, vp, i32, i32, i32,
@@ -73,7 +76,7 @@ def lib() -> ctypes.CDLL:
         L.pkv_version.restype = ctypes.c_char_p
         for name in ("pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_paged_decode",
                      "pkv_paged_decode_window", "pkv_paged_decode_append",
-                     "pkv_paged_prefill", "pkv_paged_mixed", "pkv_gather_kv", "pkv_validate_host"):
+                     "pkv_paged_decode_noalloc", "pkv_paged_prefill", "pkv_paged_mixed", "pkv_gather_kv", "pkv_validate_host"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -236,6 +239,27 @@ def paged_decode(cache: PagedKVCache, q, block_tables, context_lens, max_context
         _check(lib().pkv_paged_decode_window(*args, int(sliding_window), *tail))
     else:
         _check(lib().pkv_paged_decode(*args, *tail))
+    return out
+
+
+def paged_decode_noalloc(cache: PagedKVCache, q, block_tables, context_lens, max_context_len,
+                         scale=None, partition_size=0, out=None, out_dtype=None):
+    """``paged_decode`` with the split partials in the library's static device scratch
+    (pkv_paged_decode_noalloc): no workspace is allocated.  ``out`` is still the caller's."""
+    S, Hq, dq = q.shape
+    if dq != cache.head_dim:
+        raise ValueError("q head_dim does not match the cache")
+    _need_rows(block_tables, S, "block_tables")
+    _need_rows(context_lens, S, "context_lens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(cache.head_dim)
+    out = _out(q, out, out_dtype)
+    d = cache.desc()
+    _check(lib().pkv_paged_decode_noalloc(
+        ctypes.byref(d), _dev_ptr(out, "out"), _TORCH_TO_PKV[out.dtype],
+        _dev_ptr(q, "q", cache.model_dtype), Hq, _dev_ptr(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev_ptr(context_lens, "context_lens", torch.int32), S,
+        int(max_context_len), float(scale), int(partition_size), _stream()))
     return out
 
 

@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpkv.so")
 
-SOURCES = ["pkv_api.cpp", "cache_ops.hip", "decode.hip", "decode_gqa.hip", "prefill.hip"]
+SOURCES = ["pkv_api.cpp", "cache_ops.hip", "decode.hip", "decode_gqa.hip", "prefill.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

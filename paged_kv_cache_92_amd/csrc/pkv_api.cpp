@@ -314,6 +314,14 @@ pkv_status side_stream(SideStream **out) {
 
 namespace pkv {
 
+int report_error(int status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
 int resident_workgroups(const void *kernel, int threads, size_t lds_bytes) {
   static std::mutex mu;
   static std::map<std::tuple<const void *, size_t, int>, int> cache;

@@ -79,6 +79,10 @@ struct PrefillArgs {
   float scale;
 };
 
+// Sets this thread's last-error message (pkv_last_error) and returns
+// `status`; for entry points defined outside pkv_api.cpp.
+int report_error(int status, const char *fmt, ...);
+
 // Workgroups of `kernel` (with `threads` threads and `lds_bytes` of dynamic
 // LDS) that the current device keeps resident at once: the size of a
 // persistent grid.  Cached per (kernel, LDS size, device).

@@ -211,3 +211,16 @@ def test_workloads_satisfy_the_device_contract():
             if op.kind == "scatter":
                 pkv.validate_host(wl.num_blocks, wl.block_size, slot_mapping=op.slots)
 
+
+def test_noalloc_decode_refuses_beyond_its_scratch_without_launching():
+    # 4,096 sequences x 64 heads x 32 partitions need far more than the 64 MiB
+    # static scratch: refused on the host (no pointer is dereferenced).
+    lib = pkv.lib()
+    d = _desc(num_kv_heads=64, head_dim=64)
+    st = lib.pkv_paged_decode_noalloc(ctypes.byref(d), FAKE, 1, FAKE, 64, FAKE, 32, FAKE, 4096, 512,
+                                      0.125, 16, None)
+    assert st == 3
+    assert "scratch" in lib.pkv_last_error().decode()
+    # Invalid arguments are still reported as for pkv_paged_decode.
+    assert lib.pkv_paged_decode_noalloc(ctypes.byref(d), None, 1, FAKE, 64, FAKE, 32, FAKE, 2, 512,
+                                        0.125, 0, None) == 1
