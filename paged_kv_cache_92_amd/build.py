@@ -15,6 +15,9 @@ SOURCES = ["pkv_api.cpp", "cache_ops.hip", "decode.hip", "decode_gqa.hip", "pref
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
+# Per-source code-generation flags (none at present).
+SOURCE_FLAGS: dict[str, list[str]] = {}
+
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
@@ -42,7 +45,7 @@ def build(verbose: bool = False, out: str = LIB, extra: tuple[str, ...] = ()) ->
 
     def compile_one(src: str) -> str:
         obj = os.path.join(OBJ_DIR, f"{tag}_{os.path.splitext(src)[0]}.o")
-        cmd = [HIPCC, *compile_flags, *extra, "-I", INCLUDE, "-I", CSRC, "-c",
+        cmd = [HIPCC, *compile_flags, *SOURCE_FLAGS.get(src, []), *extra, "-I", INCLUDE, "-I", CSRC, "-c",
                os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

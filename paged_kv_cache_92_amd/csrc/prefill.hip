@@ -6,21 +6,29 @@
 // attention is a matrix-matrix product ("vLLM: LLM 서빙 메모리 최적화의 교과서",
 // velog.io, section 01, prompt phase), causal over j <= i.
 //
-// Workgroup = 8 waves = one (sequence, query head, 256-row query tile); wave
-// w owns 32 rows.  The key/value positions 0..last row's position are walked
-// in 64-token tiles gathered through the block table into LDS (the next
-// tile's global loads are in flight while the current one is computed); each
-// tile is two 32-token halves:
+// Workgroup = 4 waves (one per SIMD) = one (sequence, query head, 256-row
+// query tile); wave w owns 64 rows as two 32-row groups r = 0, 1.  The
+// key/value positions 0..last row's position are walked in 64-token tiles
+// gathered through the block table into LDS (three tile buffers: tile t+2 is
+// stored while tiles t and t+1 are read, one barrier per tile).  Per group:
 //
-//   S^T (32 tokens x 32 rows) = K (32 x D) . Q^T (D x 32)     D/16 k-steps per half
-//   O^T (D x 32 rows)        += V^T (D x 32) . P^T (32 x 32)   2 k-steps per half
+//   S^T (32 tokens x 32 rows) = K (32 x D) . Q^T (D x 32)     per 32-token half
+//   O^T (D x 32 rows)        += V^T (D x 32) . P^T (32 x 32)
 //
 // with 32x32x16 MFMAs.  The key rows are fed to the first product in a
 // permuted order chosen so that each lane's 16 result rows are, per 16-token
 // k-step of the second product, 8 consecutive tokens: the B operand P^T is
-// then built from the lane's own registers and the A operand V^T is one
-// 16-byte LDS read from the dimension-major value tile.  Online softmax per
-// row, log2 domain.  Tiles entirely in a wave's future are skipped.
+// built from the lane's own registers and the A operand V^T is one 16-byte
+// LDS read from the dimension-major value tile.  Online softmax per row in
+// the log2 domain.
+//
+// Each wave computes 32-token sub-tiles, software-pipelined across its two
+// row groups so the softmax of one group (vector ALU) runs while the matrix
+// cores work on the other:
+//   A: S1 = QK(u, group 1)         || P0 = exp(S0)
+//   B: O0 += PV(u, P0)             || P1 = exp(S1)
+//   C: S0 = QK(u+1, group 0), O1 += PV(u, P1)
+// and after each 64-token tile, the tile two ahead is staged.
 #include <stdint.h>
 
 #include <algorithm>
@@ -32,14 +40,20 @@
 namespace pkv {
 namespace {
 
-#ifndef PKV_PREFILL_WAVES
-#define PKV_PREFILL_WAVES 8
+// Query rows per wave: NG groups of 32 (the matrix-core tile's columns).
+// Each key and value operand read from LDS feeds the products of all NG
+// groups, and a wave's registers hold NG groups' queries and accumulators.
+#ifndef PKV_PREFILL_NG
+#define PKV_PREFILL_NG 1
 #endif
-constexpr int kWaves = PKV_PREFILL_WAVES;
+constexpr int NG = PKV_PREFILL_NG;
+constexpr int kWaves = 8 / NG;         // two waves per SIMD at NG = 1, one at NG = 2
 constexpr int kThreads = 64 * kWaves;
-constexpr int kQT = 32 * kWaves;  // query rows per workgroup
-constexpr int kKT = 64;           // key/value tokens per tile
-constexpr int kVPad = 8;          // LDS row padding (elements) against bank conflicts
+constexpr int kRowsW = 32 * NG;
+constexpr int kQT = kRowsW * kWaves;   // 256 query rows per workgroup
+constexpr int kKT = 64;               // key/value tokens per tile: two 32-token halves
+constexpr int kNBuf = 3;              // LDS tile buffers
+constexpr int kLptClasses = 256;      // (sequence, query tile) classes ranked in LDS
 
 template <typename E>
 struct Mfma32;
@@ -63,34 +77,39 @@ struct Mfma32<BF16> {
   __device__ static uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
 };
 
-// bf16 inputs run P.V on the fp16 matrix cores: value tiles are re-encoded to
-// fp16 when staged in LDS (exact over fp16's range) and the softmax weights
-// pack to fp16 (11 significant bits, against 8 in bf16, so no hi + lo split).
-// A tile holding a value outside fp16's range is flagged while staged and
-// takes the exact bf16 route instead (values read from HBM, weights split).
-#ifndef PKV_PREFILL_CONV_V
-#define PKV_PREFILL_CONV_V 1
-#endif
-
-// Operand reads issued a whole product ahead (1) or next to each product (0).
-#ifndef PKV_PREFILL_EARLY_LDS
-#define PKV_PREFILL_EARLY_LDS 1
-#endif
-
 // Row i of a 32-token score product (i = 8a + 4h + b) holds token perm(i) of
 // its half-tile.
 __device__ __forceinline__ int perm_row(int i) {
   const int a = i >> 3, h = (i >> 2) & 1, b = i & 3;
   return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
 }
+// LDS row of tile token k.  Rows are D + 8 elements (an odd number of 16-byte
+// bank groups), and bit 2 is flipped on odd 8-token groups: the 8 tokens that
+// one 8-lane group of a score-operand read touches (perm rows 0-3 and 8-11,
+// and the like) then sit in 8 distinct bank groups.
+__device__ __forceinline__ int kslot(int k) { return k ^ (((k >> 3) & 1) << 2); }
 
-// Lazy rescaling: a row keeps its reference maximum until a new score beats it
-// by more than 2^kRescaleLog2; weights stay <= 2^kRescaleLog2 meanwhile (no
-// overflow in fp32 or bf16), and the final o = acc / l is unaffected.
+// Lazy rescaling (exact route): a row keeps its reference maximum until a new
+// score beats it by more than 2^kRescaleLog2; weights stay <= 2^kRescaleLog2
+// meanwhile (no overflow in fp32, fp16 or bf16), and the final o = acc / l is
+// unaffected.
 constexpr float kRescaleLog2 = 8.f;
+// Fixed reference (fast route): each row's reference is the maximum of its
+// first 32 keys, kept for the whole walk.  Later weights 2^(s - ref) may
+// exceed 1; the walk is valid as long as they fit fp16 (s - ref < 16).  A
+// weight beyond that packs to an infinity, which makes that row's
+// accumulators or denominator non-finite: the workgroup then redoes the walk
+// on the exact route.
+
+template <int R>
+using Grp = std::integral_constant<int, R>;
+
+// Max and sum of x over lanes l and l ^ 32.
+__device__ __forceinline__ float pair_max(float x) { return __builtin_fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float pair_sum(float x) { return x + __shfl_xor(x, 32); }
 
 template <typename E, int D, int BS>
-__global__ __launch_bounds__(kThreads, 512 / kThreads) void prefill_kernel(
+__global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(
     void *__restrict__ out, int out_f32, const uint16_t *__restrict__ q,
     const uint16_t *__restrict__ kpool, const uint16_t *__restrict__ vpool,
     const int32_t *__restrict__ query_start_loc, const int32_t *__restrict__ context_lens,
@@ -98,24 +117,57 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void prefill_kernel(
     int staged, int nqt, float scale_log2) {
   // staged: block-table entries per sequence that fit the dynamic LDS
   // (enough for max_context_len); positions beyond them are never walked.
-  constexpr int KS = D / 16;          // k-steps of the score product
-  constexpr int DT = D / 32;          // 32-dimension tiles of the output
-  constexpr int KCH = kKT * D / 8;    // 16-byte chunks of a key tile
-  constexpr int VCH = D * kKT / 8;    // 16-byte chunks of a value tile
-  constexpr int KPT = KCH / kThreads; // key chunks per thread
-  constexpr int VPT = VCH / kThreads; // value chunks per thread
-  static_assert(KCH % kThreads == 0 && VCH % kThreads == 0, "tile must split evenly over the workgroup");
-  constexpr int KROW = D + kVPad;     // LDS key row (elements)
-  constexpr int VROW = kKT + kVPad;   // LDS value row (elements)
+  constexpr int KS = D / 16;           // k-steps of the score product
+  constexpr int DT = D / 32;           // 32-dimension tiles of the output
+  constexpr int KX = 32;               // elements per 64-byte key piece
+  constexpr int KROW = D + 8;          // LDS key row (elements)
+  constexpr int VROW = kKT + 8;        // LDS value row (elements)
+  constexpr int KPR = kThreads / 256;  // key pieces per chunk round
+  constexpr int KPT = D / KX / KPR;    // 16-byte key chunks per thread
+  constexpr int VDR = kThreads / 8;    // value dimensions per chunk round
+  constexpr int VPT = D / VDR;         // 16-byte value chunks per thread
+  static_assert(KPT * KPR * KX == D && VPT * VDR == D, "whole rows per chunk round");
 
-  // Work item: XCD-aware order keeps the tiles of one (sequence, head) on one
-  // XCD (consecutive block ids go round-robin over the 8 XCDs), longest tile first.
-  const int nwork = gridDim.x;
-  int wid = blockIdx.x;
-  if ((nwork & 7) == 0) wid = (wid & 7) * (nwork >> 3) + (wid >> 3);
-  const int qt = nqt - 1 - wid % nqt;
-  const int hq = (wid / nqt) % Hq;
-  const int s = wid / (nqt * Hq);
+  // Work item.  The hardware hands out block ids in order as workgroups
+  // finish, so the longest items go first (greedy longest-processing-time
+  // order): the (sequence, query tile) classes are ranked by their number of
+  // 64-token tiles, and block b takes head b % Hq of the class ranked b / Hq.
+  // Every workgroup ranks the classes itself (in LDS, from the lengths); with
+  // more than kLptClasses classes the order is the XCD-aware one instead,
+  // which keeps the query tiles of one (sequence, head) on one XCD.
+  const int tid = threadIdx.x;
+  __shared__ int sLen[kLptClasses];
+  __shared__ int sPick;
+  int qt, hq, s;
+  const int ncls = gridDim.x / Hq;  // S * nqt: the grid is S * Hq * nqt blocks
+  if (ncls <= kLptClasses) {
+    for (int c = tid; c < ncls; c += kThreads) {
+      const int cs = c / nqt, cq = c % nqt;
+      const int ql = query_start_loc[cs + 1] - query_start_loc[cs];
+      const int h0 = min(context_lens[cs], staged * BS) - ql;
+      sLen[c] = (cq * kQT < ql && h0 >= 0) ? (h0 + min(cq * kQT + kQT, ql) - 1) / kKT + 1 : 0;
+    }
+    __syncthreads();
+    const int want = blockIdx.x / Hq;
+    for (int c = tid; c < ncls; c += kThreads) {
+      const int lc = sLen[c];
+      int rank = 0;
+      for (int o = 0; o < ncls; ++o) rank += sLen[o] > lc || (sLen[o] == lc && o < c);
+      if (rank == want) sPick = c;
+    }
+    __syncthreads();
+    const int c = sPick;
+    s = c / nqt;
+    qt = c % nqt;
+    hq = blockIdx.x % Hq;
+  } else {
+    const int nwork = gridDim.x;
+    int wid = blockIdx.x;
+    if ((nwork & 7) == 0) wid = (wid & 7) * (nwork >> 3) + (wid >> 3);
+    qt = nqt - 1 - wid % nqt;
+    hq = (wid / nqt) % Hq;
+    s = wid / (nqt * Hq);
+  }
 
   const int qs = query_start_loc[s];
   const int qlen = query_start_loc[s + 1] - qs;
@@ -125,28 +177,33 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void prefill_kernel(
   if (hist < 0) return;
   const int hkv = hq / (Hq / Hkv);
 
-  const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = uniform(tid >> 6);
-  const int j32 = lane & 31;  // query column of this lane
-  const int h = lane >> 5;    // k-half / row group
+  const int j32 = lane & 31;  // query column of this lane within its group
+  const int h = lane >> 5;    // k-half / row group of the MFMA layouts
 
-  // Two LDS tile buffers: tile t+1 is stored while tile t is computed.
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKT * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VROW];
+  // Three LDS tile buffers: tile t+2 is stored while tiles t and t+1 are read.
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kNBuf][kKT * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kNBuf][D * VROW];
+  __shared__ int sBad;        // the fast route produced a non-finite result
   extern __shared__ int sBT[];  // block ids of the positions this workgroup reads
 
-  const int wrow0 = qt * kQT + 32 * w;                  // first chunk row of this wave
-  const int myrow = wrow0 + j32;
-  const int qpos = hist + min(myrow, qlen - 1);         // position of this lane's query
-  const int wave_min_pos = hist + min(wrow0, qlen - 1);
-  const int wave_max_pos = hist + min(wrow0 + 31, qlen - 1);
-  const int wg_max_pos = hist + min(qt * kQT + kQT - 1, qlen - 1);
-  const int ntiles = (wg_max_pos + kKT) / kKT;
+  const int wrow0 = qt * kQT + kRowsW * w;  // first chunk row of this wave
+  const int wg_last = min(qt * kQT + kQT, qlen) - 1;
+  const int ntiles = (hist + wg_last) / kKT + 1;
+  // 32-token sub-tiles this wave computes (up to its rows' last position);
+  // the workgroup's remaining tiles it only stages.
+  const int nu_w = wrow0 < qlen ? (hist + min(wrow0 + kRowsW, qlen) - 1) / 32 + 1 : 0;
+  // Position of this lane's query in each group, and of each group's first row.
+  int qpos[NG], gmin[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    qpos[g] = hist + min(wrow0 + 32 * g + j32, qlen - 1);
+    gmin[g] = hist + min(wrow0 + 32 * g, qlen - 1);
+  }
 
   // Stage the block table once; tile loads then look block ids up in LDS.
-  __shared__ int sOvf;  // a staged value lay outside fp16's range
-  if (tid == 0) sOvf = 0;
+  if (tid == 0) sBad = 0;
   {
     const int32_t *bt = block_tables + (size_t)s * mbps;
     const int nbt = min((ntiles * kKT + BS - 1) / BS, staged);
@@ -156,26 +213,25 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void prefill_kernel(
     }
   }
 
-  // Q^T operand: query column j32, dimensions 16*ks + 8*h .. +8 (zero past the chunk).
-  u32x4 qb[KS];
-  {
-    const bool valid = myrow < qlen;
-    const uint16_t *qrow = q + ((size_t)(qs + (valid ? myrow : 0)) * Hq + hq) * D;
+  // Q^T operands: query column j32 of group g, dimensions 16*ks + 8*h .. +8
+  // (zero past the chunk).
+  u32x4 qb[NG][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qb[ks] = valid ? load16(qrow + 16 * ks + 8 * h) : u32x4{0, 0, 0, 0};
+  for (int g = 0; g < NG; ++g) {
+    const int row = wrow0 + 32 * g + j32;
+    const bool valid = row < qlen;
+    const uint16_t *qrow = q + ((size_t)(qs + (valid ? row : 0)) * Hq + hq) * D + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[g][ks] = valid ? load16(qrow + 16 * ks) : u32x4{0, 0, 0, 0};
   }
   __syncthreads();
 
-  // Global -> register staging of one tile.  Thread tid moves key pieces
-  // (token (tid/4) % 64, bytes 16*(tid%4).. of 64-byte pieces
-  // tid/256 + KPR*i of the row, so a wave reads 16 tokens x 64 bytes
-  // contiguously) and value chunks (dimension tid/8 + VDR*i, tokens
-  // 8*(tid%8)..+8); a block id comes from the staged table.
-  constexpr int KX = 32;              // elements per 64-byte key piece
-  constexpr int KPR = kThreads / 256; // key pieces per chunk round
-  constexpr int VDR = kThreads / 8;   // value dimensions per chunk round
-  static_assert(KPT * KPR == D / KX, "whole key pieces per chunk round");
+  // Global -> register staging of one tile.  Thread tid moves the 16-byte
+  // column tid%4 of token (tid/4)%64's key row in pieces tid/256 + KPR*i (a
+  // wave reads 16 tokens x 64 bytes contiguously per piece), and value
+  // chunks (dimension tid/8 + VDR*i, tokens 8*(tid%8)..+8).
   const int ktok = (tid >> 2) & (kKT - 1), ksub = tid & 3, kpc = tid >> 8;
+  const int vtok = 8 * (tid & 7), vdim = tid >> 3;
   auto load_tile = [&](int t, u32x4 (&kreg)[KPT], u32x4 (&vreg)[VPT]) {
     const int t0 = t * kKT;
     const bool full = t0 + kKT <= ctx;
@@ -190,15 +246,14 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void prefill_kernel(
       for (int i = 0; i < KPT; ++i) kreg[i] = load16(kb + (size_t)(kpc + KPR * i) * BS * KX);
     }
     {
-      const int pos = t0 + 8 * (tid % 8);
+      const int pos = t0 + vtok;
       const int blk = (full || pos < ctx) ? max(sBT[pos / BS], 0) : 0;
       const uint16_t *vblk = vpool + ((size_t)blk * Hkv + hkv) * D * BS + pos % BS;
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
-        const int e = tid / 8 + VDR * i;
-        u32x4 x = load16(vblk + (size_t)e * BS);
+        u32x4 x = load16(vblk + (size_t)(vdim + VDR * i) * BS);
         if (!full && pos + 8 > ctx) {
-          // Slots past the context may hold anything: zero them.
+          // Slots past the context may hold anything (NaN included): zero them.
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const uint32_t keep = (pos + 2 * k < ctx ? 0x0000ffffu : 0u) |
@@ -210,191 +265,269 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void prefill_kernel(
       }
     }
   };
-  // Staging of one tile into LDS buffer buf.  CONV: values re-encoded to fp16;
-  // returns (through sOvf) whether any of them lay outside fp16's range.
+  // Registers -> LDS buffer buf.  CONV: bf16 values re-encoded to fp16 (exact
+  // below 65536 in magnitude; larger ones become infinities, which the walk's
+  // result check catches).
   auto store_tile = [&](auto conv, int buf, const u32x4 (&kreg)[KPT], const u32x4 (&vreg)[VPT]) {
     constexpr bool CONV = decltype(conv)::value;
+    uint16_t *kd = &sK[buf][kslot(ktok) * KROW + 8 * ksub];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) *(u32x4 *)&sK[buf][ktok * KROW + KX * (kpc + KPR * i) + 8 * ksub] = kreg[i];
-    u16x2 mag = {0, 0};
+    for (int i = 0; i < KPT; ++i) *(u32x4 *)(kd + KX * (kpc + KPR * i)) = kreg[i];
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       u32x4 x = vreg[i];
       if constexpr (CONV) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) x[k] = bf16x2_to_f16x2(x[k], mag);
+        for (int k = 0; k < 4; ++k) x[k] = pack_f16x2(as_f32(x[k] << 16), as_f32(x[k] & 0xffff0000u));
       }
-      *(u32x4 *)&sV[buf][(tid / 8 + VDR * i) * VROW + 8 * (tid % 8)] = x;
+      *(u32x4 *)&sV[buf][(vdim + VDR * i) * VROW + vtok] = x;
     }
-    if (CONV && bf16_beyond_f16(mag)) sOvf = 1;
   };
 
-  float m, l;  // running max (scaled log2 units) and this lane's denominator share
-  f32x16 acc[DT];
+  // Per-lane LDS operand bases: key row kslot(perm(j32)) (half 1: +32 rows),
+  // column 8*h; value row j32 (dimension tile dt: +32 rows), token 8*h.
+  const int kop0 = kslot(perm_row(j32)) * KROW + 8 * h;
+  const int vop0 = j32 * VROW + 8 * h;
+
+  float m[NG], l[NG];   // reference max (scaled log2 units) and this lane's denominator share
+  f32x16 acc[NG][DT];
   const f32x16 zero16 = {};
-  const int krow = perm_row(j32);  // key row (within a 32-token half) this lane feeds
 
   // The whole walk over the key/value tiles.  CONV (bf16 only): P.V on the
-  // fp16 matrix cores; the walk reports whether every staged value fit fp16.
-  auto attend = [&](auto conv) -> bool {
+  // fp16 matrix cores.  FIXED: the fast route with a fixed reference max per
+  // row (no rescaling of the accumulators); otherwise the exact route with
+  // lazy rescaling.  Compute runs in 32-token sub-tiles u = 2t + half.
+  auto attend = [&](auto conv, auto fixed) {
     constexpr bool CONV = decltype(conv)::value;
-    using PV = typename std::conditional<CONV, Mfma32<F16>, Mfma32<E>>::type;
-    m = -INFINITY;
-    l = 0.f;
+    constexpr bool FIXED = decltype(fixed)::value;
+    using PV = typename std::conditional<CONV || std::is_same<E, F16>::value, Mfma32<F16>, Mfma32<E>>::type;
+    constexpr bool kSplit = PV::kSplitP;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int g = 0; g < NG; ++g) {
+      m[g] = -INFINITY;
+      l[g] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
-    // One tile's scores, softmax update and P.V: tile t, staged in LDS buffer cur.
-    auto tile = [&](int t, int cur) {
-      constexpr int HALVES = kKT / 32;
-      f32x16 st[HALVES];  // raw scores q.k
-      const uint16_t *krp = &sK[cur][krow * KROW + 8 * h];
-#if PKV_PREFILL_EARLY_LDS
-      // All key operands of the tile are read before the first product, so
-      // the LDS latency is paid once rather than before every product; the
-      // fence keeps the compiler from sinking the reads back.
-      u32x4 kop[HALVES][KS];
+      for (int dt = 0; dt < DT; ++dt) acc[g][dt] = zero16;
+    }
+
+    // Scores of every row group against sub-tile `half` of tile buffer buf:
+    // each key operand read from LDS feeds all groups' products.
+    auto qk = [&](int buf, int half, f32x16 (&st)[NG]) {
+      const uint16_t *kb = &sK[buf][kop0 + 32 * half * KROW];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 a = *(const u32x4 *)(kb + 16 * ks);
 #pragma unroll
-        for (int hf = 0; hf < HALVES; ++hf)
-          kop[hf][ks] = *(const u32x4 *)(krp + 32 * hf * KROW + 16 * ks);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int hf = 0; hf < HALVES; ++hf) st[hf] = Mfma32<E>::mma(kop[hf][0], qb[0], zero16);
-#pragma unroll
-      for (int ks = 1; ks < KS; ++ks)
-#pragma unroll
-        for (int hf = 0; hf < HALVES; ++hf)  // independent chains back to back
-          st[hf] = Mfma32<E>::mma(kop[hf][ks], qb[ks], st[hf]);
-      // The value operands of the whole tile, in flight during the softmax.
-      u32x4 vop[2 * HALVES][DT];
-#pragma unroll
-      for (int c = 0; c < 2 * HALVES; ++c)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          vop[c][dt] = *(const u32x4 *)&sV[cur][(32 * dt + j32) * VROW + 16 * c + 8 * h];
-      __builtin_amdgcn_sched_barrier(0);
-#else
-#pragma unroll
-      for (int hf = 0; hf < HALVES; ++hf)
-        st[hf] = Mfma32<E>::mma(*(const u32x4 *)(krp + 32 * hf * KROW), qb[0], zero16);
-#pragma unroll
-      for (int ks = 1; ks < KS; ++ks)
-#pragma unroll
-        for (int hf = 0; hf < HALVES; ++hf)  // independent chains back to back
-          st[hf] = Mfma32<E>::mma(*(const u32x4 *)(krp + 32 * hf * KROW + 16 * ks), qb[ks], st[hf]);
-#endif
-      // Item 4a+b of half hf is tile token 32*hf + perm(8a+4h+b).  Only a
-      // tile that crosses this wave's diagonal needs the causal mask (the
-      // hint keeps the compiler from turning the branch into selects that
-      // every tile would pay for).
-      if (__builtin_expect(t * kKT + kKT - 1 > wave_min_pos, 0)) {
-#pragma unroll
-        for (int hf = 0; hf < HALVES; ++hf)
-#pragma unroll
-          for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              const int pos = t * kKT + 32 * hf + 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
-              if (pos > qpos) st[hf][4 * a + b] = -INFINITY;
-            }
+        for (int g = 0; g < NG; ++g) st[g] = Mfma32<E>::mma(a, qb[g][ks], ks == 0 ? zero16 : st[g]);
       }
-      float mraw = -INFINITY;
+    };
+    // Causal mask of group g's scores (only on sub-tiles that reach past the
+    // group's first row; MAYBE: the caller's tile may); u0 is the sub-tile's
+    // first position.
+    auto mask = [&](int g, int u0, f32x16 &st, auto maybe) {
+      if (decltype(maybe)::value && u0 + 31 > gmin[g]) {
 #pragma unroll
-      for (int hf = 0; hf < HALVES; ++hf)
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, st[hf][i]);
-      mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
-      const float mb = mraw * scale_log2;  // scale > 0: the max commutes with scaling
-      if (__any(mb > m + kRescaleLog2)) {
-        const float mnew = fmaxf(m, mb);
-        const float alpha = fast_exp2(m - mnew);  // 1 for rows that keep their reference
-        m = mnew;
-        l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+          for (int b = 0; b < 4; ++b) {
+            const int pos = u0 + 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
+            if (pos > qpos[g]) st[4 * a + b] = -INFINITY;
+          }
       }
-      float psum = 0.f;
+    };
+    // Row max of scores (log2 units).
+    auto row_max = [&](const f32x16 &st) -> float {
+      float mraw = __builtin_fmaxf(__builtin_fmaxf(st[0], st[1]), st[2]);
 #pragma unroll
-      for (int c = 0; c < 2 * HALVES; ++c) {
-        // This lane's 8 weights of k-step c (16 tokens) against the value
-        // rows 32dt + j32, tokens 16c + 8h .. +8 of the staged tile.
-        const int hf = c >> 1, c2 = c & 1;
+      for (int i = 3; i < 15; i += 2) mraw = __builtin_fmaxf(__builtin_fmaxf(mraw, st[i]), st[i + 1]);
+      mraw = __builtin_fmaxf(mraw, st[15]);
+      return pair_max(mraw) * scale_log2;  // scale > 0: the max commutes with scaling
+    };
+    // Exact route: running-max update and lazy rescale of group g.
+    auto rescale = [&](int g, const f32x16 &st) {
+      const float mb = row_max(st);
+      if (__any(mb > m[g] + kRescaleLog2)) {
+        const float mnew = __builtin_fmaxf(m[g], mb);
+        const float alpha = fast_exp2(m[g] - mnew);  // 1 for rows that keep their reference
+        m[g] = mnew;
+        l[g] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[g][dt] *= alpha;
+      }
+    };
+    // Weights of group g, packed as the P^T operands of the sub-tile's two
+    // 16-token k-steps (c: tokens 16c .. 16c+15; this lane's 8 are
+    // 16c + 8h .. +8), and the lane's share of the denominator.
+    auto weights = [&](int g, const f32x16 &st, u32x4 (&pk)[2], u32x4 (&pl)[2]) {
+      const float mr = m[g];
+      float lsum = l[g];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
         float p[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          p[k] = fast_exp2(fmaf(st[hf][8 * c2 + k], scale_log2, -m));
-          psum += p[k];
-        }
-        u32x4 pb, pl;
-        if constexpr (PV::kSplitP) {
+        for (int k = 0; k < 8; ++k) p[k] = fast_exp2(fmaf(st[8 * c + k], scale_log2, -mr));
+        if constexpr (kSplit) {
           uint32_t hi[4], lo[4];
 #pragma unroll
           for (int k = 0; k < 4; ++k) split_bf16x2(p[2 * k], p[2 * k + 1], hi[k], lo[k]);
-          pb = u32x4{hi[0], hi[1], hi[2], hi[3]};
-          pl = u32x4{lo[0], lo[1], lo[2], lo[3]};
+          pk[c] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+          pl[c] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+#pragma unroll
+          for (int k = 0; k < 8; ++k) lsum += p[k];
         } else {
-          pb = u32x4{PV::pack2(p[0], p[1]), PV::pack2(p[2], p[3]), PV::pack2(p[4], p[5]),
-                     PV::pack2(p[6], p[7])};
+          // fp16 weights; the denominator sums the same rounded weights the
+          // product uses (two per dot instruction, fp32 accumulation).
+          const f16x2 one2 = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t wv = pack_f16x2(p[2 * k], p[2 * k + 1]);
+            pk[c][k] = wv;
+            lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, wv), one2, lsum, false);
+          }
         }
+      }
+      l[g] = lsum;
+    };
+    // O^T of every group += V^T . P^T over sub-tile `half` of tile buffer
+    // buf, each value operand read once for all groups.
+    auto pv = [&](int buf, int half, const u32x4 (&pk)[NG][2], const u32x4 (&pl)[NG][2]) {
+      const uint16_t *vb = &sV[buf][vop0 + 32 * half];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-#if PKV_PREFILL_EARLY_LDS
-          const u32x4 a = vop[c][dt];
-#else
-          const u32x4 a = *(const u32x4 *)&sV[cur][(32 * dt + j32) * VROW + 16 * c + 8 * h];
-#endif
-          acc[dt] = PV::mma(a, pb, acc[dt]);
-          if constexpr (PV::kSplitP) acc[dt] = PV::mma(a, pl, acc[dt]);
+          const u32x4 a = *(const u32x4 *)(vb + 32 * dt * VROW + 16 * c);
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            acc[g][dt] = PV::mma(a, pk[g][c], acc[g][dt]);
+            if constexpr (kSplit) acc[g][dt] = PV::mma(a, pl[g][c], acc[g][dt]);
+          }
         }
-      }
-      l += psum;
     };
+
     u32x4 kreg[KPT], vreg[VPT];
+    // Prologue: tiles 0 and 1 in LDS, tile 2 in registers.
     load_tile(0, kreg, vreg);
     store_tile(conv, 0, kreg, vreg);
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-      const int cur = t & 1;
-      if (t + 1 < ntiles) load_tile(t + 1, kreg, vreg);  // in flight while this tile is computed
-      if (t * kKT <= wave_max_pos) tile(t, cur);  // else entirely in this wave's future
-      // The other buffer was last read in the previous iteration, before the
-      // barrier that ended it; the barrier below publishes tile t+1.
-      if (t + 1 < ntiles) store_tile(conv, cur ^ 1, kreg, vreg);
-      __syncthreads();
+    if (ntiles > 1) {
+      load_tile(1, kreg, vreg);
+      store_tile(conv, 1, kreg, vreg);
     }
-    return !CONV || uniform(sOvf) == 0;
+    if (ntiles > 2) load_tile(2, kreg, vreg);
+    __syncthreads();
+
+    f32x16 sc[NG];
+    qk(0, 0, sc);
+    if constexpr (FIXED) {
+      // Reference max of each row: its first 32 keys (key 0 is always one of
+      // them, so it is finite).
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        mask(g, 0, sc[g], std::true_type{});
+        m[g] = row_max(sc[g]);
+      }
+    }
+    // One 64-token tile t (buffer cur; nxt and aft hold tiles t+1 and t+2):
+    // its two 32-token sub-tiles u = 2t + half, then tile t+2 goes from
+    // registers to LDS and tile t+3 from HBM to registers.  A sub-tile
+    // starts with its scores (computed by the previous one) masked and, on
+    // the exact route, their maxima handled; then it computes the next
+    // sub-tile's scores while its own weights are formed, then its P.V.  The
+    // next scores are computed even past the wave's last sub-tile (then from
+    // a stale buffer, and never used), so every sub-tile runs the same code.
+    // MASKED: the tile may reach past the wave's first row (causal mask, and
+    // sub-tiles past the wave's last row skipped).
+    auto tile_step = [&](int t, int cur, int nxt, int aft, auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
+      auto sub = [&](auto hv) {
+        constexpr int half = decltype(hv)::value;
+        const int u0 = t * kKT + 32 * half;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          mask(g, u0, sc[g], masked);
+          if constexpr (!FIXED) rescale(g, sc[g]);
+        }
+        f32x16 nx[NG];
+        qk(half ? nxt : cur, half ^ 1, nx);
+        u32x4 pk[NG][2], pl[NG][2];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) weights(g, sc[g], pk[g], pl[g]);
+        pv(cur, half, pk, pl);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) sc[g] = nx[g];
+      };
+      if (!MASKED || 2 * t < nu_w) sub(Grp<0>{});
+      if (!MASKED || 2 * t + 1 < nu_w) sub(Grp<1>{});
+      if (t + 2 < ntiles) {
+        store_tile(conv, aft, kreg, vreg);
+        if (t + 3 < ntiles) load_tile(t + 3, kreg, vreg);
+      }
+      __syncthreads();
+    };
+    // Tiles before the first that reaches past the wave's first row need no
+    // mask (and are all within the wave's sub-tiles).
+    const int t_diag = nu_w > 0 ? min(ntiles, (gmin[0] + 1) / kKT) : 0;
+    int t = 0, cur = 0;
+    for (; t < t_diag; ++t) {
+      const int nxt = cur == kNBuf - 1 ? 0 : cur + 1;
+      tile_step(t, cur, nxt, nxt == kNBuf - 1 ? 0 : nxt + 1, std::false_type{});
+      cur = nxt;
+    }
+    for (; t < ntiles; ++t) {
+      const int nxt = cur == kNBuf - 1 ? 0 : cur + 1;
+      tile_step(t, cur, nxt, nxt == kNBuf - 1 ? 0 : nxt + 1, std::true_type{});
+      cur = nxt;
+    }
   };
 
-  // bf16: the fp16 route first; if any staged value lay outside fp16's range
-  // (a flag every thread reads after the walk's last barrier), the whole walk
-  // is redone on the exact bf16 route.  Nothing was written meanwhile.
-  constexpr bool kConvV = std::is_same<E, BF16>::value && PKV_PREFILL_CONV_V;
-  bool done = false;
-  if constexpr (kConvV) done = attend(std::true_type{});
-  if (!done) attend(std::false_type{});
+  // The fast route first: fixed reference maxima and, for bf16, P.V on the
+  // fp16 matrix cores.  The workgroup redoes the walk on the exact route
+  // (lazy rescaling, bf16 products for bf16) if any row's accumulators or
+  // denominator came out non-finite: a weight beyond fp16 (a row whose max
+  // outgrew its reference by 2^16), or for bf16 a value of magnitude >= 65536
+  // (no fp16 encoding).  A non-finite input gives the same answer on both
+  // routes.  The decision is the workgroup's (its waves share the barriers);
+  // nothing was written meanwhile.
+  constexpr bool kConvV = std::is_same<E, BF16>::value;
+  attend(std::integral_constant<bool, kConvV>{}, std::true_type{});
+  {
+    bool bad = false;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      bad |= !__builtin_isfinite(pair_sum(l[g]));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bad |= !__builtin_isfinite(acc[g][dt][i]);
+    }
+    if (__any(bad) && lane == 0) sBad = 1;
+  }
+  __syncthreads();
+  if (sBad) attend(std::false_type{}, std::false_type{});
 
   // Lanes l and l^32 hold the two row halves of the same query column.
-  const float ltot = l + __shfl_xor(l, 32);
-  if (myrow < qlen) {
-    const float inv = 1.f / ltot;
-    const size_t orow = ((size_t)(qs + myrow) * Hq + hq) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+  for (int g = 0; g < NG; ++g) {
+    const float ltot = pair_sum(l[g]);
+    const int row = wrow0 + 32 * g + j32;
+    if (row < qlen) {
+      const float inv = 1.f / ltot;
+      const size_t orow = ((size_t)(qs + row) * Hq + hq) * D;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int dim = 32 * dt + 8 * a + 4 * h;
-        const float o0 = acc[dt][4 * a] * inv, o1 = acc[dt][4 * a + 1] * inv;
-        const float o2 = acc[dt][4 * a + 2] * inv, o3 = acc[dt][4 * a + 3] * inv;
-        if (out_f32) {
-          *(f32x4 *)((float *)out + orow + dim) = f32x4{o0, o1, o2, o3};
-        } else {
-          *(u32x2 *)((uint16_t *)out + orow + dim) =
-              u32x2{Mfma32<E>::pack2(o0, o1), Mfma32<E>::pack2(o2, o3)};
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int dim = 32 * dt + 8 * a + 4 * h;
+          const float o0 = acc[g][dt][4 * a] * inv, o1 = acc[g][dt][4 * a + 1] * inv;
+          const float o2 = acc[g][dt][4 * a + 2] * inv, o3 = acc[g][dt][4 * a + 3] * inv;
+          if (out_f32) {
+            *(f32x4 *)((float *)out + orow + dim) = f32x4{o0, o1, o2, o3};
+          } else {
+            *(u32x2 *)((uint16_t *)out + orow + dim) =
+                u32x2{Mfma32<E>::pack2(o0, o1), Mfma32<E>::pack2(o2, o3)};
+          }
         }
-      }
+    }
   }
 }
 
