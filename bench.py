@@ -9,6 +9,13 @@ whole cache (+ the split-KV reduce when partitioned).  Inputs are resident
 in HBM before timing; two identical pool copies alternate between steps so
 the 256 MiB Infinity Cache cannot serve a step from the previous one.
 
+`value` comes from K steps timed back to back with nothing between them; the
+roofline's per-launch duration from K further steps with timing events around
+each attention call.  The default run also measures, in the same process,
+long-context split-KV decode, GQA decode at block sizes 16 and 32 and chunked
+prefill, each under `extra_configs` with its own roofline and a short CPU
+oracle sample.
+
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -300,79 +307,29 @@ def cpu_baseline(wl, budget_s):
                       f"{el:.1f} s wall on 1 thread, {el_all:.1f} s on {cores}"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="llama13b",
-                    choices=["llama13b", "llama13b_fp8", "long_split", "gqa16", "gqa32", "prefill",
-                             "mixed", "sliding", "tiny"])
-    ap.add_argument("--partition", type=int, default=None,
-                    help="split-KV partition size in tokens (default: the workload's)")
-    ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
-                    help="block size of the llama13b workload (paging-overhead sweep)")
-    ap.add_argument("--placement", default="shuffled", choices=["shuffled", "contiguous"],
-                    help="physical block order of the llama13b workload (paging-overhead sweep)")
-    ap.add_argument("--kv-cache", default="model", choices=["model", "fp8"],
-                    help="fp8: store the decode workload's cache as E4M3 codes (scales 0.0135)")
-    ap.add_argument("--step", default="scatter+decode", choices=["scatter+decode", "fused"],
-                    help="decode workloads: fused = one appending call that writes the new "
-                         "tokens' K/V and attends (timed as the attention launch)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="only run a plain device copy of this many MiB (counter calibration)")
-    ap.add_argument("--read-probe-gib", type=int, default=0,
-                    help="only run the HBM read-ceiling probe over this many GiB of random 4 KiB tiles")
-    ap.add_argument("--cache-ops", action="store_true",
-                    help="only time the block copy and the slot scatter alone (prefill pool shape)")
-    ap.add_argument("--no-read-probe", action="store_true",
-                    help="decode workloads: skip the read-ceiling probe after the timed steps")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported",
-              file=sys.stderr)
-        sys.exit(2)
+EXTRA_CONFIGS = ("long_split", "gqa16", "gqa32", "prefill")
 
+
+def run_config(torch, pkv, name, args, cpu_budget, read_probe, fused=False, kv_cache="model",
+               block_size=16, placement="shuffled", partition=None):
+    """One workload: generate, upload two pool copies, time the step, report its roofline.
+
+    The step (the new tokens' scatter, then the attention call) is timed twice over the same
+    inputs: first K steps with nothing between them (ms_per_step, value), then K steps with a
+    pair of timing events around each attention call (the roofline's per-launch duration; each
+    event pair costs the stream a few microseconds, so it stays out of the first loop)."""
     import numpy as np
-    import torch
 
-    import paged_kv_cache_92_amd as pkv
     from paged_kv_cache_92_amd.runner import DeviceWorkload, new_cache
 
-    torch.cuda.set_device(0)
-    if args.copy_probe_mib:
-        # A copy of known size: reads and writes exactly n bytes per launch.
-        n = args.copy_probe_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(args.steps):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes": n, "launches": args.steps}), flush=True)
-        return
-    if args.cache_ops:
-        print(json.dumps({"cache_ops": cache_ops(torch, pkv, args.steps), "steps": args.steps,
-                          "peak_GBps": HBM_PEAK_GBS}), flush=True)
-        return
-    if args.read_probe_gib:
-        g = read_probe_gbps(torch, gib=args.read_probe_gib, reps=args.steps)
-        print(json.dumps({"read_probe_GBps": round(g, 1), "tile_bytes": 4096,
-                          "bytes": args.read_probe_gib << 30, "launches": args.steps}), flush=True)
-        return
-    pkv.lib()
     t0 = time.time()
-    if args.config != "llama13b" and (args.block_size != 16 or args.placement != "shuffled"):
-        raise SystemExit("--block-size/--placement apply to the llama13b workload only")
-    wl, desc = make_workload(args.config, args.partition, args.block_size, args.placement)
-    if args.kv_cache == "fp8" and wl.cache_dtype != 3:
+    wl, desc = make_workload(name, partition, block_size, placement)
+    if kv_cache == "fp8" and wl.cache_dtype != 3:
         if wl.mode != "decode":
             raise SystemExit("--kv-cache fp8 applies to decode workloads")
         from paged_kv_cache_92_amd import workloads as W
         wl.kv_dtype, wl.k_scale, wl.v_scale = W.FP8, 0.0135, 0.0135
         desc += ", stored as fp8 e4m3 codes (per-tensor scales)"
-    fused = args.step == "fused"
     if fused and wl.mode != "decode":
         raise SystemExit("--step fused applies to decode workloads")
     log(f"[bench] generated {wl.name} in {time.time() - t0:.1f}s "
@@ -416,20 +373,25 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # Throughput: K whole steps back to back.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
+    # Per-launch duration of the attention call: K more steps, events around each call.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
     attn_ms = [a.elapsed_time(b) for a, b in evs]
     attn_avg = float(np.mean(attn_ms))
-    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step, attention "
+    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step; attention call "
         f"{attn_avg * 1e3:.1f} us avg (median {np.median(attn_ms) * 1e3:.1f}, "
         f"min {np.min(attn_ms) * 1e3:.1f})")
 
@@ -456,9 +418,7 @@ def main():
     flops = attention_flops(wl)
     res = {
         "metric": "paged decode effective KV GB/s (% of HBM peak) + decode tokens/s, 13B shape",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "ms_per_step": round(ms_step, 5), "dtype": dt,
     }
     if wl.mode == "decode":
         gbs_step = kv / (ms_step * 1e-3) / 1e9
@@ -469,21 +429,23 @@ def main():
             "decode_tokens_per_s": round(wl.S / (ms_step * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs_attn, 2), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs_attn / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic(args.config),
+                         "traffic": measured_traffic(name),
                          "kernel": "paged decode (partial + reduce when split)" if not fused
                          else "appending paged decode (partial + reduce when split)",
                          "algorithmic_bytes_per_launch": kv,
                          "avg_launch_us": round(attn_avg * 1e3, 2),
                          "median_launch_us": round(float(np.median(attn_ms)) * 1e3, 2)},
         })
-        if not args.no_read_probe:
+        if read_probe:
             probe = read_probe_gbps(torch)
             res["roofline"]["read_probe_GBps"] = round(probe, 1)
             res["roofline"]["frac_of_read_probe"] = round(gbs_attn / probe, 4)
             log(f"[bench] read-ceiling probe: {probe:.0f} GB/s (decode call at "
                 f"{100 * gbs_attn / probe:.1f}% of it)")
-        if args.config.startswith("llama13b"):
+        if name.startswith("llama13b"):
             res["decode_tokens_per_s_40_layer_attention_only"] = round(wl.S / (40 * ms_step * 1e-3), 1)
+        else:
+            res["metric"] = "paged decode effective KV GB/s (% of HBM peak)"
         if wl.window:
             res["metric"] = "sliding-window paged decode effective KV GB/s (window tokens only)"
     elif wl.mode == "mixed":
@@ -509,7 +471,7 @@ def main():
                          "peak": HBM_PEAK_GBS if bound == "hbm" else MFMA_PEAK_TFLOPS[dt],
                          "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
                          "frac": round(max(t_hbm, t_mfma) / t_attn, 4),
-                         "traffic": measured_traffic(args.config),
+                         "traffic": measured_traffic(name),
                          "kernel": "mixed step (decode kernel and prefill kernel at once)",
                          "algorithmic_bytes_decode": dec_bytes,
                          "algorithmic_flops_prefill": pre_flops,
@@ -528,7 +490,7 @@ def main():
             "value": round(tf_step, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf_attn, 2), "peak": MFMA_PEAK_TFLOPS[dt],
                          "unit": "TFLOP/s", "frac": round(tf_attn / MFMA_PEAK_TFLOPS[dt], 4),
-                         "traffic": measured_traffic(args.config), "kernel": "paged prefill",
+                         "traffic": measured_traffic(name), "kernel": "paged prefill",
                          "algorithmic_flops_per_launch": flops,
                          "avg_launch_us": round(attn_avg * 1e3, 2)},
         })
@@ -536,15 +498,109 @@ def main():
     res["config"] = {"workload": desc, "seqs": wl.S, "q_heads": wl.num_q_heads,
                      "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                      "block_size": wl.block_size, "pool_blocks": wl.num_blocks,
-                     "placement": args.placement,
-                     "step": args.step if wl.mode == "decode" else None,
+                     "placement": placement,
+                     "step": ("fused" if fused else "scatter+decode") if wl.mode == "decode" else None,
                      "total_context_tokens": int(wl.context_lens.sum()),
                      "sliding_window": wl.window or None,
                      "partition_size": wl.partition_size if wl.mode != "prefill" else None,
                      "kv_bytes": kv, "attention_flops": flops}
-    if not args.no_cpu_baseline:
+    if cpu_budget > 0:
         log("[bench] timing the CPU oracle on a bounded sample")
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(wl, cpu_budget)
+    del copies, out, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="llama13b",
+                    choices=["llama13b", "llama13b_fp8", "long_split", "gqa16", "gqa32", "prefill",
+                             "mixed", "sliding", "tiny"])
+    ap.add_argument("--partition", type=int, default=None,
+                    help="split-KV partition size in tokens (default: the workload's)")
+    ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
+                    help="block size of the llama13b workload (paging-overhead sweep)")
+    ap.add_argument("--placement", default="shuffled", choices=["shuffled", "contiguous"],
+                    help="physical block order of the llama13b workload (paging-overhead sweep)")
+    ap.add_argument("--kv-cache", default="model", choices=["model", "fp8"],
+                    help="fp8: store the decode workload's cache as E4M3 codes (scales 0.0135)")
+    ap.add_argument("--step", default="scatter+decode", choices=["scatter+decode", "fused"],
+                    help="decode workloads: fused = one appending call that writes the new "
+                         "tokens' K/V and attends (timed as the attention launch)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--extra-cpu-budget", type=float, default=3.0,
+                    help="seconds of oracle work for each extra configuration")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="default run: skip the long-split, GQA and prefill configurations")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--read-probe-gib", type=int, default=0,
+                    help="only run the HBM read-ceiling probe over this many GiB of random 4 KiB tiles")
+    ap.add_argument("--cache-ops", action="store_true",
+                    help="only time the block copy and the slot scatter alone (prefill pool shape)")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="decode workloads: skip the read-ceiling probe after the timed steps")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_92_amd as pkv
+
+    torch.cuda.set_device(0)
+    if args.copy_probe_mib:
+        # A copy of known size: reads and writes exactly n bytes per launch.
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": args.steps}), flush=True)
+        return
+    if args.cache_ops:
+        print(json.dumps({"cache_ops": cache_ops(torch, pkv, args.steps), "steps": args.steps,
+                          "peak_GBps": HBM_PEAK_GBS}), flush=True)
+        return
+    if args.read_probe_gib:
+        g = read_probe_gbps(torch, gib=args.read_probe_gib, reps=args.steps)
+        print(json.dumps({"read_probe_GBps": round(g, 1), "tile_bytes": 4096,
+                          "bytes": args.read_probe_gib << 30, "launches": args.steps}), flush=True)
+        return
+    pkv.lib()
+    if args.config != "llama13b" and (args.block_size != 16 or args.placement != "shuffled"):
+        raise SystemExit("--block-size/--placement apply to the llama13b workload only")
+    fused = args.step == "fused"
+    res = {"metric": None, "value": None, "unit": None, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": None, "data": "synthetic"}
+    main_res = run_config(torch, pkv, args.config, args,
+                          0.0 if args.no_cpu_baseline else args.cpu_budget,
+                          not args.no_read_probe, fused=fused, kv_cache=args.kv_cache,
+                          block_size=args.block_size, placement=args.placement,
+                          partition=args.partition)
+    res.update(main_res)
+    # The default run also measures the other configurations' hot paths, each
+    # with its own roofline, in this process.
+    default_sweep = (args.config == "llama13b" and args.block_size == 16 and args.placement == "shuffled"
+                     and args.kv_cache == "model" and not fused and args.partition is None)
+    if default_sweep and not args.no_extras:
+        extras = {}
+        for name in EXTRA_CONFIGS:
+            log(f"[bench] configuration {name}")
+            extras[name] = run_config(torch, pkv, name, args,
+                                      0.0 if args.no_cpu_baseline else args.extra_cpu_budget,
+                                      False)
+        res["extra_configs"] = extras
     print(json.dumps(res), flush=True)
 
 
