@@ -1,6 +1,8 @@
 """Drive the CPU oracle through a workload (test-side helper)."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 import oracle
@@ -38,9 +40,27 @@ def reference_output(wl, k, v):
                                 wl.block_tables, wl.scale, **_kv(wl))
 
 
-def sampled_rows(wl, k, v, rows):
-    """fp64 oracle output for selected query rows only (all heads)."""
+def oracle_threads():
+    """Threads for row-parallel oracle calls (the C entry points run without the
+    interpreter lock and share no state): the host's cores, at most 16."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def sampled_rows(wl, k, v, rows, threads=None):
+    """fp64 oracle output for selected query rows only (all heads), the rows
+    spread over a thread pool."""
     rows = np.asarray(rows, dtype=np.int64)
+    n = oracle_threads() if threads is None else threads
+    if n > 1 and rows.size > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        parts = [p for p in np.array_split(rows, min(n * 4, rows.size)) if p.size]
+        with ThreadPoolExecutor(max_workers=n) as pool:
+            outs = list(pool.map(lambda p: _rows(wl, k, v, p), parts))
+        return np.concatenate(outs, axis=0)
+    return _rows(wl, k, v, rows)
+
+
+def _rows(wl, k, v, rows):
     if wl.mode == "decode":
         seq = rows
         pos = wl.context_lens[rows] - 1

@@ -91,13 +91,13 @@ def test_append_sliding_window(B, G, part):
 
 def test_append_llama13b():
     # The LLaMA-2-13B-shaped decode step as benchmarked, fused: whole pools bit
-    # for bit against scatter + decode and the oracle, sampled rows.
+    # for bit against scatter + decode and the oracle, every row.
     wl = W.llama13b_decode_f16()
     cache, o32 = _both_ways(wl)
     k_ref, v_ref = fill_pools(wl)
     for dev, ref in ((cache.k_pool, k_ref), (cache.v_pool, v_ref)):
         assert np.array_equal(bits_of(dev).view(np.uint8), np.ascontiguousarray(ref).view(np.uint8))
-    rows = sorted({0, int(np.argmin(wl.context_lens)), int(np.argmax(wl.context_lens)), wl.S - 1})
+    rows = list(range(wl.S))
     assert_close(values_of(o32)[rows], sampled_rows(wl, k_ref, v_ref, rows), wl.dtype, wl.name)
 
 
@@ -112,5 +112,5 @@ def test_append_beyond_plan_limit(G, part):
     k_ref, v_ref = fill_pools(wl)
     for dev, ref in ((cache.k_pool, k_ref), (cache.v_pool, v_ref)):
         assert np.array_equal(bits_of(dev).view(np.uint8), np.ascontiguousarray(ref).view(np.uint8))
-    rows = sorted(set(np.random.default_rng(6).choice(wl.S, size=24, replace=False).tolist()) | {8199})
+    rows = list(range(wl.S))
     assert_close(values_of(o32)[rows], sampled_rows(wl, k_ref, v_ref, rows), wl.dtype, wl.name)
