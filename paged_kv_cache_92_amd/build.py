@@ -64,6 +64,50 @@ def build(verbose: bool = False, out: str = LIB, extra: tuple[str, ...] = ()) ->
     return out
 
 
+# Host-side instrumentation: AddressSanitizer and UndefinedBehaviorSanitizer on
+# the host pass only (each flag behind -Xarch_host), so device code is built
+# exactly as in the regular library.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def host_asan_runtime() -> str:
+    """The clang AddressSanitizer runtime a host-sanitized build needs preloaded."""
+    import glob
+    llvm = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(HIPCC))), "llvm")
+    hits = sorted(glob.glob(os.path.join(llvm, "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise RuntimeError(f"no clang ASan runtime under {llvm}")
+    return hits[-1]
+
+
+def build_host_sanitized(out: str, verbose: bool = False) -> str:
+    """libpkv whose host C++ (argument checks, schedule planning, workspace
+    arithmetic, pkv_validate_host: pkv_api.cpp) runs under ASan + UBSan; the
+    kernel objects are the regular build's (compiled first if absent).  Load
+    it with host_asan_runtime() preloaded."""
+    tag = os.path.splitext(os.path.basename(LIB))[0]
+    objs = [os.path.join(OBJ_DIR, f"{tag}_{os.path.splitext(src)[0]}.o") for src in SOURCES
+            if src != "pkv_api.cpp"]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose=verbose)
+    api = out + ".api.o"
+    compile_flags = [f for f in FLAGS if f not in ("-shared", "-O3")]
+    cmd = [HIPCC, *compile_flags, "-O1", "-g", *HOST_SANITIZE, "-I", INCLUDE, "-I", CSRC, "-c",
+           os.path.join(CSRC, "pkv_api.cpp"), "-o", api]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *HOST_SANITIZE[:4],
+           "-Xarch_host", "-shared-libasan", api, *objs, "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return out
+
+
 PROBE_SRC = os.path.join(PKG, "probe", "hbm_read_probe.hip")
 PROBE_LIB = os.path.join(PKG, "probe", "libpkv_probe.so")
 
