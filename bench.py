@@ -325,8 +325,6 @@ def run_config(torch, pkv, name, args, cpu_budget, read_probe, fused=False, kv_c
     t0 = time.time()
     wl, desc = make_workload(name, partition, block_size, placement)
     if kv_cache == "fp8" and wl.cache_dtype != 3:
-        if wl.mode != "decode":
-            raise SystemExit("--kv-cache fp8 applies to decode workloads")
         from paged_kv_cache_92_amd import workloads as W
         wl.kv_dtype, wl.k_scale, wl.v_scale = W.FP8, 0.0135, 0.0135
         desc += ", stored as fp8 e4m3 codes (per-tensor scales)"
@@ -414,6 +412,8 @@ def run_config(torch, pkv, name, args, cpu_budget, read_probe, fused=False, kv_c
             log(f"[bench] {how}: {ways[how] * 1e3:.1f} us avg")
 
     dt = {0: "f32", 1: "f16", 2: "bf16", 3: "fp8_e4m3"}[wl.cache_dtype]
+    # The products run in the model dtype (an 8-bit cache is widened to it).
+    mdt = {0: "f32", 1: "f16", 2: "bf16"}[wl.dtype]
     kv = wl.kv_bytes()
     flops = attention_flops(wl)
     res = {
@@ -459,7 +459,7 @@ def run_config(torch, pkv, name, args, cpu_budget, read_probe, fused=False, kv_c
         # Lower bound of the step: decode KV at HBM peak and chunk products at
         # MFMA peak, overlapped perfectly; the larger of the two names the bound.
         t_hbm = dec_bytes / (HBM_PEAK_GBS * 1e9)
-        t_mfma = pre_flops / (MFMA_PEAK_TFLOPS[dt] * 1e12)
+        t_mfma = pre_flops / (MFMA_PEAK_TFLOPS[mdt] * 1e12)
         bound = "hbm" if t_hbm >= t_mfma else "mfma"
         t_attn = attn_avg * 1e-3
         res["metric"] = "mixed decode + chunked-prefill step: query rows/s (one call)"
@@ -468,7 +468,7 @@ def run_config(torch, pkv, name, args, cpu_budget, read_probe, fused=False, kv_c
             "roofline": {"bound": bound,
                          "achieved": round(dec_bytes / t_attn / 1e9, 2) if bound == "hbm"
                          else round(pre_flops / t_attn / 1e12, 2),
-                         "peak": HBM_PEAK_GBS if bound == "hbm" else MFMA_PEAK_TFLOPS[dt],
+                         "peak": HBM_PEAK_GBS if bound == "hbm" else MFMA_PEAK_TFLOPS[mdt],
                          "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
                          "frac": round(max(t_hbm, t_mfma) / t_attn, 4),
                          "traffic": measured_traffic(name),
@@ -488,8 +488,8 @@ def run_config(torch, pkv, name, args, cpu_budget, read_probe, fused=False, kv_c
         tf_attn = flops / (attn_avg * 1e-3) / 1e12
         res.update({
             "value": round(tf_step, 2), "unit": "TFLOP/s",
-            "roofline": {"bound": "mfma", "achieved": round(tf_attn, 2), "peak": MFMA_PEAK_TFLOPS[dt],
-                         "unit": "TFLOP/s", "frac": round(tf_attn / MFMA_PEAK_TFLOPS[dt], 4),
+            "roofline": {"bound": "mfma", "achieved": round(tf_attn, 2), "peak": MFMA_PEAK_TFLOPS[mdt],
+                         "unit": "TFLOP/s", "frac": round(tf_attn / MFMA_PEAK_TFLOPS[mdt], 4),
                          "traffic": measured_traffic(name), "kernel": "paged prefill",
                          "algorithmic_flops_per_launch": flops,
                          "avg_launch_us": round(attn_avg * 1e3, 2)},
@@ -528,7 +528,7 @@ def main():
     ap.add_argument("--placement", default="shuffled", choices=["shuffled", "contiguous"],
                     help="physical block order of the llama13b workload (paging-overhead sweep)")
     ap.add_argument("--kv-cache", default="model", choices=["model", "fp8"],
-                    help="fp8: store the decode workload's cache as E4M3 codes (scales 0.0135)")
+                    help="fp8: store the workload's cache as E4M3 codes (scales 0.0135)")
     ap.add_argument("--step", default="scatter+decode", choices=["scatter+decode", "fused"],
                     help="decode workloads: fused = one appending call that writes the new "
                          "tokens' K/V and attends (timed as the attention launch)")

@@ -285,9 +285,13 @@ pkv_status pkv_paged_decode_append(const pkv_cache *cache, const void *key, cons
  * at position context_lens[s] - qlen_s + i and attends to positions 0..that
  * position.  Blocks may be shared between sequences (prefix sharing).
  *
- *   out, q            [total_rows][num_q_heads][head_dim]; cache dtype f16 or
- *                     bf16 (8-bit caches: PKV_ERR_UNSUPPORTED); out_dtype as
- *                     for pkv_paged_decode
+ *   out, q            [total_rows][num_q_heads][head_dim] in the model dtype:
+ *                     an f16 or bf16 cache's own, or an 8-bit cache's
+ *                     model_dtype ([W] section "PagedAttention 커널: 비연속
+ *                     메모리 접근": the cache write's kv_cache_dtype, k_scale
+ *                     and v_scale serve every later read; an element's value
+ *                     is code * scale).  out_dtype as for pkv_paged_decode
+ *                     (fp32 cache: PKV_ERR_UNSUPPORTED)
  *   query_start_loc   int32 [num_seqs + 1], non-decreasing, starts at 0
  *   context_lens      int32 [num_seqs], >= qlen_s, >= 1
  *   max_query_len     host bound on every qlen_s
@@ -318,9 +322,9 @@ pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, int32_t out_dtyp
  *   sequences num_decode_seqs .. num_seqs-1   chunks, as for pkv_paged_prefill
  *                     (query_start_loc holds absolute row numbers)
  *   out, q            [total_rows][num_q_heads][head_dim], model dtype; out
- *                     also PKV_F32.  A cache with chunk sequences must be f16
- *                     or bf16 (8-bit: PKV_ERR_UNSUPPORTED); decode-only calls
- *                     take every cache pkv_paged_decode takes
+ *                     also PKV_F32.  A cache with chunk sequences must be f16,
+ *                     bf16 or 8-bit (fp32: PKV_ERR_UNSUPPORTED); decode-only
+ *                     calls take every cache pkv_paged_decode takes
  *   partition_size, workspace   as for pkv_paged_decode over the decode
  *                     sequences: pkv_decode_workspace_bytes(cache,
  *                     num_decode_seqs, num_q_heads, max_context_len,

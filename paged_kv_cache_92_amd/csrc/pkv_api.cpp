@@ -232,13 +232,13 @@ pkv_status prepare_prefill(const pkv::CacheDesc &c, void *out, int32_t out_dtype
                            const int32_t *context_lens, const int32_t *block_tables,
                            int32_t max_blocks_per_seq, int32_t num_seqs, int32_t max_query_len,
                            int32_t max_context_len, float scale, pkv::PrefillArgs *a) {
-  if (c.dtype != PKV_F16 && c.dtype != PKV_BF16)
-    return fail(PKV_ERR_UNSUPPORTED, "prefill supports f16 and bf16 caches");
+  if (c.mdtype != PKV_F16 && c.mdtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "prefill supports f16, bf16 and 8-bit caches of f16/bf16 models");
   if (!out || !q || !query_start_loc || !context_lens || !block_tables)
     return fail(PKV_ERR_INVALID, "a required pointer is NULL");
   if (!aligned16(out) || !aligned16(q)) return fail(PKV_ERR_INVALID, "q/out must be 16-byte aligned");
-  if (out_dtype != c.dtype && out_dtype != PKV_F32)
-    return fail(PKV_ERR_INVALID, "out_dtype must be the cache dtype or PKV_F32");
+  if (out_dtype != c.mdtype && out_dtype != PKV_F32)
+    return fail(PKV_ERR_INVALID, "out_dtype must be the model dtype or PKV_F32");
   if (num_q_heads <= 0 || num_q_heads % c.H != 0)
     return fail(PKV_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                 num_q_heads, c.H);
@@ -456,8 +456,8 @@ pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, int32_t out_dtyp
   pkv::CacheDesc c;
   pkv_status st = check_cache(cache, &c);
   if (st) return st;
-  if (c.dtype != PKV_F16 && c.dtype != PKV_BF16)
-    return fail(PKV_ERR_UNSUPPORTED, "prefill supports f16 and bf16 caches");
+  if (c.mdtype != PKV_F16 && c.mdtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "prefill supports f16, bf16 and 8-bit caches of f16/bf16 models");
   if (num_seqs < 0 || max_query_len < 0) return fail(PKV_ERR_INVALID, "negative size");
   if (num_seqs == 0 || max_query_len == 0) return ok();
   pkv::PrefillArgs a;

@@ -108,25 +108,58 @@ using Grp = std::integral_constant<int, R>;
 __device__ __forceinline__ float pair_max(float x) { return __builtin_fmaxf(x, __shfl_xor(x, 32)); }
 __device__ __forceinline__ float pair_sum(float x) { return x + __shfl_xor(x, 32); }
 
-template <typename E, int D, int BS>
+// E4M3 codes -> 16-bit values, exactly (every E4M3 value is an fp16 and a
+// bf16 value): the 16 codes of c become two 8-element operands.
+template <typename T>
+__device__ __forceinline__ void widen16(const u32x4 &c, u32x4 &lo, u32x4 &hi) {
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // One scaled conversion (scale 1) per code pair: bytes 0-1, then 2-3.
+    if constexpr (std::is_same<T, F16>::value) {
+      w[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[i], 1.f, false));
+      w[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[i], 1.f, true));
+    } else {
+      w[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.f, false));
+      w[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.f, true));
+    }
+  }
+  lo = u32x4{w[0], w[1], w[2], w[3]};
+  hi = u32x4{w[4], w[5], w[6], w[7]};
+}
+
+// E: the queries' and outputs' type (f16 or bf16).  KV: the cache's elements,
+// E itself or FP8 (E4M3 codes: keys widened to E and values to fp16 as tiles
+// are staged; the key scale is folded into scale_log2, the value scale
+// multiplies the normalised output).
+template <typename E, typename KV, int D, int BS>
 __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(
     void *__restrict__ out, int out_f32, const uint16_t *__restrict__ q,
-    const uint16_t *__restrict__ kpool, const uint16_t *__restrict__ vpool,
+    const void *__restrict__ kpool_, const void *__restrict__ vpool_,
     const int32_t *__restrict__ query_start_loc, const int32_t *__restrict__ context_lens,
     const int32_t *__restrict__ block_tables, int64_t num_blocks, int Hkv, int Hq, int mbps,
-    int staged, int nqt, float scale_log2) {
+    int staged, int nqt, float scale_log2, float v_scale) {
   // staged: block-table entries per sequence that fit the dynamic LDS
   // (enough for max_context_len); positions beyond them are never walked.
+  constexpr bool kFP8 = KV::kBytes == 1;
   constexpr int KS = D / 16;           // k-steps of the score product
   constexpr int DT = D / 32;           // 32-dimension tiles of the output
-  constexpr int KX = 32;               // elements per 64-byte key piece
-  constexpr int KROW = D + 8;          // LDS key row (elements)
-  constexpr int VROW = kKT + 8;        // LDS value row (elements)
+  constexpr int KX = 64 / KV::kBytes;  // elements per 64-byte key piece
+  constexpr int KROW = D + 8;          // LDS key row (16-bit elements)
+  constexpr int VROW = kKT + 8;        // LDS value row (16-bit elements)
   constexpr int KPR = kThreads / 256;  // key pieces per chunk round
-  constexpr int KPT = D / KX / KPR;    // 16-byte key chunks per thread
-  constexpr int VDR = kThreads / 8;    // value dimensions per chunk round
-  constexpr int VPT = D / VDR;         // 16-byte value chunks per thread
-  static_assert(KPT * KPR * KX == D && VPT * VDR == D, "whole rows per chunk round");
+  constexpr int NPC = D / KX;          // key pieces per row
+  // 16-byte key chunks per thread (an 8-bit row of 64 dimensions has one
+  // piece: half of the threads then load none).
+  constexpr int KPT = NPC >= KPR ? NPC / KPR : 1;
+  // Value chunks: 8 tokens (16-bit) or 16 tokens (8-bit) of one dimension.
+  constexpr int VTC = 16 / KV::kBytes;           // tokens per chunk
+  constexpr int VDR = kThreads / (kKT / VTC);    // value dimensions per chunk round
+  constexpr int VPT = D >= VDR ? D / VDR : 1;    // chunks per thread
+  static_assert((KPT * KPR * KX == D || (NPC < KPR && KX == D)) && (VPT * VDR == D || VDR == 2 * D),
+                "whole rows per chunk round");
+  const uint8_t *kpool = (const uint8_t *)kpool_;
+  const uint8_t *vpool = (const uint8_t *)vpool_;
 
   // Work item.  The hardware hands out block ids in order as workgroups
   // finish, so the longest items go first (greedy longest-processing-time
@@ -229,35 +262,52 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(
   // Global -> register staging of one tile.  Thread tid moves the 16-byte
   // column tid%4 of token (tid/4)%64's key row in pieces tid/256 + KPR*i (a
   // wave reads 16 tokens x 64 bytes contiguously per piece), and value
-  // chunks (dimension tid/8 + VDR*i, tokens 8*(tid%8)..+8).
+  // chunks (dimension tid/(64/VTC) + VDR*i, tokens VTC*(tid%(64/VTC))..+VTC).
   const int ktok = (tid >> 2) & (kKT - 1), ksub = tid & 3, kpc = tid >> 8;
-  const int vtok = 8 * (tid & 7), vdim = tid >> 3;
+  const int vtok = VTC * (tid % (kKT / VTC)), vdim = tid / (kKT / VTC);
+  const bool kload = NPC >= KPR || kpc < NPC;   // this thread has key chunks
+  const bool vload = D >= VDR || vdim < D;      // ... and value chunks
   auto load_tile = [&](int t, u32x4 (&kreg)[KPT], u32x4 (&vreg)[VPT]) {
     const int t0 = t * kKT;
     const bool full = t0 + kKT <= ctx;
-    {
+    if (kload) {
       const int pos = t0 + ktok;
       // Positions past the context read a harmless in-pool address; their
       // scores are masked.  An invalid block id (a broken caller contract)
       // reads block 0 instead of faulting.
       const int blk = (full || pos < ctx) ? max(sBT[pos / BS], 0) : 0;
-      const uint16_t *kb = kpool + ((size_t)blk * Hkv + hkv) * D * BS + (pos % BS) * KX + 8 * ksub;
+      const uint8_t *kb = kpool + (((size_t)blk * Hkv + hkv) * D * BS + (pos % BS) * KX) * KV::kBytes + 16 * ksub;
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) kreg[i] = load16(kb + (size_t)(kpc + KPR * i) * BS * KX);
+      for (int i = 0; i < KPT; ++i) kreg[i] = load16(kb + (size_t)(kpc + KPR * i) * BS * 64);
     }
-    {
+    if (vload) {
       const int pos = t0 + vtok;
       const int blk = (full || pos < ctx) ? max(sBT[pos / BS], 0) : 0;
-      const uint16_t *vblk = vpool + ((size_t)blk * Hkv + hkv) * D * BS + pos % BS;
+      const uint8_t *vblk = vpool + (((size_t)blk * Hkv + hkv) * D * BS + pos % BS) * KV::kBytes;
+      // 8-bit values in 8-token blocks: the chunk's second half is the next block's.
+      const uint8_t *vblk2 = vblk;
+      if constexpr (VTC > BS) {
+        const int blk2 = (full || pos + BS < ctx) ? max(sBT[(pos + BS) / BS], 0) : 0;
+        vblk2 = vpool + ((size_t)blk2 * Hkv + hkv) * D * BS;
+      }
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
-        u32x4 x = load16(vblk + (size_t)(vdim + VDR * i) * BS);
-        if (!full && pos + 8 > ctx) {
+        const size_t row = (size_t)(vdim + VDR * i) * BS * KV::kBytes;
+        u32x4 x;
+        if constexpr (VTC > BS) {
+          const u32x2 a = load8(vblk + row), b = load8(vblk2 + row);
+          x = u32x4{a[0], a[1], b[0], b[1]};
+        } else {
+          x = load16(vblk + row);
+        }
+        if (!full && pos + VTC > ctx) {
           // Slots past the context may hold anything (NaN included): zero them.
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            const uint32_t keep = (pos + 2 * k < ctx ? 0x0000ffffu : 0u) |
-                                  (pos + 2 * k + 1 < ctx ? 0xffff0000u : 0u);
+            uint32_t keep = 0;
+#pragma unroll
+            for (int e = 0; e < 4 / KV::kBytes; ++e)
+              if (pos + (4 / KV::kBytes) * k + e < ctx) keep |= (KV::kBytes == 1 ? 0xffu : 0xffffu) << (8 * KV::kBytes * e);
             x[k] &= keep;
           }
         }
@@ -267,20 +317,41 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(
   };
   // Registers -> LDS buffer buf.  CONV: bf16 values re-encoded to fp16 (exact
   // below 65536 in magnitude; larger ones become infinities, which the walk's
-  // result check catches).
+  // result check catches).  8-bit codes: keys widened to E, values to fp16.
   auto store_tile = [&](auto conv, int buf, const u32x4 (&kreg)[KPT], const u32x4 (&vreg)[VPT]) {
     constexpr bool CONV = decltype(conv)::value;
-    uint16_t *kd = &sK[buf][kslot(ktok) * KROW + 8 * ksub];
+    uint16_t *kd = &sK[buf][kslot(ktok) * KROW + (16 / KV::kBytes) * ksub];
+    if (kload) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) *(u32x4 *)(kd + KX * (kpc + KPR * i)) = kreg[i];
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      u32x4 x = vreg[i];
-      if constexpr (CONV) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) x[k] = pack_f16x2(as_f32(x[k] << 16), as_f32(x[k] & 0xffff0000u));
+      for (int i = 0; i < KPT; ++i) {
+        if constexpr (kFP8) {
+          u32x4 lo, hi;
+          widen16<E>(kreg[i], lo, hi);
+          *(u32x4 *)(kd + KX * (kpc + KPR * i)) = lo;
+          *(u32x4 *)(kd + KX * (kpc + KPR * i) + 8) = hi;
+        } else {
+          *(u32x4 *)(kd + KX * (kpc + KPR * i)) = kreg[i];
+        }
       }
-      *(u32x4 *)&sV[buf][(vdim + VDR * i) * VROW + vtok] = x;
+    }
+    if (vload) {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        uint16_t *vd = &sV[buf][(vdim + VDR * i) * VROW + vtok];
+        if constexpr (kFP8) {
+          u32x4 lo, hi;
+          widen16<F16>(vreg[i], lo, hi);
+          *(u32x4 *)vd = lo;
+          *(u32x4 *)(vd + 8) = hi;
+        } else {
+          u32x4 x = vreg[i];
+          if constexpr (CONV) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) x[k] = pack_f16x2(as_f32(x[k] << 16), as_f32(x[k] & 0xffff0000u));
+          }
+          *(u32x4 *)vd = x;
+        }
+      }
     }
   };
 
@@ -300,7 +371,10 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(
   auto attend = [&](auto conv, auto fixed) {
     constexpr bool CONV = decltype(conv)::value;
     constexpr bool FIXED = decltype(fixed)::value;
-    using PV = typename std::conditional<CONV || std::is_same<E, F16>::value, Mfma32<F16>, Mfma32<E>>::type;
+    // Values in LDS are fp16 for an f16 cache, for bf16 on the fast route and
+    // for 8-bit codes; bf16 on bf16's exact route.
+    using PV = typename std::conditional<CONV || kFP8 || std::is_same<E, F16>::value, Mfma32<F16>,
+                                         Mfma32<E>>::type;
     constexpr bool kSplit = PV::kSplitP;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -511,7 +585,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(
     const float ltot = pair_sum(l[g]);
     const int row = wrow0 + 32 * g + j32;
     if (row < qlen) {
-      const float inv = 1.f / ltot;
+      const float inv = (kFP8 ? v_scale : 1.f) / ltot;
       const size_t orow = ((size_t)(qs + row) * Hq + hq) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -537,12 +611,12 @@ int staged_entries(const PrefillArgs &a, int B) {
   return std::min(a.max_blocks_per_seq, (a.max_context_len + B - 1) / B);
 }
 
-template <typename E, int D, int BS>
+template <typename E, typename KV, int D, int BS>
 size_t lds_bytes_t(const PrefillArgs &a) {
   // The kernel's static LDS is a property of its code: asked once.
   static const size_t static_bytes = [] {
     hipFuncAttributes fa{};
-    return hipFuncGetAttributes(&fa, (const void *)prefill_kernel<E, D, BS>) == hipSuccess
+    return hipFuncGetAttributes(&fa, (const void *)prefill_kernel<E, KV, D, BS>) == hipSuccess
                ? fa.sharedSizeBytes
                : SIZE_MAX;
   }();
@@ -550,48 +624,58 @@ size_t lds_bytes_t(const PrefillArgs &a) {
   return static_bytes + sizeof(int) * (size_t)staged_entries(a, BS);
 }
 
-template <typename E>
+template <typename E, typename KV>
 size_t lds_bytes_e(const CacheDesc &c, const PrefillArgs &a) {
-  if (c.D == 64 && c.B == 8) return lds_bytes_t<E, 64, 8>(a);
-  if (c.D == 128 && c.B == 8) return lds_bytes_t<E, 128, 8>(a);
-  if (c.D == 64 && c.B == 16) return lds_bytes_t<E, 64, 16>(a);
-  if (c.D == 64 && c.B == 32) return lds_bytes_t<E, 64, 32>(a);
-  if (c.D == 128 && c.B == 16) return lds_bytes_t<E, 128, 16>(a);
-  return lds_bytes_t<E, 128, 32>(a);
+  if (c.D == 64 && c.B == 8) return lds_bytes_t<E, KV, 64, 8>(a);
+  if (c.D == 128 && c.B == 8) return lds_bytes_t<E, KV, 128, 8>(a);
+  if (c.D == 64 && c.B == 16) return lds_bytes_t<E, KV, 64, 16>(a);
+  if (c.D == 64 && c.B == 32) return lds_bytes_t<E, KV, 64, 32>(a);
+  if (c.D == 128 && c.B == 16) return lds_bytes_t<E, KV, 128, 16>(a);
+  return lds_bytes_t<E, KV, 128, 32>(a);
 }
 
-template <typename E, int D, int BS>
+template <typename E, typename KV, int D, int BS>
 void launch_t(const CacheDesc &c, const PrefillArgs &a, hipStream_t stream) {
   const int nqt = (a.max_query_len + kQT - 1) / kQT;
   const int64_t nwork = (int64_t)a.S * a.Hq * nqt;
   const int staged = staged_entries(a, BS);
   const size_t lds = sizeof(int) * (size_t)staged;   // staged block table
-  hipLaunchKernelGGL((prefill_kernel<E, D, BS>), dim3((unsigned)nwork), dim3(kThreads), lds, stream,
-                     a.out, (int)a.out_f32, (const uint16_t *)a.q, (const uint16_t *)c.k,
-                     (const uint16_t *)c.v, a.query_start_loc, a.context_lens, a.block_tables,
-                     c.num_blocks, c.H, a.Hq, a.max_blocks_per_seq, staged, nqt, a.scale * kLog2e);
+  // k_scale and v_scale are 1 unless the cache is 8-bit.
+  hipLaunchKernelGGL((prefill_kernel<E, KV, D, BS>), dim3((unsigned)nwork), dim3(kThreads), lds, stream,
+                     a.out, (int)a.out_f32, (const uint16_t *)a.q, (const void *)c.k, (const void *)c.v,
+                     a.query_start_loc, a.context_lens, a.block_tables, c.num_blocks, c.H, a.Hq,
+                     a.max_blocks_per_seq, staged, nqt, a.scale * kLog2e * c.k_scale, c.v_scale);
 }
 
-template <typename E>
+template <typename E, typename KV>
 void launch_e(const CacheDesc &c, const PrefillArgs &a, hipStream_t stream) {
-  if (c.D == 64 && c.B == 8) launch_t<E, 64, 8>(c, a, stream);
-  else if (c.D == 128 && c.B == 8) launch_t<E, 128, 8>(c, a, stream);
-  else if (c.D == 64 && c.B == 16) launch_t<E, 64, 16>(c, a, stream);
-  else if (c.D == 64 && c.B == 32) launch_t<E, 64, 32>(c, a, stream);
-  else if (c.D == 128 && c.B == 16) launch_t<E, 128, 16>(c, a, stream);
-  else launch_t<E, 128, 32>(c, a, stream);
+  if (c.D == 64 && c.B == 8) launch_t<E, KV, 64, 8>(c, a, stream);
+  else if (c.D == 128 && c.B == 8) launch_t<E, KV, 128, 8>(c, a, stream);
+  else if (c.D == 64 && c.B == 16) launch_t<E, KV, 64, 16>(c, a, stream);
+  else if (c.D == 64 && c.B == 32) launch_t<E, KV, 64, 32>(c, a, stream);
+  else if (c.D == 128 && c.B == 16) launch_t<E, KV, 128, 16>(c, a, stream);
+  else launch_t<E, KV, 128, 32>(c, a, stream);
 }
 
 }  // namespace
 
+// The queries' and outputs' type is the cache's, or for an 8-bit cache the
+// model dtype (f16 or bf16).
 size_t prefill_lds_bytes(const CacheDesc &c, const PrefillArgs &a) {
-  return c.dtype == 1 ? lds_bytes_e<F16>(c, a) : lds_bytes_e<BF16>(c, a);
+  if (c.fp8()) return c.mdtype == 1 ? lds_bytes_e<F16, FP8>(c, a) : lds_bytes_e<BF16, FP8>(c, a);
+  return c.dtype == 1 ? lds_bytes_e<F16, F16>(c, a) : lds_bytes_e<BF16, BF16>(c, a);
 }
 
 hipError_t launch_prefill(const CacheDesc &c, const PrefillArgs &a, hipStream_t stream) {
   if (a.max_query_len == 0 || a.S == 0) return hipSuccess;
-  if (c.dtype == 1) launch_e<F16>(c, a, stream);
-  else launch_e<BF16>(c, a, stream);
+  if (c.fp8()) {
+    if (c.mdtype == 1) launch_e<F16, FP8>(c, a, stream);
+    else launch_e<BF16, FP8>(c, a, stream);
+  } else if (c.dtype == 1) {
+    launch_e<F16, F16>(c, a, stream);
+  } else {
+    launch_e<BF16, BF16>(c, a, stream);
+  }
   return hipGetLastError();
 }
 

@@ -106,14 +106,16 @@ def test_window_and_mixed_argument_checks():
     assert "sliding_window" in lib.pkv_last_error().decode()
     assert win(16, out=None) == 1                     # null pointer
     assert win(16, out=None, S=0) == 0                # zero sequences: no-op
-    mixed = lambda S, nd, maxq=16, qsl=FAKE, dd=d: lib.pkv_paged_mixed(  # noqa: E731
-        ctypes.byref(dd), FAKE, 1, FAKE, 2, qsl, FAKE, FAKE, 4, S, nd, maxq, 64, 0.125, 0, None, 0,
+    mixed = lambda S, nd, maxq=16, qsl=FAKE, dd=d, od=1: lib.pkv_paged_mixed(  # noqa: E731
+        ctypes.byref(dd), FAKE, od, FAKE, 2, qsl, FAKE, FAKE, 4, S, nd, maxq, 64, 0.125, 0, None, 0,
         None)
     assert mixed(2, 3) == 1                           # more decode sequences than sequences
     assert mixed(-1, 0) == 1
     assert mixed(3, 1, qsl=None) == 1                 # chunk sequences need query_start_loc
     assert mixed(3, 1, maxq=65) == 1                  # chunk longer than max_context_len
-    assert mixed(2, 1, dd=_desc(dtype=3, model_dtype=1)) == 2   # chunks over an 8-bit cache
+    # Over an 8-bit cache the output is in the model dtype (or fp32), not in codes.
+    assert mixed(2, 1, dd=_desc(dtype=3, model_dtype=1), od=3) == 1
+    assert "model dtype" in lib.pkv_last_error().decode()
     assert mixed(0, 0) == 0                           # nothing to do
 
 

@@ -128,13 +128,29 @@ def test_mixed_fp8_cache():
                       Hkv=2, d=128, B=16, dtype=W.F16, max_context_len=256)
     wl.kv_dtype, wl.k_scale, wl.v_scale = W.FP8, float(np.float32(0.02)), float(np.float32(0.03))
     _full_check(wl)
-    wl = W.make_mixed("fp8_with_chunks", 8, lambda rng: [30], lambda rng: [10], [5], Hq=4, Hkv=2,
-                      d=128, B=16, dtype=W.F16, max_context_len=256)
-    wl.kv_dtype, wl.k_scale, wl.v_scale = W.FP8, float(np.float32(0.02)), float(np.float32(0.03))
+    for dtype in (W.F16, W.BF16):
+        for d, B, G in ((128, 16, 1), (128, 32, 4), (64, 8, 2)):
+            wl = _mixed(dtype, d, B, G, partition_size=64)
+            wl.kv_dtype, wl.k_scale, wl.v_scale = W.FP8, float(np.float32(0.02)), float(np.float32(0.03))
+            _full_check(wl)
+
+
+def test_mixed_step_fp8_cache_full():
+    # The 13B-shaped step over an 8-bit cache: every row against the oracle.
+    wl = W.mixed_step_f16()
+    wl.kv_dtype, wl.k_scale, wl.v_scale = W.FP8, 0.0135, 0.0135
+    k_ref, v_ref = fill_pools(wl)
     dw = DeviceWorkload(wl)
     cache = new_cache(wl)
-    with pytest.raises(pkv.PkvError, match="UNSUPPORTED"):
-        dw.attend(cache)
+    dw.run(cache)
+    o32 = dw.attend(cache, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _pools_equal(cache, k_ref, v_ref, wl.cache_dtype)
+    got = values_of(o32)
+    assert np.isfinite(got).all()
+    rows = list(range(int(wl.query_start_loc[-1])))
+    worst = assert_close(got[rows], sampled_rows(wl, k_ref, v_ref, rows), wl.dtype, wl.name)
+    print(f"fp8-cache mixed step worst err/bound {worst:.3f}")
 
 
 def test_mixed_step_full():

@@ -573,11 +573,64 @@ def test_fp8_cache_llama13b_full():
     print(f"13B fp8-cache decode: worst err/bound {worst:.3f}")
 
 
-def test_fp8_cache_prefill_is_unsupported():
-    wl = W.make_decode("fp8pf", 3, lambda rng: [20], Hq=2, Hkv=2, d=64, B=16, dtype=W.BF16,
-                       max_context_len=32, kv_dtype=W.FP8, k_scale=0.1, v_scale=0.1)
-    dw = DeviceWorkload(wl)
-    cache = new_cache(wl)
-    qsl = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
-    with pytest.raises(pkv.PkvError, match="UNSUPPORTED"):
-        pkv.paged_prefill(cache, dw.q, qsl, dw.context_lens, dw.block_tables, 1, 32)
+FP8_SCALES = dict(k_scale=float(np.float32(0.0123)), v_scale=float(np.float32(0.0317)))
+
+
+def _as_fp8(wl, k_scale, v_scale):
+    wl.kv_dtype, wl.k_scale, wl.v_scale = W.FP8, k_scale, v_scale
+    return wl
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16], ids=["f16", "bf16"])
+@pytest.mark.parametrize("d,B,G", [(128, 16, 1), (128, 32, 4), (64, 16, 2), (64, 32, 1), (128, 8, 2),
+                                    (64, 8, 1)])
+def test_fp8_cache_prefill_variants(dtype, d, B, G):
+    # Ragged chunks (1 row up to more than one 256-row tile) over an 8-bit
+    # cache: codes bit-exact, attention over the dequantised cache.
+    hist = np.array([0, 5, 16, 33, 200, 7])
+    chunks = [1, 37, 128, 130, 64, 300]
+    _full_check(_as_fp8(_ragged_prefill(dtype, d, B, G, hist, chunks), **FP8_SCALES))
+
+
+def test_fp8_cache_prefill_shared_prefix_with_copy_on_write():
+    wl = W.chunked_prefill_bf16(S=4, chunk=96, shared_prefix=20, Hq=4, Hkv=4, max_context_len=512,
+                                hist_fn=lambda rng: np.array([30, 41, 200, 150]))
+    assert wl.info["cow_copies"] == 2
+    _full_check(_as_fp8(wl, **FP8_SCALES))
+
+
+def test_fp8_cache_prefill_reads_every_code_exactly():
+    # One row attends to a key whose score dominates by far; its value row
+    # holds every finite E4M3 code but negative zero (v_scale 1): the fp32
+    # output must be exactly those values, which pins the kernel's code ->
+    # fp16 conversion of values and its byte order in the tile.
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF, 0x80)] + [0x38] * 3, np.uint8)
+    vals = np.array([oracle.fp8_to_double(int(c)) for c in codes], np.float32).reshape(2, 128)
+    for dtype in (W.F16, W.BF16):
+        hist = np.array([40, 3])
+        chunks = [1, 1]
+        wl = _ragged_prefill(dtype, 128, 16, 1, hist, chunks)
+        wl.kv_dtype, wl.k_scale, wl.v_scale = W.FP8, 1.0, 1.0
+        for arr in (wl.setup[0].key, wl.setup[0].value, wl.step_scatter.key, wl.step_scatter.value):
+            arr[:] = 0
+        # Sequence 0: its query (all ones) meets key position 17 (all 448): that
+        # value row wins by a margin no other weight survives in fp32.
+        wl.q[:] = W.round_to(np.ones_like(wl.q, dtype=np.float32), dtype)
+        wl.setup[0].key[17] = W.round_to(np.full((2, 128), 448.0, np.float32), dtype)
+        wl.setup[0].value[17] = W.round_to(vals, dtype)
+        wl.seq_tokens_key[0][17] = wl.setup[0].key[17]
+        wl.seq_tokens_value[0][17] = wl.setup[0].value[17]
+        dw = DeviceWorkload(wl)
+        cache = new_cache(wl)
+        dw.run(cache)
+        o32 = bits_of(dw.attend(cache, out_dtype=torch.float32))
+        assert np.array_equal(o32[0].view(np.uint32), vals.view(np.uint32)), dtype
+
+
+def test_fp8_cache_prefill_full():
+    # The chunked-prefill workload as benchmarked, its cache stored as E4M3
+    # codes: whole pools bit for bit, every row against the oracle.
+    wl = _as_fp8(W.chunked_prefill_bf16(), 0.0135, 0.0135)
+    rows = list(range(int(wl.query_start_loc[-1])))
+    worst, *_ = _sampled_check(wl, rows)
+    print(f"fp8-cache prefill worst err/bound {worst:.3f}")
