@@ -312,9 +312,12 @@ pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, int32_t out_dtyp
  * one row at position context_lens[s] - 1), computed by two kernels that run
  * at once: the decode kernel of pkv_paged_decode over the decode sequences
  * and the prefill kernel over the chunk sequences.  The decode part is
- * enqueued on a stream the library owns (one per device, default priority,
- * forked from and joined back into `stream` with events), so work enqueued on
- * `stream` after this call sees both parts finished.
+ * enqueued on a stream the library owns, forked from and joined back into
+ * `stream` with two events, so work enqueued on `stream` after this call sees
+ * both parts finished.  The library keeps that stream and its events (default
+ * priority) for each (device, caller stream) pair it has served, until the
+ * process ends: the one call of this interface that holds handles, so that
+ * the two parts can run at once on one caller stream.
  *
  *   sequences 0 .. num_decode_seqs-1   decode: one query row each, row s
  *                     (query_start_loc[s] == s for s <= num_decode_seqs; the
@@ -331,8 +334,8 @@ pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, int32_t out_dtyp
  *                     partition_size) bytes
  *   max_query_len     host bound on the chunk lengths; max_context_len a host
  *                     bound on every context length
- * Host-side locking serialises concurrent calls on one device while they
- * enqueue; the side stream may be captured into a graph with `stream`.
+ * Host-side locking serialises concurrent calls on one caller stream while
+ * they enqueue; a graph capture on `stream` takes in its side stream only.
  */
 pkv_status pkv_paged_mixed(const pkv_cache *cache, void *out, int32_t out_dtype, const void *q,
                            int32_t num_q_heads, const int32_t *query_start_loc,

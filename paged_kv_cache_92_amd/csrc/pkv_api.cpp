@@ -272,24 +272,29 @@ pkv_status prepare_prefill(const pkv::CacheDesc &c, void *out, int32_t out_dtype
   return PKV_OK;
 }
 
-// A second stream per device, with the events that fork work onto it from a
-// caller's stream and join it back.  Created on first use with the device
-// current; default priority.  `mu` serialises the record/wait sequence of
-// concurrent callers on one device.
+// A second stream, with the events that fork work onto it from a caller's
+// stream and join it back.  Created on first use with the device current;
+// default priority.  `mu` serialises the record/wait sequence of concurrent
+// callers on one caller stream.
 struct SideStream {
   hipStream_t stream = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
   std::mutex mu;
 };
 
-pkv_status side_stream(SideStream **out) {
+// The side stream of (current device, caller stream): every caller stream gets
+// its own, so mixed steps from different streams never queue behind each
+// other, and a graph capture on one caller's stream forks only into that
+// caller's side stream.  Created on first use, kept until the process ends.
+pkv_status side_stream(hipStream_t caller, SideStream **out) {
   static std::mutex mu;
-  static std::map<int, SideStream *> streams;  // lives until the process ends
+  static std::map<std::pair<int, hipStream_t>, SideStream *> streams;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_status(e, "hipGetDevice");
   std::lock_guard<std::mutex> lock(mu);
-  auto it = streams.find(dev);
+  const auto key = std::make_pair(dev, caller);
+  auto it = streams.find(key);
   if (it != streams.end()) {
     *out = it->second;
     return PKV_OK;
@@ -305,7 +310,7 @@ pkv_status side_stream(SideStream **out) {
     delete ss;
     return hip_status(e, "side stream setup");
   }
-  streams[dev] = ss;
+  streams[key] = ss;
   *out = ss;
   return PKV_OK;
 }
@@ -513,7 +518,7 @@ pkv_status pkv_paged_mixed(const pkv_cache *cache, void *out, int32_t out_dtype,
   // rows on the side stream, so the matrix-core prefill and the HBM-bound
   // decode share the chip; the caller's stream then waits for both.
   SideStream *ss = nullptr;
-  st = side_stream(&ss);
+  st = side_stream(stream, &ss);
   if (st) return st;
   std::lock_guard<std::mutex> lock(ss->mu);
   hipError_t e = hipEventRecord(ss->fork, stream);

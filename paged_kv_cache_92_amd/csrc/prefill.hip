@@ -1,4 +1,4 @@
-// Causal chunked prefill over the paged cache on the matrix cores (f16/bf16).
+// Causal chunked prefill over the paged cache on the matrix cores.
 //
 // A chunk of a long prompt is processed as one step ("Sparse Computation and
 // Memory Management for Efficient LLM Inference", pyy0715.github.io, section
@@ -6,29 +6,33 @@
 // attention is a matrix-matrix product ("vLLM: LLM 서빙 메모리 최적화의 교과서",
 // velog.io, section 01, prompt phase), causal over j <= i.
 //
-// Workgroup = 4 waves (one per SIMD) = one (sequence, query head, 256-row
-// query tile); wave w owns 64 rows as two 32-row groups r = 0, 1.  The
-// key/value positions 0..last row's position are walked in 64-token tiles
-// gathered through the block table into LDS (three tile buffers: tile t+2 is
-// stored while tiles t and t+1 are read, one barrier per tile).  Per group:
+// Workgroup = 8 waves (two per SIMD) = one (sequence, query head, 256-row
+// query tile); wave w owns 32 query rows.  The key/value positions
+// 0..last row's position are walked in 64-token tiles gathered through the
+// block table (staged in LDS once per workgroup) into LDS: three tile
+// buffers, tile t+2 stored while tiles t and t+1 are read, one barrier per
+// tile.  Each wave computes 32-token sub-tiles:
 //
-//   S^T (32 tokens x 32 rows) = K (32 x D) . Q^T (D x 32)     per 32-token half
+//   S^T (32 tokens x 32 rows) = K (32 x D) . Q^T (D x 32)
 //   O^T (D x 32 rows)        += V^T (D x 32) . P^T (32 x 32)
 //
 // with 32x32x16 MFMAs.  The key rows are fed to the first product in a
 // permuted order chosen so that each lane's 16 result rows are, per 16-token
 // k-step of the second product, 8 consecutive tokens: the B operand P^T is
 // built from the lane's own registers and the A operand V^T is one 16-byte
-// LDS read from the dimension-major value tile.  Online softmax per row in
-// the log2 domain.
+// LDS read from the dimension-major value tile.  Scores live in the log2
+// domain.  Tiles wholly below a wave's first row take an unmasked loop; only
+// the tiles that reach the diagonal are masked.
 //
-// Each wave computes 32-token sub-tiles, software-pipelined across its two
-// row groups so the softmax of one group (vector ALU) runs while the matrix
-// cores work on the other:
-//   A: S1 = QK(u, group 1)         || P0 = exp(S0)
-//   B: O0 += PV(u, P0)             || P1 = exp(S1)
-//   C: S0 = QK(u+1, group 0), O1 += PV(u, P1)
-// and after each 64-token tile, the tile two ahead is staged.
+// Two routes.  The fast one keeps a fixed reference maximum per row (the
+// maximum over its first 32 keys) for the whole walk, so accumulators are
+// never rescaled, and runs P.V on the fp16 matrix cores (bf16 values are
+// re-encoded to fp16 as tiles are staged).  If any row's accumulators or
+// denominator come out non-finite (a weight beyond fp16 range, or a bf16
+// value beyond it), the workgroup redoes the walk on the exact route: lazy
+// rescaling of a running maximum, and bf16 products for bf16.  Workgroups
+// are dispatched longest first (the (sequence, query tile) classes ranked by
+// their tile counts on the device).
 #include <stdint.h>
 
 #include <algorithm>

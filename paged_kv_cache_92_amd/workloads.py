@@ -499,7 +499,7 @@ def lognormal_lengths(S, median=1024, sigma=1.0, lo=16, hi=8192):
     return draw
 
 
-def gqa_decode_bf16(B=16, S=256, seed=4, max_context_len=8192, lengths=None, partition_size=1024):
+def gqa_decode_bf16(B=16, S=256, seed=4, max_context_len=8192, lengths=None, partition_size=2048):
     """GQA decode: 32 query heads over 8 KV heads, d 128, bf16, lognormal(median 1024) lengths."""
     fn = lengths or lognormal_lengths(S, hi=max_context_len)
     return make_decode(f"gqa_decode_bf16_B{B}_S{S}", seed, fn, Hq=32, Hkv=8, d=128, B=B,

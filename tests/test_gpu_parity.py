@@ -426,7 +426,8 @@ def test_long_context_split_full():
     print(f"split decode worst err/bound {worst:.3f}")
 
 
-@pytest.mark.parametrize("B,part", [(16, 1024), (16, -1), (32, 1024), (32, -1), (8, 1024), (8, -1)])
+@pytest.mark.parametrize("B,part", [(16, 2048), (16, 1024), (16, -1), (32, 2048), (32, -1), (8, 2048),
+                                    (8, -1)])
 def test_gqa_decode_full(B, part):
     wl = W.gqa_decode_bf16(B=B)
     worst, *_ = _sampled_check(wl, _all_rows(wl), partition_size=part)
@@ -565,6 +566,15 @@ def test_fp8_cache_reads_every_code_exactly(dtype, G, B):
     want = np.repeat(vals.reshape(2, 128), G, axis=0)      # query head hq reads KV head hq // G
     for s in range(len(lens)):
         assert np.array_equal(o32[s].view(np.uint32), want.view(np.uint32)), s
+
+
+@pytest.mark.parametrize("B", [16, 32])
+def test_fp8_cache_gqa_full(B):
+    # The GQA workload as benchmarked over an 8-bit cache (2,048-token
+    # partitions): every sequence's output against the oracle.
+    wl = _as_fp8(W.gqa_decode_bf16(B=B), 0.0135, 0.0135)
+    worst, *_ = _sampled_check(wl, _all_rows(wl))
+    print(f"GQA B={B} fp8-cache decode worst err/bound {worst:.3f}")
 
 
 def test_fp8_cache_llama13b_full():

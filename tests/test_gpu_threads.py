@@ -1,8 +1,8 @@
 """Calls from several host threads at once, each on its own stream.
 
 The library keeps per-device state behind locks (occupancy figures, LDS size,
-the mixed call's side stream and its two events); the kernels share nothing
-but read-only inputs.  Every thread's result must equal, bit for bit, the
+the mixed call's side stream and two events per caller stream); the kernels
+share nothing but read-only inputs.  Every thread's result must equal, bit for bit, the
 same call made alone.
 """
 import threading
