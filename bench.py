@@ -314,10 +314,10 @@ def run_config(torch, pkv, name, args, cpu_budget, read_probe, fused=False, kv_c
                block_size=16, placement="shuffled", partition=None):
     """One workload: generate, upload two pool copies, time the step, report its roofline.
 
-    The step (the new tokens' scatter, then the attention call) is timed twice over the same
-    inputs: first K steps with nothing between them (ms_per_step, value), then K steps with a
-    pair of timing events around each attention call (the roofline's per-launch duration; each
-    event pair costs the stream a few microseconds, so it stays out of the first loop)."""
+    Two timed loops over the same inputs, each bracketed by one pair of events (an event
+    pair around every call would cost the stream a few microseconds per call): K whole steps
+    (the new tokens' scatter, then the attention call) back to back give ms_per_step and
+    value; K attention calls back to back give the roofline's per-launch duration."""
     import numpy as np
 
     from paged_kv_cache_92_amd.runner import DeviceWorkload, new_cache
@@ -353,18 +353,30 @@ def run_config(torch, pkv, name, args, cpu_budget, read_probe, fused=False, kv_c
         if need:
             ws = torch.empty(need, dtype=torch.uint8, device="cuda")
 
-    def step(i, ev=None):
+    def attend(i):
         dw, cache = copies[i % 2]
-        if not fused:
-            dw.apply(cache, dw.step)
-        if ev is not None:
-            ev[0].record()
         if fused:
             dw.append_attend(cache, out=out, workspace=ws)
         else:
             dw.attend(cache, out=out, workspace=ws)
-        if ev is not None:
-            ev[1].record()
+
+    def step(i):
+        if not fused:
+            dw, cache = copies[i % 2]
+            dw.apply(cache, dw.step)
+        attend(i)
+
+    def timed(fn, n):
+        """Average ms of n calls fn(0) .. fn(n-1), back to back, after a synchronisation."""
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(n):
+            fn(i)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / n
 
     for i in range(args.warmup):
         step(i)
@@ -372,43 +384,23 @@ def run_config(torch, pkv, name, args, cpu_budget, read_probe, fused=False, kv_c
     log(f"[bench] warmup {args.warmup} steps done")
 
     # Throughput: K whole steps back to back.
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(args.steps):
-        step(i)
-    end.record()
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / args.steps
-    # Per-launch duration of the attention call: K more steps, events around each call.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    attn_ms = [a.elapsed_time(b) for a, b in evs]
-    attn_avg = float(np.mean(attn_ms))
+    ms_step = timed(step, args.steps)
+    # Per-launch duration of the attention call: K calls back to back (for the
+    # appending call the step is that call).
+    attn_avg = timed(attend, args.steps)
     log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step; attention call "
-        f"{attn_avg * 1e3:.1f} us avg (median {np.median(attn_ms) * 1e3:.1f}, "
-        f"min {np.min(attn_ms) * 1e3:.1f})")
+        f"{attn_avg * 1e3:.1f} us avg")
 
     ways = {}
     if wl.mode == "mixed":
         # The same step served other ways, attention only, same alternation.
         for how in ("sequential", "unified", "decode", "prefill"):
-            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                     for _ in range(args.steps)]
-            for i in range(args.warmup + args.steps):
+            def split_call(i, how=how):
                 dw, cache = copies[i % 2]
-                j = i - args.warmup
-                if j >= 0:
-                    pairs[j][0].record()
                 dw.attend_split(cache, how, out, workspace=ws)
-                if j >= 0:
-                    pairs[j][1].record()
-            torch.cuda.synchronize()
-            ways[how] = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+            for i in range(args.warmup):
+                split_call(i)
+            ways[how] = timed(split_call, args.steps)
             log(f"[bench] {how}: {ways[how] * 1e3:.1f} us avg")
 
     dt = {0: "f32", 1: "f16", 2: "bf16", 3: "fp8_e4m3"}[wl.cache_dtype]
@@ -433,8 +425,7 @@ def run_config(torch, pkv, name, args, cpu_budget, read_probe, fused=False, kv_c
                          "kernel": "paged decode (partial + reduce when split)" if not fused
                          else "appending paged decode (partial + reduce when split)",
                          "algorithmic_bytes_per_launch": kv,
-                         "avg_launch_us": round(attn_avg * 1e3, 2),
-                         "median_launch_us": round(float(np.median(attn_ms)) * 1e3, 2)},
+                         "avg_launch_us": round(attn_avg * 1e3, 2)},
         })
         if read_probe:
             probe = read_probe_gbps(torch)
