@@ -78,12 +78,20 @@ def test_sliding_window_odd_groups(G, part, kv):
 
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16], ids=["f16", "bf16"])
 @pytest.mark.parametrize("d,B,G", [(128, 16, 7), (64, 8, 3), (128, 32, 6), (128, 16, 16)])
-def test_prefill_odd_groups(dtype, d, B, G):
+@pytest.mark.parametrize("kv", ["model", "fp8"])
+def test_prefill_odd_groups(dtype, d, B, G, kv):
     hist = np.array([0, 5, 16, 33, 200, 7])
     chunks = [1, 37, 128, 130, 64, 256]
-    _full_check(_ragged_prefill(dtype, d, B, G, hist, chunks))
+    wl = _ragged_prefill(dtype, d, B, G, hist, chunks)
+    if kv == "fp8":
+        _fp8(wl)
+    _full_check(wl)
 
 
 @pytest.mark.parametrize("G,part", [(7, -1), (5, 64), (16, -1)])
-def test_mixed_step_odd_groups(G, part):
-    _full_check(_mixed(W.BF16, 128, 16, G, partition_size=part, seed=371))
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_mixed_step_odd_groups(G, part, kv):
+    wl = _mixed(W.BF16, 128, 16, G, partition_size=part, seed=371)
+    if kv == "fp8":
+        _fp8(wl)
+    _full_check(wl)
