@@ -1,7 +1,8 @@
-// HBM read-ceiling probe: how fast the memory system delivers 4 KiB tiles in
-// random order to waves that read them with non-temporal 16-byte loads, the
-// access pattern of the paged decode kernels (one 4 KiB key or value tile per
-// (block, head) at 16-token blocks of head_dim 128, fp16).  Measurement
+// HBM read-ceiling probe: how fast the memory system delivers tiles of 1, 2, 4
+// or 8 KiB in random order to waves that read them with non-temporal 16-byte
+// loads, the access pattern of the paged decode kernels (one key or value tile
+// per (block, head): 4 KiB at 16-token blocks of head_dim 128 in fp16, 2 KiB
+// for 8-bit codes).  Measurement
 // infrastructure only: the attention library does not use it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -38,7 +39,13 @@ extern "C" int pkv_probe_read_tiles(const void *buf, const int32_t *idx, int til
                                     int tiles_per_wave, uint32_t *sink, hipStream_t stream) {
   if (waves <= 0 || waves % 4 != 0 || tiles_per_wave <= 0) return 1;
   const dim3 grid((unsigned)(waves / 4)), block(256);
-  if (tile_bytes == 4096)
+  if (tile_bytes == 1024)
+    hipLaunchKernelGGL(read_tiles<1024>, grid, block, 0, stream, (const uint8_t *)buf, idx,
+                       tiles_per_wave, sink);
+  else if (tile_bytes == 2048)
+    hipLaunchKernelGGL(read_tiles<2048>, grid, block, 0, stream, (const uint8_t *)buf, idx,
+                       tiles_per_wave, sink);
+  else if (tile_bytes == 4096)
     hipLaunchKernelGGL(read_tiles<4096>, grid, block, 0, stream, (const uint8_t *)buf, idx,
                        tiles_per_wave, sink);
   else if (tile_bytes == 8192)
