@@ -114,13 +114,11 @@ __device__ __forceinline__ void mfma_item(
   constexpr bool kFP8 = KV::kBytes == 1;
   constexpr int KS = D / 32;    // k-steps of the score product
   constexpr int NT = D / 16;    // 16-dimension tiles of the output
-  // 8-token blocks, and 16-token blocks of an 8-bit cache, are taken two at a
-  // time: a step covers GB tokens (the 8-bit cache's fixed work per token
-  // weighs twice as much per byte, and a 32-token step halves it).
-#ifndef PKV_MFMA_PAIR16_FP8
-#define PKV_MFMA_PAIR16_FP8 1
-#endif
-  constexpr bool kPair = BS == 8 || (BS == 16 && kFP8 && PKV_MFMA_PAIR16_FP8);
+  // 8- and 16-token blocks are taken two at a time: a step covers GB tokens,
+  // and 32-token steps halve the fixed work per token (scores, softmax and
+  // products are issued per step) and let P.V run as 16x16x32 products over
+  // 16-byte value operands.
+  constexpr bool kPair = BS == 8 || BS == 16;
   constexpr int GB = kPair ? 2 * BS : BS;
   constexpr int SUB = GB / 16;  // 16-token sub-tiles per step
   // 32-token steps: the two sub-tiles' score rows are interleaved so each
@@ -495,10 +493,10 @@ __device__ __forceinline__ void mfma_item(
 #ifndef PKV_MFMA_MIN_WAVES_FP8
 #define PKV_MFMA_MIN_WAVES_FP8 3
 #endif
-// The appending variant over 32-token blocks gives up one wave per SIMD rather
-// than spill the new token's staging.
+// The appending variants over 32-token steps (16- and 32-token blocks) give up
+// one wave per SIMD rather than spill the new token's staging.
 template <typename E, typename KV, int D, int BS, int SCHED, bool APPEND>
-__global__ __launch_bounds__(256, KV::kBytes == 1 ? PKV_MFMA_MIN_WAVES_FP8 : (APPEND && BS == 32 ? 3 : PKV_MFMA_MIN_WAVES)) void decode_mfma_kernel(
+__global__ __launch_bounds__(256, KV::kBytes == 1 ? PKV_MFMA_MIN_WAVES_FP8 : (APPEND && BS >= 16 ? 3 : PKV_MFMA_MIN_WAVES)) void decode_mfma_kernel(
     void *__restrict__ out, int out_f32, const uint16_t *__restrict__ q,
     const typename KV::storage *__restrict__ kpool, const typename KV::storage *__restrict__ vpool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
