@@ -1,5 +1,5 @@
-"""The decode step captured in a HIP graph (torch.cuda.graph) and replayed:
-scatter + split decode, and the appending decode.  Every replay, with eager
+"""Steps captured in a HIP graph (torch.cuda.graph) and replayed: scatter +
+split decode, the appending decode, and scatter + chunked prefill.  Every replay, with eager
 work and synchronisation between replays, must give the eager result bit
 for bit, and leave the pools as the eager step left them."""
 import numpy as np
@@ -73,6 +73,30 @@ def test_appending_decode_graph_replays(G):
 
     def step():
         dw.append_attend(cache, out=out, workspace=ws, out_dtype=torch.float32)
+    step()
+    torch.cuda.synchronize()
+    want = bits_of(out).copy()
+    pools = (bits_of(cache.k_pool).copy(), bits_of(cache.v_pool).copy())
+    _replays_match(_capture(step), out, want, cache, pools)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_prefill_step_graph_replays(kv):
+    # The chunk scatter + causal prefill: the workgroups rank their work items
+    # on the device and may redo a walk on the exact route; a replay must
+    # still give the eager result bit for bit.
+    wl = W.chunked_prefill_bf16(S=4, chunk=300, shared_prefix=20, Hq=8, Hkv=4, max_context_len=1024,
+                                hist_fn=lambda rng: np.array([30, 41, 600, 150]))
+    if kv == "fp8":
+        wl.kv_dtype, wl.k_scale, wl.v_scale = W.FP8, float(np.float32(0.02)), float(np.float32(0.03))
+    dw = DeviceWorkload(wl)
+    cache = new_cache(wl)
+    dw.fill(cache)
+    out = torch.empty(dw.q.shape, dtype=torch.float32, device="cuda")
+
+    def step():
+        dw.apply(cache, dw.step)
+        dw.attend(cache, out=out, out_dtype=torch.float32)
     step()
     torch.cuda.synchronize()
     want = bits_of(out).copy()
