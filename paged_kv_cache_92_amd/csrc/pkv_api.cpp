@@ -301,8 +301,12 @@ pkv_status side_stream(hipStream_t caller, SideStream **out) {
   }
   SideStream *ss = new SideStream;
   e = hipStreamCreateWithFlags(&ss->stream, hipStreamNonBlocking);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&ss->join, hipEventDisableTiming);
+  // Both ends of the fork and the join are queues of this device, and each
+  // kernel's own end-of-dispatch release makes its writes visible device-wide;
+  // the events skip the system-scope fence, which only serves the host.
+  const unsigned ev_flags = hipEventDisableTiming | hipEventDisableSystemFence;
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&ss->fork, ev_flags);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&ss->join, ev_flags);
   if (e != hipSuccess) {
     if (ss->join) (void)hipEventDestroy(ss->join);
     if (ss->fork) (void)hipEventDestroy(ss->fork);
