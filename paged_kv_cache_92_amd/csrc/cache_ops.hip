@@ -16,7 +16,10 @@ namespace {
 // lanes write consecutive tokens of one dimension: when the 16 slots are
 // consecutive (a prompt chunk) each dimension row of a value tile receives
 // contiguous runs.  Any slot mapping is handled (negative or out-of-range
-// slots are skipped).
+// slots are skipped).  All pool stores are non-temporal: the attention call
+// that follows reads the tiles back from HBM anyway, and lines the scatter
+// leaves dirty in L2 would otherwise be written back while that call streams
+// the pool (measured: about 9 us more per decode step at 256 sequences).
 template <int EB, int D, int kTok>
 __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict__ key,
                                                       const uint8_t *__restrict__ value,
@@ -78,8 +81,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict_
     if (sl < 0) continue;
     const int64_t blk = sl >> lgB;
     const int off = (int)(sl & (B - 1));
-    *(u32x4 *)(kpool + ((((size_t)(blk * H + h) * NC + ch / 4) * B + off) * X + (ch % 4) * VEC) * EB) =
-        kc[i];
+    __builtin_nontemporal_store(
+        kc[i], (u32x4 *)(kpool + ((((size_t)(blk * H + h) * NC + ch / 4) * B + off) * X + (ch % 4) * VEC) * EB));
   }
   Elem *vp = (Elem *)vpool;
   // 16-token groups: a wave writes 4 dimensions x 16 tokens.
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict_
     if (sl < 0) continue;
     const int64_t blk = sl >> lgB;
     const int off = (int)(sl & (B - 1));
-    vp[((size_t)(blk * H + h) * D + e) * B + off] = sv[e][tt];
+    __builtin_nontemporal_store(sv[e][tt], &vp[((size_t)(blk * H + h) * D + e) * B + off]);
   }
 }
 
@@ -100,7 +103,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict_
 // nearest even and saturating (the cache-write call's kv_cache_dtype,
 // k_scale and v_scale, [vLLM] PagedAttention, blog.secrett2633.cloud).  Key
 // codes go out 8 at a time into the 64-byte pieces; value codes are
-// transposed through LDS like the 16-bit values.
+// transposed through LDS like the 16-bit values; stores are non-temporal, as
+// there.
 template <typename M, int D>
 __global__ __launch_bounds__(256) void scatter_fp8_kernel(const uint16_t *__restrict__ key,
                                                           const uint16_t *__restrict__ value,
@@ -162,7 +166,7 @@ __global__ __launch_bounds__(256) void scatter_fp8_kernel(const uint16_t *__rest
     const int64_t blk = sl >> lgB;
     const int off = (int)(sl & (B - 1));
     const int e0 = g * 8;
-    *(u32x2 *)(kpool + (((size_t)(blk * H + h) * NC + e0 / 64) * B + off) * 64 + e0 % 64) = kq[i];
+    __builtin_nontemporal_store(kq[i], (u32x2 *)(kpool + (((size_t)(blk * H + h) * NC + e0 / 64) * B + off) * 64 + e0 % 64));
   }
   for (int c = tid; c < D * kTok; c += blockDim.x) {
     const int tt = c % kTok, e = c / kTok;
@@ -170,7 +174,7 @@ __global__ __launch_bounds__(256) void scatter_fp8_kernel(const uint16_t *__rest
     if (sl < 0) continue;
     const int64_t blk = sl >> lgB;
     const int off = (int)(sl & (B - 1));
-    vpool[((size_t)(blk * H + h) * D + e) * B + off] = sv[e][tt];
+    __builtin_nontemporal_store(sv[e][tt], &vpool[((size_t)(blk * H + h) * D + e) * B + off]);
   }
 }
 

@@ -346,12 +346,13 @@ __device__ __forceinline__ float elem_value(uint32_t bits) {
   return f[0];
 }
 
-// Stores the low EB bytes of bits at p.
+// Stores the low EB bytes of bits at p, non-temporally (a cache element
+// written for a later attention call, which reads it back from HBM).
 template <int EB>
 __device__ __forceinline__ void store_bits(void *p, uint32_t bits) {
-  if constexpr (EB == 1) *(uint8_t *)p = (uint8_t)bits;
-  else if constexpr (EB == 2) *(uint16_t *)p = (uint16_t)bits;
-  else *(uint32_t *)p = bits;
+  if constexpr (EB == 1) __builtin_nontemporal_store((uint8_t)bits, (uint8_t *)p);
+  else if constexpr (EB == 2) __builtin_nontemporal_store((uint16_t)bits, (uint16_t *)p);
+  else __builtin_nontemporal_store(bits, (uint32_t *)p);
 }
 
 // v with element e (of EB bytes each) replaced by the low EB bytes of bits.
