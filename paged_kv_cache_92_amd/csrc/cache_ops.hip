@@ -16,10 +16,12 @@ namespace {
 // lanes write consecutive tokens of one dimension: when the 16 slots are
 // consecutive (a prompt chunk) each dimension row of a value tile receives
 // contiguous runs.  Any slot mapping is handled (negative or out-of-range
-// slots are skipped).  All pool stores are non-temporal: the attention call
-// that follows reads the tiles back from HBM anyway, and lines the scatter
-// leaves dirty in L2 would otherwise be written back while that call streams
-// the pool (measured: about 9 us more per decode step at 256 sequences).
+// slots are skipped).  The 16-token instantiation (decode batches: one token
+// per sequence, every value store a partial line) stores non-temporally:
+// lines it left dirty in L2 were otherwise written back while the following
+// decode streamed the pool (about 9 us more per 13B-shaped decode step).  The
+// 64-token one (prompt chunks, whole lines) keeps plain stores, which measured
+// faster there when the scatter follows a prefill kernel.
 template <int EB, int D, int kTok>
 __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict__ key,
                                                       const uint8_t *__restrict__ value,
@@ -34,6 +36,10 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict_
   using Elem = typename std::conditional<EB == 4, uint32_t, uint16_t>::type;
   __shared__ int64_t sslot[kTok];
   __shared__ Elem sv[D][kTok + 1];
+  auto put = [](auto x, auto *p) {
+    if constexpr (kTok == 16) __builtin_nontemporal_store(x, p);
+    else *p = x;
+  };
 
   const int h = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * kTok;
@@ -81,8 +87,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict_
     if (sl < 0) continue;
     const int64_t blk = sl >> lgB;
     const int off = (int)(sl & (B - 1));
-    __builtin_nontemporal_store(
-        kc[i], (u32x4 *)(kpool + ((((size_t)(blk * H + h) * NC + ch / 4) * B + off) * X + (ch % 4) * VEC) * EB));
+    put(kc[i], (u32x4 *)(kpool + ((((size_t)(blk * H + h) * NC + ch / 4) * B + off) * X + (ch % 4) * VEC) * EB));
   }
   Elem *vp = (Elem *)vpool;
   // 16-token groups: a wave writes 4 dimensions x 16 tokens.
@@ -93,7 +98,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict_
     if (sl < 0) continue;
     const int64_t blk = sl >> lgB;
     const int off = (int)(sl & (B - 1));
-    __builtin_nontemporal_store(sv[e][tt], &vp[((size_t)(blk * H + h) * D + e) * B + off]);
+    put(sv[e][tt], &vp[((size_t)(blk * H + h) * D + e) * B + off]);
   }
 }
 
