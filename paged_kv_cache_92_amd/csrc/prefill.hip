@@ -271,28 +271,36 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(
   const int vtok = VTC * (tid % (kKT / VTC)), vdim = tid / (kKT / VTC);
   const bool kload = NPC >= KPR || kpc < NPC;   // this thread has key chunks
   const bool vload = D >= VDR || vdim < D;      // ... and value chunks
-  auto load_tile = [&](int t, u32x4 (&kreg)[KPT], u32x4 (&vreg)[VPT]) {
-    const int t0 = t * kKT;
-    const bool full = t0 + kKT <= ctx;
+  // Byte offsets of this thread's chunks within one block's key / value tile
+  // (for every tile: 64-token tiles start on block boundaries), and the bytes
+  // between consecutive blocks of a pool.
+  const uint32_t blk_bytes = (uint32_t)Hkv * D * BS * KV::kBytes;
+  const uint8_t *kbase = kpool + ((size_t)hkv * D * BS + (ktok % BS) * KX) * KV::kBytes + 16 * ksub;
+  const uint8_t *vbase = vpool + ((size_t)hkv * D * BS + vtok % BS) * KV::kBytes;
+  const uint8_t *vbase2 = vpool + (size_t)hkv * D * BS * KV::kBytes;
+  // FULL: the tile lies within the context (every tile but the last), so no
+  // position needs a bounds check or a mask.
+  auto load_rows = [&](int t0, auto full_t, u32x4 (&kreg)[KPT], u32x4 (&vreg)[VPT]) {
+    constexpr bool FULL = decltype(full_t)::value;
     if (kload) {
       const int pos = t0 + ktok;
       // Positions past the context read a harmless in-pool address; their
       // scores are masked.  An invalid block id (a broken caller contract)
       // reads block 0 instead of faulting.
-      const int blk = (full || pos < ctx) ? max(sBT[pos / BS], 0) : 0;
-      const uint8_t *kb = kpool + (((size_t)blk * Hkv + hkv) * D * BS + (pos % BS) * KX) * KV::kBytes + 16 * ksub;
+      const int blk = (FULL || pos < ctx) ? max(sBT[pos / BS], 0) : 0;
+      const uint8_t *kb = kbase + (size_t)(uint32_t)blk * blk_bytes;
 #pragma unroll
       for (int i = 0; i < KPT; ++i) kreg[i] = load16(kb + (size_t)(kpc + KPR * i) * BS * 64);
     }
     if (vload) {
       const int pos = t0 + vtok;
-      const int blk = (full || pos < ctx) ? max(sBT[pos / BS], 0) : 0;
-      const uint8_t *vblk = vpool + (((size_t)blk * Hkv + hkv) * D * BS + pos % BS) * KV::kBytes;
+      const int blk = (FULL || pos < ctx) ? max(sBT[pos / BS], 0) : 0;
+      const uint8_t *vblk = vbase + (size_t)(uint32_t)blk * blk_bytes;
       // 8-bit values in 8-token blocks: the chunk's second half is the next block's.
       const uint8_t *vblk2 = vblk;
       if constexpr (VTC > BS) {
-        const int blk2 = (full || pos + BS < ctx) ? max(sBT[(pos + BS) / BS], 0) : 0;
-        vblk2 = vpool + ((size_t)blk2 * Hkv + hkv) * D * BS;
+        const int blk2 = (FULL || pos + BS < ctx) ? max(sBT[(pos + BS) / BS], 0) : 0;
+        vblk2 = vbase2 + (size_t)(uint32_t)blk2 * blk_bytes;
       }
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
@@ -304,7 +312,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(
         } else {
           x = load16(vblk + row);
         }
-        if (!full && pos + VTC > ctx) {
+        if (!FULL && pos + VTC > ctx) {
           // Slots past the context may hold anything (NaN included): zero them.
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
@@ -318,6 +326,11 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(
         vreg[i] = x;
       }
     }
+  };
+  auto load_tile = [&](int t, u32x4 (&kreg)[KPT], u32x4 (&vreg)[VPT]) {
+    const int t0 = t * kKT;
+    if (t0 + kKT <= ctx) load_rows(t0, std::true_type{}, kreg, vreg);
+    else load_rows(t0, std::false_type{}, kreg, vreg);
   };
   // Registers -> LDS buffer buf.  CONV: bf16 values re-encoded to fp16 (exact
   // below 65536 in magnitude; larger ones become infinities, which the walk's
