@@ -85,6 +85,7 @@ __device__ __forceinline__ void valu_item(
   using C = ValuCfg<E, D, GB>;
   using T = typename E::storage;
   constexpr bool kFP8 = E::kBytes == 1;
+  constexpr bool kF64 = E::kBytes == 4;   // fp32 cache: scores in fp64
   const Span sp = seq_span(context_lens, s, cap, window);
   const int lo = sp.lo;                      // first attended position
   const int tok0 = max(b0 * BS, lo);
@@ -248,15 +249,32 @@ __device__ __forceinline__ void valu_item(
     // Only the last step can end past the length, only the first start
     // before the window.
     const bool partial = tbase + GB > tok1 || tbase < lo;
+    // Scores.  Over an fp32 cache each score is formed in fp64 and kept
+    // (sd) until its weight is taken: a score of a few hundred log2 units
+    // rounded to fp32 would already move its weight by ~1e-5, so the weight
+    // is 2^(sd - m) with the fp64 difference, and only the reference maximum
+    // m is an fp32 value (the rounded score).
     float sc[C::TG];
+    double sd[kF64 ? C::TG : 1];
 #pragma unroll
     for (int r = 0; r < C::TG; ++r) {
-      float x = dot(kr[r], 0);
+      bool masked = partial && (unsigned)(tbase + 16 * r + kt - lo) >= (unsigned)(tok1 - lo);
+      if constexpr (kF64) {
+        double x = dot16_f64(kr[r], qc[0]);
 #pragma unroll
-      for (int c = 1; c < C::NC; ++c) x += dot(kr[c * C::TG + r], c);
-      x = group_sum<4>(x) * scale_log2;
-      if (partial && (unsigned)(tbase + 16 * r + kt - lo) >= (unsigned)(tok1 - lo)) x = -INFINITY;
-      sc[r] = x;
+        for (int c = 1; c < C::NC; ++c) x += dot16_f64(kr[c * C::TG + r], qc[c]);
+        x = quad_sum_f64(x) * (double)scale_log2;
+        if (masked) x = -INFINITY;
+        sd[r] = x;
+        sc[r] = (float)x;
+      } else {
+        float x = dot(kr[r], 0);
+#pragma unroll
+        for (int c = 1; c < C::NC; ++c) x += dot(kr[c * C::TG + r], c);
+        x = group_sum<4>(x) * scale_log2;
+        if (masked) x = -INFINITY;
+        sc[r] = x;
+      }
     }
     float mb = sc[0];
 #pragma unroll
@@ -267,7 +285,10 @@ __device__ __forceinline__ void valu_item(
     m = mnew;
     if (kq == 0) {
 #pragma unroll
-      for (int r = 0; r < C::TG; ++r) lds_p[w][16 * r + kt] = fast_exp2(sc[r] - mnew);
+      for (int r = 0; r < C::TG; ++r) {
+        if constexpr (kF64) lds_p[w][16 * r + kt] = fast_exp2((float)(sd[r] - (double)mnew));
+        else lds_p[w][16 * r + kt] = fast_exp2(sc[r] - mnew);
+      }
     }
     __builtin_amdgcn_wave_barrier();
     float p[C::VEC];

@@ -153,6 +153,17 @@ __device__ __forceinline__ float dot16<F32>(const u32x4 &k, const u32x4 &q) {
   }
   return d;
 }
+// q.k over four fp32 elements in fp64: the products are exact, one rounding
+// per addition at 53 bits.
+__device__ __forceinline__ double dot16_f64(const u32x4 &k, const u32x4 &q) {
+  double d = 0.0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t ku = k[i], qu = q[i];
+    d = __builtin_fma((double)as_f32(qu), (double)as_f32(ku), d);
+  }
+  return d;
+}
 template <>
 __device__ __forceinline__ float dot16<F16>(const u32x4 &k, const u32x4 &q) {
   float d = 0.f;
@@ -236,6 +247,21 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
                                                                0xf, 0xf, false));
+}
+
+// The same lane permutation applied to both halves of a double.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xf, 0xf, false);
+  return __builtin_bit_cast(double, (uint64_t)lo | ((uint64_t)hi << 32));
+}
+
+// Sum of a double over each aligned quad of lanes.
+__device__ __forceinline__ double quad_sum_f64(double x) {
+  x += dpp_f64<0xB1>(x);
+  return x + dpp_f64<0x4E>(x);
 }
 
 template <int WIDTH>

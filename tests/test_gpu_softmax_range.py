@@ -8,8 +8,7 @@ blocks.  Here every key is a ramp in its position, so the scores rise (or
 fall) by about 5 log2 units per 16-token block and by about 20 per 64-key
 prefill tile: rising, the maximum grows at every block and passes the
 prefill kernel's lazy-rescale threshold at every tile; falling, it never
-moves after the first block (over an fp32 cache the slope is a quarter of
-that; see test_decode_moving_maximum).  The queries are all ones, so a score is
+moves after the first block.  The queries are all ones, so a score is
 sqrt(d) times the key's value.  Pools, gathers and outputs are compared with
 the oracle as in the other parity tests.
 """
@@ -47,12 +46,20 @@ def _decode(dtype, G, part, slope, lens, kv=None, d=128, B=16):
                                             (W.F16, 1, -1, 8), (W.BF16, 4, 0, 16), (W.BF16, 4, 64, 32),
                                             (W.BF16, 4, -1, 16), (W.F16, 7, -1, 8)])
 def test_decode_moving_maximum(dtype, G, part, B, sign):
-    # fp32 cache: a quarter of the slope (scores up to ~80 log2 units, still
-    # rising by ~1.3 per block).  At the full slope they reach ~330, where one
-    # fp32 ulp of a score (3e-5) already moves a weight by ~1e-5 relative: no
-    # fp32 computation of the scores meets the 1e-5 bound against fp64 there.
-    slope = sign * (0.005 if dtype == W.F32 else 0.02)
+    # The scores reach ~330 log2 units, where one fp32 ulp of a score (3e-5)
+    # moves a weight by ~1e-5 relative: over an fp32 cache the kernel forms
+    # scores and weight exponents in fp64, so the 1e-5 bound holds here too.
+    slope = sign * 0.02
     _full_check(_decode(dtype, G, part, slope, [300, 513, 1000, 17], B=B))
+
+
+@pytest.mark.parametrize("sign", [1, -1], ids=["rising", "falling"])
+@pytest.mark.parametrize("part,B", [(0, 16), (64, 16), (-1, 8), (128, 32)])
+def test_fp32_cache_scores_near_one_thousand(part, B, sign):
+    # Three times the slope: scores up to ~1,000 log2 units, where an fp32
+    # score is off by up to 3e-5 of a unit after one rounding (weights by
+    # 4e-5); the fp64 score and exponent path keeps every output within 1e-5.
+    _full_check(_decode(W.F32, 1, part, sign * 0.06, [300, 513, 1000, 17], B=B))
 
 
 @pytest.mark.parametrize("slope", [0.02, -0.02], ids=["rising", "falling"])
