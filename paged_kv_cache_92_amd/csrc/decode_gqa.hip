@@ -98,8 +98,10 @@ __device__ __forceinline__ u32x2 widen4(uint32_t w) {
 // masked; head h's merged result goes to the output or to workspace
 // partial row dest.base + h * dest.stride.  `lds_dyn` holds the cross-wave
 // merge buffers.  E is the query / matrix-core type; KV the cache element
-// (E itself, or FP8: codes are widened to E right after the loads, the key
-// scale is folded into scale_log2 and v_scale multiplies the merged sums).
+// (E itself, or FP8: key codes are widened to E and value codes to fp16
+// right after the loads, so that P.V takes the weights as one fp16 operand
+// instead of a bf16 hi + lo pair; the key scale is folded into scale_log2
+// and v_scale multiplies the merged sums).
 // APPEND: the sequence's new token (position L-1) is taken from the input
 // rows ap.k / ap.v, in cache format, instead of the pool, whose slot is
 // written by the reduce kernel.
@@ -112,6 +114,7 @@ __device__ __forceinline__ void mfma_item(
     int cap, int window, float scale_log2, float v_scale, float *__restrict__ ws_ml,
     float *__restrict__ ws_acc, const Append<E> &ap) {
   constexpr bool kFP8 = KV::kBytes == 1;
+  using PVE = typename std::conditional<kFP8, F16, E>::type;   // the P.V product's type
   constexpr int KS = D / 32;    // k-steps of the score product
   constexpr int NT = D / 16;    // 16-dimension tiles of the output
   // 8- and 16-token blocks are taken two at a time: a step covers GB tokens,
@@ -246,7 +249,7 @@ __device__ __forceinline__ void mfma_item(
       for (int nt = 0; nt < NT; ++nt) {
         if constexpr (kFP8) {
           const u32x2 raw = load8_stream(vt + (16 * nt + n16) * BS + 8 * g4 + vtok);
-          const u32x2 lo = widen4<E>(raw[0]), hi = widen4<E>(raw[1]);
+          const u32x2 lo = widen4<PVE>(raw[0]), hi = widen4<PVE>(raw[1]);
           vw[nt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         } else {
           vw[nt] = load16_stream(vt + (16 * nt + n16) * BS + 8 * g4 + vtok);
@@ -258,7 +261,7 @@ __device__ __forceinline__ void mfma_item(
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           if constexpr (kFP8)
-            va[sb][nt] = widen4<E>(load4_stream(vt + (16 * nt + n16) * BS + 16 * sb + 4 * g4 + vtok));
+            va[sb][nt] = widen4<PVE>(load4_stream(vt + (16 * nt + n16) * BS + 16 * sb + 4 * g4 + vtok));
           else
             va[sb][nt] = load8_stream(vt + (16 * nt + n16) * BS + 16 * sb + 4 * g4 + vtok);
         }
@@ -349,12 +352,12 @@ __device__ __forceinline__ void mfma_item(
         p[j] = fast_exp2(st[sb][j] - mnew);
         psum += p[j];
       }
-      if constexpr (Mfma<E>::kSplitP) {
+      if constexpr (Mfma<PVE>::kSplitP) {
         split_bf16x2(p[0], p[1], ph[2 * sb], plo[2 * sb]);
         split_bf16x2(p[2], p[3], ph[2 * sb + 1], plo[2 * sb + 1]);
       } else {
-        ph[2 * sb] = Mfma<E>::pack2(p[0], p[1]);
-        ph[2 * sb + 1] = Mfma<E>::pack2(p[2], p[3]);
+        ph[2 * sb] = Mfma<PVE>::pack2(p[0], p[1]);
+        ph[2 * sb + 1] = Mfma<PVE>::pack2(p[2], p[3]);
       }
     }
     l = l * alpha + psum;
@@ -391,7 +394,7 @@ __device__ __forceinline__ void mfma_item(
         for (int nt = 0; nt < NT; ++nt) {
           // The element as the product reads it: an 8-bit code widened to E.
           uint32_t e = vnew[nt];
-          if constexpr (kFP8) e = widen4<E>(e)[0] & 0xffffu;
+          if constexpr (kFP8) e = widen4<PVE>(e)[0] & 0xffffu;
           if constexpr (kWide) {
             vw[nt] = put_elem<2>(vw[nt], vj, e);
           } else {
@@ -409,17 +412,17 @@ __device__ __forceinline__ void mfma_item(
       const u32x4 pw = {ph[0], ph[1], ph[2], ph[3]};
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        acc[nt] = Mfma<E>::qk(vw[nt], pw, acc[nt]);
-        if constexpr (Mfma<E>::kSplitP) acc[nt] = Mfma<E>::qk(vw[nt], u32x4{plo[0], plo[1], plo[2], plo[3]}, acc[nt]);
+        acc[nt] = Mfma<PVE>::qk(vw[nt], pw, acc[nt]);
+        if constexpr (Mfma<PVE>::kSplitP) acc[nt] = Mfma<PVE>::qk(vw[nt], u32x4{plo[0], plo[1], plo[2], plo[3]}, acc[nt]);
       }
     } else {
 #pragma unroll
       for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          acc[nt] = Mfma<E>::pv(va[sb][nt], u32x2{ph[2 * sb], ph[2 * sb + 1]}, acc[nt]);
-          if constexpr (Mfma<E>::kSplitP)
-            acc[nt] = Mfma<E>::pv(va[sb][nt], u32x2{plo[2 * sb], plo[2 * sb + 1]}, acc[nt]);
+          acc[nt] = Mfma<PVE>::pv(va[sb][nt], u32x2{ph[2 * sb], ph[2 * sb + 1]}, acc[nt]);
+          if constexpr (Mfma<PVE>::kSplitP)
+            acc[nt] = Mfma<PVE>::pv(va[sb][nt], u32x2{plo[2 * sb], plo[2 * sb + 1]}, acc[nt]);
         }
     }
   };
