@@ -192,9 +192,10 @@ size_t pkv_decode_workspace_bytes(const pkv_cache *cache, int32_t num_seqs, int3
  *
  * Grouped heads (num_q_heads > num_kv_heads) over an f16/bf16/8-bit cache
  * run on the matrix cores with the group's queries stacked into one tile
- * (group size <= 16; 8-bit codes are widened to the model dtype as they
- * arrive); fp32 caches and single heads run the wavefront dot-product
- * kernel.
+ * (group size <= 16; 8-bit key codes are widened to the model dtype and
+ * value codes to fp16 as they arrive, both exactly); fp32 caches and single
+ * heads run the wavefront dot-product kernel, over an fp32 cache with each
+ * score and weight exponent formed in fp64.
  */
 pkv_status pkv_paged_decode(const pkv_cache *cache, void *out, int32_t out_dtype, const void *q,
                             int32_t num_q_heads,
