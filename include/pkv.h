@@ -312,10 +312,11 @@ pkv_status pkv_paged_prefill(const pkv_cache *cache, void *out, int32_t out_dtyp
  * pkv_paged_prefill over all num_seqs sequences (a decode row is a chunk of
  * one row at position context_lens[s] - 1), computed by two kernels that run
  * at once: the decode kernel of pkv_paged_decode over the decode sequences
- * and the prefill kernel over the chunk sequences.  The decode part is
+ * and the prefill kernel over the chunk sequences.  The decode kernel is
  * enqueued on a stream the library owns, forked from and joined back into
- * `stream` with two events, so work enqueued on `stream` after this call sees
- * both parts finished.  The library keeps that stream and its events (default
+ * `stream` with two events; the reduce of its split rows then runs on
+ * `stream`, so work enqueued on `stream` after this call sees both parts
+ * finished.  The library keeps that stream and its events (default
  * priority) for each (device, caller stream) pair it has served, until the
  * process ends: the one call of this interface that holds handles, so that
  * the two parts can run at once on one caller stream.

@@ -520,7 +520,8 @@ pkv_status pkv_paged_mixed(const pkv_cache *cache, void *out, int32_t out_dtype,
   }
   // Both kinds: the chunk rows go on the caller's stream first, the decode
   // rows on the side stream, so the matrix-core prefill and the HBM-bound
-  // decode share the chip; the caller's stream then waits for both.
+  // decode share the chip; the caller's stream then waits for the decode
+  // kernel and reduces its split rows.
   SideStream *ss = nullptr;
   st = side_stream(stream, &ss);
   if (st) return st;
@@ -530,13 +531,23 @@ pkv_status pkv_paged_mixed(const pkv_cache *cache, void *out, int32_t out_dtype,
   if (e != hipSuccess) return hip_status(e, "paged_mixed fork");
   e = pkv::launch_prefill(c, pa, stream);
   if (e != hipSuccess) return hip_status(e, "paged_mixed prefill launch");
-  st = launch_decode(c, da, plan, ss->stream);
-  // Join even after a failed decode launch: the side stream must not run
-  // ahead of later work on the caller's stream.
+  // Only the decode kernel goes on the side stream; the reduce of its split
+  // rows follows the join on the caller's stream, where the next call's work
+  // then follows it without another cross-queue wait (a call 2-3 us shorter
+  // than with the reduce on the side stream).  Join even after a failed
+  // decode launch: the side stream must not run ahead of later work on the
+  // caller's stream.
+  const hipError_t ed = plan.mfma ? pkv::launch_decode_mfma(c, da, ss->stream)
+                                  : pkv::launch_decode_valu(c, da, ss->stream);
   e = hipEventRecord(ss->join, ss->stream);
   if (e == hipSuccess) e = hipStreamWaitEvent(stream, ss->join, 0);
-  if (st) return st;
-  return hip_status(e, "paged_mixed join");
+  if (ed != hipSuccess) return hip_status(ed, "paged_mixed decode launch");
+  if (e != hipSuccess) return hip_status(e, "paged_mixed join");
+  if (plan.reduce()) {
+    e = pkv::launch_decode_reduce(c, da, stream);
+    if (e != hipSuccess) return hip_status(e, "paged_mixed reduce launch");
+  }
+  return ok();
 }
 
 pkv_status pkv_gather_kv(const pkv_cache *cache, void *k_out, void *v_out,
