@@ -447,10 +447,15 @@ def run_config(torch, pkv, name, args, cpu_budget, read_probe, fused=False, kv_c
             wl.head_dim * elt
         pre_flops = attention_flops(wl) - float(wl.context_lens[:nd].astype(np.int64).sum()) * \
             wl.num_q_heads * wl.head_dim * 4
+        # KV bytes of the chunk rows' contexts: the step reads them too.
+        pre_kv_bytes = int(wl.context_lens[nd:].astype(np.int64).sum()) * 2 * wl.num_kv_heads * \
+            wl.head_dim * elt
         # Lower bound of the step: decode KV at HBM peak and chunk products at
         # MFMA peak, overlapped perfectly; the larger of the two names the bound.
         t_hbm = dec_bytes / (HBM_PEAK_GBS * 1e9)
         t_mfma = pre_flops / (MFMA_PEAK_TFLOPS[mdt] * 1e12)
+        # The same bound with the chunks' KV bytes added to the HBM side.
+        t_hbm_all = (dec_bytes + pre_kv_bytes) / (HBM_PEAK_GBS * 1e9)
         bound = "hbm" if t_hbm >= t_mfma else "mfma"
         t_attn = attn_avg * 1e-3
         res["metric"] = "mixed decode + chunked-prefill step: query rows/s (one call)"
@@ -466,6 +471,8 @@ def run_config(torch, pkv, name, args, cpu_budget, read_probe, fused=False, kv_c
                          "kernel": "mixed step (decode kernel and prefill kernel at once)",
                          "algorithmic_bytes_decode": dec_bytes,
                          "algorithmic_flops_prefill": pre_flops,
+                         "algorithmic_bytes_prefill_kv": pre_kv_bytes,
+                         "frac_with_prefill_kv": round(max(t_hbm_all, t_mfma) / t_attn, 4),
                          "avg_launch_us": round(attn_avg * 1e3, 2)},
             "mixed": {"one_call_us": round(attn_avg * 1e3, 2),
                       "sequential_calls_us": round(ways["sequential"] * 1e3, 2),
