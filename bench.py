@@ -12,9 +12,10 @@ the 256 MiB Infinity Cache cannot serve a step from the previous one.
 `value` comes from K steps timed back to back with nothing between them; the
 roofline's per-launch duration from K further steps with timing events around
 each attention call.  The default run also measures, in the same process,
-long-context split-KV decode, GQA decode at block sizes 16 and 32 and chunked
-prefill, each under `extra_configs` with its own roofline and a short CPU
-oracle sample.
+the tiny fp32 decode (launch-bound; its roofline fraction is reported, not
+tuned for), long-context split-KV decode, GQA decode at block sizes 16 and 32
+and chunked prefill, each under `extra_configs` with its own roofline and a
+short CPU oracle sample.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -307,7 +308,7 @@ def cpu_baseline(wl, budget_s):
                       f"{el:.1f} s wall on 1 thread, {el_all:.1f} s on {cores}"}
 
 
-EXTRA_CONFIGS = ("long_split", "gqa16", "gqa32", "prefill")
+EXTRA_CONFIGS = ("tiny", "long_split", "gqa16", "gqa32", "prefill")
 
 
 def run_config(torch, pkv, name, args, cpu_budget, read_probe, fused=False, kv_cache="model",
@@ -535,7 +536,7 @@ def main():
                     help="seconds of oracle work for each extra configuration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="default run: skip the long-split, GQA and prefill configurations")
+                    help="default run: skip the tiny, long-split, GQA and prefill configurations")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--read-probe-gib", type=int, default=0,
