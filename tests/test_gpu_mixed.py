@@ -123,6 +123,35 @@ def test_mixed_graph_capture_replays():
         _ = (eager * 2).sum().item()                # eager work between replays
 
 
+def test_mixed_first_call_on_a_stream_inside_graph_capture():
+    # The library meets the capturing stream for the first time inside the
+    # capture, so its side stream and events are created there; every replay,
+    # with eager work and synchronisation between them, gives the eager result.
+    wl = _mixed(W.F16, 128, 16, 4, seed=17, partition_size=64)
+    dw = DeviceWorkload(wl)
+    cache = new_cache(wl)
+    dw.fill(cache)
+    dw.apply(cache, dw.step)
+    eager = dw.attend(cache, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    nd = wl.info["num_decode_seqs"]
+    need = pkv.decode_workspace_bytes(cache, nd, wl.num_q_heads, wl.max_context_len, 64)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(eager)
+    fresh = torch.cuda.Stream()      # no library call has used it yet
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=fresh):
+        dw.attend(cache, out=out, workspace=ws)
+    want = bits_of(eager)
+    for i in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(out), want), f"replay {i}"
+        _ = (eager * 2).sum().item()                # eager work between replays
+
+
 def test_mixed_fp8_cache():
     wl = W.make_mixed("fp8_decode_only", 8, lambda rng: [1, 30, 200], lambda rng: [], [], Hq=4,
                       Hkv=2, d=128, B=16, dtype=W.F16, max_context_len=256)
