@@ -311,6 +311,30 @@ def cpu_baseline(wl, budget_s):
 EXTRA_CONFIGS = ("tiny", "long_split", "gqa16", "gqa32", "prefill")
 
 
+def gemm_probe_tflops(torch, n=16384, reps=20):
+    """Dense bf16 matrix-product rate this GPU sustains in practice: one n x n x n product
+    y = x w^T (torch.nn.functional.linear: both operands contiguous along the reduced
+    dimension, the library's fastest layout here) repeated back to back.  TFLOP/s.  A
+    calibration of what the matrix cores deliver under load, beside the nominal peak; not
+    part of the path."""
+    import torch.nn.functional as F
+    g = torch.Generator(device="cuda").manual_seed(0)
+    x = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    w = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    for _ in range(3):
+        c = F.linear(x, w)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(reps):
+        c = F.linear(x, w)
+    t1.record()
+    torch.cuda.synchronize()
+    sec = t0.elapsed_time(t1) * 1e-3 / reps
+    del x, w, c
+    return 2.0 * n ** 3 / sec / 1e12
+
+
 def run_config(torch, pkv, name, args, cpu_budget, read_probe, fused=False, kv_cache="model",
                block_size=16, placement="shuffled", partition=None):
     """One workload: generate, upload two pool copies, time the step, report its roofline.
@@ -493,6 +517,12 @@ def run_config(torch, pkv, name, args, cpu_budget, read_probe, fused=False, kv_c
                          "algorithmic_flops_per_launch": flops,
                          "avg_launch_us": round(attn_avg * 1e3, 2)},
         })
+        if read_probe:
+            gp = gemm_probe_tflops(torch)
+            res["roofline"]["gemm_probe_TFLOPs"] = round(gp, 1)
+            res["roofline"]["frac_of_gemm_probe"] = round(tf_attn / gp, 4)
+            log(f"[bench] dense bf16 product probe: {gp:.0f} TFLOP/s (prefill call at "
+                f"{100 * tf_attn / gp:.1f}% of it)")
         res["metric"] = "chunked prefill attention TFLOP/s (% of MFMA peak)"
     res["config"] = {"workload": desc, "seqs": wl.S, "q_heads": wl.num_q_heads,
                      "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
@@ -544,7 +574,10 @@ def main():
     ap.add_argument("--cache-ops", action="store_true",
                     help="only time the block copy and the slot scatter alone (prefill pool shape)")
     ap.add_argument("--no-read-probe", action="store_true",
-                    help="decode workloads: skip the read-ceiling probe after the timed steps")
+                    help="skip the ceiling probes after the timed steps (decode: HBM reads of random "
+                         "4 KiB tiles; prefill: a dense bf16 matrix product)")
+    ap.add_argument("--gemm-probe", action="store_true",
+                    help="only time the dense bf16 matrix-product probe (16384^3, torch.nn.functional.linear)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported",
@@ -569,6 +602,11 @@ def main():
     if args.cache_ops:
         print(json.dumps({"cache_ops": cache_ops(torch, pkv, args.steps), "steps": args.steps,
                           "peak_GBps": HBM_PEAK_GBS}), flush=True)
+        return
+    if args.gemm_probe:
+        gp = gemm_probe_tflops(torch, reps=args.steps)
+        print(json.dumps({"gemm_probe_TFLOPs": round(gp, 1), "n": 16384, "dtype": "bf16",
+                          "launches": args.steps}), flush=True)
         return
     if args.read_probe_gib:
         g = read_probe_gbps(torch, gib=args.read_probe_gib, reps=args.steps)
@@ -598,7 +636,7 @@ def main():
             log(f"[bench] configuration {name}")
             extras[name] = run_config(torch, pkv, name, args,
                                       0.0 if args.no_cpu_baseline else args.extra_cpu_budget,
-                                      False)
+                                      name == "prefill" and not args.no_read_probe)
         res["extra_configs"] = extras
     print(json.dumps(res), flush=True)
 
