@@ -331,6 +331,18 @@ def test_prefill_bf16_values_beyond_f16_range():
     _full_check(wl)
 
 
+@pytest.mark.parametrize("S,Hq", [(300, 2), (261, 1)])
+def test_prefill_more_classes_than_the_ranking_holds(S, Hq):
+    # More (sequence, query tile) classes than the kernel ranks longest-first:
+    # the work order falls back to the XCD-grouped one (block ids remapped when
+    # their count is a multiple of 8, as for S = 300 x 2 heads; in launch order
+    # otherwise, as for S = 261 x 1 head).
+    wl = W.make_prefill(f"many_{S}_{Hq}", 77 + S, S, 20, lambda rng: rng.integers(0, 61, size=S), 0,
+                        Hq=Hq, Hkv=Hq, d=64, B=16, dtype=W.BF16, max_context_len=96,
+                        pair_sharing=False)
+    _full_check(wl)
+
+
 def test_prefill_shared_prefix_with_copy_on_write():
     # Shared prefix of 20 tokens ends inside block 1: the partner's first own
     # token forces a block copy before its history is written.
