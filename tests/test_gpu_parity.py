@@ -343,6 +343,28 @@ def test_prefill_more_classes_than_the_ranking_holds(S, Hq):
     _full_check(wl)
 
 
+def test_prefill_long_context_table_staged_in_lds():
+    # A 65,536-token context at block size 8: the staged block table takes
+    # 32 KiB of dynamic LDS beside the three tile buffers.
+    L = 65536
+    wl = W.make_prefill("long_table", 13, 1, 16, lambda rng: np.array([L - 16]), 0, Hq=1, Hkv=1,
+                        d=128, B=8, dtype=W.F16, max_context_len=L, pair_sharing=False)
+    _full_check(wl)
+
+
+def test_prefill_refuses_a_table_beyond_lds():
+    # 40,000 staged block ids do not fit beside the tile buffers: the call is
+    # refused on the host before anything is launched.
+    wl = W.make_prefill("lds_refusal", 14, 1, 16, lambda rng: np.array([16]), 0, Hq=1, Hkv=1,
+                        d=128, B=8, dtype=W.F16, max_context_len=32, pair_sharing=False)
+    dw = DeviceWorkload(wl)
+    cache = new_cache(wl)
+    width = 40_000
+    bt = torch.zeros((1, width), dtype=torch.int32, device="cuda")
+    with pytest.raises(pkv.PkvError, match="LDS"):
+        pkv.paged_prefill(cache, dw.q, dw.qsl, dw.context_lens, bt, 16, width * 8)
+
+
 def test_prefill_shared_prefix_with_copy_on_write():
     # Shared prefix of 20 tokens ends inside block 1: the partner's first own
     # token forces a block copy before its history is written.
