@@ -1,7 +1,8 @@
 """A broken caller contract must give wrong numbers, never a memory fault.
 
 Here the lengths run past the call's max_context_len (the host bound the
-launch and the split workspace are sized from).  Every schedule clamps each
+launch, the split workspace and, for prefill, the staged block table are
+sized from).  Every schedule clamps each
 length to what the call's partitions cover, so the kernels stay inside the
 workspace the call asked for, and each output is still a weighted mean of
 stored values: finite and no larger in magnitude than the largest of them.
@@ -31,6 +32,31 @@ def test_lengths_beyond_max_context_len_stay_in_bounds(part, G):
     print(f"contract case G={G} part={part}", flush=True)
     out = pkv.paged_decode(cache, dw.q, dw.block_tables, dw.context_lens, 512, scale=wl.scale,
                            partition_size=part, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    v = cache.v_pool.float()
+    vmax = float(v[torch.isfinite(v)].abs().max())
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert np.abs(got).max() <= vmax * (1 + 1e-6)
+
+
+@pytest.mark.parametrize("claimed", [64, 256, 500])
+def test_prefill_lengths_beyond_max_context_len_stay_in_bounds(claimed):
+    # Contexts reach 764 tokens; the call claims they are <= `claimed`.  The
+    # kernel stages only the table entries the claim covers and clamps each
+    # context to them, so its reads stay within those blocks; a chunk longer
+    # than its clamped context is skipped and leaves its rows as they were.
+    wl = W.make_prefill(f"contract_prefill_{claimed}", 73, 4, 64,
+                        lambda rng: np.array([0, 100, 300, 700]), 0, Hq=4, Hkv=2, d=128, B=16,
+                        dtype=W.BF16, max_context_len=768, pair_sharing=False)
+    dw = DeviceWorkload(wl)
+    cache = new_cache(wl)
+    dw.fill(cache)
+    dw.apply(cache, dw.step)
+    print(f"prefill contract case claimed={claimed}", flush=True)
+    out = torch.zeros(dw.q.shape, dtype=torch.float32, device="cuda")
+    pkv.paged_prefill(cache, dw.q, dw.qsl, dw.context_lens, dw.block_tables, 64, claimed,
+                      scale=wl.scale, out=out)
     torch.cuda.synchronize()
     v = cache.v_pool.float()
     vmax = float(v[torch.isfinite(v)].abs().max())
