@@ -227,6 +227,42 @@ def test_negative_slots_are_skipped_and_copy_blocks_copies():
     _pools_equal(cache, k_ref, v_ref, wl.cache_dtype)
 
 
+@pytest.mark.parametrize("kv", ["model", "fp8"])
+def test_out_of_range_slots_and_block_pairs_are_skipped(kv):
+    # Slots at or past num_blocks * B and block pairs naming a block outside
+    # the pool are skipped on the device: the pools equal the oracle's with
+    # those entries left out (the oracle itself refuses them).
+    wl = W.make_decode(f"oob_{kv}", 29, lambda rng: [20, 40, 33], Hq=2, Hkv=2, d=64, B=16,
+                       dtype=W.BF16, max_context_len=48)
+    if kv == "fp8":
+        _as_fp8(wl, float(np.float32(0.02)), float(np.float32(0.03)))
+    nslots = wl.num_blocks * wl.block_size
+    dw = DeviceWorkload(wl)
+    cache = new_cache(wl)
+    dw.fill(cache)
+    _, key, value, slots = dw.step
+    bad = slots.clone()
+    bad[0], bad[2] = nslots, nslots + 12345        # tokens 0 and 2 are skipped
+    pkv.reshape_and_cache(cache, key, value, bad)
+    pkv.copy_blocks(cache, torch.tensor([[0, wl.num_blocks], [-1, 1], [wl.num_blocks + 7, 2]],
+                                        dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    ref_k, ref_v = wl.empty_pools()
+    for o in wl.setup:
+        if o.kind == "scatter":
+            oracle.reshape_and_cache(ref_k, ref_v, wl.cache_dtype, o.key, o.value, o.slots,
+                                     in_dtype=wl.dtype, k_scale=wl.k_scale, v_scale=wl.v_scale)
+        else:
+            oracle.copy_blocks(ref_k, ref_v, wl.cache_dtype, o.pairs)
+    op = wl.step_scatter
+    keep = np.ones(len(op.slots), bool)
+    keep[[0, 2]] = False
+    oracle.reshape_and_cache(ref_k, ref_v, wl.cache_dtype, op.key[keep], op.value[keep],
+                             op.slots[keep], in_dtype=wl.dtype, k_scale=wl.k_scale,
+                             v_scale=wl.v_scale)
+    _pools_equal(cache, ref_k, ref_v, wl.cache_dtype)
+
+
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16], ids=["f16", "bf16"])
 @pytest.mark.parametrize("d,B", [(64, 8), (128, 16), (128, 32), (64, 16)])
 def test_large_scatter_matches_oracle(dtype, d, B):
