@@ -227,6 +227,32 @@ def test_negative_slots_are_skipped_and_copy_blocks_copies():
     _pools_equal(cache, k_ref, v_ref, wl.cache_dtype)
 
 
+def test_gather_skips_out_of_range_table_entries():
+    # Table entries outside the pool leave their rows of the gathered output
+    # unwritten; every other row is the oracle's gather, bit for bit.
+    wl = W.make_decode("gather_oob", 31, lambda rng: [20, 40, 33], Hq=2, Hkv=2, d=64, B=16,
+                       dtype=W.F16, max_context_len=48)
+    k_ref, v_ref = fill_pools(wl)
+    dw = DeviceWorkload(wl)
+    cache = new_cache(wl)
+    dw.run(cache)
+    ctx = wl.context_lens
+    cu = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)
+    bt = dw.block_tables.clone()
+    bt[1, 1], bt[2, 0] = wl.num_blocks + 3, -2
+    k, v = pkv.gather_kv(cache, bt, dw.context_lens, torch.from_numpy(cu).cuda(), int(cu[-1]),
+                         wl.max_context_len)
+    torch.cuda.synchronize()
+    ref_k, ref_v = oracle.gather_kv(k_ref, v_ref, wl.cache_dtype, wl.block_tables, wl.context_lens)
+    skipped = np.zeros(int(cu[-1]), bool)
+    skipped[cu[1] + 16:cu[1] + 32] = True              # sequence 1, block 1
+    skipped[cu[2]:cu[2] + 16] = True                   # sequence 2, block 0
+    for got, want in ((k, ref_k), (v, ref_v)):
+        g = bits_of(got).view(np.uint16)
+        w = want.view(np.uint16)
+        assert np.array_equal(g[~skipped], w[~skipped])
+
+
 @pytest.mark.parametrize("kv", ["model", "fp8"])
 def test_out_of_range_slots_and_block_pairs_are_skipped(kv):
     # Slots at or past num_blocks * B and block pairs naming a block outside
