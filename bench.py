@@ -518,11 +518,18 @@ def run_config(torch, pkv, name, args, cpu_budget, read_probe, fused=False, kv_c
                          "avg_launch_us": round(attn_avg * 1e3, 2)},
         })
         if read_probe:
-            gp = gemm_probe_tflops(torch)
-            res["roofline"]["gemm_probe_TFLOPs"] = round(gp, 1)
-            res["roofline"]["frac_of_gemm_probe"] = round(tf_attn / gp, 4)
-            log(f"[bench] dense bf16 product probe: {gp:.0f} TFLOP/s (prefill call at "
-                f"{100 * tf_attn / gp:.1f}% of it)")
+            # A calibration beside the measurement: if the library product fails,
+            # the line is still reported, with the probe's fields null.
+            try:
+                gp = gemm_probe_tflops(torch)
+            except RuntimeError as e:
+                log(f"[bench] dense bf16 product probe failed: {e}")
+                gp = None
+            res["roofline"]["gemm_probe_TFLOPs"] = None if gp is None else round(gp, 1)
+            res["roofline"]["frac_of_gemm_probe"] = None if gp is None else round(tf_attn / gp, 4)
+            if gp is not None:
+                log(f"[bench] dense bf16 product probe: {gp:.0f} TFLOP/s (prefill call at "
+                    f"{100 * tf_attn / gp:.1f}% of it)")
         res["metric"] = "chunked prefill attention TFLOP/s (% of MFMA peak)"
     res["config"] = {"workload": desc, "seqs": wl.S, "q_heads": wl.num_q_heads,
                      "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
